@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Throughput of block-sparse attention on one MI355X.
+
+Prints one JSON line.  The step is one fused prefill (block means of Q and
+K, block scores, top-k selection, sparse attention) over inputs already
+resident in device memory; `value` is prefill tokens/s.  `roofline` prices
+the sparse-attention kernel (where nearly all the time goes) against the
+bf16 MFMA peak using its algorithmic FLOPs (4*b*b*d per executed tile) over
+its average launch time from HIP events on the stream it runs on.  `decode`
+reports a single-token decode step of 32 sequences against the HBM peak.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+prefill workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn prefill tokens/s + % MFMA peak; decode tokens/s + % HBM BW"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "attn_fwd.hip")
+DECODE_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "decode.hip")
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel_src):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on a different kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("src_sha256_16") != src_hash(kernel_src):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_events(fn, n, stream):
+    import torch
+
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / n  # ms per launch
+
+
+def bench_prefill(args, dev, stream):
+    import torch
+
+    import dynamic_block_sparse_dsa_amd as dsa
+    from dynamic_block_sparse_dsa_amd import work
+    from dynamic_block_sparse_dsa_amd.inputs import WORKLOADS, make_prefill
+
+    w = WORKLOADS[args.workload]
+    q, k, v = make_prefill(w, device=dev)
+    B, Hq, Hkv, N, d, nB = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_blocks
+    shape = dsa.make_shape(B, Hq, Hkv, N, d, w.block, w.topk, w.topk_num, w.topk_den)
+    km = dsa.dsa_prefill_kmax(shape)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, nB, km), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hkv, nB), dtype=torch.int32, device=dev)
+    ws = torch.empty(dsa.dsa_prefill_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        dsa.dsa_prefill(shape, q, k, v, o, lse, idx, cnt, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # the dominant kernel alone, same inputs and indices, HIP events on its stream
+    def attn():
+        dsa.dsa_sparse_attn_fwd(shape, q, k, v, idx, cnt, o, lse, stream=stream)
+
+    for _ in range(args.warmup):
+        attn()
+    ms_attn = time_events(attn, args.steps, stream)
+    flops = work.prefill_flops(cnt.cpu().numpy(), w.group, w.block, d)
+    tflops = flops / (ms_attn * 1e-3) / 1e12
+    tiles = work.prefill_tiles(cnt.cpu().numpy(), w.group)
+    traffic = measured_traffic(w.name, ATTN_SRC)
+    res = dict(
+        ms_per_step=ms_step,
+        value=B * N / (ms_step * 1e-3),
+        config=dict(workload=w.name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, seq_len=N, head_dim=d, block=w.block,
+                    topk=w.topk, topk_num=w.topk_num, topk_den=w.topk_den, structure=w.structure),
+        roofline=dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                      frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel="sparse_attn_fwd_kernel",
+                      avg_launch_us=round(ms_attn * 1e3, 2), flops_per_launch=flops, executed_tiles=tiles,
+                      step_frac=round(flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)),
+    )
+    return res, (q, k, v, w)
+
+
+def bench_decode(args, dev, stream):
+    import torch
+
+    import dynamic_block_sparse_dsa_amd as dsa
+    from dynamic_block_sparse_dsa_amd import work
+    from dynamic_block_sparse_dsa_amd.inputs import WORKLOADS, make_decode
+
+    w = WORKLOADS[args.decode_workload]
+    q, kc, vc = make_decode(w, device=dev)
+    S, Hq, Hkv, L, d, nB = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_blocks
+    shape = dsa.make_shape(S, Hq, Hkv, L, d, w.block, w.topk, w.topk_num, w.topk_den)
+    km = dsa.dsa_decode_kmax(shape)
+    kbar = torch.empty((S, Hkv, nB, d), dtype=torch.float32, device=dev)
+    dsa.dsa_kv_block_means(shape, kc, kbar, stream=stream)  # cache-time work, outside the step
+    o = torch.empty_like(q)
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=dev)
+    idx = torch.empty((S, Hkv, km), dtype=torch.int32, device=dev)
+    ws = torch.empty(dsa.dsa_decode_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # larger than the 256 MiB last-level cache
+    torch.cuda.synchronize()
+
+    def step():
+        dsa.dsa_decode(shape, q, kc, vc, kbar, o, lse, idx, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    # each step timed alone with events, the cache flushed in between
+    tot = 0.0
+    for _ in range(args.steps):
+        with torch.cuda.stream(stream):
+            flush.zero_()
+        tot += time_events(step, 1, stream)
+    ms = tot / args.steps
+    nbytes = work.decode_bytes(S, Hq, Hkv, L, d, w.block, km)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(
+        value=S / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
+        config=dict(workload=w.name, sequences=S, n_q_heads=Hq, n_kv_heads=Hkv, cache_len=L, head_dim=d,
+                    block=w.block, topk=w.topk),
+        roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=round(gbs / PEAK_HBM_GBS, 4), traffic=measured_traffic(w.name, DECODE_SRC),
+                      kernel="decode step (4 launches)", bytes_per_step=nbytes),
+    )
+
+
+def cpu_baseline(args, inputs):
+    """The oracle, as it stands, on whole heads of the prefill workload until
+    about --cpu-seconds have passed; scaled to tokens/s of the full problem."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    q, k, v, w = inputs
+    G = w.group
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for g in range(w.n_kv_heads):
+            qn = q[:, g * G : (g + 1) * G].float().cpu().numpy().astype(np.float64)
+            kn = k[:, g : g + 1].float().cpu().numpy().astype(np.float64)
+            vn = v[:, g : g + 1].float().cpu().numpy().astype(np.float64)
+            O.prefill(qn, kn, vn, w.block, w.topk, w.topk_num, w.topk_den)
+            done += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+    el = time.perf_counter() - t0
+    frac = done / w.n_kv_heads
+    return dict(value=w.batch * w.seq_len * frac / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{done} of {w.n_kv_heads} KV-head groups of {w.name} (all {w.seq_len} rows each: pool, "
+                       f"score, select, attend), {el:.1f} s, 1 thread")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_n8192_h32")
+    ap.add_argument("--decode-workload", default="decode_s32_l65536")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}); the library has no multi-GPU path",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import dynamic_block_sparse_dsa_amd as dsa
+
+    dsa.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    pre, inputs = bench_prefill(args, dev, stream)
+    out = {
+        "metric": METRIC,
+        "value": round(pre["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": pre["config"],
+        "roofline": pre["roofline"],
+    }
+    if not args.no_decode:
+        out["decode"] = bench_decode(args, dev, stream)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, inputs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,285 @@
+"""Python binding of libdsa: content-aware dynamic block-sparse causal attention
+on AMD MI355X (gfx950).
+
+The functions named ``dsa_*`` mirror the C ABI in ``include/dsa.h`` one to one:
+they check that the torch tensors match the shape (dtype, device, size,
+contiguity -- the C side cannot see tensor sizes), pass raw device pointers
+and the current HIP stream, and raise ``DsaError`` on a non-zero status.
+Every step of the computation runs in the HIP library; there is no fallback.
+``prefill`` and ``decode`` are conveniences that allocate the outputs and
+the workspace with torch and call the fused entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import functools
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+FORCE_SINK = 1
+FORCE_DIAG = 2
+MAX_BLOCKS = 4096
+
+DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4, -5
+
+EXPORTS = [
+    "dsa_prefill_kmax",
+    "dsa_decode_kmax",
+    "dsa_block_means",
+    "dsa_block_scores",
+    "dsa_select_topk",
+    "dsa_sparse_attn_fwd",
+    "dsa_prefill_workspace_bytes",
+    "dsa_prefill",
+    "dsa_kv_block_means",
+    "dsa_decode_workspace_bytes",
+    "dsa_decode",
+    "dsa_status_str",
+    "dsa_last_error",
+]
+
+
+class Shape(ctypes.Structure):
+    """Mirror of ``dsa_shape``."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("topk_num", ctypes.c_int32),
+        ("topk_den", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+    @property
+    def n_blocks(self) -> int:
+        return -(-self.seq_len // self.block)
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, seq_len, head_dim, block, topk=0, topk_num=0, topk_den=1,
+               flags=FORCE_SINK | FORCE_DIAG) -> Shape:
+    return Shape(batch, n_q_heads, n_kv_heads, seq_len, head_dim, block, topk, topk_num, topk_den, flags)
+
+
+class DsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libdsa status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libdsa.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m dynamic_block_sparse_dsa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, S, I32, SZ = ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "dsa_prefill_kmax": ([S, ctypes.POINTER(I32)], ctypes.c_int),
+        "dsa_decode_kmax": ([S, ctypes.POINTER(I32)], ctypes.c_int),
+        "dsa_block_means": ([S, I32, P, P, P], ctypes.c_int),
+        "dsa_block_scores": ([S, P, P, P, P], ctypes.c_int),
+        "dsa_select_topk": ([S, P, P, P, P], ctypes.c_int),
+        "dsa_sparse_attn_fwd": ([S, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "dsa_prefill_workspace_bytes": ([S], SZ),
+        "dsa_prefill": ([S, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "dsa_kv_block_means": ([S, P, P, P], ctypes.c_int),
+        "dsa_decode_workspace_bytes": ([S], SZ),
+        "dsa_decode": ([S, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "dsa_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        "dsa_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != DSA_OK:
+        lib = load()
+        raise DsaError(rc, f"{lib.dsa_status_str(rc).decode()}: {lib.dsa_last_error().decode()}")
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(stream)
+
+
+def _ptr(t, dtype, shape, name, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ws(ws, need):
+    if need == 0:
+        return None, 0
+    if ws is None or ws.device.type != "cuda" or not ws.is_contiguous() or ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace must be a contiguous device tensor of at least {need} bytes")
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def _key(shape: Shape):
+    return tuple(getattr(shape, f) for f, _ in Shape._fields_)
+
+
+# host-side queries depend only on the shape: cache them per shape
+@functools.lru_cache(maxsize=256)
+def _query(name: str, key):
+    s = Shape(*key)
+    lib = load()
+    if name.endswith("kmax"):
+        out = ctypes.c_int32(0)
+        _check(getattr(lib, name)(ctypes.byref(s), ctypes.byref(out)))
+        return out.value
+    return int(getattr(lib, name)(ctypes.byref(s)))
+
+
+# ----------------------------------------------------------------- C ABI mirrors
+def dsa_prefill_kmax(shape: Shape) -> int:
+    return _query("dsa_prefill_kmax", _key(shape))
+
+
+def dsa_decode_kmax(shape: Shape) -> int:
+    return _query("dsa_decode_kmax", _key(shape))
+
+
+def dsa_block_means(shape: Shape, n_heads: int, x, xbar, stream=None):
+    B, N, d, nB = shape.batch, shape.seq_len, shape.head_dim, shape.n_blocks
+    _check(load().dsa_block_means(ctypes.byref(shape), n_heads, _ptr(x, torch.bfloat16, (B, n_heads, N, d), "x"),
+                                  _ptr(xbar, torch.float32, (B, n_heads, nB, d), "xbar"), _stream(stream)))
+
+
+def dsa_block_scores(shape: Shape, qbar, kbar, scores, stream=None):
+    B, Hq, Hkv, d, nB = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_blocks
+    _check(load().dsa_block_scores(ctypes.byref(shape), _ptr(qbar, torch.float32, (B, Hq, nB, d), "qbar"),
+                                   _ptr(kbar, torch.float32, (B, Hkv, nB, d), "kbar"),
+                                   _ptr(scores, torch.float32, (B, Hkv, nB, nB), "scores"), _stream(stream)))
+
+
+def dsa_select_topk(shape: Shape, scores, idx, cnt, stream=None):
+    B, Hkv, nB = shape.batch, shape.n_kv_heads, shape.n_blocks
+    km = dsa_prefill_kmax(shape)
+    _check(load().dsa_select_topk(ctypes.byref(shape), _ptr(scores, torch.float32, (B, Hkv, nB, nB), "scores"),
+                                  _ptr(idx, torch.int32, (B, Hkv, nB, km), "idx"),
+                                  _ptr(cnt, torch.int32, (B, Hkv, nB), "cnt"), _stream(stream)))
+
+
+def dsa_sparse_attn_fwd(shape: Shape, q, k, v, idx, cnt, o, lse=None, stream=None):
+    B, Hq, Hkv, N, d, nB = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_len, shape.head_dim, shape.n_blocks
+    km = dsa_prefill_kmax(shape)
+    _check(load().dsa_sparse_attn_fwd(
+        ctypes.byref(shape), _ptr(q, torch.bfloat16, (B, Hq, N, d), "q"), _ptr(k, torch.bfloat16, (B, Hkv, N, d), "k"),
+        _ptr(v, torch.bfloat16, (B, Hkv, N, d), "v"), _ptr(idx, torch.int32, (B, Hkv, nB, km), "idx"),
+        _ptr(cnt, torch.int32, (B, Hkv, nB), "cnt"), _ptr(o, torch.bfloat16, (B, Hq, N, d), "o"),
+        _ptr(lse, torch.float32, (B, Hq, N), "lse", optional=True), _stream(stream)))
+
+
+def dsa_prefill_workspace_bytes(shape: Shape) -> int:
+    return _query("dsa_prefill_workspace_bytes", _key(shape))
+
+
+def dsa_prefill(shape: Shape, q, k, v, o, lse, idx, cnt, ws, stream=None):
+    B, Hq, Hkv, N, d, nB = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_len, shape.head_dim, shape.n_blocks
+    km = dsa_prefill_kmax(shape)
+    wp, wb = _ws(ws, dsa_prefill_workspace_bytes(shape))
+    _check(load().dsa_prefill(
+        ctypes.byref(shape), _ptr(q, torch.bfloat16, (B, Hq, N, d), "q"), _ptr(k, torch.bfloat16, (B, Hkv, N, d), "k"),
+        _ptr(v, torch.bfloat16, (B, Hkv, N, d), "v"), _ptr(o, torch.bfloat16, (B, Hq, N, d), "o"),
+        _ptr(lse, torch.float32, (B, Hq, N), "lse", optional=True), _ptr(idx, torch.int32, (B, Hkv, nB, km), "idx"),
+        _ptr(cnt, torch.int32, (B, Hkv, nB), "cnt"), wp, wb, _stream(stream)))
+
+
+def dsa_kv_block_means(shape: Shape, k_cache, kbar, stream=None):
+    S, Hkv, L, d, nB = shape.batch, shape.n_kv_heads, shape.seq_len, shape.head_dim, shape.n_blocks
+    _check(load().dsa_kv_block_means(ctypes.byref(shape), _ptr(k_cache, torch.bfloat16, (S, Hkv, L, d), "k_cache"),
+                                     _ptr(kbar, torch.float32, (S, Hkv, nB, d), "kbar"), _stream(stream)))
+
+
+def dsa_decode_workspace_bytes(shape: Shape) -> int:
+    return _query("dsa_decode_workspace_bytes", _key(shape))
+
+
+def dsa_decode(shape: Shape, q, k_cache, v_cache, kbar, o, lse, idx, ws, stream=None):
+    S, Hq, Hkv, L, d, nB = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_len, shape.head_dim, shape.n_blocks
+    km = dsa_decode_kmax(shape)
+    wp, wb = _ws(ws, dsa_decode_workspace_bytes(shape))
+    _check(load().dsa_decode(
+        ctypes.byref(shape), _ptr(q, torch.bfloat16, (S, Hq, d), "q"),
+        _ptr(k_cache, torch.bfloat16, (S, Hkv, L, d), "k_cache"),
+        _ptr(v_cache, torch.bfloat16, (S, Hkv, L, d), "v_cache"), _ptr(kbar, torch.float32, (S, Hkv, nB, d), "kbar"),
+        _ptr(o, torch.bfloat16, (S, Hq, d), "o"), _ptr(lse, torch.float32, (S, Hq), "lse", optional=True),
+        _ptr(idx, torch.int32, (S, Hkv, km), "idx"), wp, wb, _stream(stream)))
+
+
+# ----------------------------------------------------------------- conveniences
+def prefill(q, k, v, block: int, topk: int = 0, topk_num: int = 0, topk_den: int = 1,
+            flags: int = FORCE_SINK | FORCE_DIAG, want_lse: bool = True, stream=None):
+    """Fused prefill; allocates O, LSE, idx, cnt and the workspace."""
+    B, Hq, N, d = q.shape
+    shape = make_shape(B, Hq, k.shape[1], N, d, block, topk, topk_num, topk_den, flags)
+    km = dsa_prefill_kmax(shape)
+    dev = q.device
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if want_lse else None
+    idx = torch.empty((B, k.shape[1], shape.n_blocks, km), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, k.shape[1], shape.n_blocks), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, dsa_prefill_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
+    dsa_prefill(shape, q, k, v, o, lse, idx, cnt, ws, stream)
+    return o, lse, idx, cnt
+
+
+def decode(q, k_cache, v_cache, kbar, block: int, topk: int = 0, topk_num: int = 0, topk_den: int = 1,
+           flags: int = FORCE_SINK | FORCE_DIAG, want_lse: bool = True, stream=None):
+    """One decode step; allocates o, lse, idx and the workspace."""
+    S, Hq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    shape = make_shape(S, Hq, Hkv, L, d, block, topk, topk_num, topk_den, flags)
+    km = dsa_decode_kmax(shape)
+    dev = q.device
+    o = torch.empty_like(q)
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=dev) if want_lse else None
+    idx = torch.empty((S, Hkv, km), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, dsa_decode_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
+    dsa_decode(shape, q, k_cache, v_cache, kbar, o, lse, idx, ws, stream)
+    return o, lse, idx
+
+
+def kv_block_means(k_cache, block: int, stream=None):
+    S, Hkv, L, d = k_cache.shape
+    shape = make_shape(S, Hkv, Hkv, L, d, block, 1)
+    kbar = torch.empty((S, Hkv, shape.n_blocks, d), dtype=torch.float32, device=k_cache.device)
+    dsa_kv_block_means(shape, k_cache, kbar, stream)
+    return kbar

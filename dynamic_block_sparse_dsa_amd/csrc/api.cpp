@@ -1,0 +1,286 @@
+// libdsa C ABI: argument validation, workspace layout and kernel dispatch.
+// Every check runs on the host before anything is enqueued, so a rejected
+// call has no side effect on the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "dsa.h"
+#include "dsa_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t n_blocks(const dsa_shape* s) { return ((int64_t)s->seq_len + s->block - 1) / s->block; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// common shape checks; decode adds its own
+int check_shape(const dsa_shape* s) {
+  if (!s) return fail(DSA_ERR_NULL, "shape is NULL");
+  if (s->batch < 0) return fail(DSA_ERR_SHAPE, "batch %d < 0", s->batch);
+  if (s->seq_len < 0) return fail(DSA_ERR_SHAPE, "seq_len %d < 0", s->seq_len);
+  if (s->n_q_heads < 1 || s->n_kv_heads < 1)
+    return fail(DSA_ERR_SHAPE, "head counts must be >= 1 (Hq %d, Hkv %d)", s->n_q_heads, s->n_kv_heads);
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(DSA_ERR_SHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d", s->n_q_heads, s->n_kv_heads);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", s->head_dim);
+  if (s->block != 64 && s->block != 128) return fail(DSA_ERR_UNSUPPORTED, "block %d (built: 64, 128)", s->block);
+  if (s->topk < 0) return fail(DSA_ERR_SHAPE, "topk %d < 0", s->topk);
+  if (s->flags & ~(DSA_FORCE_SINK | DSA_FORCE_DIAG)) return fail(DSA_ERR_SHAPE, "unknown flags 0x%x", s->flags);
+  if (s->topk == 0) {
+    if (s->topk_den < 1) return fail(DSA_ERR_SHAPE, "topk_den %d < 1", s->topk_den);
+    if (s->topk_num < 0) return fail(DSA_ERR_SHAPE, "topk_num %d < 0", s->topk_num);
+    if (s->topk_num == 0 && s->flags == 0) return fail(DSA_ERR_SHAPE, "topk, topk_num and flags are all 0: no block kept");
+  }
+  if (n_blocks(s) > DSA_MAX_BLOCKS)
+    return fail(DSA_ERR_UNSUPPORTED, "%lld blocks > %d", (long long)n_blocks(s), DSA_MAX_BLOCKS);
+  // grid sizes must fit the 32-bit launch dimensions
+  const int64_t units = (int64_t)s->batch * std::max(s->n_q_heads, s->n_kv_heads);
+  if (units * n_blocks(s) >= (1ll << 31)) return fail(DSA_ERR_UNSUPPORTED, "problem too large for one launch");
+  return DSA_OK;
+}
+
+int check_decode(const dsa_shape* s) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (s->batch > 0 && s->seq_len < 1) return fail(DSA_ERR_SHAPE, "decode needs a cache of at least 1 position");
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(DSA_ERR_UNSUPPORTED, "decode group size %d (built: 1, 2, 4, 8)", G);
+  return DSA_OK;
+}
+
+int row_budget(const dsa_shape* s, int visible) {
+  int nf = 0;
+  if (s->flags & DSA_FORCE_SINK) nf++;
+  if ((s->flags & DSA_FORCE_DIAG) && !((s->flags & DSA_FORCE_SINK) && visible == 1)) nf++;
+  int64_t k = s->topk > 0 ? s->topk : ((int64_t)s->topk_num * visible + s->topk_den - 1) / s->topk_den;
+  k = std::max<int64_t>(k, nf);
+  k = std::min<int64_t>(k, visible);
+  return (int)k;
+}
+
+int prefill_kmax(const dsa_shape* s) {
+  int best = 0;
+  for (int i = 0; i < n_blocks(s); ++i) best = std::max(best, row_budget(s, i + 1));
+  return best;
+}
+
+dsa::TopkParams topk_params(const dsa_shape* s) { return dsa::TopkParams{s->topk, s->topk_num, s->topk_den, s->flags}; }
+
+bool empty_prefill(const dsa_shape* s) { return s->batch == 0 || s->seq_len == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_str(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "null pointer";
+    case DSA_ERR_SHAPE: return "invalid shape";
+    case DSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+int dsa_prefill_kmax(const dsa_shape* s, int32_t* kmax) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!kmax) return fail(DSA_ERR_NULL, "kmax is NULL");
+  *kmax = prefill_kmax(s);
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_decode_kmax(const dsa_shape* s, int32_t* kmax) {
+  int rc = check_decode(s);
+  if (rc) return rc;
+  if (!kmax) return fail(DSA_ERR_NULL, "kmax is NULL");
+  *kmax = s->seq_len > 0 ? row_budget(s, (int)n_blocks(s)) : 0;
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_block_means(const dsa_shape* s, int32_t n_heads, const void* x, float* xbar, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (n_heads < 1) return fail(DSA_ERR_SHAPE, "n_heads %d < 1", n_heads);
+  if (empty_prefill(s)) return DSA_OK;
+  if (!x || !xbar) return fail(DSA_ERR_NULL, "x or xbar is NULL");
+  hipError_t e = dsa::launch_block_means(static_cast<const uint16_t*>(x), xbar, (int64_t)s->batch * n_heads,
+                                         s->seq_len, s->head_dim, s->block, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block_means launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_kv_block_means(const dsa_shape* s, const void* k_cache, float* kbar, void* stream) {
+  int rc = check_decode(s);
+  if (rc) return rc;
+  return dsa_block_means(s, s->n_kv_heads, k_cache, kbar, stream);
+}
+
+int dsa_block_scores(const dsa_shape* s, const float* qbar, const float* kbar, float* scores, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (empty_prefill(s)) return DSA_OK;
+  if (!qbar || !kbar || !scores) return fail(DSA_ERR_NULL, "qbar, kbar or scores is NULL");
+  hipError_t e = dsa::launch_block_scores(qbar, kbar, scores, s->batch, s->n_q_heads, s->n_kv_heads, (int)n_blocks(s),
+                                          s->head_dim, 1.0f / sqrtf((float)s->head_dim),
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block_scores launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_select_topk(const dsa_shape* s, const float* scores, int32_t* idx, int32_t* cnt, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (empty_prefill(s)) return DSA_OK;
+  if (!scores || !idx || !cnt) return fail(DSA_ERR_NULL, "scores, idx or cnt is NULL");
+  const int nB = (int)n_blocks(s);
+  hipError_t e = dsa::launch_select_topk(scores, idx, cnt, (int64_t)s->batch * s->n_kv_heads * nB, nB, nB, true,
+                                         topk_params(s), prefill_kmax(s), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "select_topk launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_sparse_attn_fwd(const dsa_shape* s, const void* q, const void* k, const void* v, const int32_t* idx,
+                        const int32_t* cnt, void* o, float* lse, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (empty_prefill(s)) return DSA_OK;
+  if (!q || !k || !v || !idx || !cnt || !o) return fail(DSA_ERR_NULL, "q, k, v, idx, cnt or o is NULL");
+  dsa::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.idx = idx;
+  a.cnt = cnt;
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.B = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.N = s->seq_len;
+  a.nB = (int)n_blocks(s);
+  a.kmax = prefill_kmax(s);
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
+  hipError_t e = dsa::launch_sparse_attn_fwd(a, s->head_dim, s->block, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparse_attn_fwd launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+size_t dsa_prefill_workspace_bytes(const dsa_shape* s) {
+  if (check_shape(s)) return 0;
+  const size_t nB = (size_t)n_blocks(s), d = (size_t)s->head_dim, B = (size_t)s->batch;
+  return align256(B * s->n_q_heads * nB * d * 4) + align256(B * s->n_kv_heads * nB * d * 4) +
+         align256(B * s->n_kv_heads * nB * nB * 4);
+}
+
+int dsa_prefill(const dsa_shape* s, const void* q, const void* k, const void* v, void* o, float* lse, int32_t* idx,
+                int32_t* cnt, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (empty_prefill(s)) return DSA_OK;
+  if (!q || !k || !v || !o || !idx || !cnt) return fail(DSA_ERR_NULL, "q, k, v, o, idx or cnt is NULL");
+  const size_t need = dsa_prefill_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
+  const size_t nB = (size_t)n_blocks(s), d = (size_t)s->head_dim, B = (size_t)s->batch;
+  char* p = static_cast<char*>(ws);
+  float* qbar = reinterpret_cast<float*>(p);
+  p += align256(B * s->n_q_heads * nB * d * 4);
+  float* kbar = reinterpret_cast<float*>(p);
+  p += align256(B * s->n_kv_heads * nB * d * 4);
+  float* scores = reinterpret_cast<float*>(p);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = dsa::launch_block_means(static_cast<const uint16_t*>(q), qbar, (int64_t)B * s->n_q_heads, s->seq_len,
+                                         s->head_dim, s->block, st);
+  if (e != hipSuccess) return hip_fail(e, "block_means(q) launch");
+  e = dsa::launch_block_means(static_cast<const uint16_t*>(k), kbar, (int64_t)B * s->n_kv_heads, s->seq_len,
+                              s->head_dim, s->block, st);
+  if (e != hipSuccess) return hip_fail(e, "block_means(k) launch");
+  rc = dsa_block_scores(s, qbar, kbar, scores, stream);
+  if (rc) return rc;
+  rc = dsa_select_topk(s, scores, idx, cnt, stream);
+  if (rc) return rc;
+  return dsa_sparse_attn_fwd(s, q, k, v, idx, cnt, o, lse, stream);
+}
+
+size_t dsa_decode_workspace_bytes(const dsa_shape* s) {
+  if (check_decode(s)) return 0;
+  const size_t nB = (size_t)n_blocks(s), d = (size_t)s->head_dim;
+  const size_t units = (size_t)s->batch * s->n_kv_heads;
+  const int kmax = s->seq_len > 0 ? row_budget(s, (int)nB) : 0;
+  const size_t G = (size_t)(s->n_q_heads / s->n_kv_heads);
+  const size_t nsplit = (size_t)dsa::decode_splits(s->batch, s->n_kv_heads, kmax);
+  return align256(units * nB * 4) + align256(units * nsplit * G * (d + 2) * 4);
+}
+
+int dsa_decode(const dsa_shape* s, const void* q, const void* k_cache, const void* v_cache, const float* kbar,
+               void* o, float* lse, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_decode(s);
+  if (rc) return rc;
+  if (s->batch == 0) return DSA_OK;
+  if (!q || !k_cache || !v_cache || !kbar || !o || !idx)
+    return fail(DSA_ERR_NULL, "q, k_cache, v_cache, kbar, o or idx is NULL");
+  const size_t need = dsa_decode_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
+  const int nB = (int)n_blocks(s);
+  const int kmax = row_budget(s, nB);
+  dsa::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(k_cache);
+  a.vc = static_cast<const uint16_t*>(v_cache);
+  a.kbar = kbar;
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.idx = idx;
+  a.S = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.L = s->seq_len;
+  a.nB = nB;
+  a.kmax = kmax;
+  a.nsplit = dsa::decode_splits(s->batch, s->n_kv_heads, kmax);
+  a.block = s->block;
+  a.scale = 1.0f / sqrtf((float)s->head_dim);
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
+  char* p = static_cast<char*>(ws);
+  a.scores = reinterpret_cast<float*>(p);
+  p += align256((size_t)s->batch * s->n_kv_heads * nB * 4);
+  a.partial = reinterpret_cast<float*>(p);
+  hipError_t e = dsa::launch_decode(a, s->head_dim, topk_params(s), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Internal declarations shared by the libdsa HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// ---------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 <-> fp32.  bf16 is the top half of an fp32, so widening is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 with round-to-nearest-even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Order-preserving map of a finite fp32 onto uint32 (larger float -> larger
+// key).  -0.0 is folded onto +0.0 first so equal values get equal keys.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- XCD-aware ids
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X (id w
+// goes to XCD w % 8).  This bijection gives each XCD a contiguous range of
+// logical ids, so neighbouring logical work (the query blocks of one head,
+// which read the same K/V tiles) shares that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t w, uint32_t total) {
+  const uint32_t xcd = w & 7u, local = w >> 3;
+  const uint32_t base = total >> 3, extra = total & 7u;
+  return xcd * base + (xcd < extra ? xcd : extra) + local;
+}
+
+// ---------------------------------------------------------------- launchers
+// Every launcher enqueues on `stream` and returns hipSuccess or the launch
+// error.  Sizes are validated by the caller (api.cpp).
+
+// x [n_units, N, d] bf16 -> xbar [n_units, nB, d] fp32 (mean per block)
+hipError_t launch_block_means(const uint16_t* x, float* xbar, int64_t n_units, int N, int d, int block,
+                              hipStream_t stream);
+
+// qbar [B, Hq, nB, d], kbar [B, Hkv, nB, d] -> scores [B, Hkv, nB, nB]
+hipError_t launch_block_scores(const float* qbar, const float* kbar, float* scores, int B, int Hq, int Hkv, int nB,
+                               int d, float scale, hipStream_t stream);
+
+struct TopkParams {
+  int topk, num, den;
+  uint32_t flags;
+};
+// rows of `scores` (stride n_cols).  causal: row r sees (r % rows_per_unit) + 1
+// blocks; otherwise every row sees n_cols.  idx [n_rows, kmax], cnt [n_rows]
+// (cnt may be NULL).
+hipError_t launch_select_topk(const float* scores, int32_t* idx, int32_t* cnt, int64_t n_rows, int rows_per_unit,
+                              int n_cols, bool causal, TopkParams p, int kmax, hipStream_t stream);
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  const int32_t* cnt;
+  uint16_t* o;
+  float* lse;
+  int B, Hq, Hkv, N, nB, kmax;
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+hipError_t launch_sparse_attn_fwd(const AttnArgs& a, int d, int block, hipStream_t stream);
+
+struct DecodeArgs {
+  const uint16_t* q;   // [S, Hq, d]
+  const uint16_t* kc;  // [S, Hkv, L, d]
+  const uint16_t* vc;
+  const float* kbar;   // [S, Hkv, nB, d]
+  uint16_t* o;         // [S, Hq, d]
+  float* lse;          // [S, Hq] or null
+  int32_t* idx;        // [S, Hkv, kmax]
+  float* scores;       // workspace [S, Hkv, nB]
+  float* partial;      // workspace [S, Hkv, nsplit, G, d + 2]
+  int S, Hq, Hkv, L, nB, kmax, nsplit, block;
+  float scale;       // 1 / sqrt(d)
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+hipError_t launch_decode(const DecodeArgs& a, int d, TopkParams p, hipStream_t stream);
+
+// number of key splits a decode step uses (also sizes its workspace)
+int decode_splits(int S, int Hkv, int kmax);
+
+}  // namespace dsa

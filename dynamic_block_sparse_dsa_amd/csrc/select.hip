@@ -1,0 +1,305 @@
+// Block selection kernels: block means, causal block scores, top-k select.
+//
+// Method sources (by page and section):
+//   "dynamic sparse attention explainer" (zblog.xzdbk.com/559.html):
+//     "基于Top-k选择的局部-全局混合" -- per query keep the k best-scoring keys,
+//     plus global and local anchors; "硬件友好的稀疏计算实现" -- decide per
+//     fixed-size block; "前沿方向" -- a GQA group shares its KV cache and so
+//     one selection.
+//   "稀疏注意力 vs Flash Attention v2" (pnsm.cn/news/1249548.html), section 1:
+//     content-aware top-k ranks keys by query-key similarity.
+//   DeepSeek NSA article (pnsm.cn/news/1939904.html), section 2.2: the
+//     routing decision is made in fp32.
+// The block statistic is mean(Q tile) . mean(K tile) / sqrt(d), so all three
+// kernels work in fp32 on the block means.
+#include "dsa_internal.hpp"
+
+namespace dsa {
+
+// ============================================================== block means
+// One workgroup per (unit, block): 256 threads read the block's rows as
+// 16-byte chunks (D/8 chunks per row, 256/(D/8) row groups), sum them in fp32,
+// reduce the row groups through LDS and divide by the number of real rows.
+template <int D>
+__global__ __launch_bounds__(256) void block_means_kernel(const uint16_t* __restrict__ x, float* __restrict__ xbar,
+                                                          int N, int block, int nB) {
+  constexpr int CH = D / 8;        // 16-byte chunks per row
+  constexpr int RG = 256 / CH;     // row groups
+  __shared__ float part[RG][D + 1];
+  const int64_t wg = blockIdx.x;
+  const int64_t unit = wg / nB;
+  const int j = (int)(wg % nB);
+  const int t = threadIdx.x, c = t % CH, rg = t / CH;
+  const int r0 = j * block;
+  const int rows = min(block, N - r0);
+  const uint16_t* base = x + (unit * N + r0) * (int64_t)D + c * 8;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = rg; r < rows; r += RG) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(base + (int64_t)r * D);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bf16_lo(w[e]);
+      acc[2 * e + 1] += bf16_hi(w[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg][c * 8 + e] = acc[e];
+  __syncthreads();
+  if (t < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) s += part[g][t];
+    xbar[(unit * nB + j) * (int64_t)D + t] = s / (float)rows;
+  }
+}
+
+hipError_t launch_block_means(const uint16_t* x, float* xbar, int64_t n_units, int N, int d, int block,
+                              hipStream_t stream) {
+  const int nB = (N + block - 1) / block;
+  const int64_t n_wg = n_units * nB;
+  if (n_wg == 0) return hipSuccess;
+  if (d == 64)
+    hipLaunchKernelGGL(block_means_kernel<64>, dim3((uint32_t)n_wg), dim3(256), 0, stream, x, xbar, N, block, nB);
+  else
+    hipLaunchKernelGGL(block_means_kernel<128>, dim3((uint32_t)n_wg), dim3(256), 0, stream, x, xbar, N, block, nB);
+  return hipGetLastError();
+}
+
+// ============================================================== block scores
+// One workgroup per 64x64 tile of the score matrix of one (batch, KV head).
+// Each thread owns a 4x4 set of entries (rows ty + 16a, cols tx + 16c), the
+// means are staged through LDS 32 dims at a time, every head of the group is
+// scored and the max is kept.  Tiles strictly above the diagonal are -inf.
+template <int D>
+__global__ __launch_bounds__(256) void block_scores_kernel(const float* __restrict__ qbar,
+                                                           const float* __restrict__ kbar, float* __restrict__ scores,
+                                                           int Hq, int Hkv, int nB, float scale, int n_tiles) {
+  __shared__ float qs[64][33];
+  __shared__ float ks[64][33];
+  const int per_unit = n_tiles * n_tiles;
+  const int64_t unit = blockIdx.x / per_unit;  // b * Hkv + g
+  const int tile = blockIdx.x % per_unit;
+  const int ti = tile / n_tiles, tj = tile % n_tiles;
+  const int t = threadIdx.x, tx = t % 16, ty = t / 16;
+  const int i0 = ti * 64, j0 = tj * 64;
+  float* out = scores + unit * (int64_t)nB * nB;
+  const float NEG_INF = -__builtin_inff();
+  if (tj > ti) {
+    for (int e = t; e < 64 * 64; e += 256) {
+      const int i = i0 + e / 64, j = j0 + e % 64;
+      if (i < nB && j < nB) out[(int64_t)i * nB + j] = NEG_INF;
+    }
+    return;
+  }
+  const int G = Hq / Hkv;
+  const int64_t b = unit / Hkv, g = unit % Hkv;
+  const float* kb = kbar + unit * (int64_t)nB * D;
+  float best[4][4];
+  for (int hh = 0; hh < G; ++hh) {
+    const float* qb = qbar + ((b * Hq) + g * G + hh) * (int64_t)nB * D;
+    float acc[4][4] = {};
+    for (int d0 = 0; d0 < D; d0 += 32) {
+      for (int e = t; e < 64 * 32; e += 256) {
+        const int r = e / 32, c = e % 32;
+        qs[r][c] = (i0 + r < nB) ? qb[(int64_t)(i0 + r) * D + d0 + c] : 0.f;
+        ks[r][c] = (j0 + r < nB) ? kb[(int64_t)(j0 + r) * D + d0 + c] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int dd = 0; dd < 32; ++dd) {
+        float a[4], bb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = qs[ty + 16 * r][dd];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bb[c] = ks[tx + 16 * c][dd];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(a[r], bb[c], acc[r][c]);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float sc = acc[r][c] * scale;
+        best[r][c] = (hh == 0) ? sc : fmaxf(best[r][c], sc);
+      }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = i0 + ty + 16 * r, j = j0 + tx + 16 * c;
+      if (i < nB && j < nB) out[(int64_t)i * nB + j] = (j <= i) ? best[r][c] : NEG_INF;
+    }
+}
+
+hipError_t launch_block_scores(const float* qbar, const float* kbar, float* scores, int B, int Hq, int Hkv, int nB,
+                               int d, float scale, hipStream_t stream) {
+  const int n_tiles = (nB + 63) / 64;
+  const int64_t n_wg = (int64_t)B * Hkv * n_tiles * n_tiles;
+  if (n_wg == 0) return hipSuccess;
+  if (d == 64)
+    hipLaunchKernelGGL(block_scores_kernel<64>, dim3((uint32_t)n_wg), dim3(256), 0, stream, qbar, kbar, scores, Hq,
+                       Hkv, nB, scale, n_tiles);
+  else
+    hipLaunchKernelGGL(block_scores_kernel<128>, dim3((uint32_t)n_wg), dim3(256), 0, stream, qbar, kbar, scores, Hq,
+                       Hkv, nB, scale, n_tiles);
+  return hipGetLastError();
+}
+
+// ============================================================== top-k select
+// One 256-thread workgroup per row.  The row's scores become order-preserving
+// uint32 keys; thread t owns the contiguous run of R = ceil(visible / 256)
+// blocks starting at t * R (index order), which makes the final compaction an
+// exclusive scan.  The m-th largest candidate key is found with a most-
+// significant-digit-first radix select (4 passes of 8 bits, LDS histograms);
+// the candidates above it are kept and, among the ones equal to it, the
+// lowest indices fill the remainder (ties go to the lower block).
+constexpr int TOPK_THREADS = 256;
+constexpr int TOPK_MAX_PER_THREAD = (4096 + TOPK_THREADS - 1) / TOPK_THREADS;  // DSA_MAX_BLOCKS
+
+// inclusive prefix sum over the 256 threads of the workgroup
+__device__ __forceinline__ int block_incl_scan(int v, int* sh_waves) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  if (lane == 63) sh_waves[wave] = v;
+  __syncthreads();
+  int add = 0;
+#pragma unroll
+  for (int w = 0; w < TOPK_THREADS / 64; ++w)
+    if (w < wave) add += sh_waves[w];
+  __syncthreads();
+  return v + add;
+}
+
+__global__ __launch_bounds__(TOPK_THREADS) void select_topk_kernel(const float* __restrict__ scores,
+                                                                   int32_t* __restrict__ idx,
+                                                                   int32_t* __restrict__ cnt, int rows_per_unit,
+                                                                   int n_cols, int causal, TopkParams p, int kmax) {
+  __shared__ int hist[256];
+  __shared__ int sh_waves[TOPK_THREADS / 64];
+  __shared__ int sh_digit, sh_rem;
+  const int64_t row = blockIdx.x;
+  const int i = (int)(row % rows_per_unit);
+  const int nv = causal ? i + 1 : n_cols;
+  const int t = threadIdx.x;
+  const int f_sink = (p.flags & 1u) ? 0 : -1;
+  const int f_diag = (p.flags & 2u) ? nv - 1 : -1;
+  const int nf = (f_sink >= 0) + (f_diag >= 0) - (f_sink >= 0 && f_sink == f_diag);
+  int64_t budget = p.topk > 0 ? (int64_t)p.topk : ((int64_t)p.num * nv + p.den - 1) / p.den;
+  if (budget < nf) budget = nf;
+  if (budget > nv) budget = nv;
+  const int m = (int)budget - nf;   // candidates to keep
+  const int ncand = nv - nf;
+  const float* srow = scores + row * (int64_t)n_cols;
+  const int R = (nv + TOPK_THREADS - 1) / TOPK_THREADS;
+  const int j0 = t * R;
+
+  uint32_t key[TOPK_MAX_PER_THREAD];
+  uint32_t candbits = 0;  // bit e: block j0 + e is a candidate
+#pragma unroll
+  for (int e = 0; e < TOPK_MAX_PER_THREAD; ++e) {
+    const int j = j0 + e;
+    key[e] = 0;
+    if (e < R && j < nv && j != f_sink && j != f_diag) {
+      key[e] = order_key(srow[j]);
+      candbits |= 1u << e;
+    }
+  }
+
+  // threshold key T and how many candidates equal to T are kept
+  uint32_t T = 0;
+  int take_eq = 0;
+  bool all = (m >= ncand), none = (m <= 0);
+  if (!all && !none) {
+    uint32_t prefix = 0, pmask = 0;
+    int remaining = m;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hist[t] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < TOPK_MAX_PER_THREAD; ++e)
+        if (((candbits >> e) & 1u) && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1);
+      __syncthreads();
+      // thread t looks at digit 255 - t; incl = candidates with digit >= it
+      const int dg = 255 - t;
+      const int v = hist[dg];
+      const int incl = block_incl_scan(v, sh_waves);
+      const int excl = incl - v;
+      if (excl < remaining && remaining <= incl) {
+        sh_digit = dg;
+        sh_rem = remaining - excl;
+      }
+      __syncthreads();
+      prefix |= (uint32_t)sh_digit << shift;
+      pmask |= 0xffu << shift;
+      remaining = sh_rem;
+      __syncthreads();
+    }
+    T = prefix;
+    take_eq = remaining;
+  }
+
+  // rank of each equal-to-T candidate among the equal ones, in index order
+  int my_eq = 0;
+  if (!all && !none) {
+#pragma unroll
+    for (int e = 0; e < TOPK_MAX_PER_THREAD; ++e) my_eq += ((candbits >> e) & 1u) && key[e] == T;
+  }
+  const int eq_before = block_incl_scan(my_eq, sh_waves) - my_eq;
+
+  uint32_t selbits = 0;
+  int running_eq = eq_before;
+#pragma unroll
+  for (int e = 0; e < TOPK_MAX_PER_THREAD; ++e) {
+    const int j = j0 + e;
+    if (e >= R || j >= nv) continue;
+    bool s;
+    if (j == f_sink || j == f_diag) {
+      s = true;
+    } else if (all) {
+      s = true;
+    } else if (none) {
+      s = false;
+    } else if (key[e] > T) {
+      s = true;
+    } else if (key[e] == T) {
+      s = running_eq < take_eq;
+      ++running_eq;
+    } else {
+      s = false;
+    }
+    selbits |= (uint32_t)s << e;
+  }
+  const int my_sel = __builtin_popcount(selbits);
+  const int incl = block_incl_scan(my_sel, sh_waves);
+  int pos = incl - my_sel;
+  int32_t* out = idx + row * (int64_t)kmax;
+#pragma unroll
+  for (int e = 0; e < TOPK_MAX_PER_THREAD; ++e)
+    if ((selbits >> e) & 1u) out[pos++] = j0 + e;
+  // total kept = inclusive count of the last thread
+  __shared__ int sh_total;
+  if (t == TOPK_THREADS - 1) sh_total = incl;
+  __syncthreads();
+  const int total = sh_total;
+  for (int e = total + t; e < kmax; e += TOPK_THREADS) out[e] = -1;
+  if (t == 0 && cnt) cnt[row] = total;
+}
+
+hipError_t launch_select_topk(const float* scores, int32_t* idx, int32_t* cnt, int64_t n_rows, int rows_per_unit,
+                              int n_cols, bool causal, TopkParams p, int kmax, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_topk_kernel, dim3((uint32_t)n_rows), dim3(TOPK_THREADS), 0, stream, scores, idx, cnt,
+                     rows_per_unit, n_cols, causal ? 1 : 0, p, kmax);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

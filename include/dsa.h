@@ -1,0 +1,167 @@
+/*
+ * libdsa -- content-aware dynamic block-sparse causal attention for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (sources are cited by page and section):
+ *   - "dynamic sparse attention explainer" (zblog.xzdbk.com/559.html),
+ *     section "基于Top-k选择的局部-全局混合": per query keep the k
+ *     highest-scoring keys and drop the rest, with global + local anchors;
+ *     sections "硬件友好的稀疏计算实现" and "工程实践建议": make that
+ *     decision per 64x64 or 128x128 block so the kept work stays dense;
+ *     section "动态开销与计算收益的权衡": precompute the index data at
+ *     cache time; section "前沿方向": GQA/MQA groups share one KV cache.
+ *   - "稀疏注意力 vs Flash Attention v2" (pnsm.cn/news/1249548.html),
+ *     section 1: content-aware top-k by query-key similarity, the
+ *     sparse_attention pseudo-code (softmax of masked logits / sqrt(d_k),
+ *     times V), and FlashAttention-2's tiling with an incremental softmax.
+ *   - DeepSeek NSA article (pnsm.cn/news/1939904.html), section 2.2:
+ *     routing scores in fp32, the weighted sum in bf16.
+ *
+ * One prefill call runs four steps:
+ *   1. block means of Q and K (fp32)                 dsa_block_means
+ *   2. block scores, causal, max over a GQA group     dsa_block_scores
+ *   3. top-k blocks per query block, sink and
+ *      diagonal forced                               dsa_select_topk
+ *   4. attention over the kept tiles                  dsa_sparse_attn_fwd
+ * dsa_prefill chains them; dsa_decode is the single-token variant.
+ *
+ * Conventions for every call below:
+ *   - All tensor pointers are DEVICE pointers, contiguous, row-major.  bf16
+ *     tensors are passed as their 16-bit storage (void*).
+ *   - Layouts: Q, O [B, Hq, N, d]; K, V [B, Hkv, N, d]; block means
+ *     [B, H, nB, d] fp32; scores [B, Hkv, nB, nB] fp32; idx [B, Hkv, nB, kmax]
+ *     int32; cnt [B, Hkv, nB] int32; LSE [B, Hq, N] fp32 (natural log).
+ *     nB = ceil(N / block); a ragged last block is allowed (its mean is over
+ *     the rows it has).  Query head h reads KV head h / (Hq / Hkv).
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     memory, keeps no state between calls and is re-entrant; scratch space
+ *     comes from the caller's workspace (sizes from *_workspace_bytes).
+ *   - Errors: every call returns DSA_OK (0) or a negative DSA_ERR_* code.
+ *     Argument errors are detected on the host before anything is enqueued;
+ *     launch errors are reported from the HIP runtime.  Work is enqueued
+ *     asynchronously on `stream` (a hipStream_t; NULL = the null stream) and
+ *     no call synchronises, so device faults surface at the caller's next
+ *     synchronisation.  dsa_last_error() gives the calling thread's message.
+ *   - Inputs are assumed finite.  An empty problem (B == 0 or N == 0 for
+ *     prefill, S == 0 for decode) returns DSA_OK and enqueues nothing.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = -1,        /* a required pointer is NULL */
+  DSA_ERR_SHAPE = -2,       /* sizes are inconsistent (e.g. Hq % Hkv != 0) */
+  DSA_ERR_UNSUPPORTED = -3, /* head_dim / block not built, too many blocks */
+  DSA_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required */
+  DSA_ERR_HIP = -5          /* the HIP runtime reported an error */
+};
+
+/* flags: which blocks every row keeps regardless of score */
+#define DSA_FORCE_SINK 1u /* block 0 */
+#define DSA_FORCE_DIAG 2u /* the row's own block: the diagonal block in prefill,
+                             the last cache block in decode */
+
+/* limits of the built kernels */
+#define DSA_MAX_BLOCKS 4096 /* nB = ceil(N / block) */
+
+typedef struct dsa_shape {
+  int32_t batch;      /* B (prefill) or number of sequences S (decode), >= 0 */
+  int32_t n_q_heads;  /* Hq >= 1 */
+  int32_t n_kv_heads; /* Hkv >= 1, Hq % Hkv == 0 (Hkv == Hq: one selection per head) */
+  int32_t seq_len;    /* prefill: N >= 0; decode: cache length L >= 1 (the new
+                         token is at position L - 1 and is already in the cache) */
+  int32_t head_dim;   /* d: 64 or 128 */
+  int32_t block;      /* b: 64 or 128 */
+  int32_t topk;       /* > 0: blocks kept per row, forced ones included;
+                         0: use the fraction below */
+  int32_t topk_num;   /* topk == 0: keep ceil(topk_num * visible / topk_den)  */
+  int32_t topk_den;   /*   blocks (integer arithmetic), num >= 0, den >= 1    */
+  uint32_t flags;     /* DSA_FORCE_SINK | DSA_FORCE_DIAG (or a subset) */
+} dsa_shape;
+
+/* A row that sees `visible` blocks keeps
+ *   min(max(k, |forced|), visible)  blocks, k = topk or the fraction above.
+ * Kept blocks are listed ascending; the rest of the row of idx is -1.
+ * Ties in score go to the lower block index. */
+
+/* Width of the prefill index array: the largest per-row budget.  Host only.
+ * Returns DSA_OK and writes *kmax, or an error code. */
+int dsa_prefill_kmax(const dsa_shape* shape, int32_t* kmax);
+
+/* Width of the decode index array [S, Hkv, kmax] (every row sees all nB
+ * blocks, so every row keeps exactly kmax).  Host only. */
+int dsa_decode_kmax(const dsa_shape* shape, int32_t* kmax);
+
+/* Step 1: block means.  x: [B, n_heads, N, d] bf16 -> xbar: [B, n_heads, nB, d]
+ * fp32 (N = shape->seq_len, B = shape->batch).  Used for Q (n_heads = Hq),
+ * for K (n_heads = Hkv), and for a decode key cache (see dsa_kv_block_means).
+ * fp32 because the selection is made from these values. */
+int dsa_block_means(const dsa_shape* shape, int32_t n_heads, const void* x, float* xbar, void* stream);
+
+/* Step 2: block scores.  scores[b, g, i, j] = max over the query heads h of
+ * group g of (1/sqrt(d)) * <qbar[b, h, i], kbar[b, g, j]> for j <= i, and
+ * -inf for j > i.  qbar [B, Hq, nB, d], kbar [B, Hkv, nB, d], fp32. */
+int dsa_block_scores(const dsa_shape* shape, const float* qbar, const float* kbar, float* scores, void* stream);
+
+/* Step 3: per-row selection from a score matrix [B, Hkv, nB, nB] (only
+ * j <= i is read).  Row i keeps the forced blocks {0, i} (per flags) plus
+ * the best-scoring other blocks up to its budget.  idx [B, Hkv, nB, kmax]
+ * with kmax from dsa_prefill_kmax; cnt [B, Hkv, nB]. */
+int dsa_select_topk(const dsa_shape* shape, const float* scores, int32_t* idx, int32_t* cnt, void* stream);
+
+/* Step 4: causal attention over the listed blocks.  Row p of query block i
+ * attends to the keys c <= p of the blocks idx[b, g, i, 0..cnt-1] (which
+ * must be ascending, distinct, in 0..i); logits are (1/sqrt(d)) q_p . k_c;
+ * P is rounded to bf16 for the P V product, accumulation is fp32.
+ * o: [B, Hq, N, d] bf16.  lse: [B, Hq, N] fp32 natural-log normaliser, or
+ * NULL to skip it. */
+int dsa_sparse_attn_fwd(const dsa_shape* shape, const void* q, const void* k, const void* v, const int32_t* idx,
+                        const int32_t* cnt, void* o, float* lse, void* stream);
+
+/* Workspace for dsa_prefill, in bytes (block means of Q and K + scores). */
+size_t dsa_prefill_workspace_bytes(const dsa_shape* shape);
+
+/* Steps 1-4 in one call.  idx, cnt: outputs as for dsa_select_topk.
+ * ws: device workspace of at least dsa_prefill_workspace_bytes(shape)
+ * bytes; after the call it holds Q means, K means, then the scores. */
+int dsa_prefill(const dsa_shape* shape, const void* q, const void* k, const void* v, void* o, float* lse,
+                int32_t* idx, int32_t* cnt, void* ws, size_t ws_bytes, void* stream);
+
+/* Cache-time block means of a decode key cache: k_cache [S, Hkv, L, d] bf16
+ * -> kbar [S, Hkv, nB, d] fp32 (the index data precomputed when the cache
+ * is written, so a decode step does not re-pool raw keys). */
+int dsa_kv_block_means(const dsa_shape* shape, const void* k_cache, float* kbar, void* stream);
+
+/* Workspace for dsa_decode, in bytes. */
+size_t dsa_decode_workspace_bytes(const dsa_shape* shape);
+
+/* One decode step for S sequences.  q: [S, Hq, d] bf16 (the new tokens, at
+ * cache position L - 1); k_cache, v_cache: [S, Hkv, L, d] bf16; kbar: the
+ * dsa_kv_block_means of k_cache.  Per (sequence, KV head) the blocks are
+ * scored by max over the group's heads of (1/sqrt(d)) q_h . kbar_j, the
+ * sink and the last block are forced (per flags), the best others fill the
+ * budget, and every key of the kept blocks is attended to.
+ * o: [S, Hq, d] bf16; lse: [S, Hq] fp32 or NULL; idx: [S, Hkv, kmax] with
+ * kmax from dsa_decode_kmax.  ws: at least dsa_decode_workspace_bytes. */
+int dsa_decode(const dsa_shape* shape, const void* q, const void* k_cache, const void* v_cache, const float* kbar,
+               void* o, float* lse, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* dsa_status_str(int status);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

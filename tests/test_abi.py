@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle as O
+import dynamic_block_sparse_dsa_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsa.LIB_PATH):
+        pytest.fail("libdsa.so is not built (run __graft_entry__.build())")
+    return dsa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(dsa.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dsa_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.dsa_status_str(code)
+    assert lib.dsa_status_str(17) == b"unknown status"
+
+
+def shape(**kw):
+    base = dict(batch=1, n_q_heads=4, n_kv_heads=2, seq_len=1024, head_dim=128, block=64, topk=4, topk_num=0,
+                topk_den=1, flags=3)
+    base.update(kw)
+    return dsa.Shape(**base)
+
+
+BAD = [
+    (dict(head_dim=96), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(block=32), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(n_q_heads=5, n_kv_heads=2), dsa.DSA_ERR_SHAPE),
+    (dict(n_kv_heads=0), dsa.DSA_ERR_SHAPE),
+    (dict(batch=-1), dsa.DSA_ERR_SHAPE),
+    (dict(seq_len=-5), dsa.DSA_ERR_SHAPE),
+    (dict(topk=-1), dsa.DSA_ERR_SHAPE),
+    (dict(topk=0, topk_num=1, topk_den=0), dsa.DSA_ERR_SHAPE),
+    (dict(topk=0, topk_num=-1, topk_den=3), dsa.DSA_ERR_SHAPE),
+    (dict(topk=0, topk_num=0, flags=0), dsa.DSA_ERR_SHAPE),
+    (dict(flags=4), dsa.DSA_ERR_SHAPE),
+    (dict(seq_len=64 * 4096 + 1), dsa.DSA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_bad_shapes_are_rejected_everywhere(lib, kw, code):
+    s = shape(**kw)
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    out = ctypes.c_int32()
+    calls = [
+        lambda: lib.dsa_prefill_kmax(ctypes.byref(s), ctypes.byref(out)),
+        lambda: lib.dsa_block_means(ctypes.byref(s), 2, p, p, None),
+        lambda: lib.dsa_block_scores(ctypes.byref(s), p, p, p, None),
+        lambda: lib.dsa_select_topk(ctypes.byref(s), p, p, p, None),
+        lambda: lib.dsa_sparse_attn_fwd(ctypes.byref(s), p, p, p, p, p, p, None, None),
+        lambda: lib.dsa_prefill(ctypes.byref(s), p, p, p, p, None, p, p, p, 1 << 40, None),
+        lambda: lib.dsa_decode(ctypes.byref(s), p, p, p, p, p, None, p, p, 1 << 40, None),
+    ]
+    for c in calls:
+        assert c() == code
+        assert lib.dsa_last_error()
+    assert lib.dsa_prefill_workspace_bytes(ctypes.byref(s)) == 0
+
+
+def test_null_arguments(lib):
+    s = shape()
+    p = ctypes.c_void_p(16)
+    assert lib.dsa_prefill_kmax(None, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_prefill_kmax(ctypes.byref(s), None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_block_means(ctypes.byref(s), 4, None, p, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_block_scores(ctypes.byref(s), p, None, p, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_select_topk(ctypes.byref(s), p, p, None, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_sparse_attn_fwd(ctypes.byref(s), p, p, None, p, p, p, None, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_prefill(ctypes.byref(s), p, p, p, None, None, p, p, p, 1 << 40, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_decode(ctypes.byref(s), p, p, p, None, p, None, p, p, 1 << 40, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_block_means(ctypes.byref(s), 0, p, p, None) == dsa.DSA_ERR_SHAPE
+
+
+def test_workspace_too_small(lib):
+    s = shape()
+    p = ctypes.c_void_p(16)
+    need = lib.dsa_prefill_workspace_bytes(ctypes.byref(s))
+    nb = 1024 // 64
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert need == a256(4 * nb * 128 * 4) + a256(2 * nb * 128 * 4) + a256(2 * nb * nb * 4)
+    assert lib.dsa_prefill(ctypes.byref(s), p, p, p, p, None, p, p, p, need - 1, None) == dsa.DSA_ERR_WORKSPACE
+    assert lib.dsa_prefill(ctypes.byref(s), p, p, p, p, None, p, p, None, need, None) == dsa.DSA_ERR_WORKSPACE
+    d = shape(batch=3, seq_len=1000)
+    dneed = lib.dsa_decode_workspace_bytes(ctypes.byref(d))
+    assert dneed > 0
+    assert lib.dsa_decode(ctypes.byref(d), p, p, p, p, p, None, p, p, dneed - 1, None) == dsa.DSA_ERR_WORKSPACE
+
+
+def test_decode_specific_checks(lib):
+    p = ctypes.c_void_p(16)
+    s = shape(n_q_heads=24, n_kv_heads=2)  # group of 12: prefill yes, decode no
+    out = ctypes.c_int32()
+    assert lib.dsa_prefill_kmax(ctypes.byref(s), ctypes.byref(out)) == 0
+    assert lib.dsa_decode_kmax(ctypes.byref(s), ctypes.byref(out)) == dsa.DSA_ERR_UNSUPPORTED
+    z = shape(seq_len=0)
+    assert lib.dsa_decode(ctypes.byref(z), p, p, p, p, p, None, p, p, 1 << 40, None) == dsa.DSA_ERR_SHAPE
+
+
+def test_empty_problems_are_no_ops(lib):
+    """B == 0 or N == 0 returns OK without touching the (invalid) pointers."""
+    p = ctypes.c_void_p(16)
+    for s in (shape(batch=0), shape(seq_len=0)):
+        assert lib.dsa_prefill(ctypes.byref(s), p, p, p, p, None, p, p, None, 0, None) == 0
+        assert lib.dsa_sparse_attn_fwd(ctypes.byref(s), p, p, p, p, p, p, None, None) == 0
+        assert lib.dsa_block_means(ctypes.byref(s), 4, p, p, None) == 0
+    d = shape(batch=0)
+    assert lib.dsa_decode(ctypes.byref(d), p, p, p, p, p, None, p, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("N,b,topk,num,den,flags", [
+    (1024, 64, 4, 0, 1, 3), (8192, 64, 16, 0, 1, 3), (32768, 64, 0, 15, 100, 3), (131072, 128, 64, 0, 1, 3),
+    (100, 64, 4, 0, 1, 3), (1000, 64, 1, 0, 1, 0), (5000, 128, 0, 1, 3, 1), (640, 64, 50, 0, 1, 2)])
+def test_kmax_matches_the_oracle(lib, N, b, topk, num, den, flags):
+    s = shape(seq_len=N, block=b, topk=topk, topk_num=num, topk_den=den, flags=flags)
+    nb = -(-N // b)
+    assert dsa.dsa_prefill_kmax(s) == O.kmax(nb, topk, num, den, flags, True, nb)
+    assert dsa.dsa_decode_kmax(s) == O.kmax(1, topk, num, den, flags, False, nb)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    s = shape(batch=1, n_q_heads=2, n_kv_heads=2, seq_len=128, head_dim=64)
+    x = torch.zeros((1, 2, 128, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dsa.dsa_block_means(s, 2, x, torch.zeros((1, 2, 2, 64)), stream=0)
