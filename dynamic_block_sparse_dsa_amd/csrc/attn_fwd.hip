@@ -14,56 +14,109 @@
 //
 // Design (gfx950):
 //   * one workgroup per (batch, KV head, group of HG query heads, query block
-//     i); wave w owns 32 query rows of one head; the K/V tile of each kept
-//     block is loaded once per workgroup and shared by all HG heads;
+//     i); wave w owns 32 query rows of one head, so the K/V tile of each kept
+//     block is read from HBM/L2 once per workgroup and shared by its HG heads;
+//   * K and V tiles go global -> LDS directly (global_load_lds_dwordx4: no
+//     staging registers).  A wave instruction fills 1 KiB of LDS in lane
+//     order, so each lane fetches the 16-byte chunk that an XOR swizzle
+//     assigns to its LDS slot -- the swizzle spreads the MFMA operand reads
+//     over all banks;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows are the A operand
-//     (read from LDS), Q^T the B operand (kept in registers for the whole
-//     workgroup).  The output puts one query row in each lane (lanes l and
-//     l+32 hold the two halves of the keys), so the softmax row reductions
-//     are in-lane plus one cross-half exchange;
+//     (ds_read_b128), Q^T the B operand (registers, for the whole workgroup).
+//     One query row per lane (lanes l and l+32 hold the two key halves), so
+//     the row max and sum are in-lane plus one cross-half exchange;
 //   * O^T += V^T P^T: P leaves the S^T accumulators already in B-operand
-//     order; V is written to LDS transposed ([d][key]) so its A operand is two
-//     8-byte reads;
-//   * exp2 with log2(e)/sqrt(d) folded into one multiply; the running max is
-//     only raised (and O rescaled) when it grows by more than 2^8, which keeps
+//     order; the V^T A operand comes straight from the row-major V tile with
+//     ds_read_b64_tr_b16 (within 16 lanes, lane i slot j receives element
+//     i % 4 of the 8-byte chunk of source lane 4j + i / 4);
+//   * the max is kept in raw logit units and 1/sqrt(d) * log2(e) is folded
+//     into the single FMA that feeds exp2; the running max is only raised
+//     (and O rescaled) when it grows by more than 8 (log2 units), which keeps
 //     every P <= 256 and is exact after the final division;
-//   * the diagonal block masks key > row by select (never by adding -inf to
-//     a value), and rows/keys past N are zero-filled, so no garbage can reach
-//     an output;
+//   * single K and V buffers, 4 barriers per tile: K(t+1) streams in while
+//     the softmax and P V of tile t run, V(t+1) while Q K^T of tile t+1 runs;
+//   * the diagonal block masks key > row by select; rows/keys past N read a
+//     clamped (finite) row, are masked or discarded, never stored;
 //   * workgroups are numbered XCD-aware (one head's query blocks share an
 //     XCD's L2) and the heaviest (last) query blocks go first.
-#include <mutex>
-
 #include "dsa_internal.hpp"
 
 namespace dsa {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
 
 template <int D, int BLK, int HG>
 struct AttnCfg {
   static constexpr int SLABS = BLK / 32;  // 32-row slabs per head
   static constexpr int WAVES = HG * SLABS;
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int KP = D + 8;    // K tile pitch in LDS (elements): 16 B pad
-  static constexpr int VP = BLK + 4;  // V^T tile pitch in LDS (elements): 8 B pad
-  static constexpr int K_CHUNKS = BLK * D / 8;         // 16-byte chunks of a K tile
-  static constexpr int V_PATCHES = (BLK / 4) * (D / 8);  // 4 keys x 8 dims patches
-  static constexpr int K_PER_T = (K_CHUNKS + THREADS - 1) / THREADS;
-  static constexpr int V_PER_T = (V_PATCHES + THREADS - 1) / THREADS;
-  static constexpr int LDS_BYTES = (BLK * KP + D * VP) * 2;
+  static constexpr int CH = D / 8;                  // 16-byte chunks per row
+  static constexpr int RPI = 1024 / (2 * D);        // rows per 1 KiB wave load
+  static constexpr int LOADS = BLK * D * 2 / 1024;  // wave loads per tile (K or V)
+  static constexpr int LOADS_PER_WAVE = LOADS / WAVES;
+  static_assert(LOADS % WAVES == 0, "tile loads must split evenly over waves");
 };
 
-__device__ __forceinline__ uint32_t half_of(u32x4 w, int e) {
-  // 16-bit element e (0..7) of an 8 x bf16 vector
-  const uint32_t word = w[e >> 1];
-  return (e & 1) ? (word >> 16) : (word & 0xffffu);
+// XOR swizzles of the 16-byte chunk index within a row (see header comment).
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+// wait until at most n vector-memory operations of this wave are in flight
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte-per-lane DMA from global memory into LDS (lane l lands at
+// lds_addr + 16 * l).  Written as a small asm block because the compiler
+// cannot tell LDS DMA into one tile from reads of the other tile: with the
+// builtin it drains every outstanding load before each LDS read, which would
+// serialise the prefetch.  The block has no register outputs (the data goes
+// to LDS); M0 is saved and restored so the compiler's view of it holds; the
+// waits for the data are the explicit vmcnt waits + barriers in the loop.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "memory");
 }
 
 template <int D, int BLK, int HG>
-__global__ __launch_bounds__((AttnCfg<D, BLK, HG>::THREADS)) void sparse_attn_fwd_kernel(AttnArgs a) {
+__device__ __forceinline__ void issue_tile(const uint16_t* g, uint32_t lds_base, int key0, int N, int wave, int lane,
+                                           bool v_swizzle) {
   using C = AttnCfg<D, BLK, HG>;
-  extern __shared__ __align__(16) uint16_t lds[];
-  uint16_t* Ks = lds;                 // [BLK][KP]   key-major
-  uint16_t* Vt = lds + BLK * C::KP;   // [D][VP]     dim-major (transposed)
+#pragma unroll
+  for (int n = 0; n < C::LOADS_PER_WAVE; ++n) {
+    const int inst = wave + n * C::WAVES;
+    const int r = inst * C::RPI + lane / C::CH;
+    const int p = lane % C::CH;
+    const int c = p ^ (v_swizzle ? vswz<D>(r) : kswz<D>(r));
+    const int key = min(key0 + r, N - 1);
+    dma16(g, (uint32_t)(key * D + c * 8) * 2u, __builtin_amdgcn_readfirstlane(lds_base + inst * 1024));
+  }
+}
+
+template <int D, int BLK, int HG>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks_l, LDS_AS uint16_t* vs_l) {
+  using C = AttnCfg<D, BLK, HG>;
+  constexpr int NV = C::LOADS_PER_WAVE;  // loads per wave per tile (K or V)
 
   const int G = a.Hq / a.Hkv;
   const int hchunks = G / HG;
@@ -75,7 +128,8 @@ __global__ __launch_bounds__((AttnCfg<D, BLK, HG>::THREADS)) void sparse_attn_fw
   const int64_t b = bg / a.Hkv;
   const int g = (int)(bg % a.Hkv);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = wave / C::SLABS, slab = wave % C::SLABS;
   const int h = g * G + hc * HG + hl;
   const int half = lane >> 5;
@@ -86,152 +140,135 @@ __global__ __launch_bounds__((AttnCfg<D, BLK, HG>::THREADS)) void sparse_attn_fw
   const uint16_t* qh = a.q + (b * a.Hq + h) * (int64_t)N * D;
   const uint16_t* kgp = a.k + bg * (int64_t)N * D;
   const uint16_t* vgp = a.v + bg * (int64_t)N * D;
-  const int32_t* irow = a.idx + (bg * a.nB + i) * (int64_t)a.kmax;
-  const int n_sel = a.cnt[bg * a.nB + i];
+  // the index row is read through the constant address space: uniform scalar
+  // loads, counted by lgkmcnt, so they never wait on the tile DMA (vmcnt)
+  const CONST_AS int32_t* irow = (const CONST_AS int32_t*)(a.idx + (bg * a.nB + i) * (int64_t)a.kmax);
+  const int n_sel = ((const CONST_AS int32_t*)a.cnt)[bg * a.nB + i];
+  const uint32_t ks_base = (uint32_t)(uintptr_t)ks_l, vs_base = (uint32_t)(uintptr_t)vs_l;
 
-  // Q^T fragments: lane holds its row, dims ks*16 + 8*half .. +7
+  if (n_sel > 0) {
+    const int j0 = irow[0];
+    issue_tile<D, BLK, HG>(kgp, ks_base, j0 * BLK, N, wave, lane, false);
+    issue_tile<D, BLK, HG>(vgp, vs_base, j0 * BLK, N, wave, lane, true);
+  }
+
+  // Q^T fragments (B operand): lane holds its row, dims ks*16 + 8*half .. +7.
+  // The empty asm "uses" them here so the compiler's waits for these loads
+  // land before the loop (where they would otherwise also wait on the DMA).
   u32x4 qf[D / 16];
+  {
+    const uint16_t* qr = qh + (int64_t)min(row, N - 1) * D + 8 * half;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    qf[ks] = (u32x4){0, 0, 0, 0};
-    if (row < N) qf[ks] = *reinterpret_cast<const u32x4*>(qh + (int64_t)row * D + ks * 16 + 8 * half);
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qr + ks * 16);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = (f32x16){};
   const float NEG_INF = -__builtin_inff();
-  float m_run = NEG_INF;  // running max (log2 domain), same in lanes l and l^32
-  float l_part = 0.f;     // this lane's share of the row sum
+  const float c2 = a.scale_log2;  // log2(e) / sqrt(d)
+  float m_run = NEG_INF;          // running max of raw logits, same in lanes l and l^32
+  float l_part = 0.f;             // this lane's share of the row sum
 
-  u32x4 kst[C::K_PER_T];
-  u32x4 vst[C::V_PER_T][4];
-
-  auto load_tile = [&](int j) {
-    const int key0 = j * BLK;
-#pragma unroll
-    for (int n = 0; n < C::K_PER_T; ++n) {
-      const int c = tid + n * C::THREADS;
-      kst[n] = (u32x4){0, 0, 0, 0};
-      if (c < C::K_CHUNKS) {
-        const int r = c / (D / 8), col = c % (D / 8);
-        if (key0 + r < N) kst[n] = *reinterpret_cast<const u32x4*>(kgp + (int64_t)(key0 + r) * D + col * 8);
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < C::V_PER_T; ++n) {
-      const int p = tid + n * C::THREADS;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) vst[n][rr] = (u32x4){0, 0, 0, 0};
-      if (p < C::V_PATCHES) {
-        const int kq = p / (D / 8), dg = p % (D / 8);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int key = key0 + 4 * kq + rr;
-          if (key < N) vst[n][rr] = *reinterpret_cast<const u32x4*>(vgp + (int64_t)key * D + dg * 8);
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int n = 0; n < C::K_PER_T; ++n) {
-      const int c = tid + n * C::THREADS;
-      if (c < C::K_CHUNKS) {
-        const int r = c / (D / 8), col = c % (D / 8);
-        *reinterpret_cast<u32x4*>(Ks + r * C::KP + col * 8) = kst[n];
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < C::V_PER_T; ++n) {
-      const int p = tid + n * C::THREADS;
-      if (p < C::V_PATCHES) {
-        const int kq = p / (D / 8), dg = p % (D / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          u32x2 w;
-          w[0] = half_of(vst[n][0], e) | (half_of(vst[n][1], e) << 16);
-          w[1] = half_of(vst[n][2], e) | (half_of(vst[n][3], e) << 16);
-          *reinterpret_cast<u32x2*>(Vt + (dg * 8 + e) * C::VP + 4 * kq) = w;
-        }
-      }
-    }
-  };
-
-  if (n_sel > 0) load_tile(irow[0]);
   for (int t = 0; t < n_sel; ++t) {
     const int j = irow[t];
-    __syncthreads();  // every wave is done with the previous tile
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_sel) load_tile(irow[t + 1]);  // in flight during the math below
     const bool diag = (j == i);
+    const bool more = t + 1 < n_sel;
+    const int jn = more ? irow[t + 1] : 0;
 
+    // ---- K(t) resident (V(t) may still be in flight; Q loads are older)
+    wait_vm<NV>();
+    __syncthreads();
+    f32x16 s[BLK / 32];
 #pragma unroll
-    for (int hb = 0; hb < BLK / 64; ++hb) {
-      // ---- S^T = K Q^T for keys hb*64 .. hb*64+63 (two 32-key subtiles)
-      f32x16 s[2] = {(f32x16){}, (f32x16){}};
+    for (int st = 0; st < BLK / 32; ++st) s[st] = (f32x16){};
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 kf =
-              *reinterpret_cast<const u32x4*>(Ks + (hb * 64 + st * 32 + (lane & 31)) * C::KP + ks * 16 + 8 * half);
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), s[st], 0, 0, 0);
-        }
+      for (int st = 0; st < BLK / 32; ++st) {
+        const int kr = st * 32 + (lane & 31);
+        const int c = (2 * ks + half) ^ kswz<D>(kr);
+        const u32x4 kf = *reinterpret_cast<const LDS_AS u32x4*>(ks_l + kr * D + c * 8);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), s[st], 0, 0, 0);
       }
-      // ---- scale, causal mask on the diagonal block, row max
-      float mloc = NEG_INF;
+    }
+    __syncthreads();  // every wave is done reading K(t)
+    if (more) issue_tile<D, BLK, HG>(kgp, ks_base, jn * BLK, N, wave, lane, false);
+
+    // ---- causal mask on the diagonal block, row max (raw units)
+    if (diag) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < BLK / 32; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[st][r] * a.scale_log2;
-          if (diag) {
-            const int key_in_blk = hb * 64 + st * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            x = (key_in_blk > row_in_blk) ? NEG_INF : x;
-          }
-          s[st][r] = x;
-          mloc = fmaxf(mloc, x);
+          const int key_in_blk = st * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          s[st][r] = (key_in_blk > row_in_blk) ? NEG_INF : s[st][r];
         }
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float m_new = fmaxf(m_run, mloc);
-      if (__any(m_new > m_run + 8.0f)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    }
+    float mloc = NEG_INF;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-        l_part *= alpha;
-        m_run = m_new;
-      }
-      // ---- P = exp2(S - m), packed to bf16 in B-operand order
-      u32x4 pf[4];
+    for (int st = 0; st < BLK / 32; ++st)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int st = kk >> 1, rb = 8 * (kk & 1);
-        float p[8];
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[st][r]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);
+    if (__any((m_new - m_run) * c2 > 8.0f)) {
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(s[st][rb + e] - m_run);
-          l_part += p[e];
-        }
-        pf[kk] = (u32x4){pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                         pack_bf16x2(p[6], p[7])};
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+      l_part *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c2;
+    // ---- P = exp2(s * c2 - m * c2), packed to bf16 in B-operand order
+    u32x4 pf[BLK / 16];
+#pragma unroll
+    for (int kk = 0; kk < BLK / 16; ++kk) {
+      const int st = kk >> 1, rb = 8 * (kk & 1);
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][rb + e], c2, -mc));
+        l_part += p[e];
       }
-      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_t pk = {(__bf16)p[2 * e], (__bf16)p[2 * e + 1]};
+        pf[kk][e] = __builtin_bit_cast(uint32_t, pk);
+      }
+    }
+
+    // ---- V(t) resident (K(t+1) may be in flight)
+    if (more) wait_vm<NV>(); else wait_vm<0>();
+    __syncthreads();
+    // ---- O^T += V^T P^T, A operand by transposed LDS reads
+    {
+      const int grp = (lane >> 4) & 1, si = lane & 15;  // 16-lane group within the half; source index
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
+        const int d = dt * 32 + 16 * grp + 4 * (si & 3);
+        const int cbase = d >> 3, sub = (d & 7) * 2;  // 16-byte chunk and byte offset (0 or 8)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint16_t* vr = Vt + (dt * 32 + (lane & 31)) * C::VP + hb * 64 + kk * 16 + 4 * half;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-          const u32x4 vf = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        for (int kk = 0; kk < BLK / 16; ++kk) {
+          u32x4 vf;
+#pragma unroll
+          for (int sg = 0; sg < 2; ++sg) {
+            const int key = 16 * kk + 8 * sg + 4 * half + (si >> 2);
+            const int c = cbase ^ vswz<D>(key);
+            const LDS_AS char* addr = reinterpret_cast<const LDS_AS char*>(vs_l + key * D + c * 8) + sub;
+            const i16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)addr);
+            const u32x2 w = __builtin_bit_cast(u32x2, v4);
+            vf[2 * sg] = w[0];
+            vf[2 * sg + 1] = w[1];
+          }
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[kk]), oacc[dt], 0, 0, 0);
         }
       }
     }
+    __syncthreads();  // every wave is done reading V(t)
+    if (more) issue_tile<D, BLK, HG>(vgp, vs_base, jn * BLK, N, wave, lane, true);
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = ln(sum) + max
@@ -243,31 +280,34 @@ __global__ __launch_bounds__((AttnCfg<D, BLK, HG>::THREADS)) void sparse_attn_fw
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
+        const bf16x2_t lo = {(__bf16)(oacc[dt][4 * q4 + 0] * inv), (__bf16)(oacc[dt][4 * q4 + 1] * inv)};
+        const bf16x2_t hi = {(__bf16)(oacc[dt][4 * q4 + 2] * inv), (__bf16)(oacc[dt][4 * q4 + 3] * inv)};
         u32x2 w;
-        w[0] = pack_bf16x2(oacc[dt][4 * q4 + 0] * inv, oacc[dt][4 * q4 + 1] * inv);
-        w[1] = pack_bf16x2(oacc[dt][4 * q4 + 2] * inv, oacc[dt][4 * q4 + 3] * inv);
+        w[0] = __builtin_bit_cast(uint32_t, lo);
+        w[1] = __builtin_bit_cast(uint32_t, hi);
         *reinterpret_cast<u32x2*>(orow + dt * 32 + 8 * q4 + 4 * half) = w;
       }
     }
-    if (a.lse && half == 0) a.lse[(b * a.Hq + h) * (int64_t)N + row] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+    if (a.lse && half == 0)
+      a.lse[(b * a.Hq + h) * (int64_t)N + row] = (m_run * c2 + __log2f(l_tot)) * 0.69314718055994531f;
   }
+}
+
+template <int D, int BLK, int HG>
+__global__ __launch_bounds__((AttnCfg<D, BLK, HG>::THREADS)) __attribute__((amdgpu_waves_per_eu(2)))
+void sparse_attn_fwd_kernel(AttnArgs a) {
+  __shared__ __align__(1024) uint16_t Ks[BLK * D];
+  __shared__ __align__(1024) uint16_t Vs[BLK * D];
+  attn_body<D, BLK, HG>(a, (LDS_AS uint16_t*)(Ks), (LDS_AS uint16_t*)(Vs));
 }
 
 template <int D, int BLK, int HG>
 static hipError_t launch_attn_cfg(const AttnArgs& a, hipStream_t stream) {
   using C = AttnCfg<D, BLK, HG>;
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_attn_fwd_kernel<D, BLK, HG>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-  });
-  if (attr_err != hipSuccess) return attr_err;
   const int G = a.Hq / a.Hkv;
   const int64_t n_wg = (int64_t)a.B * a.Hkv * (G / HG) * a.nB;
   if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BLK, HG>), dim3((uint32_t)n_wg), dim3(C::THREADS), C::LDS_BYTES,
-                     stream, a);
+  hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BLK, HG>), dim3((uint32_t)n_wg), dim3(C::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
