@@ -98,18 +98,39 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
       : "memory");
 }
 
+// Byte offset, relative to the first row of the tile, of the 16-byte chunk
+// lane `lane` fetches for wave load n (row r, swizzled chunk c).
 template <int D, int BLK, int HG>
-__device__ __forceinline__ void issue_tile(const uint16_t* g, uint32_t lds_base, int key0, int N, int wave, int lane,
-                                           bool v_swizzle) {
+__device__ __forceinline__ uint32_t tile_lane_offset(int n, int wave, int lane, bool v_swizzle, int* row_out) {
   using C = AttnCfg<D, BLK, HG>;
+  const int inst = wave + n * C::WAVES;
+  const int r = inst * C::RPI + lane / C::CH;
+  const int c = (lane % C::CH) ^ (v_swizzle ? vswz<D>(r) : kswz<D>(r));
+  *row_out = r;
+  return (uint32_t)(r * D + c * 8) * 2u;
+}
+
+// Enqueue this wave's share of one K or V tile (rows key0 .. key0+BLK-1).
+// off[n] are the precomputed lane offsets; a full tile only moves the
+// scalar base, a ragged last tile clamps each row to N-1.
+template <int D, int BLK, int HG>
+__device__ __forceinline__ void issue_tile(const uint16_t* g, uint32_t lds_base, const uint32_t* off, int key0, int N,
+                                           int wave, int lane, bool v_swizzle) {
+  using C = AttnCfg<D, BLK, HG>;
+  if (key0 + BLK <= N) {
+    const uint16_t* base = g + (int64_t)key0 * D;
 #pragma unroll
-  for (int n = 0; n < C::LOADS_PER_WAVE; ++n) {
-    const int inst = wave + n * C::WAVES;
-    const int r = inst * C::RPI + lane / C::CH;
-    const int p = lane % C::CH;
-    const int c = p ^ (v_swizzle ? vswz<D>(r) : kswz<D>(r));
-    const int key = min(key0 + r, N - 1);
-    dma16(g, (uint32_t)(key * D + c * 8) * 2u, __builtin_amdgcn_readfirstlane(lds_base + inst * 1024));
+    for (int n = 0; n < C::LOADS_PER_WAVE; ++n)
+      dma16(base, off[n], __builtin_amdgcn_readfirstlane(lds_base + (wave + n * C::WAVES) * 1024));
+  } else {
+#pragma unroll
+    for (int n = 0; n < C::LOADS_PER_WAVE; ++n) {
+      int r;
+      const uint32_t o = tile_lane_offset<D, BLK, HG>(n, wave, lane, v_swizzle, &r);
+      const int key = min(key0 + r, N - 1);
+      const uint32_t clamped = o - (uint32_t)(r * D * 2) + (uint32_t)(key * D * 2);
+      dma16(g, clamped, __builtin_amdgcn_readfirstlane(lds_base + (wave + n * C::WAVES) * 1024));
+    }
   }
 }
 
@@ -146,10 +167,18 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
   const int n_sel = ((const CONST_AS int32_t*)a.cnt)[bg * a.nB + i];
   const uint32_t ks_base = (uint32_t)(uintptr_t)ks_l, vs_base = (uint32_t)(uintptr_t)vs_l;
 
+  uint32_t koff[C::LOADS_PER_WAVE], voff[C::LOADS_PER_WAVE];
+#pragma unroll
+  for (int n = 0; n < C::LOADS_PER_WAVE; ++n) {
+    int r;
+    koff[n] = tile_lane_offset<D, BLK, HG>(n, wave, lane, false, &r);
+    voff[n] = tile_lane_offset<D, BLK, HG>(n, wave, lane, true, &r);
+  }
+
   if (n_sel > 0) {
     const int j0 = irow[0];
-    issue_tile<D, BLK, HG>(kgp, ks_base, j0 * BLK, N, wave, lane, false);
-    issue_tile<D, BLK, HG>(vgp, vs_base, j0 * BLK, N, wave, lane, true);
+    issue_tile<D, BLK, HG>(kgp, ks_base, koff, j0 * BLK, N, wave, lane, false);
+    issue_tile<D, BLK, HG>(vgp, vs_base, voff, j0 * BLK, N, wave, lane, true);
   }
 
   // Q^T fragments (B operand): lane holds its row, dims ks*16 + 8*half .. +7.
@@ -195,7 +224,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
       }
     }
     __syncthreads();  // every wave is done reading K(t)
-    if (more) issue_tile<D, BLK, HG>(kgp, ks_base, jn * BLK, N, wave, lane, false);
+    if (more) issue_tile<D, BLK, HG>(kgp, ks_base, koff, jn * BLK, N, wave, lane, false);
 
     // ---- causal mask on the diagonal block, row max (raw units)
     if (diag) {
@@ -268,7 +297,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
       }
     }
     __syncthreads();  // every wave is done reading V(t)
-    if (more) issue_tile<D, BLK, HG>(vgp, vs_base, jn * BLK, N, wave, lane, true);
+    if (more) issue_tile<D, BLK, HG>(vgp, vs_base, voff, jn * BLK, N, wave, lane, true);
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = ln(sum) + max

@@ -66,27 +66,29 @@ hipError_t launch_block_means(const uint16_t* x, float* xbar, int64_t n_units, i
 }
 
 // ============================================================== block scores
-// One workgroup per 64x64 tile of the score matrix of one (batch, KV head).
-// Each thread owns a 4x4 set of entries (rows ty + 16a, cols tx + 16c), the
-// means are staged through LDS 32 dims at a time, every head of the group is
-// scored and the max is kept.  Tiles strictly above the diagonal are -inf.
+// One 256-thread workgroup per 32x32 tile of the score matrix of one (batch,
+// KV head): thread (ty, tx) owns rows ty, ty+16 and columns tx, tx+16.  Both
+// tiles of means are staged whole in LDS (row pitch D+1 floats: the column
+// reads of the K tile hit distinct banks, the Q reads are broadcasts); every
+// head of the group is scored against the K tile and the max is kept.  Tiles
+// strictly above the diagonal are -inf.
 template <int D>
 __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restrict__ qbar,
                                                            const float* __restrict__ kbar, float* __restrict__ scores,
                                                            int Hq, int Hkv, int nB, float scale, int n_tiles) {
-  __shared__ float qs[64][33];
-  __shared__ float ks[64][33];
+  __shared__ float qs[32][D + 1];
+  __shared__ float ks[32][D + 1];
   const int per_unit = n_tiles * n_tiles;
   const int64_t unit = blockIdx.x / per_unit;  // b * Hkv + g
   const int tile = blockIdx.x % per_unit;
   const int ti = tile / n_tiles, tj = tile % n_tiles;
   const int t = threadIdx.x, tx = t % 16, ty = t / 16;
-  const int i0 = ti * 64, j0 = tj * 64;
+  const int i0 = ti * 32, j0 = tj * 32;
   float* out = scores + unit * (int64_t)nB * nB;
   const float NEG_INF = -__builtin_inff();
   if (tj > ti) {
-    for (int e = t; e < 64 * 64; e += 256) {
-      const int i = i0 + e / 64, j = j0 + e % 64;
+    for (int e = t; e < 32 * 32; e += 256) {
+      const int i = i0 + e / 32, j = j0 + e % 32;
       if (i < nB && j < nB) out[(int64_t)i * nB + j] = NEG_INF;
     }
     return;
@@ -94,43 +96,47 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restri
   const int G = Hq / Hkv;
   const int64_t b = unit / Hkv, g = unit % Hkv;
   const float* kb = kbar + unit * (int64_t)nB * D;
-  float best[4][4];
+  for (int e = t; e < 32 * D / 4; e += 256) {
+    const int r = e / (D / 4), c = e % (D / 4);
+    f32x4 v = (f32x4){0, 0, 0, 0};
+    if (j0 + r < nB) v = *reinterpret_cast<const f32x4*>(kb + (int64_t)(j0 + r) * D + 4 * c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ks[r][4 * c + q] = v[q];
+  }
+  float best[2][2];
   for (int hh = 0; hh < G; ++hh) {
     const float* qb = qbar + ((b * Hq) + g * G + hh) * (int64_t)nB * D;
-    float acc[4][4] = {};
-    for (int d0 = 0; d0 < D; d0 += 32) {
-      for (int e = t; e < 64 * 32; e += 256) {
-        const int r = e / 32, c = e % 32;
-        qs[r][c] = (i0 + r < nB) ? qb[(int64_t)(i0 + r) * D + d0 + c] : 0.f;
-        ks[r][c] = (j0 + r < nB) ? kb[(int64_t)(j0 + r) * D + d0 + c] : 0.f;
-      }
-      __syncthreads();
+    __syncthreads();  // previous head's reads of qs are done
+    for (int e = t; e < 32 * D / 4; e += 256) {
+      const int r = e / (D / 4), c = e % (D / 4);
+      f32x4 v = (f32x4){0, 0, 0, 0};
+      if (i0 + r < nB) v = *reinterpret_cast<const f32x4*>(qb + (int64_t)(i0 + r) * D + 4 * c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) qs[r][4 * c + q] = v[q];
+    }
+    __syncthreads();
+    float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll 8
-      for (int dd = 0; dd < 32; ++dd) {
-        float a[4], bb[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = qs[ty + 16 * r][dd];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) bb[c] = ks[tx + 16 * c][dd];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(a[r], bb[c], acc[r][c]);
-      }
-      __syncthreads();
+    for (int dd = 0; dd < D; ++dd) {
+      const float a0 = qs[ty][dd], a1 = qs[ty + 16][dd];
+      const float b0 = ks[tx][dd], b1 = ks[tx + 16][dd];
+      acc[0][0] = __builtin_fmaf(a0, b0, acc[0][0]);
+      acc[0][1] = __builtin_fmaf(a0, b1, acc[0][1]);
+      acc[1][0] = __builtin_fmaf(a1, b0, acc[1][0]);
+      acc[1][1] = __builtin_fmaf(a1, b1, acc[1][1]);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < 2; ++c) {
         const float sc = acc[r][c] * scale;
         best[r][c] = (hh == 0) ? sc : fmaxf(best[r][c], sc);
       }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2; ++c) {
       const int i = i0 + ty + 16 * r, j = j0 + tx + 16 * c;
       if (i < nB && j < nB) out[(int64_t)i * nB + j] = (j <= i) ? best[r][c] : NEG_INF;
     }
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restri
 
 hipError_t launch_block_scores(const float* qbar, const float* kbar, float* scores, int B, int Hq, int Hkv, int nB,
                                int d, float scale, hipStream_t stream) {
-  const int n_tiles = (nB + 63) / 64;
+  const int n_tiles = (nB + 31) / 32;
   const int64_t n_wg = (int64_t)B * Hkv * n_tiles * n_tiles;
   if (n_wg == 0) return hipSuccess;
   if (d == 64)
@@ -294,11 +300,152 @@ __global__ __launch_bounds__(TOPK_THREADS) void select_topk_kernel(const float* 
   if (t == 0 && cnt) cnt[row] = total;
 }
 
+// ---------------------------------------------------------------- wave per row
+// The same selection with one 64-lane wave per row (rows of up to 64*R
+// blocks; 4 rows per workgroup).  No workgroup barrier: histograms are per
+// wave in LDS and every scan is a wave-level shuffle scan.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void select_topk_wave_kernel(const float* __restrict__ scores,
+                                                               int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
+                                                               int64_t n_rows, int rows_per_unit, int n_cols,
+                                                               int causal, TopkParams p, int kmax) {
+  __shared__ int hist_all[4][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= n_rows) return;  // whole wave; no workgroup barrier below
+  int* hist = hist_all[wave];
+  const int i = (int)(row % rows_per_unit);
+  const int nv = causal ? i + 1 : n_cols;
+  const int f_sink = (p.flags & 1u) ? 0 : -1;
+  const int f_diag = (p.flags & 2u) ? nv - 1 : -1;
+  const int nf = (f_sink >= 0) + (f_diag >= 0) - (f_sink >= 0 && f_sink == f_diag);
+  int64_t budget = p.topk > 0 ? (int64_t)p.topk : ((int64_t)p.num * nv + p.den - 1) / p.den;
+  if (budget < nf) budget = nf;
+  if (budget > nv) budget = nv;
+  const int m = (int)budget - nf;
+  const int ncand = nv - nf;
+  const float* srow = scores + row * (int64_t)n_cols;
+  const int j0 = lane * R;  // this lane owns blocks j0 .. j0+R-1 (index order)
+
+  uint32_t key[R];
+  uint32_t candbits = 0;
+#pragma unroll
+  for (int e = 0; e < R; ++e) {
+    const int j = j0 + e;
+    key[e] = 0;
+    if (j < nv && j != f_sink && j != f_diag) {
+      key[e] = order_key(srow[j]);
+      candbits |= 1u << e;
+    }
+  }
+  const bool all = (m >= ncand), none = (m <= 0);
+  uint32_t T = 0;
+  int take_eq = 0;
+  if (!all && !none) {
+    uint32_t prefix = 0, pmask = 0;
+    int remaining = m;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
+      wave_lds_sync();
+#pragma unroll
+      for (int e = 0; e < R; ++e)
+        if (((candbits >> e) & 1u) && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1);
+      wave_lds_sync();
+      // lane owns digits 255-4*lane-q (q = 0..3): descending order over (lane, q)
+      int c[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[q] = hist[255 - 4 * lane - q];
+        sum += c[q];
+      }
+      const int incl = wave_incl_scan(sum);
+      int before = incl - sum;  // candidates with a larger digit than this lane's first
+      int dg = -1, rem_new = 0;
+      if (before < remaining && remaining <= incl) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (dg < 0 && before + c[q] >= remaining) {
+            dg = 255 - 4 * lane - q;
+            rem_new = remaining - before;
+          }
+          before += c[q];
+        }
+      }
+      const uint64_t who = __ballot(dg >= 0);
+      const int src = max(__ffsll((unsigned long long)who) - 1, 0);  // exactly one lane holds the digit
+      const int digit = __shfl(dg, src, 64);
+      remaining = __shfl(rem_new, src, 64);
+      prefix |= (uint32_t)digit << shift;
+      pmask |= 0xffu << shift;
+      wave_lds_sync();
+    }
+    T = prefix;
+    take_eq = remaining;
+  }
+
+  int my_eq = 0;
+  if (!all && !none) {
+#pragma unroll
+    for (int e = 0; e < R; ++e) my_eq += ((candbits >> e) & 1u) && key[e] == T;
+  }
+  int running_eq = wave_incl_scan(my_eq) - my_eq;
+  uint32_t selbits = 0;
+#pragma unroll
+  for (int e = 0; e < R; ++e) {
+    const int j = j0 + e;
+    if (j >= nv) continue;
+    bool s;
+    if (j == f_sink || j == f_diag) s = true;
+    else if (all) s = true;
+    else if (none) s = false;
+    else if (key[e] > T) s = true;
+    else if (key[e] == T) { s = running_eq < take_eq; ++running_eq; }
+    else s = false;
+    selbits |= (uint32_t)s << e;
+  }
+  const int my_sel = __builtin_popcount(selbits);
+  const int incl = wave_incl_scan(my_sel);
+  int pos = incl - my_sel;
+  const int total = __shfl(incl, 63, 64);
+  int32_t* out = idx + row * (int64_t)kmax;
+#pragma unroll
+  for (int e = 0; e < R; ++e)
+    if ((selbits >> e) & 1u) out[pos++] = j0 + e;
+  for (int e = total + lane; e < kmax; e += 64) out[e] = -1;
+  if (lane == 0 && cnt) cnt[row] = total;
+}
+
 hipError_t launch_select_topk(const float* scores, int32_t* idx, int32_t* cnt, int64_t n_rows, int rows_per_unit,
                               int n_cols, bool causal, TopkParams p, int kmax, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_topk_kernel, dim3((uint32_t)n_rows), dim3(TOPK_THREADS), 0, stream, scores, idx, cnt,
-                     rows_per_unit, n_cols, causal ? 1 : 0, p, kmax);
+  const int longest = causal ? rows_per_unit : n_cols;
+  const dim3 wave_grid((uint32_t)((n_rows + 3) / 4)), wave_block(256);
+  if (longest <= 64 * 4)
+    hipLaunchKernelGGL(select_topk_wave_kernel<4>, wave_grid, wave_block, 0, stream, scores, idx, cnt, n_rows,
+                       rows_per_unit, n_cols, causal ? 1 : 0, p, kmax);
+  else if (longest <= 64 * 16)
+    hipLaunchKernelGGL(select_topk_wave_kernel<16>, wave_grid, wave_block, 0, stream, scores, idx, cnt, n_rows,
+                       rows_per_unit, n_cols, causal ? 1 : 0, p, kmax);
+  else
+    hipLaunchKernelGGL(select_topk_kernel, dim3((uint32_t)n_rows), dim3(TOPK_THREADS), 0, stream, scores, idx, cnt,
+                       rows_per_unit, n_cols, causal ? 1 : 0, p, kmax);
   return hipGetLastError();
 }
 

@@ -199,6 +199,48 @@ def test_zero_queries_take_lowest_blocks(cuda_device):
     check_out(np64(o), ref, what="zero-q")
 
 
+@pytest.mark.parametrize("nb,topk,num,den,flags", [(100, 7, 0, 1, 3), (700, 20, 0, 1, 3), (2000, 33, 0, 1, 3),
+                                                  (300, 0, 3, 10, 1), (1500, 0, 1, 7, 2), (64, 5, 0, 1, 0)])
+def test_select_topk_exact_with_ties(cuda_device, nb, topk, num, den, flags):
+    """dsa_select_topk on integer-valued scores (many exact ties) equals the
+    oracle's selection exactly: the tie rule (lower block first) and the
+    budget are the same on both sides.  Covers the 64-lane variants (rows up
+    to 256 and 1024 blocks) and the workgroup variant (longer rows)."""
+    say(f"select exact nb{nb} k{topk} {num}/{den} flags{flags}")
+    rng = np.random.default_rng(nb + topk)
+    raw = rng.integers(-6, 6, size=(1, 2, nb, nb)).astype(np.float32)
+    causal = np.tril(np.ones((nb, nb), dtype=bool))
+    sc = np.where(causal, raw, -np.inf).astype(np.float32)
+    shape = dsa.make_shape(1, 2, 2, nb * 64, 128, 64, topk, num, den, flags)
+    km = dsa.dsa_prefill_kmax(shape)
+    scores = torch.from_numpy(sc).to(cuda_device)
+    idx = torch.empty((1, 2, nb, km), dtype=torch.int32, device=cuda_device)
+    cnt = torch.empty((1, 2, nb), dtype=torch.int32, device=cuda_device)
+    dsa.dsa_select_topk(shape, scores, idx, cnt)
+    torch.cuda.synchronize()
+    ref_idx, ref_cnt, _ = O.select_topk(sc.astype(np.float64), topk, num, den, flags)
+    assert np.array_equal(cnt.cpu().numpy(), ref_cnt)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
+def test_prefill_rows_longer_than_1024_blocks(cuda_device):
+    """N = 64 * 1300: selection rows longer than 1024 blocks (workgroup
+    select), checked on every row; attention on sampled query blocks."""
+    w = Workload("long", "prefill", 1, 2, 1, 64 * 1300, 64, 64, 8, seed=60)
+    say("prefill nB=1300")
+    q, k, v = make_prefill(w, device=cuda_device)
+    o, lse, idx, cnt = dsa.prefill(q, k, v, w.block, w.topk)
+    torch.cuda.synchronize()
+    qn, kn, vn = np64(q), np64(k), np64(v)
+    ref = O.prefill(qn, kn, vn, w.block, w.topk, attend_blocks=[])
+    gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    check_rows(ref["rows"], gidx, gcnt)
+    for (h, i) in [(0, 1299), (1, 1025), (0, 3)]:
+        o_ref, lse_ref = O.attend(qn[:, h : h + 1], kn, vn, gidx, gcnt, w.block, units=[(0, 0, i)])
+        lo, hi = i * 64, (i + 1) * 64
+        check_out(np64(o[:, h, lo:hi]), o_ref[:, 0, lo:hi], np64(lse[:, h, lo:hi]), lse_ref[:, 0, lo:hi], f"h{h} i{i}")
+
+
 # ------------------------------------------------------------------ full sizes
 def full_prefill_check(cuda_device, wname, sample_units):
     w = WORKLOADS[wname]
@@ -285,6 +327,7 @@ DECODE_SMALL = [
     ("single_key", Workload("d5", "decode", 2, 4, 2, 1, 128, 64, 4, seed=54), 3),
     ("no_forcing_k2", Workload("d6", "decode", 2, 4, 2, 2048, 128, 64, 2, seed=55), 0),
     ("fraction", Workload("d7", "decode", 1, 4, 1, 4096, 128, 64, 0, 1, 8, seed=56), 3),
+    ("rows_over_1024_blocks", Workload("d8", "decode", 2, 4, 2, 64 * 1100 + 5, 128, 64, 12, seed=58), 3),
 ]
 
 
