@@ -240,7 +240,8 @@ size_t dsa_decode_workspace_bytes(const dsa_shape* s) {
   const int kmax = s->seq_len > 0 ? row_budget(s, (int)nB) : 0;
   const size_t G = (size_t)(s->n_q_heads / s->n_kv_heads);
   const size_t nsplit = (size_t)dsa::decode_splits(s->batch, s->n_kv_heads, kmax);
-  return align256(units * nB * 4) + align256(units * nsplit * G * (d + 2) * 4);
+  (void)nB;
+  return align256(units * nsplit * G * (d + 2) * 4);
 }
 
 int dsa_decode(const dsa_shape* s, const void* q, const void* k_cache, const void* v_cache, const float* kbar,
@@ -273,10 +274,7 @@ int dsa_decode(const dsa_shape* s, const void* q, const void* k_cache, const voi
   a.block = s->block;
   a.scale = 1.0f / sqrtf((float)s->head_dim);
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
-  char* p = static_cast<char*>(ws);
-  a.scores = reinterpret_cast<float*>(p);
-  p += align256((size_t)s->batch * s->n_kv_heads * nB * 4);
-  a.partial = reinterpret_cast<float*>(p);
+  a.partial = static_cast<float*>(ws);
   hipError_t e = dsa::launch_decode(a, s->head_dim, topk_params(s), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   g_err[0] = 0;

@@ -5,99 +5,151 @@
 //     "动态开销与计算收益的权衡": compute the index data when the cache is
 //     written rather than reselecting from raw keys every step (the fp32 block
 //     means of the key cache are built once, by dsa_kv_block_means);
-//     "前沿方向": GQA/MQA share the KV cache and so one selection per group.
+//     "前沿方向": GQA/MQA share the KV cache and so one selection per group;
+//     "基于Top-k选择的局部-全局混合": keep the best blocks plus anchors.
 //   "稀疏注意力 vs Flash Attention v2" (pnsm.cn/news/1249548.html), section 1:
 //     softmax of the scaled logits over the kept keys, times V.
 //
-// A step is four launches on the caller's stream:
-//   1. decode_scores_kernel: score[j] = max over the group's heads of
-//      (1/sqrt(d)) q_h . kbar_j, one 256-thread workgroup per 64 blocks of a
-//      (sequence, KV head) unit -- a pure fp32 stream over the block means;
-//   2. the shared top-k select, one row per unit (every row sees all blocks);
-//   3. decode_attn_kernel: split-K over the kept blocks, one workgroup per
-//      (unit, split), one kept block per wave at a time.  Q K^T uses
-//      v_mfma_f32_16x16x32_bf16 with the key rows loaded straight from HBM as
-//      the A operand and the group's query heads as B columns; P V is fp32
-//      VALU over 16-byte V rows.  The workgroup writes its partial
-//      (max, sum, acc[d]) per head;
-//   4. decode_combine_kernel: merges the partials of each unit.
-// The step is bound by HBM bandwidth: it must read the kept K/V blocks and
-// the whole block-mean cache.
+// A step is three launches on the caller's stream; it is bound by HBM
+// bandwidth (it must read the block means of the whole key cache and the kept
+// K/V blocks).  Both streams are read once per step, with non-temporal loads:
+//   1. decode_select_kernel: one 512-thread workgroup per (sequence, KV head)
+//      streams that unit's fp32 block means with 16-byte loads (d/8 lanes per
+//      block row; waves take batches of rows from an LDS counter and keep the
+//      next batch in flight while one is scored; row dot products reduced
+//      with DPP), scores each block by the max over the group's heads of
+//      q_h . kbar_j / sqrt(d) into LDS, then one wave runs the top-k on the
+//      LDS scores -- no score round trip;
+//   2. decode_attn_kernel: split-K over the kept blocks, one workgroup per
+//      (unit, split), one 32-key chunk of a kept block per wave at a time.  A
+//      wave issues the loads of its chunk's K and V together, then Q K^T on
+//      v_mfma_f32_16x16x32_bf16 (key rows as the A operand, the group's heads
+//      as B columns) and P V as fp32 VALU over 16-byte V rows.  The workgroup
+//      merges its waves and writes a partial (max, sum, acc[d]) per head;
+//   3. decode_combine_kernel: one thread per (unit, head, dim) merges the
+//      partials.
 #include "dsa_internal.hpp"
+#include "topk_row.hpp"
 
 namespace dsa {
 
-constexpr int DEC_MAXG = 8;
+#define CONST_AS __attribute__((address_space(4)))
 
-// ============================================================== 1. scores
-template <int D>
-__global__ __launch_bounds__(256) void decode_scores_kernel(const uint16_t* __restrict__ q,
-                                                            const float* __restrict__ kbar,
-                                                            float* __restrict__ scores, int Hq, int Hkv, int nB,
-                                                            float scale, int nchunks) {
-  __shared__ f32x4 qs[DEC_MAXG][D / 4];
-  const int G = Hq / Hkv;
-  const int64_t unit = blockIdx.x / nchunks;
-  const int chunk = blockIdx.x % nchunks;
-  const int64_t s = unit / Hkv;
-  const int g = (int)(unit % Hkv);
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  for (int e = t; e < G * D; e += 256) {
-    const int hh = e / D, dd = e % D;
-    const uint16_t raw = q[(s * Hq + g * G + hh) * (int64_t)D + dd];
-    reinterpret_cast<float*>(&qs[hh][0])[dd] = __uint_as_float((uint32_t)raw << 16);
-  }
-  __syncthreads();
-  const int blk = chunk * 64 + wave * 16 + (lane >> 2);
-  const int quarter = lane & 3;
-  float part[DEC_MAXG];
-#pragma unroll
-  for (int hh = 0; hh < DEC_MAXG; ++hh) part[hh] = 0.f;
-  if (blk < nB) {
-    const f32x4* krow = reinterpret_cast<const f32x4*>(kbar + (unit * nB + blk) * (int64_t)D);
-#pragma unroll
-    for (int m = 0; m < D / 16; ++m) {
-      const int c = 4 * m + quarter;  // float4 chunk of the row
-      const f32x4 kv = krow[c];
-#pragma unroll
-      for (int hh = 0; hh < DEC_MAXG; ++hh) {
-        if (hh < G) {
-          const f32x4 qv = qs[hh][c];
-          part[hh] = __builtin_fmaf(kv[0], qv[0], part[hh]);
-          part[hh] = __builtin_fmaf(kv[1], qv[1], part[hh]);
-          part[hh] = __builtin_fmaf(kv[2], qv[2], part[hh]);
-          part[hh] = __builtin_fmaf(kv[3], qv[3], part[hh]);
-        }
-      }
-    }
-  }
-  float best = -__builtin_inff();
-#pragma unroll
-  for (int hh = 0; hh < DEC_MAXG; ++hh) {
-    if (hh < G) {
-      float v = part[hh];
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
-      best = fmaxf(best, v * scale);
-    }
-  }
-  if (quarter == 0 && blk < nB) scores[unit * nB + blk] = best;
+// ============================================================== 1. score + select
+// sum over aligned groups of W = 8 or 16 lanes, in every lane of the group
+// (DPP: two quad permutes, then the half-row and row mirrors)
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half mirror
+  if (W == 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
 }
 
-// ============================================================== 3. split attention
-template <int D, int BLK, int G>
+template <int D, int G, int R>
+__global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a, TopkParams p) {
+  constexpr int NT = 512, NW = NT / 64;
+  constexpr int TPR = D / 8;       // lanes per block row (8 floats each)
+  constexpr int WROWS = 64 / TPR;  // rows per wave per pass
+  constexpr int UNR = 8;           // passes per batch
+  constexpr int BR = WROWS * UNR;  // rows per batch (16 KiB of fp32 means at d = 128)
+  __shared__ float sc[64 * R];     // scores, block l * R + e at e * 64 + l
+  __shared__ uint32_t lds_key[128];
+  __shared__ int32_t lds_idx[128];
+  __shared__ int next_batch;
+  const int unit = blockIdx.x;
+  const int64_t s = unit / a.Hkv;
+  const int g = unit % a.Hkv;
+  const int t = threadIdx.x, lane = t & 63, c = lane % TPR, rl = lane / TPR;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int nB = a.nB;
+  const int nbatch = (nB + BR - 1) / BR;
+  if (t == 0) next_batch = NW;  // batches 0 .. NW-1 go to the waves in order
+  __syncthreads();
+
+  float qv[G][8];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(a.q + (s * a.Hq + g * G + hh) * (int64_t)D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[hh][2 * e] = bf16_lo(w[e]);
+      qv[hh][2 * e + 1] = bf16_hi(w[e]);
+    }
+  }
+  // A wave scores batches of BR consecutive rows; after its first batch it
+  // takes the next free one from an LDS counter, so waves that see shorter
+  // memory latency do more of them.  The next batch is in flight while one is
+  // scored; rows past the end are clamped (loaded again, never stored).
+  const float* kb = a.kbar + (int64_t)unit * nB * D + 8 * c;
+  auto load = [&](f32x4(&kv)[UNR][2], int b) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int row = min(b * BR + u * WROWS + rl, nB - 1);
+      kv[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kb + (int64_t)row * D));
+      kv[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kb + (int64_t)row * D + 4));
+    }
+  };
+  auto score = [&](const f32x4(&kv)[UNR][2], int b) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float best = -__builtin_inff();
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          part = __builtin_fmaf(qv[hh][e], kv[u][0][e], part);
+          part = __builtin_fmaf(qv[hh][4 + e], kv[u][1][e], part);
+        }
+        best = fmaxf(best, group_sum<TPR>(part) * a.scale);
+      }
+      const int row = b * BR + u * WROWS + rl;
+      if (c == 0 && row < nB) sc[(row % R) * 64 + row / R] = best;
+    }
+  };
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_batch, 1);
+    return __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
+  };
+  f32x4 k0[UNR][2], k1[UNR][2];
+  int b0 = wave;
+  if (b0 < nbatch) load(k0, b0);
+  int b1 = grab();
+  while (b0 < nbatch) {
+    if (b1 < nbatch) load(k1, b1);
+    score(k0, b0);
+    b0 = grab();
+    if (b1 >= nbatch) break;
+    if (b0 < nbatch) load(k0, b0);
+    score(k1, b1);
+    b1 = grab();
+  }
+  __syncthreads();
+  if (t < 64)  // one wave selects
+    wave_select_row<R, true>(sc, nB, p, a.idx + (int64_t)unit * a.kmax, a.kmax, lds_key, lds_idx);
+}
+
+// ============================================================== 2. split attention
+// Work unit of a wave: a 32-key chunk of a kept block.
+template <int D, int G>
 struct DecCfg {
   static constexpr int WAVES = 4;
-  static constexpr int CHK = D / 8;         // 16-byte chunks per row
-  static constexpr int KGR = 64 / CHK;      // key groups in a wave for P V
-  static constexpr int SUB = BLK / 16;      // 16-key MFMA subtiles per block
+  static constexpr int CK = 32;           // keys per chunk
+  static constexpr int CHK = D / 8;       // 16-byte pieces per row
+  static constexpr int KGR = 64 / CHK;    // key groups in a wave for P V
+  static constexpr int SUB = CK / 16;     // 16-key MFMA subtiles per chunk
+  static constexpr int VPL = CK / KGR;    // V rows per lane
 };
 
 template <int D, int BLK, int G>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
-  using C = DecCfg<D, BLK, G>;
-  __shared__ float pbuf[C::WAVES][BLK][G];   // P of the wave's current block
-  __shared__ float abuf[C::WAVES][G];        // rescale factor of the wave's heads
+  using C = DecCfg<D, G>;
+  constexpr int CPB = BLK / C::CK;           // chunks per block
+  __shared__ float pbuf[C::WAVES][C::CK][G];  // P of the wave's current chunk
+  __shared__ float abuf[C::WAVES][G];         // rescale factor of the wave's heads
   __shared__ float mw[C::WAVES][G], lw[C::WAVES][G];
   __shared__ float accw[C::WAVES][G][D];
 
@@ -107,11 +159,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   const int t0 = split * bps, t1 = min(a.kmax, t0 + bps);
   const int64_t s = unit / a.Hkv;
   const int g = unit % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = a.L;
   const uint16_t* kb = a.kc + (int64_t)unit * L * D;
   const uint16_t* vb = a.vc + (int64_t)unit * L * D;
-  const int32_t* irow = a.idx + (int64_t)unit * a.kmax;
+  const CONST_AS int32_t* irow = (const CONST_AS int32_t*)(a.idx + (int64_t)unit * a.kmax);
   const float NEG_INF = -__builtin_inff();
 
   // B operand: column n = lane % 16 is query head n of the group (zero past G),
@@ -133,22 +186,36 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
 
-  for (int t = t0 + wave; t < t1; t += C::WAVES) {
-    const int key0 = irow[t] * BLK;
-    // ---- scores of the BLK keys for the G heads
+  for (int ch = t0 * CPB + wave; ch < t1 * CPB; ch += C::WAVES) {
+    const int blk = irow[ch / CPB];
+    if (blk < 0) continue;  // padding (a shorter row): nothing to attend
+    const int key0 = blk * BLK + (ch % CPB) * C::CK;
+    if (key0 >= L) continue;  // a chunk past the end of a ragged last block
+    // ---- all loads of the chunk first: K as MFMA A operands, V rows
+    u32x4 kf[C::SUB][D / 32];
+    u32x4 vv[C::VPL];
+#pragma unroll
+    for (int sb = 0; sb < C::SUB; ++sb) {
+      const int key = min(key0 + sb * 16 + (lane & 15), L - 1);
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        kf[sb][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (int64_t)key * D + ks * 32 + 8 * lq));
+    }
+#pragma unroll
+    for (int r = 0; r < C::VPL; ++r) {
+      const int key = min(key0 + pk + C::KGR * r, L - 1);
+      vv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (int64_t)key * D + pc * 8));
+    }
+    // ---- scores of the chunk's keys for the G heads
     f32x4 sc[C::SUB];
 #pragma unroll
     for (int sb = 0; sb < C::SUB; ++sb) {
       sc[sb] = (f32x4){0, 0, 0, 0};
-      const int key = key0 + sb * 16 + (lane & 15);
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        u32x4 kf = (u32x4){0, 0, 0, 0};
-        if (key < L) kf = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * D + ks * 32 + 8 * lq);
-        sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), sc[sb], 0, 0, 0);
-      }
+      for (int ks = 0; ks < D / 32; ++ks)
+        sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[sb][ks]), as_bf16x8(qf[ks]), sc[sb], 0, 0, 0);
     }
-    // output: lane holds head column n, keys sb * 16 + 4 * lq + r
+    // output: lane holds head column n, keys sb * 16 + 4 * lq + r (keys past L masked)
     float mloc = NEG_INF;
 #pragma unroll
     for (int sb = 0; sb < C::SUB; ++sb)
@@ -161,7 +228,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
+    const float m_new = fmaxf(m_run, mloc);  // finite: a chunk holds a key below L
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float lsum = 0.f;
@@ -169,9 +236,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
     for (int sb = 0; sb < C::SUB; ++sb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sc[sb][r] - m_run);
-        lsum += p;
-        if (n < G) pbuf[wave][sb * 16 + 4 * lq + r][n] = p;
+        const float pv = __builtin_amdgcn_exp2f(sc[sb][r] - m_run);
+        lsum += pv;
+        if (n < G) pbuf[wave][sb * 16 + 4 * lq + r][n] = pv;
       }
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
@@ -187,21 +254,20 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[hh][e] *= al;
     }
-    for (int kk = pk; kk < BLK; kk += C::KGR) {
-      const int key = key0 + kk;
-      u32x4 vv = (u32x4){0, 0, 0, 0};
-      if (key < L) vv = *reinterpret_cast<const u32x4*>(vb + (int64_t)key * D + pc * 8);
+#pragma unroll
+    for (int r = 0; r < C::VPL; ++r) {
+      const int kk = pk + C::KGR * r;
       float vf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vf[2 * e] = bf16_lo(vv[e]);
-        vf[2 * e + 1] = bf16_hi(vv[e]);
+        vf[2 * e] = bf16_lo(vv[r][e]);
+        vf[2 * e + 1] = bf16_hi(vv[r][e]);
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float p = pbuf[wave][kk][hh];
+        const float pw = pbuf[wave][kk][hh];  // 0 for keys past L
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(p, vf[e], acc[hh][e]);
+        for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(pw, vf[e], acc[hh][e]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -215,6 +281,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = acc[hh][e];
+#pragma unroll
       for (int off = C::CHK; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
       acc[hh][e] = v;
     }
@@ -236,11 +303,11 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
     for (int w = 0; w < C::WAVES; ++w) M = fmaxf(M, mw[w][hh]);
     float v = 0.f;
     if (c == 0) {
-      v = M;
-    } else {
+      v = M;  // -inf: the split attended nothing, and the combine skips it
+    } else if (M != NEG_INF) {
 #pragma unroll
       for (int w = 0; w < C::WAVES; ++w) {
-        const float f = __builtin_amdgcn_exp2f(mw[w][hh] - M);  // 0 for a wave with no block
+        const float f = __builtin_amdgcn_exp2f(mw[w][hh] - M);  // 0 for a wave with no chunk
         v += f * (c == 1 ? lw[w][hh] : accw[w][hh][c - 2]);
       }
     }
@@ -248,85 +315,102 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   }
 }
 
-// ============================================================== 4. combine
+// ============================================================== 3. combine
+// One thread per (unit, head, dim); the split maxima are read first, then the
+// sums and accumulators, all loads independent.
+constexpr int DEC_MAX_SPLITS = 32;
+// Split count aims at about this many attention workgroups: fewer, longer
+// lived waves (each walks several chunks) beat one chunk per wave.
+constexpr int DEC_TARGET_WG = 1024;
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ partial,
                                                              uint16_t* __restrict__ o, float* __restrict__ lse,
-                                                             int Hq, int Hkv, int nsplit) {
+                                                             int Hq, int Hkv, int nsplit, int64_t n_items) {
   const int G = Hq / Hkv;
-  const int unit = blockIdx.x;
-  const int64_t s = unit / Hkv;
-  const int g = unit % Hkv;
-  for (int e = threadIdx.x; e < G * D; e += 256) {
-    const int hh = e / D, dd = e % D;
-    const float* p = partial + ((int64_t)unit * nsplit * G + hh) * (D + 2);
-    const int stride = G * (D + 2);
-    float M = -__builtin_inff();
-    for (int c = 0; c < nsplit; ++c) M = fmaxf(M, p[c * stride]);
-    float l = 0.f, v = 0.f;
-    for (int c = 0; c < nsplit; ++c) {
-      const float f = __builtin_amdgcn_exp2f(p[c * stride] - M);
+  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (unit, hh, dd)
+  if (item >= n_items) return;
+  const int dd = (int)(item % D);
+  const int64_t uh = item / D;
+  const int hh = (int)(uh % G);
+  const int64_t unit = uh / G;
+  const float* p = partial + (unit * nsplit * G + hh) * (D + 2);
+  const int stride = G * (D + 2);
+  float mv[DEC_MAX_SPLITS];
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int c = 0; c < DEC_MAX_SPLITS; ++c) {
+    mv[c] = (c < nsplit) ? p[c * stride] : -__builtin_inff();
+    M = fmaxf(M, mv[c]);
+  }
+  float l = 0.f, v = 0.f;
+#pragma unroll
+  for (int c = 0; c < DEC_MAX_SPLITS; ++c) {
+    if (c < nsplit && mv[c] != -__builtin_inff()) {
+      const float f = __builtin_amdgcn_exp2f(mv[c] - M);
       l += f * p[c * stride + 1];
       v += f * p[c * stride + 2 + dd];
     }
-    const int64_t oh = s * Hq + g * G + hh;
-    o[oh * D + dd] = (uint16_t)f32_to_bf16_rne(v / l);
-    if (lse && dd == 0) lse[oh] = (M + __log2f(l)) * 0.69314718055994531f;
   }
+  const int64_t s = unit / Hkv;
+  const int g = (int)(unit % Hkv);
+  const int64_t oh = s * Hq + g * G + hh;
+  o[oh * D + dd] = (uint16_t)f32_to_bf16_rne(v / l);
+  if (lse && dd == 0) lse[oh] = (M + __log2f(l)) * 0.69314718055994531f;
 }
 
 // ============================================================== launch
 int decode_splits(int S, int Hkv, int kmax) {
   const int64_t units = (int64_t)S * Hkv;
   if (units == 0 || kmax == 0) return 1;
-  int64_t want = (2048 + units - 1) / units;  // aim for >= 2048 workgroups
+  int64_t want = (DEC_TARGET_WG + units - 1) / units;
   if (want < 1) want = 1;
   if (want > kmax) want = kmax;
+  if (want > DEC_MAX_SPLITS) want = DEC_MAX_SPLITS;
   const int bps = (int)((kmax + want - 1) / want);
   return (kmax + bps - 1) / bps;  // every split gets at least one block
 }
 
+template <int D, int G>
+static void launch_select(const DecodeArgs& a, TopkParams p, hipStream_t stream) {
+  const dim3 grid((uint32_t)((int64_t)a.S * a.Hkv)), blk(512);
+  if (a.nB <= 64 * 16)
+    hipLaunchKernelGGL((decode_select_kernel<D, G, 16>), grid, blk, 0, stream, a, p);
+  else
+    hipLaunchKernelGGL((decode_select_kernel<D, G, 64>), grid, blk, 0, stream, a, p);
+}
+
 template <int D, int BLK>
-static hipError_t launch_decode_attn(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_decode_d(const DecodeArgs& a, TopkParams p, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const dim3 grid((uint32_t)((int64_t)a.S * a.Hkv * a.nsplit)), blk(256);
+  switch (G) {
+    case 1: launch_select<D, 1>(a, p, stream); break;
+    case 2: launch_select<D, 2>(a, p, stream); break;
+    case 4: launch_select<D, 4>(a, p, stream); break;
+    case 8: launch_select<D, 8>(a, p, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   switch (G) {
     case 1: hipLaunchKernelGGL((decode_attn_kernel<D, BLK, 1>), grid, blk, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_attn_kernel<D, BLK, 2>), grid, blk, 0, stream, a); break;
     case 4: hipLaunchKernelGGL((decode_attn_kernel<D, BLK, 4>), grid, blk, 0, stream, a); break;
     case 8: hipLaunchKernelGGL((decode_attn_kernel<D, BLK, 8>), grid, blk, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
   }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t items = (int64_t)a.S * a.Hq * D;
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((uint32_t)((items + 255) / 256)), dim3(256), 0, stream,
+                     a.partial, a.o, a.lse, a.Hq, a.Hkv, a.nsplit, items);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int d, TopkParams p, hipStream_t stream) {
-  const int64_t units = (int64_t)a.S * a.Hkv;
-  if (units == 0) return hipSuccess;
-  const int nchunks = (a.nB + 63) / 64;
-  const dim3 g1((uint32_t)(units * nchunks)), b1(256);
-  if (d == 64)
-    hipLaunchKernelGGL(decode_scores_kernel<64>, g1, b1, 0, stream, a.q, a.kbar, a.scores, a.Hq, a.Hkv, a.nB,
-                       a.scale, nchunks);
-  else
-    hipLaunchKernelGGL(decode_scores_kernel<128>, g1, b1, 0, stream, a.q, a.kbar, a.scores, a.Hq, a.Hkv, a.nB,
-                       a.scale, nchunks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = launch_select_topk(a.scores, a.idx, nullptr, units, 1, a.nB, false, p, a.kmax, stream);
-  if (e != hipSuccess) return e;
-  if (d == 64)
-    e = a.block == 64 ? launch_decode_attn<64, 64>(a, stream) : launch_decode_attn<64, 128>(a, stream);
-  else
-    e = a.block == 64 ? launch_decode_attn<128, 64>(a, stream) : launch_decode_attn<128, 128>(a, stream);
-  if (e != hipSuccess) return e;
-  if (d == 64)
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((uint32_t)units), dim3(256), 0, stream, a.partial, a.o, a.lse,
-                       a.Hq, a.Hkv, a.nsplit);
-  else
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((uint32_t)units), dim3(256), 0, stream, a.partial, a.o,
-                       a.lse, a.Hq, a.Hkv, a.nsplit);
-  return hipGetLastError();
+  if ((int64_t)a.S * a.Hkv == 0) return hipSuccess;
+  if (d == 64) return a.block == 64 ? launch_decode_d<64, 64>(a, p, stream) : launch_decode_d<64, 128>(a, p, stream);
+  return a.block == 64 ? launch_decode_d<128, 64>(a, p, stream) : launch_decode_d<128, 128>(a, p, stream);
 }
 
 }  // namespace dsa

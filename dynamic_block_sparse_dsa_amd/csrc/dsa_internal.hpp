@@ -90,7 +90,6 @@ struct DecodeArgs {
   uint16_t* o;         // [S, Hq, d]
   float* lse;          // [S, Hq] or null
   int32_t* idx;        // [S, Hkv, kmax]
-  float* scores;       // workspace [S, Hkv, nB]
   float* partial;      // workspace [S, Hkv, nsplit, G, d + 2]
   int S, Hq, Hkv, L, nB, kmax, nsplit, block;
   float scale;       // 1 / sqrt(d)

@@ -13,6 +13,7 @@
 // The block statistic is mean(Q tile) . mean(K tile) / sqrt(d), so all three
 // kernels work in fp32 on the block means.
 #include "dsa_internal.hpp"
+#include "topk_row.hpp"
 
 namespace dsa {
 
@@ -157,295 +158,40 @@ hipError_t launch_block_scores(const float* qbar, const float* kbar, float* scor
 }
 
 // ============================================================== top-k select
-// One 256-thread workgroup per row.  The row's scores become order-preserving
-// uint32 keys; thread t owns the contiguous run of R = ceil(visible / 256)
-// blocks starting at t * R (index order), which makes the final compaction an
-// exclusive scan.  The m-th largest candidate key is found with a most-
-// significant-digit-first radix select (4 passes of 8 bits, LDS histograms);
-// the candidates above it are kept and, among the ones equal to it, the
-// lowest indices fill the remainder (ties go to the lower block).
-constexpr int TOPK_THREADS = 256;
-constexpr int TOPK_MAX_PER_THREAD = (4096 + TOPK_THREADS - 1) / TOPK_THREADS;  // DSA_MAX_BLOCKS
-
-// inclusive prefix sum over the 256 threads of the workgroup
-__device__ __forceinline__ int block_incl_scan(int v, int* sh_waves) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
-  if (lane == 63) sh_waves[wave] = v;
-  __syncthreads();
-  int add = 0;
-#pragma unroll
-  for (int w = 0; w < TOPK_THREADS / 64; ++w)
-    if (w < wave) add += sh_waves[w];
-  __syncthreads();
-  return v + add;
-}
-
-__global__ __launch_bounds__(TOPK_THREADS) void select_topk_kernel(const float* __restrict__ scores,
-                                                                   int32_t* __restrict__ idx,
-                                                                   int32_t* __restrict__ cnt, int rows_per_unit,
-                                                                   int n_cols, int causal, TopkParams p, int kmax) {
-  __shared__ int hist[256];
-  __shared__ int sh_waves[TOPK_THREADS / 64];
-  __shared__ int sh_digit, sh_rem;
-  const int64_t row = blockIdx.x;
-  const int i = (int)(row % rows_per_unit);
-  const int nv = causal ? i + 1 : n_cols;
-  const int t = threadIdx.x;
-  const int f_sink = (p.flags & 1u) ? 0 : -1;
-  const int f_diag = (p.flags & 2u) ? nv - 1 : -1;
-  const int nf = (f_sink >= 0) + (f_diag >= 0) - (f_sink >= 0 && f_sink == f_diag);
-  int64_t budget = p.topk > 0 ? (int64_t)p.topk : ((int64_t)p.num * nv + p.den - 1) / p.den;
-  if (budget < nf) budget = nf;
-  if (budget > nv) budget = nv;
-  const int m = (int)budget - nf;   // candidates to keep
-  const int ncand = nv - nf;
-  const float* srow = scores + row * (int64_t)n_cols;
-  const int R = (nv + TOPK_THREADS - 1) / TOPK_THREADS;
-  const int j0 = t * R;
-
-  uint32_t key[TOPK_MAX_PER_THREAD];
-  uint32_t candbits = 0;  // bit e: block j0 + e is a candidate
-#pragma unroll
-  for (int e = 0; e < TOPK_MAX_PER_THREAD; ++e) {
-    const int j = j0 + e;
-    key[e] = 0;
-    if (e < R && j < nv && j != f_sink && j != f_diag) {
-      key[e] = order_key(srow[j]);
-      candbits |= 1u << e;
-    }
-  }
-
-  // threshold key T and how many candidates equal to T are kept
-  uint32_t T = 0;
-  int take_eq = 0;
-  bool all = (m >= ncand), none = (m <= 0);
-  if (!all && !none) {
-    uint32_t prefix = 0, pmask = 0;
-    int remaining = m;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[t] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < TOPK_MAX_PER_THREAD; ++e)
-        if (((candbits >> e) & 1u) && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1);
-      __syncthreads();
-      // thread t looks at digit 255 - t; incl = candidates with digit >= it
-      const int dg = 255 - t;
-      const int v = hist[dg];
-      const int incl = block_incl_scan(v, sh_waves);
-      const int excl = incl - v;
-      if (excl < remaining && remaining <= incl) {
-        sh_digit = dg;
-        sh_rem = remaining - excl;
-      }
-      __syncthreads();
-      prefix |= (uint32_t)sh_digit << shift;
-      pmask |= 0xffu << shift;
-      remaining = sh_rem;
-      __syncthreads();
-    }
-    T = prefix;
-    take_eq = remaining;
-  }
-
-  // rank of each equal-to-T candidate among the equal ones, in index order
-  int my_eq = 0;
-  if (!all && !none) {
-#pragma unroll
-    for (int e = 0; e < TOPK_MAX_PER_THREAD; ++e) my_eq += ((candbits >> e) & 1u) && key[e] == T;
-  }
-  const int eq_before = block_incl_scan(my_eq, sh_waves) - my_eq;
-
-  uint32_t selbits = 0;
-  int running_eq = eq_before;
-#pragma unroll
-  for (int e = 0; e < TOPK_MAX_PER_THREAD; ++e) {
-    const int j = j0 + e;
-    if (e >= R || j >= nv) continue;
-    bool s;
-    if (j == f_sink || j == f_diag) {
-      s = true;
-    } else if (all) {
-      s = true;
-    } else if (none) {
-      s = false;
-    } else if (key[e] > T) {
-      s = true;
-    } else if (key[e] == T) {
-      s = running_eq < take_eq;
-      ++running_eq;
-    } else {
-      s = false;
-    }
-    selbits |= (uint32_t)s << e;
-  }
-  const int my_sel = __builtin_popcount(selbits);
-  const int incl = block_incl_scan(my_sel, sh_waves);
-  int pos = incl - my_sel;
-  int32_t* out = idx + row * (int64_t)kmax;
-#pragma unroll
-  for (int e = 0; e < TOPK_MAX_PER_THREAD; ++e)
-    if ((selbits >> e) & 1u) out[pos++] = j0 + e;
-  // total kept = inclusive count of the last thread
-  __shared__ int sh_total;
-  if (t == TOPK_THREADS - 1) sh_total = incl;
-  __syncthreads();
-  const int total = sh_total;
-  for (int e = total + t; e < kmax; e += TOPK_THREADS) out[e] = -1;
-  if (t == 0 && cnt) cnt[row] = total;
-}
-
-// ---------------------------------------------------------------- wave per row
-// The same selection with one 64-lane wave per row (rows of up to 64*R
-// blocks; 4 rows per workgroup).  No workgroup barrier: histograms are per
-// wave in LDS and every scan is a wave-level shuffle scan.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
-  return v;
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
+// One 64-lane wave per row (rows of up to 64 * R blocks), 4 rows per
+// workgroup; the selection itself is wave_select_row (topk_row.hpp).
 template <int R>
 __global__ __launch_bounds__(256) void select_topk_wave_kernel(const float* __restrict__ scores,
                                                                int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
                                                                int64_t n_rows, int rows_per_unit, int n_cols,
                                                                int causal, TopkParams p, int kmax) {
-  __shared__ int hist_all[4][256];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ uint32_t lds_key[4][128];
+  __shared__ int32_t lds_idx[4][128];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= n_rows) return;  // whole wave; no workgroup barrier below
-  int* hist = hist_all[wave];
   const int i = (int)(row % rows_per_unit);
   const int nv = causal ? i + 1 : n_cols;
-  const int f_sink = (p.flags & 1u) ? 0 : -1;
-  const int f_diag = (p.flags & 2u) ? nv - 1 : -1;
-  const int nf = (f_sink >= 0) + (f_diag >= 0) - (f_sink >= 0 && f_sink == f_diag);
-  int64_t budget = p.topk > 0 ? (int64_t)p.topk : ((int64_t)p.num * nv + p.den - 1) / p.den;
-  if (budget < nf) budget = nf;
-  if (budget > nv) budget = nv;
-  const int m = (int)budget - nf;
-  const int ncand = nv - nf;
-  const float* srow = scores + row * (int64_t)n_cols;
-  const int j0 = lane * R;  // this lane owns blocks j0 .. j0+R-1 (index order)
-
-  uint32_t key[R];
-  uint32_t candbits = 0;
-#pragma unroll
-  for (int e = 0; e < R; ++e) {
-    const int j = j0 + e;
-    key[e] = 0;
-    if (j < nv && j != f_sink && j != f_diag) {
-      key[e] = order_key(srow[j]);
-      candbits |= 1u << e;
-    }
-  }
-  const bool all = (m >= ncand), none = (m <= 0);
-  uint32_t T = 0;
-  int take_eq = 0;
-  if (!all && !none) {
-    uint32_t prefix = 0, pmask = 0;
-    int remaining = m;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
-      wave_lds_sync();
-#pragma unroll
-      for (int e = 0; e < R; ++e)
-        if (((candbits >> e) & 1u) && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1);
-      wave_lds_sync();
-      // lane owns digits 255-4*lane-q (q = 0..3): descending order over (lane, q)
-      int c[4], sum = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c[q] = hist[255 - 4 * lane - q];
-        sum += c[q];
-      }
-      const int incl = wave_incl_scan(sum);
-      int before = incl - sum;  // candidates with a larger digit than this lane's first
-      int dg = -1, rem_new = 0;
-      if (before < remaining && remaining <= incl) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (dg < 0 && before + c[q] >= remaining) {
-            dg = 255 - 4 * lane - q;
-            rem_new = remaining - before;
-          }
-          before += c[q];
-        }
-      }
-      const uint64_t who = __ballot(dg >= 0);
-      const int src = max(__ffsll((unsigned long long)who) - 1, 0);  // exactly one lane holds the digit
-      const int digit = __shfl(dg, src, 64);
-      remaining = __shfl(rem_new, src, 64);
-      prefix |= (uint32_t)digit << shift;
-      pmask |= 0xffu << shift;
-      wave_lds_sync();
-    }
-    T = prefix;
-    take_eq = remaining;
-  }
-
-  int my_eq = 0;
-  if (!all && !none) {
-#pragma unroll
-    for (int e = 0; e < R; ++e) my_eq += ((candbits >> e) & 1u) && key[e] == T;
-  }
-  int running_eq = wave_incl_scan(my_eq) - my_eq;
-  uint32_t selbits = 0;
-#pragma unroll
-  for (int e = 0; e < R; ++e) {
-    const int j = j0 + e;
-    if (j >= nv) continue;
-    bool s;
-    if (j == f_sink || j == f_diag) s = true;
-    else if (all) s = true;
-    else if (none) s = false;
-    else if (key[e] > T) s = true;
-    else if (key[e] == T) { s = running_eq < take_eq; ++running_eq; }
-    else s = false;
-    selbits |= (uint32_t)s << e;
-  }
-  const int my_sel = __builtin_popcount(selbits);
-  const int incl = wave_incl_scan(my_sel);
-  int pos = incl - my_sel;
-  const int total = __shfl(incl, 63, 64);
-  int32_t* out = idx + row * (int64_t)kmax;
-#pragma unroll
-  for (int e = 0; e < R; ++e)
-    if ((selbits >> e) & 1u) out[pos++] = j0 + e;
-  for (int e = total + lane; e < kmax; e += 64) out[e] = -1;
-  if (lane == 0 && cnt) cnt[row] = total;
+  const int total = wave_select_row<R>(scores + row * (int64_t)n_cols, nv, p, idx + row * (int64_t)kmax, kmax,
+                                       lds_key[wave], lds_idx[wave]);
+  if ((threadIdx.x & 63) == 0 && cnt) cnt[row] = total;
 }
 
 hipError_t launch_select_topk(const float* scores, int32_t* idx, int32_t* cnt, int64_t n_rows, int rows_per_unit,
                               int n_cols, bool causal, TopkParams p, int kmax, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   const int longest = causal ? rows_per_unit : n_cols;
-  const dim3 wave_grid((uint32_t)((n_rows + 3) / 4)), wave_block(256);
+  const dim3 grid((uint32_t)((n_rows + 3) / 4)), block(256);
+  const int c = causal ? 1 : 0;
   if (longest <= 64 * 4)
-    hipLaunchKernelGGL(select_topk_wave_kernel<4>, wave_grid, wave_block, 0, stream, scores, idx, cnt, n_rows,
-                       rows_per_unit, n_cols, causal ? 1 : 0, p, kmax);
+    hipLaunchKernelGGL(select_topk_wave_kernel<4>, grid, block, 0, stream, scores, idx, cnt, n_rows, rows_per_unit,
+                       n_cols, c, p, kmax);
   else if (longest <= 64 * 16)
-    hipLaunchKernelGGL(select_topk_wave_kernel<16>, wave_grid, wave_block, 0, stream, scores, idx, cnt, n_rows,
-                       rows_per_unit, n_cols, causal ? 1 : 0, p, kmax);
+    hipLaunchKernelGGL(select_topk_wave_kernel<16>, grid, block, 0, stream, scores, idx, cnt, n_rows, rows_per_unit,
+                       n_cols, c, p, kmax);
   else
-    hipLaunchKernelGGL(select_topk_kernel, dim3((uint32_t)n_rows), dim3(TOPK_THREADS), 0, stream, scores, idx, cnt,
-                       rows_per_unit, n_cols, causal ? 1 : 0, p, kmax);
+    hipLaunchKernelGGL(select_topk_wave_kernel<64>, grid, block, 0, stream, scores, idx, cnt, n_rows, rows_per_unit,
+                       n_cols, c, p, kmax);
   return hipGetLastError();
 }
 

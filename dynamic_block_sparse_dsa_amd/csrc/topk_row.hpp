@@ -1,0 +1,283 @@
+// Top-k selection of one row by one wavefront (shared by the prefill select
+// kernel and the fused decode select kernel).
+//
+// Method: "dynamic sparse attention explainer" (zblog.xzdbk.com/559.html),
+// "基于Top-k选择的局部-全局混合": keep the k best-scoring blocks plus the
+// anchors (the sink block 0 and the row's own, last visible block).
+//
+// Lane l owns the contiguous run of R blocks starting at l * R (index order),
+// so the final compaction is an exclusive scan.  Each visible non-forced
+// block is a candidate whose score becomes an order-preserving uint32 key.
+// The m-th largest candidate key T is found by a most-significant-bit-first
+// search over the key bits: starting from the common prefix of the largest and
+// smallest candidate key, each step tries to set the next bit and keeps it
+// when at least m candidates are >= the trial value.  A count is R vector
+// compares into wave masks whose bits the scalar unit counts, so the search
+// needs no LDS and no barrier, and all its control flow is wave-uniform.
+// When a trial value has exactly m candidates at or above it, those are the
+// answer and the search stops early; otherwise the candidates above T are
+// kept and, among the ones equal to T, the lowest indices fill the rest
+// (ties go to the lower block).
+//
+// Fast path (R >= 16, m <= 64): each lane splits its keys into 4 groups; the
+// m-th largest of the 256 group maxima, t0, is a lower bound of T (m distinct
+// keys are >= t0).  Only candidates >= t0 can be kept; when there are at most
+// 128 of them they are compacted in index order through 1 KiB of LDS, two per
+// lane, and the same search runs on those.  The forced blocks are the smallest (sink 0) and the largest (the
+// row's own block) visible indices, so they go first and last.
+#pragma once
+
+#include "dsa_internal.hpp"
+
+namespace dsa {
+
+// number of keys >= c over the R keys of each of the 64 lanes (all active):
+// one compare per key into a wave mask, counted on the scalar unit, so the
+// result is wave-uniform
+template <int R>
+__device__ __forceinline__ int wave_count_ge(const uint32_t (&key)[R], uint32_t c) {
+  int n = 0;
+#pragma unroll
+  for (int e = 0; e < R; ++e) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[e] >= c));
+  return n;
+}
+
+// inclusive prefix sum over the 64 lanes (all active): DPP shifts by 1, 2,
+// 4, 8 within each row of 16 lanes, then the row totals broadcast forward
+// (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3)
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// max / min over the 64 lanes, returned as wave-uniform values: DPP within
+// rows of 16 lanes, then the four row results through readlane
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// lanes below this one whose bit is set in mask
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// Largest T >= 1 with at least m of the values v[0..C-1] of the 64 lanes
+// >= T (0 if fewer than m values are >= 1; a 0 never counts).  *exact is set
+// when exactly m values are >= T.
+template <int C>
+__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&v)[C], int m, bool* exact) {
+  uint32_t T = 0;
+  *exact = false;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t trial = T | (1u << b);
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[c] >= trial));
+    if (n >= m) {
+      T = trial;
+      if (n == m) {
+        *exact = true;
+        break;
+      }
+    }
+  }
+  return T;
+}
+
+// Select from the scores of blocks 0 .. nv-1, nv <= 64 * R.  Without LDS_T,
+// srow[j] is block j's score (global or LDS); with LDS_T, srow is an LDS
+// array of 64 * R scores laid out so that block j = l * R + e sits at
+// srow[e * 64 + l] (conflict-free reads), entries past nv are ignored.
+// Writes the kept blocks ascending to out[0 ..], pads out[.. kmax-1] with -1
+// and returns the number kept.  Called by all 64 lanes of one wave; lds_key
+// and lds_idx are 128-entry LDS arrays private to the wave.
+template <int R, bool LDS_T = false>
+__device__ int wave_select_row(const float* srow, int nv, TopkParams p, int32_t* out, int kmax, uint32_t* lds_key,
+                               int32_t* lds_idx) {
+  const int lane = threadIdx.x & 63;
+  const int f_sink = (p.flags & 1u) ? 0 : -1;
+  const int f_diag = (p.flags & 2u) ? nv - 1 : -1;
+  const int nf = (f_sink >= 0) + (f_diag >= 0) - (f_sink >= 0 && f_sink == f_diag);
+  int64_t budget = p.topk > 0 ? (int64_t)p.topk : ((int64_t)p.num * nv + p.den - 1) / p.den;
+  if (budget < nf) budget = nf;
+  if (budget > nv) budget = nv;
+  const int m = (int)budget - nf;  // candidates to keep
+  const int ncand = nv - nf;
+  const int j0 = lane * R;
+
+  // key 0 marks a non-candidate in the counts: every trial value is >= 1
+  uint32_t key[R];
+  uint32_t candbits[(R + 31) / 32];
+  uint32_t kmx = 0, kmn = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < (R + 31) / 32; ++w) candbits[w] = 0;
+  float sv[R];
+  if constexpr (LDS_T) {
+    const __attribute__((address_space(3))) float* st = (const __attribute__((address_space(3))) float*)srow;
+#pragma unroll
+    for (int e = 0; e < R; ++e) sv[e] = st[e * 64 + lane];
+  }
+#pragma unroll
+  for (int e = 0; e < R; ++e) {
+    const int j = j0 + e;
+    key[e] = 0;
+    if (j < nv && j != f_sink && j != f_diag) {
+      key[e] = order_key(LDS_T ? sv[e] : srow[j]);
+      candbits[e / 32] |= 1u << (e % 32);
+      kmx = max(kmx, key[e]);
+      kmn = min(kmn, key[e]);
+    }
+  }
+
+  const bool all = (m >= ncand), none = (m <= 0);
+  if (R >= 16 && !all && !none && m <= 64) {
+    constexpr int GS = R / 4;  // keys per group
+    uint32_t gmax[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      gmax[g] = 0;
+#pragma unroll
+      for (int e = g * GS; e < (g + 1) * GS; ++e) gmax[g] = max(gmax[g], key[e]);  // 0 for non-candidates
+    }
+    bool ex;
+    const uint32_t t0 = wave_kth_largest<4>(gmax, m, &ex);
+    int mine = 0;  // this lane's candidates >= t0
+#pragma unroll
+    for (int e = 0; e < R; ++e) mine += ((candbits[e / 32] >> (e % 32)) & 1u) && key[e] >= t0;
+    const int incl = wave_incl_scan(mine);
+    const int ns = __builtin_amdgcn_readlane(incl, 63);
+    if (t0 > 0 && ns <= 128) {
+      int q = incl - mine;
+#pragma unroll
+      for (int e = 0; e < R; ++e)
+        if (((candbits[e / 32] >> (e % 32)) & 1u) && key[e] >= t0) {
+          lds_key[q] = key[e];
+          lds_idx[q] = j0 + e;
+          ++q;
+        }
+      wave_lds_sync();
+      // survivor positions lane and 64 + lane, in index order
+      const bool ok0 = lane < ns, ok1 = lane + 64 < ns;
+      const uint32_t k0 = ok0 ? lds_key[lane] : 0u, k1 = ok1 ? lds_key[64 + lane] : 0u;
+      const int i0 = ok0 ? lds_idx[lane] : -1, i1 = ok1 ? lds_idx[64 + lane] : -1;
+      wave_lds_sync();
+      bool exact;
+      const uint32_t kk[2] = {k0, k1};  // all >= t0 >= 1 where valid
+      const uint32_t T = wave_kth_largest<2>(kk, m, &exact);
+      const int n_gt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok0 && k0 > T)) +
+                       __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok1 && k1 > T));
+      const uint64_t eq0 = __builtin_amdgcn_ballot_w64(ok0 && k0 == T);
+      const uint64_t eq1 = __builtin_amdgcn_ballot_w64(ok1 && k1 == T);
+      const int take_eq = exact ? 128 : m - n_gt;
+      const bool s0 = ok0 && (k0 > T || (k0 == T && lanes_below(eq0) < take_eq));
+      const bool s1 = ok1 && (k1 > T || (k1 == T && __builtin_popcountll(eq0) + lanes_below(eq1) < take_eq));
+      const uint64_t sm0 = __builtin_amdgcn_ballot_w64(s0), sm1 = __builtin_amdgcn_ballot_w64(s1);
+      const int base = f_sink >= 0 ? 1 : 0;
+      const int nsel = __builtin_popcountll(sm0) + __builtin_popcountll(sm1);
+      if (s0) out[base + lanes_below(sm0)] = i0;
+      if (s1) out[base + __builtin_popcountll(sm0) + lanes_below(sm1)] = i1;
+      if (lane == 0) {
+        if (f_sink >= 0) out[0] = f_sink;
+        if (f_diag >= 0 && f_diag != f_sink) out[base + nsel] = f_diag;
+      }
+      const int total = base + nsel + (f_diag >= 0 && f_diag != f_sink ? 1 : 0);
+      for (int e = total + lane; e < kmax; e += 64) out[e] = -1;
+      return total;
+    }
+  }
+
+  uint32_t T = 0;
+  int take_eq = 0x7fffffff;  // candidates equal to T that are kept, in index order
+  if (!all && !none) {
+    const uint32_t hi = wave_max_u32(kmx), lo = wave_min_u32(kmn);
+    const uint32_t diff = hi ^ lo;
+    bool exact = false;
+    if (diff == 0) {
+      T = lo;  // every candidate has the same key
+    } else {
+      const int top = 31 - __builtin_clz(diff);
+      T = top == 31 ? 0u : hi & ~((2u << top) - 1u);  // common prefix: T <= lo, all candidates >= T
+      for (int b = top; b >= 0; --b) {
+        const uint32_t trial = T | (1u << b);
+        const int n_ge = wave_count_ge<R>(key, trial);
+        if (n_ge >= m) {
+          T = trial;
+          if (n_ge == m) {
+            exact = true;
+            break;
+          }
+        }
+      }
+    }
+    if (!exact) {
+      // T is the m-th largest candidate key: keep the ones above it, then ties
+      take_eq = T == 0xffffffffu ? m : m - wave_count_ge<R>(key, T + 1u);
+    }
+  }
+
+  // rank of each equal-to-T candidate among the equal ones, in index order
+  int my_eq = 0;
+  if (!all && !none) {
+#pragma unroll
+    for (int e = 0; e < R; ++e) my_eq += ((candbits[e / 32] >> (e % 32)) & 1u) && key[e] == T;
+  }
+  int running_eq = wave_incl_scan(my_eq) - my_eq;
+
+  uint32_t selbits[(R + 31) / 32];
+#pragma unroll
+  for (int w = 0; w < (R + 31) / 32; ++w) selbits[w] = 0;
+#pragma unroll
+  for (int e = 0; e < R; ++e) {
+    const int j = j0 + e;
+    if (j >= nv) continue;
+    const bool cand = (candbits[e / 32] >> (e % 32)) & 1u;
+    bool s;
+    if (!cand) s = true;  // forced
+    else if (all) s = true;
+    else if (none) s = false;
+    else if (key[e] > T) s = true;
+    else if (key[e] == T) {
+      s = running_eq < take_eq;
+      ++running_eq;
+    } else s = false;
+    selbits[e / 32] |= (uint32_t)s << (e % 32);
+  }
+  int my_sel = 0;
+#pragma unroll
+  for (int w = 0; w < (R + 31) / 32; ++w) my_sel += __builtin_popcount(selbits[w]);
+  const int incl = wave_incl_scan(my_sel);
+  int pos = incl - my_sel;
+#pragma unroll
+  for (int e = 0; e < R; ++e)
+    if ((selbits[e / 32] >> (e % 32)) & 1u) out[pos++] = j0 + e;
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  for (int e = total + lane; e < kmax; e += 64) out[e] = -1;
+  return total;
+}
+
+}  // namespace dsa

@@ -204,8 +204,8 @@ def test_zero_queries_take_lowest_blocks(cuda_device):
 def test_select_topk_exact_with_ties(cuda_device, nb, topk, num, den, flags):
     """dsa_select_topk on integer-valued scores (many exact ties) equals the
     oracle's selection exactly: the tie rule (lower block first) and the
-    budget are the same on both sides.  Covers the 64-lane variants (rows up
-    to 256 and 1024 blocks) and the workgroup variant (longer rows)."""
+    budget are the same on both sides.  Covers rows up to 256, 1024 and
+    4096 blocks (4, 16 and 64 keys per lane)."""
     say(f"select exact nb{nb} k{topk} {num}/{den} flags{flags}")
     rng = np.random.default_rng(nb + topk)
     raw = rng.integers(-6, 6, size=(1, 2, nb, nb)).astype(np.float32)
@@ -223,9 +223,32 @@ def test_select_topk_exact_with_ties(cuda_device, nb, topk, num, den, flags):
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
 
 
+@pytest.mark.parametrize("nb,topk,flags", [(1024, 66, 3), (1024, 67, 3), (300, 16, 3), (3000, 40, 1), (200, 64, 0),
+                                           (200, 65, 0), (1024, 2, 2)])
+def test_select_topk_distinct_scores(cuda_device, nb, topk, flags):
+    """dsa_select_topk on continuous random scores equals the oracle exactly,
+    with the number of free picks on both sides of 64 (the one-key-per-lane
+    path and the full search), short and long rows."""
+    say(f"select distinct nb{nb} k{topk} flags{flags}")
+    rng = np.random.default_rng(7 * nb + topk)
+    raw = rng.standard_normal(size=(1, 2, nb, nb)).astype(np.float32)
+    causal = np.tril(np.ones((nb, nb), dtype=bool))
+    sc = np.where(causal, raw, -np.inf).astype(np.float32)
+    shape = dsa.make_shape(1, 2, 2, nb * 64, 128, 64, topk, 0, 1, flags)
+    km = dsa.dsa_prefill_kmax(shape)
+    scores = torch.from_numpy(sc).to(cuda_device)
+    idx = torch.empty((1, 2, nb, km), dtype=torch.int32, device=cuda_device)
+    cnt = torch.empty((1, 2, nb), dtype=torch.int32, device=cuda_device)
+    dsa.dsa_select_topk(shape, scores, idx, cnt)
+    torch.cuda.synchronize()
+    ref_idx, ref_cnt, _ = O.select_topk(sc.astype(np.float64), topk, 0, 1, flags)
+    assert np.array_equal(cnt.cpu().numpy(), ref_cnt)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
 def test_prefill_rows_longer_than_1024_blocks(cuda_device):
-    """N = 64 * 1300: selection rows longer than 1024 blocks (workgroup
-    select), checked on every row; attention on sampled query blocks."""
+    """N = 64 * 1300: selection rows longer than 1024 blocks (64 keys per
+    lane), checked on every row; attention on sampled query blocks."""
     w = Workload("long", "prefill", 1, 2, 1, 64 * 1300, 64, 64, 8, seed=60)
     say("prefill nB=1300")
     q, k, v = make_prefill(w, device=cuda_device)
