@@ -55,17 +55,19 @@ def check_rows(rows, gidx, gcnt):
             flagged += 1
             ok, why = O.accepts(rs, got)
             assert ok, (r, why)
+    say(f"selection: {len(rows)} rows, {flagged} near-tie flagged (accepted set), 0 unflagged mismatches")
     return flagged, len(rows)
 
 
 def check_out(o_gpu, o_ref, lse_gpu=None, lse_ref=None, what=""):
     err = np.abs(o_gpu - o_ref)
     assert np.isfinite(o_gpu).all(), what
+    lerr = np.abs(lse_gpu - lse_ref).max() if lse_gpu is not None else float("nan")
+    say(f"error {what}: O max-abs {err.max():.3g} mean-abs {err.mean():.3g}, LSE max-abs {lerr:.3g}")
     assert err.max() <= O_MAX, (what, err.max())
     assert err.mean() <= O_MEAN, (what, err.mean())
     if lse_gpu is not None:
-        lerr = np.abs(lse_gpu - lse_ref)
-        assert lerr.max() <= LSE_ABS, (what, lerr.max())
+        assert lerr <= LSE_ABS, (what, lerr)
     return err.max(), err.mean()
 
 
