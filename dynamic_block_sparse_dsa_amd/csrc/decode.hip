@@ -47,25 +47,27 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Score every block of one (sequence, KV head) unit into LDS and select its
+// kept blocks (written ascending to out, -1 padded to kmax; out may be
+// global or LDS).  All NT = 512 threads of the workgroup take part.  Scores:
+// block l * R + e at sc[e * 64 + l].  Returns after a workgroup barrier; the
+// selection itself is complete only after the next barrier.
 template <int D, int G, int R>
-__global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a, TopkParams p) {
+__device__ __forceinline__ void score_and_select(const DecodeArgs& a, const TopkParams& p, int unit, float* sc,
+                                                 uint32_t* lds_key, int32_t* lds_idx, int* next_batch,
+                                                 int32_t* out) {
   constexpr int NT = 512, NW = NT / 64;
   constexpr int TPR = D / 8;       // lanes per block row (8 floats each)
   constexpr int WROWS = 64 / TPR;  // rows per wave per pass
   constexpr int UNR = 8;           // passes per batch
   constexpr int BR = WROWS * UNR;  // rows per batch (16 KiB of fp32 means at d = 128)
-  __shared__ float sc[64 * R];     // scores, block l * R + e at e * 64 + l
-  __shared__ uint32_t lds_key[128];
-  __shared__ int32_t lds_idx[128];
-  __shared__ int next_batch;
-  const int unit = blockIdx.x;
   const int64_t s = unit / a.Hkv;
   const int g = unit % a.Hkv;
   const int t = threadIdx.x, lane = t & 63, c = lane % TPR, rl = lane / TPR;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int nB = a.nB;
   const int nbatch = (nB + BR - 1) / BR;
-  if (t == 0) next_batch = NW;  // batches 0 .. NW-1 go to the waves in order
+  if (t == 0) *next_batch = NW;  // batches 0 .. NW-1 go to the waves in order
   __syncthreads();
 
   float qv[G][8];
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a, TopkPa
   };
   auto grab = [&]() {
     int v = 0;
-    if (lane == 0) v = atomicAdd(&next_batch, 1);
+    if (lane == 0) v = atomicAdd(next_batch, 1);
     return __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
   };
   f32x4 k0[UNR][2], k1[UNR][2];
@@ -128,15 +130,23 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a, TopkPa
     b1 = grab();
   }
   __syncthreads();
-  if (t < 64)  // one wave selects
-    wave_select_row<R, true>(sc, nB, p, a.idx + (int64_t)unit * a.kmax, a.kmax, lds_key, lds_idx);
+  if (t < 64) wave_select_row<R, true>(sc, nB, p, out, a.kmax, lds_key, lds_idx);  // one wave selects
 }
 
-// ============================================================== 2. split attention
+template <int D, int G, int R>
+__global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a, TopkParams p) {
+  __shared__ float sc[64 * R];
+  __shared__ uint32_t lds_key[128];
+  __shared__ int32_t lds_idx[128];
+  __shared__ int next_batch;
+  score_and_select<D, G, R>(a, p, blockIdx.x, sc, lds_key, lds_idx, &next_batch,
+                            a.idx + (int64_t)blockIdx.x * a.kmax);
+}
+
+// ============================================================== 2. attention
 // Work unit of a wave: a 32-key chunk of a kept block.
 template <int D, int G>
 struct DecCfg {
-  static constexpr int WAVES = 4;
   static constexpr int CK = 32;           // keys per chunk
   static constexpr int CHK = D / 8;       // 16-byte pieces per row
   static constexpr int KGR = 64 / CHK;    // key groups in a wave for P V
@@ -144,86 +154,87 @@ struct DecCfg {
   static constexpr int VPL = CK / KGR;    // V rows per lane
 };
 
-template <int D, int BLK, int G>
-__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
+// the loaded K (MFMA A operands) and V rows of one chunk
+template <int D, int G>
+struct ChunkRegs {
   using C = DecCfg<D, G>;
-  constexpr int CPB = BLK / C::CK;           // chunks per block
-  __shared__ float pbuf[C::WAVES][C::CK][G];  // P of the wave's current chunk
-  __shared__ float abuf[C::WAVES][G];         // rescale factor of the wave's heads
-  __shared__ float mw[C::WAVES][G], lw[C::WAVES][G];
-  __shared__ float accw[C::WAVES][G][D];
+  u32x4 kf[C::SUB][D / 32];
+  u32x4 vv[C::VPL];
+};
 
-  const int unit = blockIdx.x / a.nsplit;
-  const int split = blockIdx.x % a.nsplit;
-  const int bps = (a.kmax + a.nsplit - 1) / a.nsplit;
-  const int t0 = split * bps, t1 = min(a.kmax, t0 + bps);
-  const int64_t s = unit / a.Hkv;
-  const int g = unit % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int L = a.L;
-  const uint16_t* kb = a.kc + (int64_t)unit * L * D;
-  const uint16_t* vb = a.vc + (int64_t)unit * L * D;
-  const CONST_AS int32_t* irow = (const CONST_AS int32_t*)(a.idx + (int64_t)unit * a.kmax);
-  const float NEG_INF = -__builtin_inff();
-
-  // B operand: column n = lane % 16 is query head n of the group (zero past G),
-  // slots 8 * (lane / 16) + e <-> dims ks * 32 + 8 * (lane / 16) + e
-  const int n = lane & 15, lq = lane >> 4;
+// One wave's online-softmax state for the G query heads of a unit, and the
+// per-chunk work.  Q K^T on v_mfma_f32_16x16x32_bf16 (key rows as the A
+// operand, heads as B columns); P goes through a per-wave LDS row to the
+// P V layout (lane owns 8 dims of a key group), P V in fp32 VALU.
+template <int D, int G>
+struct WaveAttn {
+  using C = DecCfg<D, G>;
   u32x4 qf[D / 32];
+  float m_run, l_run;  // head n's state (lanes with n < G)
+  float acc[G][8];
+  int lane, n, lq, pc, pk;
+
+  __device__ __forceinline__ void init(const DecodeArgs& a, int64_t s, int g) {
+    lane = threadIdx.x & 63;
+    n = lane & 15;
+    lq = lane >> 4;
+    pc = lane % C::CHK;
+    pk = lane / C::CHK;
+    // B operand: column n = lane % 16 is query head n of the group (zero past
+    // G), slots 8 * (lane / 16) + e <-> dims ks * 32 + 8 * (lane / 16) + e
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    qf[ks] = (u32x4){0, 0, 0, 0};
-    if (n < G) qf[ks] = *reinterpret_cast<const u32x4*>(a.q + (s * a.Hq + g * G + n) * (int64_t)D + ks * 32 + 8 * lq);
+    for (int ks = 0; ks < D / 32; ++ks) {
+      qf[ks] = (u32x4){0, 0, 0, 0};
+      if (n < G)
+        qf[ks] = *reinterpret_cast<const u32x4*>(a.q + (s * a.Hq + g * G + n) * (int64_t)D + ks * 32 + 8 * lq);
+    }
+    m_run = -__builtin_inff();
+    l_run = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
   }
 
-  float m_run = NEG_INF, l_run = 0.f;  // head n's state (lanes with n < G)
-  // P V: lane owns dims 8 * (lane % CHK) .. +7 for keys lane / CHK + KGR * r
-  const int pc = lane % C::CHK, pk = lane / C::CHK;
-  float acc[G][8];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-
-  for (int ch = t0 * CPB + wave; ch < t1 * CPB; ch += C::WAVES) {
-    const int blk = irow[ch / CPB];
-    if (blk < 0) continue;  // padding (a shorter row): nothing to attend
-    const int key0 = blk * BLK + (ch % CPB) * C::CK;
-    if (key0 >= L) continue;  // a chunk past the end of a ragged last block
-    // ---- all loads of the chunk first: K as MFMA A operands, V rows
-    u32x4 kf[C::SUB][D / 32];
-    u32x4 vv[C::VPL];
+  // issue every load of the chunk starting at key0 (keys clamped to L-1)
+  __device__ __forceinline__ void load(ChunkRegs<D, G>& r, const uint16_t* kb, const uint16_t* vb, int key0,
+                                       int L) const {
 #pragma unroll
     for (int sb = 0; sb < C::SUB; ++sb) {
       const int key = min(key0 + sb * 16 + (lane & 15), L - 1);
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
-        kf[sb][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (int64_t)key * D + ks * 32 + 8 * lq));
+        r.kf[sb][ks] =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (int64_t)key * D + ks * 32 + 8 * lq));
     }
 #pragma unroll
-    for (int r = 0; r < C::VPL; ++r) {
-      const int key = min(key0 + pk + C::KGR * r, L - 1);
-      vv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (int64_t)key * D + pc * 8));
+    for (int v = 0; v < C::VPL; ++v) {
+      const int key = min(key0 + pk + C::KGR * v, L - 1);
+      r.vv[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (int64_t)key * D + pc * 8));
     }
-    // ---- scores of the chunk's keys for the G heads
+  }
+
+  // fold the chunk into the state; pbuf / abuf are this wave's LDS rows
+  __device__ __forceinline__ void step(const ChunkRegs<D, G>& r, int key0, int L, float scale_log2,
+                                       float (*pbuf)[G], float* abuf) {
+    const float NEG_INF = -__builtin_inff();
     f32x4 sc[C::SUB];
 #pragma unroll
     for (int sb = 0; sb < C::SUB; ++sb) {
       sc[sb] = (f32x4){0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
-        sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[sb][ks]), as_bf16x8(qf[ks]), sc[sb], 0, 0, 0);
+        sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.kf[sb][ks]), as_bf16x8(qf[ks]), sc[sb], 0, 0, 0);
     }
-    // output: lane holds head column n, keys sb * 16 + 4 * lq + r (keys past L masked)
+    // output: lane holds head column n, keys sb * 16 + 4 * lq + j (keys past L masked)
     float mloc = NEG_INF;
 #pragma unroll
     for (int sb = 0; sb < C::SUB; ++sb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + sb * 16 + 4 * lq + r;
-        const float x = (key < L) ? sc[sb][r] * a.scale_log2 : NEG_INF;
-        sc[sb][r] = x;
+      for (int j = 0; j < 4; ++j) {
+        const int key = key0 + sb * 16 + 4 * lq + j;
+        const float x = (key < L) ? sc[sb][j] * scale_log2 : NEG_INF;
+        sc[sb][j] = x;
         mloc = fmaxf(mloc, x);
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
@@ -235,37 +246,37 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
 #pragma unroll
     for (int sb = 0; sb < C::SUB; ++sb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(sc[sb][r] - m_run);
+      for (int j = 0; j < 4; ++j) {
+        const float pv = __builtin_amdgcn_exp2f(sc[sb][j] - m_run);
         lsum += pv;
-        if (n < G) pbuf[wave][sb * 16 + 4 * lq + r][n] = pv;
+        if (n < G) pbuf[sb * 16 + 4 * lq + j][n] = pv;
       }
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
     l_run = l_run * alpha + lsum;
-    if (lane < G) abuf[wave][lane] = alpha;
+    if (lane < G) abuf[lane] = alpha;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // ---- acc = alpha * acc + P V
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float al = abuf[wave][hh];
+      const float al = abuf[hh];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[hh][e] *= al;
     }
 #pragma unroll
-    for (int r = 0; r < C::VPL; ++r) {
-      const int kk = pk + C::KGR * r;
+    for (int v = 0; v < C::VPL; ++v) {
+      const int kk = pk + C::KGR * v;
       float vf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vf[2 * e] = bf16_lo(vv[r][e]);
-        vf[2 * e + 1] = bf16_hi(vv[r][e]);
+        vf[2 * e] = bf16_lo(r.vv[v][e]);
+        vf[2 * e + 1] = bf16_hi(r.vv[v][e]);
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float pw = pbuf[wave][kk][hh];  // 0 for keys past L
+        const float pw = pbuf[kk][hh];  // 0 for keys past L
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(pw, vf[e], acc[hh][e]);
       }
@@ -275,38 +286,86 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- reduce the key groups of the wave, then merge the 4 waves
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[hh][e];
-#pragma unroll
-      for (int off = C::CHK; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-      acc[hh][e] = v;
-    }
-  if (lane < G) {
-    mw[wave][lane] = m_run;
-    lw[wave][lane] = l_run;
-  }
-  if (pk == 0) {
+  // reduce the wave's key groups and leave (max, sum, acc[d]) per head in LDS
+  __device__ __forceinline__ void to_lds(float* mw, float* lw, float (*accw)[D]) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) accw[wave][hh][pc * 8 + e] = acc[hh][e];
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[hh][e];
+#pragma unroll
+        for (int off = C::CHK; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+        acc[hh][e] = v;
+      }
+    if (lane < G) {
+      mw[lane] = m_run;
+      lw[lane] = l_run;
+    }
+    if (pk == 0) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) accw[hh][pc * 8 + e] = acc[hh][e];
+    }
   }
+};
+
+// ------------------------------------------------------------ split path
+// Split-K over the kept blocks, one 256-thread workgroup per (unit, split),
+// one chunk per wave at a time; the workgroup writes a partial per head.
+constexpr int DEC_MAX_SPLITS = 32;
+// Split count aims at about this many attention workgroups: fewer, longer
+// lived waves (each walks several chunks) beat one chunk per wave.
+constexpr int DEC_TARGET_WG = 1024;
+
+template <int D, int BLK, int G>
+__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
+  using C = DecCfg<D, G>;
+  constexpr int WAVES = 4;
+  constexpr int CPB = BLK / C::CK;         // chunks per block
+  __shared__ float pbuf[WAVES][C::CK][G];  // P of the wave's current chunk
+  __shared__ float abuf[WAVES][G];         // rescale factor of the wave's heads
+  __shared__ float mw[WAVES][G], lw[WAVES][G];
+  __shared__ float accw[WAVES][G][D];
+
+  const int unit = blockIdx.x / a.nsplit;
+  const int split = blockIdx.x % a.nsplit;
+  const int bps = (a.kmax + a.nsplit - 1) / a.nsplit;
+  const int t0 = split * bps, t1 = min(a.kmax, t0 + bps);
+  const int64_t s = unit / a.Hkv;
+  const int g = unit % a.Hkv;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int L = a.L;
+  const uint16_t* kb = a.kc + (int64_t)unit * L * D;
+  const uint16_t* vb = a.vc + (int64_t)unit * L * D;
+  const CONST_AS int32_t* irow = (const CONST_AS int32_t*)(a.idx + (int64_t)unit * a.kmax);
+  const float NEG_INF = -__builtin_inff();
+
+  WaveAttn<D, G> wa;
+  wa.init(a, s, g);
+  ChunkRegs<D, G> r;
+  for (int ch = t0 * CPB + wave; ch < t1 * CPB; ch += WAVES) {
+    const int blk = irow[ch / CPB];
+    if (blk < 0) continue;  // padding (a shorter row): nothing to attend
+    const int key0 = blk * BLK + (ch % CPB) * C::CK;
+    if (key0 >= L) continue;  // a chunk past the end of a ragged last block
+    wa.load(r, kb, vb, key0, L);
+    wa.step(r, key0, L, a.scale_log2, pbuf[wave], abuf[wave]);
+  }
+  wa.to_lds(mw[wave], lw[wave], accw[wave]);
   __syncthreads();
   for (int e = tid; e < G * (D + 2); e += 256) {
     const int hh = e / (D + 2), c = e % (D + 2);
     float M = NEG_INF;
 #pragma unroll
-    for (int w = 0; w < C::WAVES; ++w) M = fmaxf(M, mw[w][hh]);
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mw[w][hh]);
     float v = 0.f;
     if (c == 0) {
       v = M;  // -inf: the split attended nothing, and the combine skips it
     } else if (M != NEG_INF) {
 #pragma unroll
-      for (int w = 0; w < C::WAVES; ++w) {
+      for (int w = 0; w < WAVES; ++w) {
         const float f = __builtin_amdgcn_exp2f(mw[w][hh] - M);  // 0 for a wave with no chunk
         v += f * (c == 1 ? lw[w][hh] : accw[w][hh][c - 2]);
       }
@@ -315,14 +374,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   }
 }
 
-// ============================================================== 3. combine
 // One thread per (unit, head, dim); the split maxima are read first, then the
 // sums and accumulators, all loads independent.
-constexpr int DEC_MAX_SPLITS = 32;
-// Split count aims at about this many attention workgroups: fewer, longer
-// lived waves (each walks several chunks) beat one chunk per wave.
-constexpr int DEC_TARGET_WG = 1024;
-
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ partial,
                                                              uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -359,6 +412,121 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   if (lse && dd == 0) lse[oh] = (M + __log2f(l)) * 0.69314718055994531f;
 }
 
+// ------------------------------------------------------------ fused path
+// One 512-thread workgroup per unit does the whole step: score + select as
+// above (the selection goes to LDS and to idx), then its 8 waves walk the
+// unit's chunks (taken from an LDS counter, two chunks in flight per wave) and
+// merge through LDS straight into o and lse.  No workspace, one launch.  Used
+// when there are enough units to give every CU one.
+template <int D, int BLK, int G, int R>
+__global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkParams p) {
+  using C = DecCfg<D, G>;
+  constexpr int NW = 8;
+  constexpr int CPB = BLK / C::CK;
+  __shared__ float sc[64 * R];
+  __shared__ uint32_t lds_key[128];
+  __shared__ int32_t lds_idx[128];
+  __shared__ int next_batch;
+  __shared__ int32_t sel[64 * R];          // kept blocks (kmax <= nB <= 64 R)
+  __shared__ float pbuf[NW][C::CK][G];
+  __shared__ float abuf[NW][G];
+  __shared__ float mw[NW][G], lw[NW][G];
+  __shared__ float accw[NW][G][D];
+  const int unit = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t s = unit / a.Hkv;
+  const int g = unit % a.Hkv;
+  const int L = a.L;
+  const float NEG_INF = -__builtin_inff();
+
+  const int kmax = a.kmax;  // every unit keeps exactly kmax blocks (all see nB)
+  const int nch = kmax * CPB;
+  const int nB = a.nB;
+  // With the sink and the last block forced (and distinct) their chunks are
+  // known before the selection: they are taken first (logical chunks
+  // 0 .. 2 CPB - 1), so waves 1 .. 2 CPB - 1 load theirs while wave 0 is still
+  // selecting.  Logical chunk j -> chunk of the ascending selection.
+  const bool early = (p.flags & 3u) == 3u && nB >= 2 && kmax >= 2;
+  auto phys = [&](int j) {
+    if (!early || j < CPB) return j;
+    return j < 2 * CPB ? nch - 2 * CPB + j : j - CPB;
+  };
+  auto forced_key = [&](int j) {  // j < 2 CPB, early only
+    const int key0 = j < CPB ? j * C::CK : (nB - 1) * BLK + (j - CPB) * C::CK;
+    return key0 < L ? key0 : -1;
+  };
+  // chunk i: part i % CPB of kept block i / CPB; -1 for padding, or past the
+  // end of a ragged last block
+  auto key_of = [&](int j) {
+    if (j >= nch) return -1;
+    const int i = phys(j);
+    const int blk = sel[i / CPB];
+    const int key0 = blk * BLK + (i % CPB) * C::CK;
+    return (blk >= 0 && key0 < L) ? key0 : -1;
+  };
+  const uint16_t* kb = a.kc + (int64_t)unit * L * D;
+  const uint16_t* vb = a.vc + (int64_t)unit * L * D;
+  WaveAttn<D, G> wa;
+  ChunkRegs<D, G> rA, rB;
+
+  score_and_select<D, G, R>(a, p, unit, sc, lds_key, lds_idx, &next_batch, sel);
+  wa.init(a, s, g);  // lane mapping + q; every later load depends on it
+  const bool pre = early && wave >= 1 && wave < 2 * CPB && wave < NW;
+  int kA = -1;
+  if (pre) {
+    kA = forced_key(wave);
+    if (kA >= 0) wa.load(rA, kb, vb, kA, L);
+  }
+  __syncthreads();
+  for (int e = tid; e < kmax; e += 512) a.idx[(int64_t)unit * kmax + e] = sel[e];
+  if (tid == 0) next_batch = NW;
+  __syncthreads();
+  // chunks 0 .. NW-1 go to the waves in order, then each wave takes the next
+  // free chunk from an LDS counter (next_batch is free again: the selection
+  // barrier is behind us), keeping one more chunk in flight than it computes
+  auto grab = [&]() {
+    int v = 0;
+    if ((tid & 63) == 0) v = atomicAdd(&next_batch, 1);
+    return __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
+  };
+  int iA = wave;
+  if (!pre) {
+    kA = key_of(iA);
+    if (kA >= 0) wa.load(rA, kb, vb, kA, L);
+  }
+  int iB = grab();
+  while (iA < nch) {
+    const int kB = key_of(iB);
+    if (kB >= 0) wa.load(rB, kb, vb, kB, L);
+    if (kA >= 0) wa.step(rA, kA, L, a.scale_log2, pbuf[wave], abuf[wave]);
+    if (iB >= nch) break;
+    iA = grab();
+    kA = key_of(iA);
+    if (kA >= 0) wa.load(rA, kb, vb, kA, L);
+    if (kB >= 0) wa.step(rB, kB, L, a.scale_log2, pbuf[wave], abuf[wave]);
+    iB = grab();
+  }
+  wa.to_lds(mw[wave], lw[wave], accw[wave]);
+  __syncthreads();
+  for (int e = tid; e < G * D; e += 512) {
+    const int hh = e / D, dd = e % D;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w][hh]);
+    float l = 0.f, v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = __builtin_amdgcn_exp2f(mw[w][hh] - M);  // 0 for a wave with no chunk
+      l += f * lw[w][hh];
+      v += f * accw[w][hh][dd];
+    }
+    const int64_t oh = s * a.Hq + g * G + hh;
+    a.o[oh * D + dd] = (uint16_t)f32_to_bf16_rne(v / l);
+    if (a.lse && dd == 0) a.lse[oh] = (M + __log2f(l)) * 0.69314718055994531f;
+  }
+}
+
 // ============================================================== launch
 int decode_splits(int S, int Hkv, int kmax) {
   const int64_t units = (int64_t)S * Hkv;
@@ -380,16 +548,38 @@ static void launch_select(const DecodeArgs& a, TopkParams p, hipStream_t stream)
     hipLaunchKernelGGL((decode_select_kernel<D, G, 64>), grid, blk, 0, stream, a, p);
 }
 
+template <int D, int BLK, int G>
+static void launch_fused(const DecodeArgs& a, TopkParams p, hipStream_t stream) {
+  const dim3 grid((uint32_t)((int64_t)a.S * a.Hkv)), blk(512);
+  if (a.nB <= 64 * 16)
+    hipLaunchKernelGGL((decode_fused_kernel<D, BLK, G, 16>), grid, blk, 0, stream, a, p);
+  else
+    hipLaunchKernelGGL((decode_fused_kernel<D, BLK, G, 64>), grid, blk, 0, stream, a, p);
+}
+
+// With at least this many (sequence, KV head) units -- one per CU of an
+// MI355X -- the fused one-workgroup-per-unit kernel fills the chip by itself.
+constexpr int64_t DEC_FUSED_MIN_UNITS = 256;
+
 template <int D, int BLK>
 static hipError_t launch_decode_d(const DecodeArgs& a, TopkParams p, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
+  if ((int64_t)a.S * a.Hkv >= DEC_FUSED_MIN_UNITS) {
+    switch (G) {
+      case 1: launch_fused<D, BLK, 1>(a, p, stream); break;
+      case 2: launch_fused<D, BLK, 2>(a, p, stream); break;
+      case 4: launch_fused<D, BLK, 4>(a, p, stream); break;
+      case 8: launch_fused<D, BLK, 8>(a, p, stream); break;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid((uint32_t)((int64_t)a.S * a.Hkv * a.nsplit)), blk(256);
   switch (G) {
     case 1: launch_select<D, 1>(a, p, stream); break;
     case 2: launch_select<D, 2>(a, p, stream); break;
     case 4: launch_select<D, 4>(a, p, stream); break;
     case 8: launch_select<D, 8>(a, p, stream); break;
-    default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -361,6 +361,28 @@ def test_decode_small(cuda_device, name, w, flags):
     decode_check(cuda_device, w, flags)
 
 
+# >= 256 (sequence, KV head) units: one workgroup per unit does the whole step
+DECODE_FUSED = [
+    ("ragged_gqa4", Workload("f1", "decode", 256, 4, 1, 1000, 128, 64, 4, structure="planted", amplitude=2.0,
+                             seed=70), 3),
+    ("d64_b128_ragged_tail", Workload("f2", "decode", 64, 8, 4, 1300, 64, 128, 3, seed=71), 3),
+    ("mha_single_key", Workload("f3", "decode", 128, 2, 2, 1, 128, 64, 4, seed=72), 3),
+    ("gqa8_no_forcing", Workload("f4", "decode", 32, 64, 8, 2048, 128, 64, 5, seed=73), 0),
+    ("fraction_sink_only", Workload("f5", "decode", 64, 16, 4, 3000, 128, 64, 0, 1, 6, seed=74), 1),
+    ("over_1024_blocks", Workload("f6", "decode", 64, 16, 4, 64 * 1100 + 5, 128, 64, 12, seed=75), 3),
+]
+
+
+@pytest.mark.parametrize("name,w,flags", DECODE_FUSED, ids=[c[0] for c in DECODE_FUSED])
+def test_decode_fused_path(cuda_device, name, w, flags):
+    units = w.batch * w.n_kv_heads
+    assert units >= 256
+    rng = np.random.default_rng(units)
+    sample = sorted({(0, 0), (w.batch - 1, w.n_kv_heads - 1)} |
+                    {(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(6)})
+    decode_check(cuda_device, w, flags, sample=sample, o_units=sample[:4])
+
+
 def test_decode_full(cuda_device):
     w = WORKLOADS["decode_s32_l65536"]
     rng = np.random.default_rng(0)
@@ -369,8 +391,9 @@ def test_decode_full(cuda_device):
 
 
 def test_decode_split_count_does_not_change_results(cuda_device):
-    """One sequence alone (many splits per unit) and inside a batch of 32
-    (fewer splits) selects the same blocks and agrees to fp32 rounding."""
+    """One sequence alone (8 units: the split path, many splits per unit) and
+    inside a batch of 32 (256 units: the fused one-workgroup-per-unit path)
+    selects the same blocks and agrees to fp32 rounding."""
     w = Workload("ds", "decode", 32, 32, 8, 4096, 128, 64, 16, seed=57)
     say("decode split invariance")
     q, kc, vc = make_decode(w, device=cuda_device)
