@@ -10,24 +10,30 @@
 //   "稀疏注意力 vs Flash Attention v2" (pnsm.cn/news/1249548.html), section 1:
 //     softmax of the scaled logits over the kept keys, times V.
 //
-// A step is three launches on the caller's stream; it is bound by HBM
-// bandwidth (it must read the block means of the whole key cache and the kept
-// K/V blocks).  Both streams are read once per step, with non-temporal loads:
-//   1. decode_select_kernel: one 512-thread workgroup per (sequence, KV head)
-//      streams that unit's fp32 block means with 16-byte loads (d/8 lanes per
-//      block row; waves take batches of rows from an LDS counter and keep the
-//      next batch in flight while one is scored; row dot products reduced
-//      with DPP), scores each block by the max over the group's heads of
-//      q_h . kbar_j / sqrt(d) into LDS, then one wave runs the top-k on the
-//      LDS scores -- no score round trip;
-//   2. decode_attn_kernel: split-K over the kept blocks, one workgroup per
-//      (unit, split), one 32-key chunk of a kept block per wave at a time.  A
-//      wave issues the loads of its chunk's K and V together, then Q K^T on
-//      v_mfma_f32_16x16x32_bf16 (key rows as the A operand, the group's heads
-//      as B columns) and P V as fp32 VALU over 16-byte V rows.  The workgroup
-//      merges its waves and writes a partial (max, sum, acc[d]) per head;
-//   3. decode_combine_kernel: one thread per (unit, head, dim) merges the
-//      partials.
+// A step is bound by HBM bandwidth: it must read the block means of the whole
+// key cache and the kept K/V blocks, each once, with non-temporal loads.
+//
+// Scoring + selection (score_and_select): one 512-thread workgroup per
+// (sequence, KV head) unit streams the unit's fp32 block means with 16-byte
+// loads (d/8 lanes per block row; waves take batches of rows from an LDS
+// counter and keep the next batch in flight; row dot products reduced with
+// DPP), scores each block by the max over the group's heads of
+// q_h . kbar_j / sqrt(d) into LDS, then one wave runs the top-k on the LDS
+// scores -- no score round trip.
+//
+// Attention over the kept blocks works in 32-key chunks (WaveAttn): a wave
+// issues all K and V loads of a chunk together, then Q K^T on
+// v_mfma_f32_16x16x32_bf16 (key rows as the A operand, the group's heads as B
+// columns) and P V as fp32 VALU over 16-byte V rows, with an online softmax.
+//
+// Two ways to run a step:
+//   * fused (>= 256 units, one per CU): decode_fused_kernel -- the unit's
+//     workgroup selects, then its 8 waves walk the unit's chunks and merge
+//     through LDS into o and lse.  One launch, no workspace.
+//   * split (fewer units): decode_select_kernel writes idx; decode_attn_kernel
+//     runs split-K over the kept blocks (one 256-thread workgroup per (unit,
+//     split)) and writes a partial (max, sum, acc[d]) per head;
+//     decode_combine_kernel merges the partials.
 #include "dsa_internal.hpp"
 #include "topk_row.hpp"
 
