@@ -22,7 +22,8 @@
 //     assigns to its LDS slot -- the swizzle spreads the MFMA operand reads
 //     over all banks;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows are the A operand
-//     (ds_read_b128), Q^T the B operand (registers, for the whole workgroup).
+//     (ds_read_b128, read four k-steps ahead for 64-key tiles), Q^T the B
+//     operand (registers, for the whole workgroup).
 //     One query row per lane (lanes l and l+32 hold the two key halves), so
 //     the row max and sum are in-lane plus one cross-half exchange;
 //   * O^T += V^T P^T: P leaves the S^T accumulators already in B-operand
@@ -213,14 +214,34 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
     f32x16 s[BLK / 32];
 #pragma unroll
     for (int st = 0; st < BLK / 32; ++st) s[st] = (f32x16){};
+    {
+      // K fragments are read KLOOK k-steps ahead of the MFMAs that use them
+      // (LDS latency exceeds two MFMAs); the scheduling barriers keep the
+      // compiler from sinking each read next to its use.  128-key tiles have
+      // no registers to spare for it.
+      constexpr int NKS = D / 16, NST = BLK / 32;
+      constexpr int KLOOK = BLK == 64 ? 4 : 0;
+      auto kread = [&](int ks, u32x4* dst) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+        for (int st = 0; st < NST; ++st) {
+          const int kr = st * 32 + (lane & 31);
+          const int c = (2 * ks + half) ^ kswz<D>(kr);
+          dst[st] = *reinterpret_cast<const LDS_AS u32x4*>(ks_l + kr * D + c * 8);
+        }
+      };
+      u32x4 kb[KLOOK + 1][NST];
 #pragma unroll
-      for (int st = 0; st < BLK / 32; ++st) {
-        const int kr = st * 32 + (lane & 31);
-        const int c = (2 * ks + half) ^ kswz<D>(kr);
-        const u32x4 kf = *reinterpret_cast<const LDS_AS u32x4*>(ks_l + kr * D + c * 8);
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), s[st], 0, 0, 0);
+      for (int p = 0; p < KLOOK && p < NKS; ++p) kread(p, kb[p]);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (KLOOK == 0) kread(ks, kb[0]);
+        else if (ks + KLOOK < NKS) kread(ks + KLOOK, kb[(ks + KLOOK) % (KLOOK + 1)]);
+        if (KLOOK > 0) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[ks % (KLOOK + 1)][st]), as_bf16x8(qf[ks]),
+                                                          s[st], 0, 0, 0);
+        if (KLOOK > 0) __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();  // every wave is done reading K(t)
