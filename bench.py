@@ -157,7 +157,8 @@ def bench_decode(args, dev, stream):
                     block=w.block, topk=w.topk),
         roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                       frac=round(gbs / PEAK_HBM_GBS, 4), traffic=measured_traffic(w.name, DECODE_SRC),
-                      kernel="decode step (3 launches)", bytes_per_step=nbytes),
+                      kernel=("decode step: decode_fused_kernel, one launch" if S * Hkv >= 256 else
+                              "decode step: select, split attention, combine"), bytes_per_step=nbytes),
     )
 
 
