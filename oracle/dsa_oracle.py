@@ -17,6 +17,8 @@ What it computes, step by step, in the order the method runs:
   O4 ``attend``        softmax(s * q k^T) v over exactly the keys of the kept
                         blocks that are causally visible to each row.
   ``prefill`` / ``decode`` chain O1-O4.
+  O5 ``attend_backward`` dQ, dK, dV of O4 with the selection held fixed (the
+                        chain rule through O4's own definition, row by row).
 
 Sources (the pages; cited by title and section):
   [ZB]  dynamic sparse attention explainer, zblog.xzdbk.com/559.html --
@@ -40,7 +42,9 @@ Readings where the pages leave a point open (all listed in the design doc):
   * fractional budget k_r = ceil(num * n_r / den) in integer arithmetic;
   * decode: the new token is the last cache position, so every cached key is
     visible; the forced "diagonal" block is the last block;
-  * query head h reads KV head floor(h / G).
+  * query head h reads KV head floor(h / G);
+  * backward: the selection is a discrete choice and is held constant; dK and
+    dV of a KV head sum the contributions of its G query heads.
 
 Parity status: every function here is pinned by tests in ``tests/`` that do
 not re-use this module's formulas (dense special case against a library
@@ -306,6 +310,55 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, cnt: np
             w, lse[b, h, p] = _softmax_row(logits)
             o[b, h, p] = w @ vs[:n_vis]
     return o, lse
+
+
+def attend_backward(q, k, v, do, idx, cnt, block: int, units=None):
+    """Gradients of ``attend`` with the selection held fixed.
+
+    Returns (dq [B, Hq, N, d], dk, dv [B, Hkv, N, d]) in float64 for the loss
+    whose gradient with respect to O is ``do``.  The selection is a discrete
+    choice and is not differentiated; the keys a row does not see get no
+    gradient from it.
+
+    Per row p, with w the softmax weights over its visible keys c (exactly as
+    in ``attend``): the chain rule through o_p = sum_c w_c v_c and
+    w = softmax(s q_p . k_c) gives dv_c += w_c do_p, dw_c = do_p . v_c,
+    dlogit_c = w_c (dw_c - sum_c' w_c' dw_c'), dq_p = s sum_c dlogit_c k_c and
+    dk_c += s dlogit_c q_p (summed over the G query heads that share a KV
+    head).  ``units`` restricts the rows as in ``attend`` (a unit (b, h, i)
+    adds its rows' contributions to dk and dv).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    nB = n_blocks(N, block)
+    if units is None:
+        units = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(nB)]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for (b, h, i) in units:
+        g = h // G
+        blocks = [int(j) for j in idx[b, g, i, : cnt[b, g, i]]]
+        keys = np.concatenate([np.arange(j * block, min(N, (j + 1) * block)) for j in blocks])
+        keys.sort()
+        ks, vs = k[b, g, keys], v[b, g, keys]
+        for p in range(i * block, min(N, (i + 1) * block)):
+            n_vis = int(np.searchsorted(keys, p, side="right"))
+            kv = keys[:n_vis]
+            logits = scale * (ks[:n_vis] @ q[b, h, p])
+            w, _ = _softmax_row(logits)
+            dw = vs[:n_vis] @ do[b, h, p]
+            dlogit = w * (dw - w @ dw)
+            dq[b, h, p] = scale * (dlogit @ ks[:n_vis])
+            dk[b, g, kv] += scale * np.outer(dlogit, q[b, h, p])
+            dv[b, g, kv] += np.outer(w, do[b, h, p])
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------
