@@ -36,6 +36,8 @@ EXPORTS = [
     "dsa_sparse_attn_fwd",
     "dsa_prefill_workspace_bytes",
     "dsa_prefill",
+    "dsa_attn_bwd_workspace_bytes",
+    "dsa_sparse_attn_bwd",
     "dsa_kv_block_means",
     "dsa_decode_workspace_bytes",
     "dsa_decode",
@@ -97,6 +99,8 @@ def load() -> ctypes.CDLL:
         "dsa_sparse_attn_fwd": ([S, P, P, P, P, P, P, P, P], ctypes.c_int),
         "dsa_prefill_workspace_bytes": ([S], SZ),
         "dsa_prefill": ([S, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "dsa_attn_bwd_workspace_bytes": ([S], SZ),
+        "dsa_sparse_attn_bwd": ([S, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "dsa_kv_block_means": ([S, P, P, P], ctypes.c_int),
         "dsa_decode_workspace_bytes": ([S], SZ),
         "dsa_decode": ([S, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
@@ -222,6 +226,23 @@ def dsa_prefill(shape: Shape, q, k, v, o, lse, idx, cnt, ws, stream=None):
         _ptr(cnt, torch.int32, (B, Hkv, nB), "cnt"), wp, wb, _stream(stream)))
 
 
+def dsa_attn_bwd_workspace_bytes(shape: Shape) -> int:
+    return _query("dsa_attn_bwd_workspace_bytes", _key(shape))
+
+
+def dsa_sparse_attn_bwd(shape: Shape, q, k, v, o, lse, dout, idx, cnt, dq, dk, dv, ws, stream=None):
+    B, Hq, Hkv, N, d, nB = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_len, shape.head_dim, shape.n_blocks
+    km = dsa_prefill_kmax(shape)
+    wp, wb = _ws(ws, dsa_attn_bwd_workspace_bytes(shape))
+    _check(load().dsa_sparse_attn_bwd(
+        ctypes.byref(shape), _ptr(q, torch.bfloat16, (B, Hq, N, d), "q"), _ptr(k, torch.bfloat16, (B, Hkv, N, d), "k"),
+        _ptr(v, torch.bfloat16, (B, Hkv, N, d), "v"), _ptr(o, torch.bfloat16, (B, Hq, N, d), "o"),
+        _ptr(lse, torch.float32, (B, Hq, N), "lse"), _ptr(dout, torch.bfloat16, (B, Hq, N, d), "dout"),
+        _ptr(idx, torch.int32, (B, Hkv, nB, km), "idx"), _ptr(cnt, torch.int32, (B, Hkv, nB), "cnt"),
+        _ptr(dq, torch.bfloat16, (B, Hq, N, d), "dq"), _ptr(dk, torch.bfloat16, (B, Hkv, N, d), "dk"),
+        _ptr(dv, torch.bfloat16, (B, Hkv, N, d), "dv"), wp, wb, _stream(stream)))
+
+
 def dsa_kv_block_means(shape: Shape, k_cache, kbar, stream=None):
     S, Hkv, L, d, nB = shape.batch, shape.n_kv_heads, shape.seq_len, shape.head_dim, shape.n_blocks
     _check(load().dsa_kv_block_means(ctypes.byref(shape), _ptr(k_cache, torch.bfloat16, (S, Hkv, L, d), "k_cache"),
@@ -259,6 +280,18 @@ def prefill(q, k, v, block: int, topk: int = 0, topk_num: int = 0, topk_den: int
     ws = torch.empty(max(1, dsa_prefill_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
     dsa_prefill(shape, q, k, v, o, lse, idx, cnt, ws, stream)
     return o, lse, idx, cnt
+
+
+def attn_backward(q, k, v, o, lse, dout, idx, cnt, block: int, topk: int = 0, topk_num: int = 0, topk_den: int = 1,
+                  flags: int = FORCE_SINK | FORCE_DIAG, stream=None):
+    """Gradients of the sparse attention (selection held fixed); allocates
+    dq, dk, dv and the workspace.  idx/cnt/o/lse as returned by prefill."""
+    B, Hq, N, d = q.shape
+    shape = make_shape(B, Hq, k.shape[1], N, d, block, topk, topk_num, topk_den, flags)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(1, dsa_attn_bwd_workspace_bytes(shape)), dtype=torch.uint8, device=q.device)
+    dsa_sparse_attn_bwd(shape, q, k, v, o, lse, dout, idx, cnt, dq, dk, dv, ws, stream)
+    return dq, dk, dv
 
 
 def decode(q, k_cache, v_cache, kbar, block: int, topk: int = 0, topk_num: int = 0, topk_den: int = 1,

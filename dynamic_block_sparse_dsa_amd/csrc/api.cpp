@@ -196,6 +196,65 @@ int dsa_sparse_attn_fwd(const dsa_shape* s, const void* q, const void* k, const 
   return DSA_OK;
 }
 
+size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* s) {
+  if (check_shape(s)) return 0;
+  const size_t nB = (size_t)n_blocks(s), B = (size_t)s->batch, N = (size_t)s->seq_len;
+  return align256(B * s->n_q_heads * N * 4) + align256(B * s->n_kv_heads * nB * 4) +
+         align256(B * s->n_kv_heads * nB * nB * 4);
+}
+
+int dsa_sparse_attn_bwd(const dsa_shape* s, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, const int32_t* idx, const int32_t* cnt, void* dq,
+                        void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (empty_prefill(s)) return DSA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !idx || !cnt || !dq || !dk || !dv)
+    return fail(DSA_ERR_NULL, "q, k, v, o, lse, dout, idx, cnt, dq, dk or dv is NULL");
+  const size_t need = dsa_attn_bwd_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
+  const size_t nB = (size_t)n_blocks(s), B = (size_t)s->batch, N = (size_t)s->seq_len;
+  char* p = static_cast<char*>(ws);
+  float* dvec = reinterpret_cast<float*>(p);
+  p += align256(B * s->n_q_heads * N * 4);
+  int32_t* inv_cnt = reinterpret_cast<int32_t*>(p);
+  p += align256(B * s->n_kv_heads * nB * 4);
+  int32_t* inv_idx = reinterpret_cast<int32_t*>(p);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = dsa::launch_bwd_prep(static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), dvec,
+                                      (int64_t)B * s->n_q_heads * N, s->head_dim, st);
+  if (e != hipSuccess) return hip_fail(e, "bwd_prep launch");
+  e = dsa::launch_bwd_invert(idx, cnt, inv_cnt, inv_idx, (int64_t)B * s->n_kv_heads, (int)nB, prefill_kmax(s), st);
+  if (e != hipSuccess) return hip_fail(e, "bwd_invert launch");
+  dsa::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.dvec = dvec;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.inv_cnt = inv_cnt;
+  a.inv_idx = inv_idx;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.B = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.N = s->seq_len;
+  a.nB = (int)nB;
+  a.kmax = prefill_kmax(s);
+  a.scale = (float)(1.0 / sqrt((double)s->head_dim));
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
+  e = dsa::launch_sparse_attn_bwd(a, s->head_dim, s->block, st);
+  if (e != hipSuccess) return hip_fail(e, "sparse_attn_bwd launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
 size_t dsa_prefill_workspace_bytes(const dsa_shape* s) {
   if (check_shape(s)) return 0;
   const size_t nB = (size_t)n_blocks(s), d = (size_t)s->head_dim, B = (size_t)s->batch;

@@ -1,0 +1,467 @@
+// Sparse attention backward over the selected key blocks: dQ, dK, dV with the
+// selection held fixed (bf16 MFMA, fp32 accumulation).
+//
+// Method: "稀疏注意力 vs Flash Attention v2" (pnsm.cn/news/1249548.html),
+// section 1, defines the forward (softmax of the scaled logits over the kept
+// keys, times V) and notes that FlashAttention-2 recomputes rather than
+// stores the score matrix; the backward is the chain rule through that
+// forward, recomputing P from the saved log-sum-exp:
+//   P = exp(s q k^T - lse),  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O),
+//   dQ = s dS K,  dK = s dS^T Q,  dV = P^T dO   (s = 1/sqrt(d), GQA: dK/dV summed
+//   over the group's query heads).
+//
+// Launches (all on the caller's stream):
+//   1. bwd_prep_kernel: D per query row (fp32), d/8 lanes per row with DPP sums;
+//   2. bwd_invert_kernel: for every KV block j the ascending list of query
+//      blocks whose selection kept j (one wave per j, membership by binary
+//      search in the sorted index rows, compaction by ballot);
+//   3. bwd_dq_kernel: one workgroup per (batch, KV head, HG query heads, query
+//      block), each wave 32 query rows, walking the kept tiles like the
+//      forward: S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS as A
+//      operands, Q^T and dO^T in registers as B), dS^T in registers, then
+//      dQ^T += K^T dS^T with K^T from transposed LDS reads.  K is used at both
+//      ends of a tile, so it is double-buffered; V is single-buffered.  Two
+//      barriers per tile;
+//   4. bwd_dkdv_kernel: one workgroup per (batch, KV head, KV block), each
+//      wave 32 keys; K and V stay in LDS, and for every (query block of the
+//      inverted list) x (query head of the group) the Q and dO tiles stream
+//      through LDS: S = Q K^T, dP = dO V^T (Q, dO rows as A operands, K, V
+//      rows as B), P and dS in registers (already in B-operand order), then
+//      dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transposed LDS
+//      reads.
+// All tiles in LDS use the row swizzle kswz; the transposed reads of a kswz
+// tile see at most 2-way bank conflicts.
+#include "attn_common.hpp"
+
+namespace dsa {
+
+// ============================================================== tile loads
+// A ROWS x D bf16 tile (rows row0 .. row0 + ROWS - 1 of a [*, D] matrix,
+// rows clamped to n_rows - 1) into LDS with the kswz layout, by WAVES waves.
+template <int D, int ROWS, int WAVES>
+__device__ __forceinline__ void load_tile(const uint16_t* g, int row0, int n_rows, uint32_t lds_base, int wave,
+                                          int lane) {
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int RPI = 1024 / (2 * D);    // rows per 1 KiB wave load
+  constexpr int LOADS = ROWS * D * 2 / 1024;
+  static_assert(LOADS % WAVES == 0, "tile loads must split evenly over waves");
+#pragma unroll
+  for (int n = 0; n < LOADS / WAVES; ++n) {
+    const int inst = wave + n * WAVES;
+    const int r = inst * RPI + lane / CH;
+    const int c = (lane % CH) ^ kswz<D>(r);
+    const int row = min(row0 + r, n_rows - 1);
+    dma16(g, (uint32_t)(row * D + c * 8) * 2u, __builtin_amdgcn_readfirstlane(lds_base + inst * 1024));
+  }
+}
+
+// 8 bf16 of the transposed operand: rows t0 + {0..3} and t0 + 8 + {0..3} of
+// a kswz tile at column block `d` (lane layout of ds_read_b64_tr_b16: within
+// 16 lanes, out lane i slot j receives element i % 4 of source lane 4j + i/4;
+// source lane s reads row base + s / 4, columns dbase + 4 (s % 4) .. + 3).
+template <int D>
+__device__ __forceinline__ u32x4 read_tr(const LDS_AS uint16_t* tile, int row_base, int d) {
+  u32x4 f;
+  const int cbase = d >> 3, sub = (d & 7) * 2;  // 16-byte chunk and byte offset (0 or 8)
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const int row = row_base + 8 * sg;
+    const int c = cbase ^ kswz<D>(row);
+    const LDS_AS char* addr = reinterpret_cast<const LDS_AS char*>(tile + row * D + c * 8) + sub;
+    const i16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)addr);
+    const u32x2 w = __builtin_bit_cast(u32x2, v4);
+    f[2 * sg] = w[0];
+    f[2 * sg + 1] = w[1];
+  }
+  return f;
+}
+
+// row-major operand fragment: row r, k-step ks (dims 16 ks + 8 half .. + 7)
+template <int D>
+__device__ __forceinline__ u32x4 read_row(const LDS_AS uint16_t* tile, int r, int ks, int half) {
+  const int c = (2 * ks + half) ^ kswz<D>(r);
+  return *reinterpret_cast<const LDS_AS u32x4*>(tile + r * D + c * 8);
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const bf16x2_t pk = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, pk);
+}
+
+// ============================================================== 1. D = rowsum(dO * O)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                                                       float* __restrict__ dvec, int64_t n_rows) {
+  constexpr int TPR = D / 8, RPW = 256 / TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < n_rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + 8 * c);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += bf16_lo(a[e]) * bf16_lo(b[e]) + bf16_hi(a[e]) * bf16_hi(b[e]);
+  }
+#pragma unroll
+  for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < n_rows && c == 0) dvec[row] = acc;
+}
+
+// ============================================================== 2. inverted selection
+// One wave per (unit, KV block j): query blocks i >= j in chunks of 64 lanes;
+// lane i keeps i if j is in the sorted row idx[i][0 .. cnt_i).
+__global__ __launch_bounds__(256) void bwd_invert_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+                                                         int32_t* __restrict__ inv_cnt, int32_t* __restrict__ inv_idx,
+                                                         int64_t n_waves, int nB, int kmax) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w >= n_waves) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = w / nB;
+  const int j = (int)(w % nB);
+  int32_t* out = inv_idx + w * nB;
+  int total = 0;
+  for (int i0 = j; i0 < nB; i0 += 64) {
+    const int i = i0 + lane;
+    bool hit = false;
+    if (i < nB) {
+      const int32_t* row = idx + (unit * nB + i) * (int64_t)kmax;
+      int lo = 0, hi = cnt[unit * nB + i];  // ascending block ids
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (row[mid] < j) lo = mid + 1;
+        else hi = mid;
+      }
+      hit = lo < cnt[unit * nB + i] && row[lo] == j;
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    if (hit) out[total + below] = i;
+    total += __builtin_popcountll(m);
+  }
+  if (lane == 0) inv_cnt[w] = total;
+}
+
+// ============================================================== 3. dQ
+template <int D, int BLK, int HG>
+struct BwdQCfg {
+  static constexpr int SLABS = BLK / 32;
+  static constexpr int WAVES = HG * SLABS;
+  static constexpr int THREADS = WAVES * 64;
+};
+
+template <int D, int BLK, int HG>
+__global__ __launch_bounds__((BwdQCfg<D, BLK, HG>::THREADS)) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_kernel(BwdArgs a) {
+  using C = BwdQCfg<D, BLK, HG>;
+  constexpr int NKS = D / 16, NST = BLK / 32;
+  __shared__ __align__(1024) uint16_t Ks[2][BLK * D];
+  __shared__ __align__(1024) uint16_t Vs[BLK * D];
+
+  const int G = a.Hq / a.Hkv;
+  const int hchunks = G / HG;
+  const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int i = a.nB - 1 - (int)(L % (uint32_t)a.nB);
+  const uint32_t u = L / (uint32_t)a.nB;
+  const int hc = (int)(u % (uint32_t)hchunks);
+  const int64_t bg = u / (uint32_t)hchunks;
+  const int64_t b = bg / a.Hkv;
+  const int g = (int)(bg % a.Hkv);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = wave / C::SLABS, slab = wave % C::SLABS;
+  const int h = g * G + hc * HG + hl;
+  const int half = lane >> 5;
+  const int row_in_blk = slab * 32 + (lane & 31);
+  const int row = i * BLK + row_in_blk;
+  const int N = a.N;
+  const int64_t qrow = (b * a.Hq + h) * (int64_t)N + min(row, N - 1);
+
+  const uint16_t* kgp = a.k + bg * (int64_t)N * D;
+  const uint16_t* vgp = a.v + bg * (int64_t)N * D;
+  const CONST_AS int32_t* irow = (const CONST_AS int32_t*)(a.idx + (bg * a.nB + i) * (int64_t)a.kmax);
+  const int n_sel = ((const CONST_AS int32_t*)a.cnt)[bg * a.nB + i];
+  const uint32_t kbase[2] = {(uint32_t)(uintptr_t)(LDS_AS uint16_t*)Ks[0], (uint32_t)(uintptr_t)(LDS_AS uint16_t*)Ks[1]};
+  const uint32_t vbase = (uint32_t)(uintptr_t)(LDS_AS uint16_t*)Vs;
+
+  if (n_sel > 0) {
+    load_tile<D, BLK, C::WAVES>(kgp, irow[0] * BLK, N, kbase[0], wave, lane);
+    load_tile<D, BLK, C::WAVES>(vgp, irow[0] * BLK, N, vbase, wave, lane);
+  }
+  // B operands: lane's row, dims 16 ks + 8 half .. + 7
+  u32x4 qf[NKS], df[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qf[ks] = *reinterpret_cast<const u32x4*>(a.q + qrow * D + ks * 16 + 8 * half);
+    df[ks] = *reinterpret_cast<const u32x4*>(a.dout + qrow * D + ks * 16 + 8 * half);
+  }
+  const float lse2 = a.lse[qrow] * 1.4426950408889634f;  // natural -> log2 units
+  const float drow = a.dvec[qrow];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(df[ks]));
+  asm volatile("" ::"v"(lse2), "v"(drow));
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dq[dt] = (f32x16){};
+  const float c2 = a.scale_log2;
+
+  for (int t = 0; t < n_sel; ++t) {
+    const int j = irow[t];
+    const bool more = t + 1 < n_sel;
+    const int jn = more ? irow[t + 1] : 0;
+    const LDS_AS uint16_t* ks_l = (const LDS_AS uint16_t*)Ks[t & 1];
+    // ---- K(t), V(t) resident; every wave is done with tile t - 1
+    wait_vm<0>();
+    __syncthreads();
+    if (more) load_tile<D, BLK, C::WAVES>(kgp, jn * BLK, N, kbase[(t + 1) & 1], wave, lane);
+    // ---- S^T = K Q^T, dP^T = V dO^T
+    f32x16 s[NST], dp[NST];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) s[st] = dp[st] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int kr = st * 32 + (lane & 31);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_row<D>(ks_l, kr, ks, half)), as_bf16x8(qf[ks]),
+                                                        s[st], 0, 0, 0);
+        dp[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(read_row<D>((const LDS_AS uint16_t*)Vs, kr, ks, half)), as_bf16x8(df[ks]), dp[st], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done reading V(t)
+    if (more) load_tile<D, BLK, C::WAVES>(vgp, jn * BLK, N, vbase, wave, lane);
+    // ---- dS^T = P^T (dP^T - D), P^T = exp2(s c2 - lse2), causal mask on the diagonal
+    const bool diag = (j == i);
+    u32x4 dsf[BLK / 16];
+#pragma unroll
+    for (int kk = 0; kk < BLK / 16; ++kk) {
+      const int st = kk >> 1, rb = 8 * (kk & 1);
+      float v8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = rb + e;
+        const int key_in_blk = st * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], c2, -lse2));
+        if (diag && key_in_blk > row_in_blk) p = 0.f;
+        v8[e] = p * (dp[st][r] - drow);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsf[kk][e] = pack2(v8[2 * e], v8[2 * e + 1]);
+    }
+    // ---- dQ^T += K^T dS^T (K^T by transposed reads)
+    {
+      const int grp = (lane >> 4) & 1, si = lane & 15;
+#pragma unroll
+      for (int kk = 0; kk < BLK / 16; ++kk) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int d = dt * 32 + 16 * grp + 4 * (si & 3);
+          const u32x4 kf = read_tr<D>(ks_l, 16 * kk + 4 * half + (si >> 2), d);
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(dsf[kk]), dq[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  wait_vm<0>();
+
+  // ---- dQ = s dS K (bf16)
+  if (row < N) {
+    uint16_t* orow = a.dq + ((b * a.Hq + h) * (int64_t)N + row) * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u32x2 w;
+        w[0] = pack2(dq[dt][4 * q4 + 0] * sc, dq[dt][4 * q4 + 1] * sc);
+        w[1] = pack2(dq[dt][4 * q4 + 2] * sc, dq[dt][4 * q4 + 3] * sc);
+        *reinterpret_cast<u32x2*>(orow + dt * 32 + 8 * q4 + 4 * half) = w;
+      }
+    }
+  }
+}
+
+// ============================================================== 4. dK, dV
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int WAVES = BLK / 32;  // each wave owns 32 keys
+  constexpr int NKS = D / 16;
+  __shared__ __align__(1024) uint16_t Ks[BLK * D];
+  __shared__ __align__(1024) uint16_t Vs[BLK * D];
+  __shared__ __align__(1024) uint16_t Qs[BLK * D];
+  __shared__ __align__(1024) uint16_t Ds[BLK * D];  // dO tile
+  __shared__ float lse_s[BLK], d_s[BLK];
+
+  const int64_t bg = blockIdx.x / a.nB;  // b * Hkv + g
+  const int j = (int)(blockIdx.x % a.nB);
+  const int64_t b = bg / a.Hkv;
+  const int g = (int)(bg % a.Hkv);
+  const int G = a.Hq / a.Hkv;
+  const int N = a.N;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int key_in_blk = wave * 32 + (lane & 31);
+  const int key = j * BLK + key_in_blk;
+  const LDS_AS uint16_t* ks_l = (const LDS_AS uint16_t*)Ks;
+  const LDS_AS uint16_t* vs_l = (const LDS_AS uint16_t*)Vs;
+  const LDS_AS uint16_t* qs_l = (const LDS_AS uint16_t*)Qs;
+  const LDS_AS uint16_t* ds_l = (const LDS_AS uint16_t*)Ds;
+  const uint32_t qbase = (uint32_t)(uintptr_t)qs_l, dbase = (uint32_t)(uintptr_t)ds_l;
+
+  load_tile<D, BLK, WAVES>(a.k + bg * (int64_t)N * D, j * BLK, N, (uint32_t)(uintptr_t)ks_l, wave, lane);
+  load_tile<D, BLK, WAVES>(a.v + bg * (int64_t)N * D, j * BLK, N, (uint32_t)(uintptr_t)vs_l, wave, lane);
+
+  const int n_list = a.inv_cnt[blockIdx.x];
+  const CONST_AS int32_t* list = (const CONST_AS int32_t*)(a.inv_idx + (int64_t)blockIdx.x * a.nB);
+  const float c2 = a.scale_log2;
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dk[dt] = dv[dt] = (f32x16){};
+
+  const int n_work = n_list * G;
+  for (int w = 0; w < n_work; ++w) {
+    const int i = list[w / G];
+    const int h = g * G + w % G;
+    const int64_t hrow0 = (b * a.Hq + h) * (int64_t)N;
+    if (w > 0) __syncthreads();  // every wave is done with the previous Q, dO tiles
+    load_tile<D, BLK, WAVES>(a.q + hrow0 * D, i * BLK, N, qbase, wave, lane);
+    load_tile<D, BLK, WAVES>(a.dout + hrow0 * D, i * BLK, N, dbase, wave, lane);
+    for (int e = tid; e < BLK; e += BLK * 2) {
+      const int64_t r = hrow0 + min(i * BLK + e, N - 1);
+      lse_s[e] = a.lse[r] * 1.4426950408889634f;
+      d_s[e] = a.dvec[r];
+    }
+    wait_vm<0>();
+    __syncthreads();
+    const bool diag = (i == j);
+    // 32 queries at a time: S = Q K^T, dP = dO V^T (M = queries, N = keys)
+#pragma unroll 1
+    for (int qb = 0; qb < BLK / 32; ++qb) {
+      f32x16 s = (f32x16){}, dp = (f32x16){};
+      const int qr = qb * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_row<D>(qs_l, qr, ks, half)),
+                                                    as_bf16x8(read_row<D>(ks_l, key_in_blk, ks, half)), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_row<D>(ds_l, qr, ks, half)),
+                                                     as_bf16x8(read_row<D>(vs_l, key_in_blk, ks, half)), dp, 0, 0, 0);
+      }
+      // element r: query qb * 32 + 8 (r / 4) + 4 half + r % 4, this lane's key.
+      // P and dS packed to bf16 in B-operand order (k-chunk kk: elements 8 kk .. 8 kk + 7)
+      u32x4 pf[2], sf[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * kk + e;
+          const int q_in_blk = qb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int qrow = i * BLK + q_in_blk;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse_s[q_in_blk]));
+          if ((diag && key_in_blk > q_in_blk) || qrow >= N) p = 0.f;
+          pv[e] = p;
+          dsv[e] = p * (dp[r] - d_s[q_in_blk]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pf[kk][e] = pack2(pv[2 * e], pv[2 * e + 1]);
+          sf[kk][e] = pack2(dsv[2 * e], dsv[2 * e + 1]);
+        }
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS (M = d, N = keys, K = these 32 queries)
+      const int grp = (lane >> 4) & 1, si = lane & 15;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int d = dt * 32 + 16 * grp + 4 * (si & 3);
+          const int rb = qb * 32 + 16 * kk + 4 * half + (si >> 2);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_tr<D>(ds_l, rb, d)), as_bf16x8(pf[kk]),
+                                                           dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_tr<D>(qs_l, rb, d)), as_bf16x8(sf[kk]),
+                                                           dk[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  wait_vm<0>();
+
+  // ---- dK = s dS^T Q, dV = P^T dO (bf16); a block no row kept gets zeros
+  if (key < N) {
+    uint16_t* krow = a.dk + (bg * (int64_t)N + key) * D;
+    uint16_t* vrow = a.dv + (bg * (int64_t)N + key) * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u32x2 wk, wv;
+        wk[0] = pack2(dk[dt][4 * q4 + 0] * sc, dk[dt][4 * q4 + 1] * sc);
+        wk[1] = pack2(dk[dt][4 * q4 + 2] * sc, dk[dt][4 * q4 + 3] * sc);
+        wv[0] = pack2(dv[dt][4 * q4 + 0], dv[dt][4 * q4 + 1]);
+        wv[1] = pack2(dv[dt][4 * q4 + 2], dv[dt][4 * q4 + 3]);
+        *reinterpret_cast<u32x2*>(krow + dt * 32 + 8 * q4 + 4 * half) = wk;
+        *reinterpret_cast<u32x2*>(vrow + dt * 32 + 8 * q4 + 4 * half) = wv;
+      }
+    }
+  }
+}
+
+// ============================================================== launch
+hipError_t launch_bwd_prep(const uint16_t* o, const uint16_t* dout, float* dvec, int64_t n_rows, int d,
+                           hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  const int rpw = 256 / (d / 8);
+  const dim3 grid((uint32_t)((n_rows + rpw - 1) / rpw)), blk(256);
+  if (d == 64) hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, blk, 0, stream, o, dout, dvec, n_rows);
+  else hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, blk, 0, stream, o, dout, dvec, n_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_invert(const int32_t* idx, const int32_t* cnt, int32_t* inv_cnt, int32_t* inv_idx,
+                             int64_t n_units, int nB, int kmax, hipStream_t stream) {
+  const int64_t n_waves = n_units * nB;
+  if (n_waves == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_invert_kernel, dim3((uint32_t)((n_waves + 3) / 4)), dim3(256), 0, stream, idx, cnt, inv_cnt,
+                     inv_idx, n_waves, nB, kmax);
+  return hipGetLastError();
+}
+
+template <int D, int BLK, int HG>
+static hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const int64_t n_wg = (int64_t)a.B * a.Hkv * (G / HG) * a.nB;
+  if (n_wg == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BLK, HG>), dim3((uint32_t)n_wg), dim3(BwdQCfg<D, BLK, HG>::THREADS), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+template <int D, int BLK>
+static hipError_t launch_bwd_d_blk(const BwdArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  hipError_t e;
+  if constexpr (BLK == 64) {
+    if (G % 2 == 0) e = launch_dq_cfg<D, BLK, 2>(a, stream);
+    else e = launch_dq_cfg<D, BLK, 1>(a, stream);
+  } else {
+    e = launch_dq_cfg<D, BLK, 1>(a, stream);
+  }
+  if (e != hipSuccess) return e;
+  const int64_t n_wg = (int64_t)a.B * a.Hkv * a.nB;
+  if (n_wg == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BLK>), dim3((uint32_t)n_wg), dim3(BLK * 2), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_bwd(const BwdArgs& a, int d, int block, hipStream_t stream) {
+  if (d == 64) return block == 64 ? launch_bwd_d_blk<64, 64>(a, stream) : launch_bwd_d_blk<64, 128>(a, stream);
+  return block == 64 ? launch_bwd_d_blk<128, 64>(a, stream) : launch_bwd_d_blk<128, 128>(a, stream);
+}
+
+}  // namespace dsa

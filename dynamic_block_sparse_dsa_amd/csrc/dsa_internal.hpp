@@ -82,6 +82,30 @@ struct AttnArgs {
 };
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, int d, int block, hipStream_t stream);
 
+struct BwdArgs {
+  const uint16_t* q;     // [B, Hq, N, d]
+  const uint16_t* k;     // [B, Hkv, N, d]
+  const uint16_t* v;
+  const uint16_t* dout;  // [B, Hq, N, d]
+  const float* lse;      // [B, Hq, N] natural log
+  const float* dvec;     // [B, Hq, N] rowsum(dO * O)
+  const int32_t* idx;    // [B, Hkv, nB, kmax]
+  const int32_t* cnt;    // [B, Hkv, nB]
+  const int32_t* inv_cnt;  // [B, Hkv, nB]
+  const int32_t* inv_idx;  // [B, Hkv, nB, nB]
+  uint16_t* dq;          // [B, Hq, N, d]
+  uint16_t* dk;          // [B, Hkv, N, d]
+  uint16_t* dv;
+  int B, Hq, Hkv, N, nB, kmax;
+  float scale;       // 1 / sqrt(d)
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+hipError_t launch_bwd_prep(const uint16_t* o, const uint16_t* dout, float* dvec, int64_t n_rows, int d,
+                           hipStream_t stream);
+hipError_t launch_bwd_invert(const int32_t* idx, const int32_t* cnt, int32_t* inv_cnt, int32_t* inv_idx,
+                             int64_t n_units, int nB, int kmax, hipStream_t stream);
+hipError_t launch_sparse_attn_bwd(const BwdArgs& a, int d, int block, hipStream_t stream);
+
 struct DecodeArgs {
   const uint16_t* q;   // [S, Hq, d]
   const uint16_t* kc;  // [S, Hkv, L, d]

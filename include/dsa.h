@@ -154,6 +154,29 @@ size_t dsa_decode_workspace_bytes(const dsa_shape* shape);
 int dsa_decode(const dsa_shape* shape, const void* q, const void* k_cache, const void* v_cache, const float* kbar,
                void* o, float* lse, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Backward of step 4 (gradients through the kept tiles; the selection
+ * is a discrete choice and is held fixed).  The chain rule through the
+ * attention definition of "稀疏注意力 vs Flash Attention v2" section 1, with P
+ * recomputed from the saved LSE (the FlashAttention-2 recompute idea of the
+ * same section): D = rowsum(dO * O), P = exp((1/sqrt(d)) q k^T - lse),
+ * dS = P * (dO V^T - D), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d),
+ * dV = P^T dO; dK and dV of a KV head sum its group's query heads.  Keys no
+ * row kept get zero gradients. */
+
+/* Workspace for dsa_sparse_attn_bwd, in bytes: D [B, Hq, N] fp32 and the
+ * inverted selection (per KV block, the query blocks that kept it)
+ * [B, Hkv, nB] + [B, Hkv, nB, nB] int32. */
+size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape);
+
+/* q, k, v, idx, cnt as given to dsa_sparse_attn_fwd; o and lse (required)
+ * as it returned them; dout: dL/dO [B, Hq, N, d] bf16.  Writes dq
+ * [B, Hq, N, d], dk and dv [B, Hkv, N, d], bf16 (fp32 accumulation; P and
+ * dS are rounded to bf16 as MFMA operands).  Every element of dq, dk, dv is
+ * written.  ws: at least dsa_attn_bwd_workspace_bytes. */
+int dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, const int32_t* idx, const int32_t* cnt, void* dq,
+                        void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* dsa_status_str(int status);
 

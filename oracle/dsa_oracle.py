@@ -312,7 +312,7 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, cnt: np
     return o, lse
 
 
-def attend_backward(q, k, v, do, idx, cnt, block: int, units=None):
+def attend_backward(q, k, v, do, idx, cnt, block: int, units=None, o=None):
     """Gradients of ``attend`` with the selection held fixed.
 
     Returns (dq [B, Hq, N, d], dk, dv [B, Hkv, N, d]) in float64 for the loss
@@ -327,6 +327,11 @@ def attend_backward(q, k, v, do, idx, cnt, block: int, units=None):
     dk_c += s dlogit_c q_p (summed over the G query heads that share a KV
     head).  ``units`` restricts the rows as in ``attend`` (a unit (b, h, i)
     adds its rows' contributions to dk and dv).
+
+    The term sum_c' w_c' dw_c' equals do_p . o_p.  By default it is taken from
+    the exact weights; with ``o`` ([B, Hq, N, d], e.g. a rounded forward
+    output) it is do_p . o[p] instead -- the quantity a backward that is handed
+    the forward's output computes.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -354,7 +359,8 @@ def attend_backward(q, k, v, do, idx, cnt, block: int, units=None):
             logits = scale * (ks[:n_vis] @ q[b, h, p])
             w, _ = _softmax_row(logits)
             dw = vs[:n_vis] @ do[b, h, p]
-            dlogit = w * (dw - w @ dw)
+            dsum = w @ dw if o is None else float(np.asarray(o[b, h, p], dtype=np.float64) @ do[b, h, p])
+            dlogit = w * (dw - dsum)
             dq[b, h, p] = scale * (dlogit @ ks[:n_vis])
             dk[b, g, kv] += scale * np.outer(dlogit, q[b, h, p])
             dv[b, g, kv] += np.outer(w, do[b, h, p])

@@ -111,3 +111,14 @@ def test_backward_closed_forms():
     k_same = np.broadcast_to(kk[:, :, :1], kk.shape).copy()
     dq2, _, _ = O.attend_backward(q, k_same, v, do, idx, cnt, block)
     assert np.abs(dq2).max() < 1e-12
+
+
+def test_backward_with_given_output_reproduces_exact_path():
+    """Handing the exact forward output as ``o`` gives the same gradients as
+    the default (the identity sum_c w_c dw_c = do . o)."""
+    q, kk, v, do, idx, cnt, block = _case(7, 1, 4, 2, 45, 8, 8, 3)
+    o, _ = O.attend(q, kk, v, idx, cnt, block)
+    a = O.attend_backward(q, kk, v, do, idx, cnt, block)
+    b = O.attend_backward(q, kk, v, do, idx, cnt, block, o=o)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-10, atol=1e-12)
