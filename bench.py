@@ -162,6 +162,42 @@ def bench_decode(args, dev, stream):
     )
 
 
+def bench_backward(args, dev, stream, inputs):
+    """dsa_sparse_attn_bwd on the prefill workload (selection and forward from
+    dsa_prefill, a seeded output gradient): event-timed over its four
+    launches.  Algorithmic FLOPs: the five products a backward needs per kept
+    tile (S recomputed, dP, dV, dQ, dK), 2.5x the forward's."""
+    import torch
+
+    import dynamic_block_sparse_dsa_amd as dsa
+    from dynamic_block_sparse_dsa_amd import work
+
+    q, k, v, w = inputs
+    B, Hq, Hkv, N, d, nB = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_blocks
+    o, lse, idx, cnt = dsa.prefill(q, k, v, w.block, w.topk, w.topk_num, w.topk_den, stream=stream)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    dout = torch.randn(q.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    shape = dsa.make_shape(B, Hq, Hkv, N, d, w.block, w.topk, w.topk_num, w.topk_den)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(dsa.dsa_attn_bwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        dsa.dsa_sparse_attn_bwd(shape, q, k, v, o, lse, dout, idx, cnt, dq, dk, dv, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    ms = time_events(step, args.steps, stream)
+    flops = 2.5 * work.prefill_flops(cnt.cpu().numpy(), w.group, w.block, d)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return dict(value=B * N / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
+                config=dict(workload=w.name),
+                roofline=dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                              frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
+                              kernel="backward step: prep, invert, dq, dkdv", flops_per_step=flops))
+
+
 def cpu_baseline(args, inputs):
     """The oracle, as it stands, on whole heads of the prefill workload until
     about --cpu-seconds have passed; scaled to tokens/s of the full problem."""
@@ -198,6 +234,7 @@ def main():
     ap.add_argument("--workload", default="prefill_n8192_h32")
     ap.add_argument("--decode-workload", default="decode_s32_l65536")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -233,6 +270,8 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(args, dev, stream)
+    if not args.no_backward:
+        out["backward"] = bench_backward(args, dev, stream, inputs)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, inputs)
     print(json.dumps(out), flush=True)

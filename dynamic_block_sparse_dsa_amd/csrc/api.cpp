@@ -199,7 +199,7 @@ int dsa_sparse_attn_fwd(const dsa_shape* s, const void* q, const void* k, const 
 size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* s) {
   if (check_shape(s)) return 0;
   const size_t nB = (size_t)n_blocks(s), B = (size_t)s->batch, N = (size_t)s->seq_len;
-  return align256(B * s->n_q_heads * N * 4) + align256(B * s->n_kv_heads * nB * 4) +
+  return align256(B * s->n_q_heads * nB * 2 * (size_t)s->block * 4) + align256(B * s->n_kv_heads * nB * 4) +
          align256(B * s->n_kv_heads * nB * nB * 4);
 }
 
@@ -216,14 +216,14 @@ int dsa_sparse_attn_bwd(const dsa_shape* s, const void* q, const void* k, const 
     return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
   const size_t nB = (size_t)n_blocks(s), B = (size_t)s->batch, N = (size_t)s->seq_len;
   char* p = static_cast<char*>(ws);
-  float* dvec = reinterpret_cast<float*>(p);
-  p += align256(B * s->n_q_heads * N * 4);
+  float* rowstat = reinterpret_cast<float*>(p);
+  p += align256(B * s->n_q_heads * nB * 2 * (size_t)s->block * 4);
   int32_t* inv_cnt = reinterpret_cast<int32_t*>(p);
   p += align256(B * s->n_kv_heads * nB * 4);
   int32_t* inv_idx = reinterpret_cast<int32_t*>(p);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = dsa::launch_bwd_prep(static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), dvec,
-                                      (int64_t)B * s->n_q_heads * N, s->head_dim, st);
+  hipError_t e = dsa::launch_bwd_prep(static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), lse, rowstat,
+                                      (int64_t)B * s->n_q_heads, (int)N, s->head_dim, s->block, (int)nB, st);
   if (e != hipSuccess) return hip_fail(e, "bwd_prep launch");
   e = dsa::launch_bwd_invert(idx, cnt, inv_cnt, inv_idx, (int64_t)B * s->n_kv_heads, (int)nB, prefill_kmax(s), st);
   if (e != hipSuccess) return hip_fail(e, "bwd_invert launch");
@@ -232,8 +232,7 @@ int dsa_sparse_attn_bwd(const dsa_shape* s, const void* q, const void* k, const 
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.dout = static_cast<const uint16_t*>(dout);
-  a.lse = lse;
-  a.dvec = dvec;
+  a.rowstat = rowstat;
   a.idx = idx;
   a.cnt = cnt;
   a.inv_cnt = inv_cnt;

@@ -23,10 +23,12 @@
 //      ends of a tile, so it is double-buffered; V is single-buffered.  Two
 //      barriers per tile;
 //   4. bwd_dkdv_kernel: one workgroup per (batch, KV head, KV block), each
-//      wave 32 keys; K and V stay in LDS, and for every (query block of the
-//      inverted list) x (query head of the group) the Q and dO tiles stream
-//      through LDS: S = Q K^T, dP = dO V^T (Q, dO rows as A operands, K, V
-//      rows as B), P and dS in registers (already in B-operand order), then
+//      wave 32 keys (64-key blocks: two waves per key group, each taking half
+//      of every query tile, added at the end); the waves' K and V operands
+//      sit in registers, and for every (query block of the inverted list) x
+//      (query head of the group) the Q and dO tiles stream through
+//      double-buffered LDS: S = Q K^T, dP = dO V^T (Q, dO rows as A operands,
+//      K, V as B), P and dS in registers (already in B-operand order), then
 //      dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transposed LDS
 //      reads.
 // All tiles in LDS use the row swizzle kswz; the transposed reads of a kswz
@@ -88,23 +90,36 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, pk);
 }
 
-// ============================================================== 1. D = rowsum(dO * O)
+// ============================================================== 1. row statistics
+// rowstat[bh][i][0][r] = lse * log2(e), rowstat[bh][i][1][r] = rowsum(dO * O)
+// for row i BLK + r of head bh; rows past N (the ragged last block) get zeros.
+// d/8 lanes per row, DPP sums.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                                       float* __restrict__ dvec, int64_t n_rows) {
+                                                       const float* __restrict__ lse, float* __restrict__ rowstat,
+                                                       int64_t n_pad_rows, int N, int BLK, int nB) {
   constexpr int TPR = D / 8, RPW = 256 / TPR;
-  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  const int64_t prow = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;  // bh * nB BLK + n
   const int c = threadIdx.x % TPR;
+  const int64_t npad = (int64_t)nB * BLK;
+  const int64_t bh = prow / npad;
+  const int n = (int)(prow % npad);
+  const bool real = prow < n_pad_rows && n < N;
+  const int64_t row = bh * N + n;
   float acc = 0.f;
-  if (row < n_rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + 8 * c);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * c);
+  if (real) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(o + row * D + 8 * c);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc += bf16_lo(a[e]) * bf16_lo(b[e]) + bf16_hi(a[e]) * bf16_hi(b[e]);
+    for (int e = 0; e < 4; ++e) acc += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
   }
 #pragma unroll
   for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < n_rows && c == 0) dvec[row] = acc;
+  if (prow < n_pad_rows && c == 0) {
+    float* st = rowstat + (bh * nB + n / BLK) * 2 * BLK + n % BLK;
+    st[0] = real ? lse[row] * 1.4426950408889634f : 0.f;
+    st[BLK] = acc;
+  }
 }
 
 // ============================================================== 2. inverted selection
@@ -195,8 +210,9 @@ void bwd_dq_kernel(BwdArgs a) {
     qf[ks] = *reinterpret_cast<const u32x4*>(a.q + qrow * D + ks * 16 + 8 * half);
     df[ks] = *reinterpret_cast<const u32x4*>(a.dout + qrow * D + ks * 16 + 8 * half);
   }
-  const float lse2 = a.lse[qrow] * 1.4426950408889634f;  // natural -> log2 units
-  const float drow = a.dvec[qrow];
+  const float* stat = a.rowstat + ((b * a.Hq + h) * a.nB + i) * 2 * BLK + row_in_blk;
+  const float lse2 = stat[0];  // log2 units
+  const float drow = stat[BLK];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(df[ks]));
   asm volatile("" ::"v"(lse2), "v"(drow));
@@ -233,7 +249,7 @@ void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();  // every wave is done reading V(t)
     if (more) load_tile<D, BLK, C::WAVES>(vgp, jn * BLK, N, vbase, wave, lane);
     // ---- dS^T = P^T (dP^T - D), P^T = exp2(s c2 - lse2), causal mask on the diagonal
-    const bool diag = (j == i);
+    const int k_hi = (j == i) ? row_in_blk : BLK;  // kept keys: key_in_blk <= k_hi
     u32x4 dsf[BLK / 16];
 #pragma unroll
     for (int kk = 0; kk < BLK / 16; ++kk) {
@@ -243,9 +259,8 @@ void bwd_dq_kernel(BwdArgs a) {
       for (int e = 0; e < 8; ++e) {
         const int r = rb + e;
         const int key_in_blk = st * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], c2, -lse2));
-        if (diag && key_in_blk > row_in_blk) p = 0.f;
-        v8[e] = p * (dp[st][r] - drow);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], c2, -lse2));
+        v8[e] = (key_in_blk <= k_hi ? p : 0.f) * (dp[st][r] - drow);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) dsf[kk][e] = pack2(v8[2 * e], v8[2 * e + 1]);
@@ -284,74 +299,135 @@ void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ============================================================== 4. dK, dV
+// Waves: KG = BLK / 32 key groups (32 keys each) x QS query splits (2 for
+// 64-row tiles, 1 for 128); a wave accumulates dK^T, dV^T of its keys over
+// its share of every query tile, and the splits are added at the end.  A
+// work item (query tile of one head) is a Q tile, a dO tile and its row
+// statistics; NBUF of them are in flight in LDS.
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2)))
-void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int WAVES = BLK / 32;  // each wave owns 32 keys
-  constexpr int NKS = D / 16;
-  __shared__ __align__(1024) uint16_t Ks[BLK * D];
-  __shared__ __align__(1024) uint16_t Vs[BLK * D];
-  __shared__ __align__(1024) uint16_t Qs[BLK * D];
-  __shared__ __align__(1024) uint16_t Ds[BLK * D];  // dO tile
-  __shared__ float lse_s[BLK], d_s[BLK];
+struct BwdKVCfg {
+  static constexpr int KG = BLK / 32;
+  static constexpr int QS = BLK == 64 ? 2 : 1;
+  static constexpr int WAVES = KG * QS;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int QB_PER_WAVE = (BLK / 32) / QS;  // 32-query sub-blocks per wave per tile
+  static constexpr int TILE = BLK * D;                  // bf16 elements
+  static constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * BLK * 4;
+  static constexpr int NBUF = 3 * STAGE_BYTES <= 100 * 1024 ? 3 : 2;
+  static constexpr int STAT_BYTES_PER_WAVE = 2 * BLK * 4 / WAVES;  // statistics DMA: one instruction per wave
+  static constexpr int LOADS_PER_ITEM = 2 * (TILE * 2 / 1024) / WAVES + 1;  // DMA instructions per wave
+  static_assert(STAT_BYTES_PER_WAVE % 16 == 0 && STAT_BYTES_PER_WAVE <= 1024, "statistics split");
+};
 
-  const int64_t bg = blockIdx.x / a.nB;  // b * Hkv + g
-  const int j = (int)(blockIdx.x % a.nB);
+template <int D, int BLK>
+__global__ __launch_bounds__((BwdKVCfg<D, BLK>::THREADS)) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = BwdKVCfg<D, BLK>;
+  constexpr int NKS = D / 16, NBUF = C::NBUF;
+  // stage s: Q tile tiles[s][0], dO tile tiles[s][1], statistics stats[s]
+  __shared__ __align__(1024) uint16_t tiles[NBUF][2][C::TILE];
+  __shared__ __align__(16) float stats[NBUF][2 * BLK];  // lse log2(e), then D
+
+  // key-block-major order: the long lists of the first blocks (the sink is
+  // kept by every query block) start first; a unit's blocks share an XCD
+  const int64_t n_units = (int64_t)a.B * a.Hkv;
+  const int j = (int)(blockIdx.x / n_units);
+  const int64_t bg = blockIdx.x % n_units;  // b * Hkv + g
+  const int64_t wl = bg * a.nB + j;         // this block's inverted list
   const int64_t b = bg / a.Hkv;
   const int g = (int)(bg % a.Hkv);
   const int G = a.Hq / a.Hkv;
   const int N = a.N;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave % C::KG, qs = wave / C::KG;
   const int half = lane >> 5;
-  const int key_in_blk = wave * 32 + (lane & 31);
+  const int key_in_blk = kg * 32 + (lane & 31);
   const int key = j * BLK + key_in_blk;
-  const LDS_AS uint16_t* ks_l = (const LDS_AS uint16_t*)Ks;
-  const LDS_AS uint16_t* vs_l = (const LDS_AS uint16_t*)Vs;
-  const LDS_AS uint16_t* qs_l = (const LDS_AS uint16_t*)Qs;
-  const LDS_AS uint16_t* ds_l = (const LDS_AS uint16_t*)Ds;
-  const uint32_t qbase = (uint32_t)(uintptr_t)qs_l, dbase = (uint32_t)(uintptr_t)ds_l;
+  const int64_t krow = bg * (int64_t)N + min(key, N - 1);
 
-  load_tile<D, BLK, WAVES>(a.k + bg * (int64_t)N * D, j * BLK, N, (uint32_t)(uintptr_t)ks_l, wave, lane);
-  load_tile<D, BLK, WAVES>(a.v + bg * (int64_t)N * D, j * BLK, N, (uint32_t)(uintptr_t)vs_l, wave, lane);
+  // B operands of this wave's keys (column = key, k-slots = dims 16 ks + 8 half ..)
+  u32x4 kf[NKS], vf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    kf[ks] = *reinterpret_cast<const u32x4*>(a.k + krow * D + ks * 16 + 8 * half);
+    vf[ks] = *reinterpret_cast<const u32x4*>(a.v + krow * D + ks * 16 + 8 * half);
+  }
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
 
-  const int n_list = a.inv_cnt[blockIdx.x];
-  const CONST_AS int32_t* list = (const CONST_AS int32_t*)(a.inv_idx + (int64_t)blockIdx.x * a.nB);
+  const int n_list = a.inv_cnt[wl];
+  const CONST_AS int32_t* list = (const CONST_AS int32_t*)(a.inv_idx + wl * a.nB);
+  const int n_work = n_list * G;
   const float c2 = a.scale_log2;
+
+  // work item w: query block list[w / G], query head g G + w % G, stage w % NBUF.
+  // Every wave issues exactly LOADS_PER_ITEM DMA instructions per item.
+  auto issue = [&](int w) {
+    const int i = list[w / G];
+    const int h = g * G + w % G;
+    const int64_t bh = b * a.Hq + h;
+    const int sg = w % NBUF;
+    const int64_t hrow0 = bh * (int64_t)N;
+    load_tile<D, BLK, C::WAVES>(a.q + hrow0 * D, i * BLK, N, (uint32_t)(uintptr_t)(LDS_AS uint16_t*)tiles[sg][0],
+                                wave, lane);
+    load_tile<D, BLK, C::WAVES>(a.dout + hrow0 * D, i * BLK, N, (uint32_t)(uintptr_t)(LDS_AS uint16_t*)tiles[sg][1],
+                                wave, lane);
+    const float* st = a.rowstat + (bh * a.nB + i) * 2 * BLK;
+    const uint32_t off = (uint32_t)(wave * C::STAT_BYTES_PER_WAVE);
+    if (lane < C::STAT_BYTES_PER_WAVE / 16)
+      dma16(st, off + 16u * (uint32_t)lane,
+            __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS float*)stats[sg] + off));
+  };
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dk[dt] = dv[dt] = (f32x16){};
 
-  const int n_work = n_list * G;
+#pragma unroll
+  for (int w = 0; w < NBUF - 1; ++w)
+    if (w < n_work) issue(w);
   for (int w = 0; w < n_work; ++w) {
+    const int sg = w % NBUF;
     const int i = list[w / G];
-    const int h = g * G + w % G;
-    const int64_t hrow0 = (b * a.Hq + h) * (int64_t)N;
-    if (w > 0) __syncthreads();  // every wave is done with the previous Q, dO tiles
-    load_tile<D, BLK, WAVES>(a.q + hrow0 * D, i * BLK, N, qbase, wave, lane);
-    load_tile<D, BLK, WAVES>(a.dout + hrow0 * D, i * BLK, N, dbase, wave, lane);
-    for (int e = tid; e < BLK; e += BLK * 2) {
-      const int64_t r = hrow0 + min(i * BLK + e, N - 1);
-      lse_s[e] = a.lse[r] * 1.4426950408889634f;
-      d_s[e] = a.dvec[r];
-    }
-    wait_vm<0>();
-    __syncthreads();
-    const bool diag = (i == j);
-    // 32 queries at a time: S = Q K^T, dP = dO V^T (M = queries, N = keys)
-#pragma unroll 1
-    for (int qb = 0; qb < BLK / 32; ++qb) {
-      f32x16 s = (f32x16){}, dp = (f32x16){};
+    // item w resident: the items issued after it may still be in flight
+    if (w + NBUF - 2 < n_work) wait_vm<(NBUF - 2) * C::LOADS_PER_ITEM>();
+    else wait_vm<0>();
+    __syncthreads();  // every wave is done with item w - 1, whose stage is refilled next
+    if (w + NBUF - 1 < n_work) issue(w + NBUF - 1);
+    const LDS_AS uint16_t* qs_l = (const LDS_AS uint16_t*)tiles[sg][0];
+    const LDS_AS uint16_t* os_l = (const LDS_AS uint16_t*)tiles[sg][1];
+    const LDS_AS float* st_l = (const LDS_AS float*)stats[sg];
+    // kept: query >= key on the diagonal block, query < N (branch-free)
+    const int q_lo = (i == j) ? key_in_blk : 0;
+    const int q_hi = N - i * BLK;
+#pragma unroll
+    for (int qq = 0; qq < C::QB_PER_WAVE; ++qq) {
+      const int qb = qs * C::QB_PER_WAVE + qq;
       const int qr = qb * 32 + (lane & 31);
+      // statistics of this lane's 16 query rows: qb 32 + 8 t + 4 half + {0..3}
+      f32x4 lse4[4], d4[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        lse4[t] = *reinterpret_cast<const LDS_AS f32x4*>(st_l + qb * 32 + 8 * t + 4 * half);
+        d4[t] = *reinterpret_cast<const LDS_AS f32x4*>(st_l + BLK + qb * 32 + 8 * t + 4 * half);
+      }
+      // S = Q K^T, dP = dO V^T (M = queries, N = keys); Q, dO row reads one
+      // k-step ahead of their MFMAs
+      f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
+      u32x4 qa = read_row<D>(qs_l, qr, 0, half), oa = read_row<D>(os_l, qr, 0, half);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_row<D>(qs_l, qr, ks, half)),
-                                                    as_bf16x8(read_row<D>(ks_l, key_in_blk, ks, half)), s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_row<D>(ds_l, qr, ks, half)),
-                                                     as_bf16x8(read_row<D>(vs_l, key_in_blk, ks, half)), dp, 0, 0, 0);
+        u32x4 qn = qa, on = oa;
+        if (ks + 1 < NKS) {
+          qn = read_row<D>(qs_l, qr, ks + 1, half);
+          on = read_row<D>(os_l, qr, ks + 1, half);
+        }
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), as_bf16x8(kf[ks]), sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(oa), as_bf16x8(vf[ks]), dpacc, 0, 0, 0);
+        qa = qn;
+        oa = on;
       }
-      // element r: query qb * 32 + 8 (r / 4) + 4 half + r % 4, this lane's key.
+      // element r: query qb 32 + 8 (r / 4) + 4 half + r % 4, this lane's key.
       // P and dS packed to bf16 in B-operand order (k-chunk kk: elements 8 kk .. 8 kk + 7)
       u32x4 pf[2], sf[2];
 #pragma unroll
@@ -361,11 +437,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * kk + e;
           const int q_in_blk = qb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const int qrow = i * BLK + q_in_blk;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse_s[q_in_blk]));
-          if ((diag && key_in_blk > q_in_blk) || qrow >= N) p = 0.f;
-          pv[e] = p;
-          dsv[e] = p * (dp[r] - d_s[q_in_blk]);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c2, -lse4[r >> 2][r & 3]));
+          const bool keep = (q_in_blk >= q_lo) & (q_in_blk < q_hi);
+          pv[e] = keep ? p : 0.f;
+          dsv[e] = pv[e] * (dpacc[r] - d4[r >> 2][r & 3]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -381,7 +456,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         for (int dt = 0; dt < D / 32; ++dt) {
           const int d = dt * 32 + 16 * grp + 4 * (si & 3);
           const int rb = qb * 32 + 16 * kk + 4 * half + (si >> 2);
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_tr<D>(ds_l, rb, d)), as_bf16x8(pf[kk]),
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_tr<D>(os_l, rb, d)), as_bf16x8(pf[kk]),
                                                            dv[dt], 0, 0, 0);
           dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_tr<D>(qs_l, rb, d)), as_bf16x8(sf[kk]),
                                                            dk[dt], 0, 0, 0);
@@ -391,10 +466,36 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
   wait_vm<0>();
 
+  // ---- add the query splits through LDS (the tile buffers are free now)
+  if constexpr (C::QS > 1) {
+    static_assert(C::QS == 2, "two query splits");
+    static_assert(C::KG * 2 * (D / 32) * 16 * 64 * 4 <= sizeof(tiles), "split merge fits the tile buffers");
+    float* red = reinterpret_cast<float*>(&tiles[0][0][0]);  // [kg][dk/dv][dt][r][lane]
+    __syncthreads();
+    if (qs == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          red[(((kg * 2 + 0) * (D / 32) + dt) * 16 + r) * 64 + lane] = dk[dt][r];
+          red[(((kg * 2 + 1) * (D / 32) + dt) * 16 + r) * 64 + lane] = dv[dt][r];
+        }
+    }
+    __syncthreads();
+    if (qs == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[dt][r] += red[(((kg * 2 + 0) * (D / 32) + dt) * 16 + r) * 64 + lane];
+        dv[dt][r] += red[(((kg * 2 + 1) * (D / 32) + dt) * 16 + r) * 64 + lane];
+      }
+  }
+
   // ---- dK = s dS^T Q, dV = P^T dO (bf16); a block no row kept gets zeros
   if (key < N) {
-    uint16_t* krow = a.dk + (bg * (int64_t)N + key) * D;
-    uint16_t* vrow = a.dv + (bg * (int64_t)N + key) * D;
+    uint16_t* kout = a.dk + (bg * (int64_t)N + key) * D;
+    uint16_t* vout = a.dv + (bg * (int64_t)N + key) * D;
     const float sc = a.scale;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
@@ -405,21 +506,24 @@ void bwd_dkdv_kernel(BwdArgs a) {
         wk[1] = pack2(dk[dt][4 * q4 + 2] * sc, dk[dt][4 * q4 + 3] * sc);
         wv[0] = pack2(dv[dt][4 * q4 + 0], dv[dt][4 * q4 + 1]);
         wv[1] = pack2(dv[dt][4 * q4 + 2], dv[dt][4 * q4 + 3]);
-        *reinterpret_cast<u32x2*>(krow + dt * 32 + 8 * q4 + 4 * half) = wk;
-        *reinterpret_cast<u32x2*>(vrow + dt * 32 + 8 * q4 + 4 * half) = wv;
+        *reinterpret_cast<u32x2*>(kout + dt * 32 + 8 * q4 + 4 * half) = wk;
+        *reinterpret_cast<u32x2*>(vout + dt * 32 + 8 * q4 + 4 * half) = wv;
       }
     }
   }
 }
 
 // ============================================================== launch
-hipError_t launch_bwd_prep(const uint16_t* o, const uint16_t* dout, float* dvec, int64_t n_rows, int d,
-                           hipStream_t stream) {
-  if (n_rows == 0) return hipSuccess;
+hipError_t launch_bwd_prep(const uint16_t* o, const uint16_t* dout, const float* lse, float* rowstat, int64_t n_heads,
+                           int N, int d, int block, int nB, hipStream_t stream) {
+  const int64_t n_pad_rows = n_heads * nB * (int64_t)block;
+  if (n_pad_rows == 0) return hipSuccess;
   const int rpw = 256 / (d / 8);
-  const dim3 grid((uint32_t)((n_rows + rpw - 1) / rpw)), blk(256);
-  if (d == 64) hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, blk, 0, stream, o, dout, dvec, n_rows);
-  else hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, blk, 0, stream, o, dout, dvec, n_rows);
+  const dim3 grid((uint32_t)((n_pad_rows + rpw - 1) / rpw)), blk(256);
+  if (d == 64)
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, blk, 0, stream, o, dout, lse, rowstat, n_pad_rows, N, block, nB);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, blk, 0, stream, o, dout, lse, rowstat, n_pad_rows, N, block, nB);
   return hipGetLastError();
 }
 
@@ -455,7 +559,7 @@ static hipError_t launch_bwd_d_blk(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t n_wg = (int64_t)a.B * a.Hkv * a.nB;
   if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BLK>), dim3((uint32_t)n_wg), dim3(BLK * 2), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BLK>), dim3((uint32_t)n_wg), dim3(BwdKVCfg<D, BLK>::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 

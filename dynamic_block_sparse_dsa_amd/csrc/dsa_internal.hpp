@@ -87,8 +87,7 @@ struct BwdArgs {
   const uint16_t* k;     // [B, Hkv, N, d]
   const uint16_t* v;
   const uint16_t* dout;  // [B, Hq, N, d]
-  const float* lse;      // [B, Hq, N] natural log
-  const float* dvec;     // [B, Hq, N] rowsum(dO * O)
+  const float* rowstat;  // [B, Hq, nB, 2, block]: lse log2(e), then rowsum(dO * O); zeros past N
   const int32_t* idx;    // [B, Hkv, nB, kmax]
   const int32_t* cnt;    // [B, Hkv, nB]
   const int32_t* inv_cnt;  // [B, Hkv, nB]
@@ -100,8 +99,8 @@ struct BwdArgs {
   float scale;       // 1 / sqrt(d)
   float scale_log2;  // log2(e) / sqrt(d)
 };
-hipError_t launch_bwd_prep(const uint16_t* o, const uint16_t* dout, float* dvec, int64_t n_rows, int d,
-                           hipStream_t stream);
+hipError_t launch_bwd_prep(const uint16_t* o, const uint16_t* dout, const float* lse, float* rowstat, int64_t n_heads,
+                           int N, int d, int block, int nB, hipStream_t stream);
 hipError_t launch_bwd_invert(const int32_t* idx, const int32_t* cnt, int32_t* inv_cnt, int32_t* inv_idx,
                              int64_t n_units, int nB, int kmax, hipStream_t stream);
 hipError_t launch_sparse_attn_bwd(const BwdArgs& a, int d, int block, hipStream_t stream);

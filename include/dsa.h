@@ -163,8 +163,9 @@ int dsa_decode(const dsa_shape* shape, const void* q, const void* k_cache, const
  * dV = P^T dO; dK and dV of a KV head sum its group's query heads.  Keys no
  * row kept get zero gradients. */
 
-/* Workspace for dsa_sparse_attn_bwd, in bytes: D [B, Hq, N] fp32 and the
- * inverted selection (per KV block, the query blocks that kept it)
+/* Workspace for dsa_sparse_attn_bwd, in bytes: per query row the LSE in
+ * log2 units and D, fp32 [B, Hq, nB, 2, block] (rows past N zero-padded),
+ * and the inverted selection (per KV block, the query blocks that kept it)
  * [B, Hkv, nB] + [B, Hkv, nB, nB] int32. */
 size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape);
 
