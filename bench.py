@@ -28,6 +28,7 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "attn_fwd.hip")
 DECODE_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "decode.hip")
+BWD_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "attn_bwd.hip")
 
 
 def src_hash(path):
@@ -194,7 +195,8 @@ def bench_backward(args, dev, stream, inputs):
     return dict(value=B * N / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
                 config=dict(workload=w.name),
                 roofline=dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                              frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
+                              frac=round(tflops / PEAK_BF16_TFLOPS, 4),
+                              traffic=measured_traffic("backward_" + w.name, BWD_SRC),
                               kernel="backward step: prep, invert, dq, dkdv", flops_per_step=flops))
 
 

@@ -2,10 +2,13 @@
 
     python3 -m dynamic_block_sparse_dsa_amd.profile_run attn   --workload prefill_n8192_h32 --reps 3
     python3 -m dynamic_block_sparse_dsa_amd.profile_run decode --workload decode_s32_l65536 --reps 3
+    python3 -m dynamic_block_sparse_dsa_amd.profile_run bwd    --workload prefill_n8192_h32 --reps 3
     python3 -m dynamic_block_sparse_dsa_amd.profile_run copy   --mib 256 --reps 3
 
 ``attn`` selects once (dsa_prefill) and then launches dsa_sparse_attn_fwd
-``reps`` times on the same indices; ``decode`` runs ``reps`` decode steps;
+``reps`` times on the same indices; ``bwd`` selects and attends once and then
+launches dsa_sparse_attn_bwd ``reps`` times (seeded output gradient);
+``decode`` runs ``reps`` decode steps;
 ``copy`` copies a ``mib`` MiB device buffer into another ``reps`` times (a plain
 copy kernel of known size: it reads and writes exactly ``mib`` MiB), which
 calibrates the HBM byte counters.  Each launch is followed by a device
@@ -29,6 +32,22 @@ def run_attn(w, reps, stream):
     torch.cuda.synchronize()
     for _ in range(reps):
         dsa.dsa_sparse_attn_fwd(shape, q, k, v, idx, cnt, o, lse, stream=stream)
+        stream.synchronize()
+
+
+def run_bwd(w, reps, stream):
+    q, k, v = make_prefill(w, device="cuda")
+    o, lse, idx, cnt = dsa.prefill(q, k, v, w.block, w.topk, w.topk_num, w.topk_den)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    dout = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    shape = dsa.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block, w.topk, w.topk_num,
+                           w.topk_den)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(dsa.dsa_attn_bwd_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dsa.dsa_sparse_attn_bwd(shape, q, k, v, o, lse, dout, idx, cnt, dq, dk, dv, ws, stream=stream)
         stream.synchronize()
 
 
@@ -61,7 +80,7 @@ def run_copy(mib, reps, stream):
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("what", choices=["attn", "decode", "copy"])
+    ap.add_argument("what", choices=["attn", "bwd", "decode", "copy"])
     ap.add_argument("--workload", default=None)
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--mib", type=int, default=256)
@@ -73,7 +92,7 @@ def main(argv=None):
     else:
         name = a.workload or ("decode_s32_l65536" if a.what == "decode" else "prefill_n8192_h32")
         w = WORKLOADS[name]
-        (run_attn if a.what == "attn" else run_decode)(w, a.reps, stream)
+        dict(attn=run_attn, bwd=run_bwd, decode=run_decode)[a.what](w, a.reps, stream)
     torch.cuda.synchronize()
     print(f"profile_run {a.what} done", flush=True)
 
