@@ -14,6 +14,9 @@ What it computes, step by step, in the order the method runs:
                         grouped-query attention the max over the group's heads.
   O3 ``select_row`` /  keep the k best-scoring blocks per query block, with the
      ``select_topk``   sink block 0 and the diagonal block always kept.
+     variants (``SelectSpec``): global anchors + a local window as the forced
+     set; threshold selection on the row's block softmax; a budget from the
+     entropy of that softmax; ``bitmap`` packs a selection into bit words.
   O4 ``attend``        softmax(s * q k^T) v over exactly the keys of the kept
                         blocks that are causally visible to each row.
   ``prefill`` / ``decode`` chain O1-O4.
@@ -44,7 +47,13 @@ Readings where the pages leave a point open (all listed in the design doc):
     visible; the forced "diagonal" block is the last block;
   * query head h reads KV head floor(h / G);
   * backward: the selection is a discrete choice and is held constant; dK and
-    dV of a KV head sum the contributions of its G query heads.
+    dV of a KV head sum the contributions of its G query heads;
+  * selection variants: the forced set is the first ``anchors`` blocks and
+    the last ``window`` visible blocks (the window ends at the row's own
+    block); a row's block distribution is the softmax of its visible block
+    scores; threshold mode keeps the candidates whose share is >= tau;
+    entropy mode keeps ceil(exp(H)) blocks (H the Shannon entropy of that
+    distribution, nats), clamped to [k_min, k_max], then runs the top-k.
 
 Parity status: every function here is pinned by tests in ``tests/`` that do
 not re-use this module's formulas (dense special case against a library
@@ -65,6 +74,44 @@ FORCE_DIAG = 2  # keep the row's own (diagonal / last visible) block
 # near-tie rule for flagging rows (see ``near``)
 TIE_REL = 1e-3
 TIE_ABS = 1e-6
+
+# selection modes (``SelectSpec.mode``)
+SELECT_TOPK = 0
+SELECT_THRESHOLD = 1
+SELECT_ENTROPY = 2
+# a candidate whose block share is within THR_REL (relative) of the threshold
+# may be kept or dropped; an exp(entropy) within ENT_REL (relative) of an
+# integer may round either way
+THR_REL = 1e-3
+ENT_REL = 1e-4
+
+
+@dataclass(frozen=True)
+class SelectSpec:
+    """How a row's kept set is chosen beyond the plain top-k.
+
+    ``anchors``: with FORCE_SINK, blocks 0 .. anchors-1 are forced (global
+    anchors; 1 = the sink alone).  ``window``: with FORCE_DIAG, the last
+    ``window`` visible blocks are forced (a local window ending at the row's
+    own block; 1 = the diagonal alone).  ``mode``: SELECT_TOPK (budget from
+    topk or the fraction), SELECT_THRESHOLD (keep candidates whose share of
+    the row's block softmax is >= ``threshold``) or SELECT_ENTROPY (budget
+    ceil(exp(H)) clamped to [k_min, k_max]).
+
+    [ZB] "基于Top-k选择的局部-全局混合" (local window + global tokens);
+    [NSA] section 2.2 (block-sparsify the fp32 scores with a threshold);
+    [ZB] "模型精度与稀疏度的动态平衡" and "工程实践建议" (set k or the threshold
+    from the attention entropy; keep more when the entropy is high)."""
+
+    mode: int = SELECT_TOPK
+    anchors: int = 1
+    window: int = 1
+    threshold: float = 0.0
+    k_min: int = 0
+    k_max: int = 0
+
+
+DEFAULT_SPEC = SelectSpec()
 
 
 def n_blocks(n: int, block: int) -> int:
@@ -145,19 +192,69 @@ def row_budget(n_visible: int, topk: int, num: int, den: int, n_forced: int) -> 
     return min(max(k, n_forced), n_visible)
 
 
-def forced_set(n_visible: int, flags: int) -> list[int]:
-    """Blocks kept regardless of score: the sink (block 0) and the row's own
-    block (the last visible one).
+def forced_set(n_visible: int, flags: int, anchors: int = 1, window: int = 1) -> list[int]:
+    """Blocks kept regardless of score: the global anchors (blocks 0 ..
+    anchors-1; anchors = 1 is the sink) and the local window (the last
+    ``window`` visible blocks; window = 1 is the row's own block).
 
     [ZB] "基于Top-k选择的局部-全局混合": global tokens plus a local window;
     [SvF] section 1 hybrid mode: local window plus periodic global anchors.
     """
     f = set()
     if flags & FORCE_SINK:
-        f.add(0)
+        f.update(range(min(anchors, n_visible)))
     if flags & FORCE_DIAG:
-        f.add(n_visible - 1)
+        f.update(range(max(n_visible - window, 0), n_visible))
     return sorted(f)
+
+
+def block_shares(scores: np.ndarray) -> np.ndarray:
+    """The row's block distribution: softmax of its visible block scores,
+    p_j = exp(S_j) / sum_c exp(S_c) (the largest score is subtracted first,
+    which leaves the quotient unchanged)."""
+    sc = np.asarray(scores, dtype=np.float64)
+    e = np.exp(sc - sc.max())
+    return e / e.sum()
+
+
+def block_entropy(scores: np.ndarray) -> float:
+    """Shannon entropy (nats) of the row's block distribution, -sum p log p
+    (terms with p = 0 contribute 0)."""
+    p = block_shares(scores)
+    nz = p[p > 0]
+    return float(-(nz * np.log(nz)).sum())
+
+
+def entropy_budgets(scores: np.ndarray, n_visible: int, k_min: int, k_max: int, n_forced: int) -> list[int]:
+    """Budget of an entropy-mode row: ceil(exp(H)) -- the effective number of
+    blocks the row attends to -- clamped to [k_min, k_max], raised to the
+    forced count and capped at the visible count.  When exp(H) is within
+    ENT_REL of an integer n, fp32 can land on either side of it: both budgets
+    (from n and from n + 1) are returned."""
+    e = math.exp(block_entropy(np.asarray(scores)[:n_visible]))
+
+    def fit(k):
+        return min(max(min(max(k, k_min), k_max), n_forced), n_visible)
+
+    n = round(e)
+    if abs(e - n) <= ENT_REL * e:
+        return sorted({fit(n), fit(n + 1)})
+    return [fit(math.ceil(e))]
+
+
+def threshold_row(scores: np.ndarray, n_visible: int, tau: float, forced: list) -> "RowSelection":
+    """Threshold selection of one row: the forced blocks plus every candidate
+    whose share of the row's block distribution is >= tau.  [NSA] section 2.2
+    block-sparsifies the fp32 scores with a threshold.  Candidates whose share
+    is within THR_REL of tau form a band: an accepted set may keep or drop
+    each of them."""
+    p = block_shares(np.asarray(scores, dtype=np.float64)[:n_visible])
+    fs = set(forced)
+    cand = [j for j in range(n_visible) if j not in fs]
+    keep = {j for j in cand if p[j] >= tau}
+    band = {j for j in cand if abs(p[j] - tau) <= THR_REL * tau}
+    return RowSelection(idx=sorted(fs | keep), forced=sorted(fs), must=keep - band, band=band, need=-1,
+                        flagged=bool(band))
 
 
 def near(a: float, b: float) -> bool:
@@ -178,8 +275,10 @@ class RowSelection:
 
     ``idx``: the kept blocks, ascending.  ``forced``: blocks kept regardless.
     ``must``: candidates any accepted set contains.  ``band``: near-tie
-    candidates of which exactly ``need`` are kept.  Unflagged rows have an
-    empty band (the selection is unique)."""
+    candidates of which exactly ``need`` are kept (need = -1: any number).
+    ``alts``: other selections that are equally correct (an entropy budget
+    that fp32 may round either way).  Unflagged rows have an empty band and
+    no alternatives (the selection is unique)."""
 
     idx: list
     forced: list
@@ -187,6 +286,7 @@ class RowSelection:
     band: set = field(default_factory=set)
     need: int = 0
     flagged: bool = False
+    alts: list = field(default_factory=list)
 
 
 def select_row(scores: np.ndarray, n_visible: int, k_budget: int, forced: list) -> RowSelection:
@@ -222,27 +322,43 @@ def select_row(scores: np.ndarray, n_visible: int, k_budget: int, forced: list) 
     return RowSelection(idx=sel, forced=sorted(fs), must=must, band=band, need=m - lo, flagged=True)
 
 
-def kmax(n_rows: int, topk: int, num: int, den: int, flags: int, causal: bool, n_cols: int) -> int:
-    """Largest per-row budget: the width of the index array."""
+def spec_tau(spec: SelectSpec) -> float:
+    """The threshold as the fp32 value a caller's float carries."""
+    return float(np.float32(spec.threshold))
+
+
+def kmax(n_rows: int, topk: int, num: int, den: int, flags: int, causal: bool, n_cols: int,
+         spec: SelectSpec = DEFAULT_SPEC) -> int:
+    """Largest per-row count of kept blocks: the width of the index array.
+    Threshold mode: the forced blocks plus floor(1 / tau), the most candidates
+    whose shares can each reach tau (the shares sum to 1)."""
     best = 0
     for i in range(n_rows):
         nv = i + 1 if causal else n_cols
-        best = max(best, row_budget(nv, topk, num, den, len(forced_set(nv, flags))))
+        nf = len(forced_set(nv, flags, spec.anchors, spec.window))
+        if spec.mode == SELECT_THRESHOLD:
+            k = min(nv, nf + math.floor(1.0 / spec_tau(spec)))
+        elif spec.mode == SELECT_ENTROPY:
+            k = min(max(spec.k_max, nf), nv)
+        else:
+            k = row_budget(nv, topk, num, den, nf)
+        best = max(best, k)
     return best
 
 
 def select_topk(scores: np.ndarray, topk: int, num: int = 0, den: int = 1, flags: int = FORCE_SINK | FORCE_DIAG,
-                causal: bool = True):
+                causal: bool = True, spec: SelectSpec = DEFAULT_SPEC):
     """Row-wise selection over a score array [..., R, C].
 
     causal=True (prefill): row i sees blocks 0..i.  causal=False (decode):
-    every row sees all C blocks.  Returns (idx, cnt, rows) where idx is int32
-    [..., R, kmax] ascending and -1 padded, cnt is int32 [..., R] and rows is a
-    flat list of ``RowSelection`` in C order.
+    every row sees all C blocks.  ``spec`` picks the forced set and the mode
+    (plain top-k by default).  Returns (idx, cnt, rows) where idx is int32
+    [..., R, kmax] ascending and -1 padded, cnt is int32 [..., R] and rows is
+    a flat list of ``RowSelection`` in C order.
     """
     lead = scores.shape[:-2]
     R, C = scores.shape[-2:]
-    km = kmax(R, topk, num, den, flags, causal, C)
+    km = kmax(R, topk, num, den, flags, causal, C, spec)
     flat = scores.reshape((-1, R, C))
     idx = np.full((flat.shape[0], R, km), -1, dtype=np.int32)
     cnt = np.zeros((flat.shape[0], R), dtype=np.int32)
@@ -250,13 +366,39 @@ def select_topk(scores: np.ndarray, topk: int, num: int = 0, den: int = 1, flags
     for u in range(flat.shape[0]):
         for i in range(R):
             nv = i + 1 if causal else C
-            f = forced_set(nv, flags)
-            kb = row_budget(nv, topk, num, den, len(f))
-            rs = select_row(flat[u, i, :nv], nv, kb, f)
+            f = forced_set(nv, flags, spec.anchors, spec.window)
+            row = flat[u, i, :nv]
+            if spec.mode == SELECT_THRESHOLD:
+                rs = threshold_row(row, nv, spec_tau(spec), f)
+            elif spec.mode == SELECT_ENTROPY:
+                ks = entropy_budgets(row, nv, spec.k_min, spec.k_max, len(f))
+                rs = select_row(row, nv, ks[0], f)
+                if len(ks) > 1:
+                    rs.alts = [select_row(row, nv, kb, f) for kb in ks[1:]]
+                    rs.flagged = True
+            else:
+                rs = select_row(row, nv, row_budget(nv, topk, num, den, len(f)), f)
             idx[u, i, : len(rs.idx)] = rs.idx
             cnt[u, i] = len(rs.idx)
             rows.append(rs)
     return idx.reshape(lead + (R, km)), cnt.reshape(lead + (R,)), rows
+
+
+def bitmap(idx: np.ndarray, cnt: np.ndarray, n_cols: int) -> np.ndarray:
+    """A selection as bit words: [..., ceil(n_cols / 32)] uint32 with bit
+    j % 32 of word j // 32 set when block j is kept.  [ZB] "工程实践建议":
+    store the sparse index as a compressed bitmap rather than a full index
+    array."""
+    words = (n_cols + 31) // 32
+    lead = cnt.shape
+    out = np.zeros(lead + (words,), dtype=np.uint32)
+    fi = idx.reshape((-1, idx.shape[-1]))
+    fc = cnt.reshape(-1)
+    fo = out.reshape((-1, words))
+    for r in range(fc.size):
+        for j in fi[r, : fc[r]]:
+            fo[r, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -371,7 +513,7 @@ def attend_backward(q, k, v, do, idx, cnt, block: int, units=None, o=None):
 # Whole paths
 # --------------------------------------------------------------------------
 def prefill(q, k, v, block: int, topk: int, num: int = 0, den: int = 1, flags: int = FORCE_SINK | FORCE_DIAG,
-            attend_blocks=None):
+            attend_blocks=None, spec: SelectSpec = DEFAULT_SPEC):
     """Pool -> score -> select -> attend (O1-O4) for a causal prefill.
 
     ``attend_blocks`` optionally restricts O4 to a list of (b, h, i) query
@@ -385,13 +527,13 @@ def prefill(q, k, v, block: int, topk: int, num: int = 0, den: int = 1, flags: i
     scale = 1.0 / math.sqrt(d)
     qbar, kbar = block_means(q, block), block_means(k, block)
     scores = block_scores(qbar, kbar, scale)
-    idx, cnt, rows = select_topk(scores, topk, num, den, flags, causal=True)
+    idx, cnt, rows = select_topk(scores, topk, num, den, flags, causal=True, spec=spec)
     o, lse = attend(q, k, v, idx, cnt, block, units=attend_blocks)
     return dict(qbar=qbar, kbar=kbar, scores=scores, idx=idx, cnt=cnt, rows=rows, o=o, lse=lse)
 
 
 def decode(q, kc, vc, block: int, topk: int, num: int = 0, den: int = 1, flags: int = FORCE_SINK | FORCE_DIAG,
-           units=None):
+           units=None, spec: SelectSpec = DEFAULT_SPEC):
     """One decode step for S sequences (O1-O4 with a single query row).
 
     q: [S, Hq, d] -- the new token of each sequence, which sits at the last
@@ -417,7 +559,7 @@ def decode(q, kc, vc, block: int, topk: int, num: int = 0, den: int = 1, flags: 
         for g in range(Hkv):
             per_head = [scale * (kbar[s, g] @ q[s, h]) for h in range(g * G, (g + 1) * G)]
             scores[s, g, 0] = np.max(np.stack(per_head), axis=0)
-    idx, cnt, rows = select_topk(scores, topk, num, den, flags, causal=False)
+    idx, cnt, rows = select_topk(scores, topk, num, den, flags, causal=False, spec=spec)
     idx, cnt = idx[:, :, 0], cnt[:, :, 0]
     o = np.zeros((S, Hq, d))
     lse = np.zeros((S, Hq))
@@ -434,9 +576,20 @@ def decode(q, kc, vc, block: int, topk: int, num: int = 0, den: int = 1, flags: 
 
 def accepts(rs: RowSelection, got: list) -> tuple[bool, str]:
     """Whether a selection ``got`` (ascending block ids, no padding) is a
-    correct answer for the row described by ``rs``: it holds every forced
-    block and every ``must`` candidate, its other candidates all lie in the
-    near-tie band, it takes exactly ``need`` of them, and it is ascending."""
+    correct answer for the row described by ``rs`` or one of its
+    alternatives: it holds every forced block and every ``must`` candidate,
+    its other candidates all lie in the near-tie band, it takes exactly
+    ``need`` of them (any number when need = -1), and it is ascending."""
+    ok, why = _accepts_one(rs, got)
+    if ok:
+        return ok, why
+    for alt in rs.alts:
+        if _accepts_one(alt, got)[0]:
+            return True, ""
+    return False, why
+
+
+def _accepts_one(rs: RowSelection, got: list) -> tuple[bool, str]:
     if list(got) != sorted(set(got)):
         return False, f"not ascending/unique: {got}"
     gs = set(got)
@@ -448,6 +601,6 @@ def accepts(rs: RowSelection, got: list) -> tuple[bool, str]:
     extra = t - rs.must
     if not extra <= rs.band:
         return False, f"outside selection/band: {sorted(extra - rs.band)}"
-    if len(extra) != rs.need:
+    if rs.need >= 0 and len(extra) != rs.need:
         return False, f"takes {len(extra)} from the tie band, needs {rs.need}"
     return True, ""
