@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import ctypes
 import functools
+import math
 import os
 
 import torch
@@ -23,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 FORCE_SINK = 1
 FORCE_DIAG = 2
+SELECT_TOPK, SELECT_THRESHOLD, SELECT_ENTROPY = 0, 1, 2
 MAX_BLOCKS = 4096
 
 DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4, -5
@@ -33,6 +35,7 @@ EXPORTS = [
     "dsa_block_means",
     "dsa_block_scores",
     "dsa_select_topk",
+    "dsa_indices_to_bitmap",
     "dsa_sparse_attn_fwd",
     "dsa_prefill_workspace_bytes",
     "dsa_prefill",
@@ -60,6 +63,12 @@ class Shape(ctypes.Structure):
         ("topk_num", ctypes.c_int32),
         ("topk_den", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("select_mode", ctypes.c_int32),
+        ("n_anchor", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("threshold", ctypes.c_float),
+        ("k_min", ctypes.c_int32),
+        ("k_max", ctypes.c_int32),
     ]
 
     @property
@@ -68,8 +77,10 @@ class Shape(ctypes.Structure):
 
 
 def make_shape(batch, n_q_heads, n_kv_heads, seq_len, head_dim, block, topk=0, topk_num=0, topk_den=1,
-               flags=FORCE_SINK | FORCE_DIAG) -> Shape:
-    return Shape(batch, n_q_heads, n_kv_heads, seq_len, head_dim, block, topk, topk_num, topk_den, flags)
+               flags=FORCE_SINK | FORCE_DIAG, select_mode=SELECT_TOPK, n_anchor=0, window=0, threshold=0.0, k_min=0,
+               k_max=0) -> Shape:
+    return Shape(batch, n_q_heads, n_kv_heads, seq_len, head_dim, block, topk, topk_num, topk_den, flags, select_mode,
+                 n_anchor, window, threshold, k_min, k_max)
 
 
 class DsaError(RuntimeError):
@@ -96,6 +107,7 @@ def load() -> ctypes.CDLL:
         "dsa_block_means": ([S, I32, P, P, P], ctypes.c_int),
         "dsa_block_scores": ([S, P, P, P, P], ctypes.c_int),
         "dsa_select_topk": ([S, P, P, P, P], ctypes.c_int),
+        "dsa_indices_to_bitmap": ([P, P, ctypes.c_int64, I32, I32, P, P], ctypes.c_int),
         "dsa_sparse_attn_fwd": ([S, P, P, P, P, P, P, P, P], ctypes.c_int),
         "dsa_prefill_workspace_bytes": ([S], SZ),
         "dsa_prefill": ([S, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
@@ -201,6 +213,18 @@ def dsa_select_topk(shape: Shape, scores, idx, cnt, stream=None):
                                   _ptr(cnt, torch.int32, (B, Hkv, nB), "cnt"), _stream(stream)))
 
 
+def dsa_indices_to_bitmap(idx, cnt, n_cols: int, bitmap, stream=None):
+    """idx [..., kmax] int32, cnt [...] int32 or None; bitmap [..., ceil(n_cols/32)]
+    int32 (the uint32 words' bits)."""
+    if not isinstance(idx, torch.Tensor):
+        raise TypeError("idx must be a torch tensor")
+    lead, km = tuple(idx.shape[:-1]), int(idx.shape[-1])
+    n_rows = math.prod(lead)
+    _check(load().dsa_indices_to_bitmap(
+        _ptr(idx, torch.int32, lead + (km,), "idx"), _ptr(cnt, torch.int32, lead, "cnt", optional=True), n_rows, km,
+        n_cols, _ptr(bitmap, torch.int32, lead + ((n_cols + 31) // 32,), "bitmap"), _stream(stream)))
+
+
 def dsa_sparse_attn_fwd(shape: Shape, q, k, v, idx, cnt, o, lse=None, stream=None):
     B, Hq, Hkv, N, d, nB = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_len, shape.head_dim, shape.n_blocks
     km = dsa_prefill_kmax(shape)
@@ -267,10 +291,11 @@ def dsa_decode(shape: Shape, q, k_cache, v_cache, kbar, o, lse, idx, ws, stream=
 
 # ----------------------------------------------------------------- conveniences
 def prefill(q, k, v, block: int, topk: int = 0, topk_num: int = 0, topk_den: int = 1,
-            flags: int = FORCE_SINK | FORCE_DIAG, want_lse: bool = True, stream=None):
-    """Fused prefill; allocates O, LSE, idx, cnt and the workspace."""
+            flags: int = FORCE_SINK | FORCE_DIAG, want_lse: bool = True, stream=None, **select):
+    """Fused prefill; allocates O, LSE, idx, cnt and the workspace.  ``select``:
+    select_mode, n_anchor, window, threshold, k_min, k_max (see make_shape)."""
     B, Hq, N, d = q.shape
-    shape = make_shape(B, Hq, k.shape[1], N, d, block, topk, topk_num, topk_den, flags)
+    shape = make_shape(B, Hq, k.shape[1], N, d, block, topk, topk_num, topk_den, flags, **select)
     km = dsa_prefill_kmax(shape)
     dev = q.device
     o = torch.empty_like(q)
@@ -283,11 +308,12 @@ def prefill(q, k, v, block: int, topk: int = 0, topk_num: int = 0, topk_den: int
 
 
 def attn_backward(q, k, v, o, lse, dout, idx, cnt, block: int, topk: int = 0, topk_num: int = 0, topk_den: int = 1,
-                  flags: int = FORCE_SINK | FORCE_DIAG, stream=None):
+                  flags: int = FORCE_SINK | FORCE_DIAG, stream=None, **select):
     """Gradients of the sparse attention (selection held fixed); allocates
-    dq, dk, dv and the workspace.  idx/cnt/o/lse as returned by prefill."""
+    dq, dk, dv and the workspace.  idx/cnt/o/lse as returned by prefill
+    (with the same selection arguments)."""
     B, Hq, N, d = q.shape
-    shape = make_shape(B, Hq, k.shape[1], N, d, block, topk, topk_num, topk_den, flags)
+    shape = make_shape(B, Hq, k.shape[1], N, d, block, topk, topk_num, topk_den, flags, **select)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(max(1, dsa_attn_bwd_workspace_bytes(shape)), dtype=torch.uint8, device=q.device)
     dsa_sparse_attn_bwd(shape, q, k, v, o, lse, dout, idx, cnt, dq, dk, dv, ws, stream)
@@ -295,11 +321,12 @@ def attn_backward(q, k, v, o, lse, dout, idx, cnt, block: int, topk: int = 0, to
 
 
 def decode(q, k_cache, v_cache, kbar, block: int, topk: int = 0, topk_num: int = 0, topk_den: int = 1,
-           flags: int = FORCE_SINK | FORCE_DIAG, want_lse: bool = True, stream=None):
+           flags: int = FORCE_SINK | FORCE_DIAG, want_lse: bool = True, stream=None, n_anchor: int = 0,
+           window: int = 0):
     """One decode step; allocates o, lse, idx and the workspace."""
     S, Hq, d = q.shape
     Hkv, L = k_cache.shape[1], k_cache.shape[2]
-    shape = make_shape(S, Hq, Hkv, L, d, block, topk, topk_num, topk_den, flags)
+    shape = make_shape(S, Hq, Hkv, L, d, block, topk, topk_num, topk_den, flags, n_anchor=n_anchor, window=window)
     km = dsa_decode_kmax(shape)
     dev = q.device
     o = torch.empty_like(q)
@@ -308,6 +335,13 @@ def decode(q, k_cache, v_cache, kbar, block: int, topk: int = 0, topk_num: int =
     ws = torch.empty(max(1, dsa_decode_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
     dsa_decode(shape, q, k_cache, v_cache, kbar, o, lse, idx, ws, stream)
     return o, lse, idx
+
+
+def bitmap(idx, cnt, n_cols: int, stream=None):
+    """Selection rows as bit words (int32 storage of uint32 words)."""
+    out = torch.empty(tuple(idx.shape[:-1]) + ((n_cols + 31) // 32,), dtype=torch.int32, device=idx.device)
+    dsa_indices_to_bitmap(idx, cnt, n_cols, out, stream)
+    return out
 
 
 def kv_block_means(k_cache, block: int, stream=None):

@@ -45,7 +45,18 @@ int check_shape(const dsa_shape* s) {
   if (s->block != 64 && s->block != 128) return fail(DSA_ERR_UNSUPPORTED, "block %d (built: 64, 128)", s->block);
   if (s->topk < 0) return fail(DSA_ERR_SHAPE, "topk %d < 0", s->topk);
   if (s->flags & ~(DSA_FORCE_SINK | DSA_FORCE_DIAG)) return fail(DSA_ERR_SHAPE, "unknown flags 0x%x", s->flags);
-  if (s->topk == 0) {
+  if (s->select_mode != DSA_SELECT_TOPK && s->select_mode != DSA_SELECT_THRESHOLD &&
+      s->select_mode != DSA_SELECT_ENTROPY)
+    return fail(DSA_ERR_SHAPE, "unknown select_mode %d", s->select_mode);
+  if (s->n_anchor < 0 || s->window < 0)
+    return fail(DSA_ERR_SHAPE, "n_anchor %d and window %d must be >= 0", s->n_anchor, s->window);
+  if (s->select_mode == DSA_SELECT_THRESHOLD && !(s->threshold > 0.f && s->threshold <= 1.f))
+    return fail(DSA_ERR_SHAPE, "threshold %g is not in (0, 1]", (double)s->threshold);
+  if (s->select_mode == DSA_SELECT_THRESHOLD && s->flags == 0)
+    return fail(DSA_ERR_SHAPE, "threshold selection needs a forced block (a row could keep none)");
+  if (s->select_mode == DSA_SELECT_ENTROPY && !(s->k_min >= 1 && s->k_min <= s->k_max))
+    return fail(DSA_ERR_SHAPE, "entropy budget needs 1 <= k_min (%d) <= k_max (%d)", s->k_min, s->k_max);
+  if (s->select_mode == DSA_SELECT_TOPK && s->topk == 0) {
     if (s->topk_den < 1) return fail(DSA_ERR_SHAPE, "topk_den %d < 1", s->topk_den);
     if (s->topk_num < 0) return fail(DSA_ERR_SHAPE, "topk_num %d < 0", s->topk_num);
     if (s->topk_num == 0 && s->flags == 0) return fail(DSA_ERR_SHAPE, "topk, topk_num and flags are all 0: no block kept");
@@ -62,17 +73,38 @@ int check_decode(const dsa_shape* s) {
   int rc = check_shape(s);
   if (rc) return rc;
   if (s->batch > 0 && s->seq_len < 1) return fail(DSA_ERR_SHAPE, "decode needs a cache of at least 1 position");
+  if (s->select_mode != DSA_SELECT_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "decode selects by top-k only (select_mode %d)", s->select_mode);
   const int G = s->n_q_heads / s->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(DSA_ERR_UNSUPPORTED, "decode group size %d (built: 1, 2, 4, 8)", G);
   return DSA_OK;
 }
 
+int anchors_of(const dsa_shape* s) { return (s->flags & DSA_FORCE_SINK) ? std::max(1, s->n_anchor) : 0; }
+int window_of(const dsa_shape* s) { return (s->flags & DSA_FORCE_DIAG) ? std::max(1, s->window) : 0; }
+
+// forced blocks of a row that sees `visible` blocks: a prefix of anchors and
+// a suffix (the window), overlapping when the row is short
+int n_forced(const dsa_shape* s, int visible) {
+  const int na = std::min(anchors_of(s), visible);
+  const int ws = std::max(visible - window_of(s), na);
+  return na + (visible - ws);
+}
+
+// most candidates a threshold row can keep: their shares sum to <= 1
+int cand_cap(const dsa_shape* s) {
+  if (s->select_mode != DSA_SELECT_THRESHOLD) return 0;
+  return (int)std::min(floor(1.0 / (double)s->threshold), (double)DSA_MAX_BLOCKS);
+}
+
+// most blocks a row that sees `visible` blocks keeps
 int row_budget(const dsa_shape* s, int visible) {
-  int nf = 0;
-  if (s->flags & DSA_FORCE_SINK) nf++;
-  if ((s->flags & DSA_FORCE_DIAG) && !((s->flags & DSA_FORCE_SINK) && visible == 1)) nf++;
-  int64_t k = s->topk > 0 ? s->topk : ((int64_t)s->topk_num * visible + s->topk_den - 1) / s->topk_den;
+  const int nf = n_forced(s, visible);
+  int64_t k;
+  if (s->select_mode == DSA_SELECT_THRESHOLD) k = (int64_t)nf + cand_cap(s);
+  else if (s->select_mode == DSA_SELECT_ENTROPY) k = s->k_max;
+  else k = s->topk > 0 ? s->topk : ((int64_t)s->topk_num * visible + s->topk_den - 1) / s->topk_den;
   k = std::max<int64_t>(k, nf);
   k = std::min<int64_t>(k, visible);
   return (int)k;
@@ -84,7 +116,10 @@ int prefill_kmax(const dsa_shape* s) {
   return best;
 }
 
-dsa::TopkParams topk_params(const dsa_shape* s) { return dsa::TopkParams{s->topk, s->topk_num, s->topk_den, s->flags}; }
+dsa::TopkParams topk_params(const dsa_shape* s) {
+  return dsa::TopkParams{s->topk,         s->topk_num,       s->topk_den, s->flags, anchors_of(s), window_of(s),
+                         s->select_mode, s->threshold, s->k_min,    s->k_max, cand_cap(s)};
+}
 
 bool empty_prefill(const dsa_shape* s) { return s->batch == 0 || s->seq_len == 0; }
 
@@ -165,6 +200,23 @@ int dsa_select_topk(const dsa_shape* s, const float* scores, int32_t* idx, int32
   hipError_t e = dsa::launch_select_topk(scores, idx, cnt, (int64_t)s->batch * s->n_kv_heads * nB, nB, nB, true,
                                          topk_params(s), prefill_kmax(s), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "select_topk launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_indices_to_bitmap(const int32_t* idx, const int32_t* cnt, int64_t n_rows, int32_t kmax, int32_t n_cols,
+                          uint32_t* bitmap, void* stream) {
+  if (n_rows < 0 || n_rows >= (1ll << 31)) return fail(DSA_ERR_SHAPE, "n_rows %lld out of range", (long long)n_rows);
+  if (kmax < 1) return fail(DSA_ERR_SHAPE, "kmax %d < 1", kmax);
+  if (n_cols < 1 || n_cols > DSA_MAX_BLOCKS)
+    return fail(DSA_ERR_SHAPE, "n_cols %d not in [1, %d]", n_cols, DSA_MAX_BLOCKS);
+  if (n_rows == 0) {
+    g_err[0] = 0;
+    return DSA_OK;
+  }
+  if (!idx || !bitmap) return fail(DSA_ERR_NULL, "idx or bitmap is NULL");
+  hipError_t e = dsa::launch_bitmap(idx, cnt, bitmap, n_rows, kmax, n_cols, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bitmap launch");
   g_err[0] = 0;
   return DSA_OK;
 }

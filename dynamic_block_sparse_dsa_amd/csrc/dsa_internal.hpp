@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dsa.h"
+
 namespace dsa {
 
 // ---------------------------------------------------------------- vector types
@@ -59,15 +61,26 @@ hipError_t launch_block_means(const uint16_t* x, float* xbar, int64_t n_units, i
 hipError_t launch_block_scores(const float* qbar, const float* kbar, float* scores, int B, int Hq, int Hkv, int nB,
                                int d, float scale, hipStream_t stream);
 
+// Selection of one row.  anchors / window are resolved (0 when the matching
+// flag is off, >= 1 when on); cand_cap = floor(1 / threshold).
 struct TopkParams {
   int topk, num, den;
   uint32_t flags;
+  int anchors, window;
+  int mode;  // DSA_SELECT_*
+  float threshold;
+  int k_min, k_max, cand_cap;
 };
 // rows of `scores` (stride n_cols).  causal: row r sees (r % rows_per_unit) + 1
 // blocks; otherwise every row sees n_cols.  idx [n_rows, kmax], cnt [n_rows]
 // (cnt may be NULL).
 hipError_t launch_select_topk(const float* scores, int32_t* idx, int32_t* cnt, int64_t n_rows, int rows_per_unit,
                               int n_cols, bool causal, TopkParams p, int kmax, hipStream_t stream);
+
+// selection rows [n_rows, kmax] (cnt may be NULL: every row has kmax
+// entries) -> bit words [n_rows, ceil(n_cols / 32)]
+hipError_t launch_bitmap(const int32_t* idx, const int32_t* cnt, uint32_t* out, int64_t n_rows, int kmax, int n_cols,
+                         hipStream_t stream);
 
 struct AttnArgs {
   const uint16_t* q;

@@ -195,4 +195,36 @@ hipError_t launch_select_topk(const float* scores, int32_t* idx, int32_t* cnt, i
   return hipGetLastError();
 }
 
+// ============================================================== bitmap
+// One wave per row: the row's kept block ids (idx[row, 0 .. n - 1], n = cnt[row]
+// or kmax) set bit j % 32 of word j / 32 in an LDS copy of the row's words
+// (LDS atomic OR), which is then stored whole.  Ids outside [0, n_cols) are
+// skipped.
+__global__ __launch_bounds__(256) void bitmap_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+                                                     uint32_t* __restrict__ out, int64_t n_rows, int kmax, int n_cols) {
+  __shared__ uint32_t words[4][DSA_MAX_BLOCKS / 32];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= n_rows) return;  // whole wave; no workgroup barrier below
+  const int W = (n_cols + 31) / 32;
+  for (int w = lane; w < W; w += 64) words[wave][w] = 0u;
+  wave_lds_sync();
+  const int n = cnt ? min(max(cnt[row], 0), kmax) : kmax;
+  for (int e = lane; e < n; e += 64) {
+    const int j = idx[row * kmax + e];
+    if (j >= 0 && j < n_cols) atomicOr(&words[wave][j >> 5], 1u << (j & 31));
+  }
+  wave_lds_sync();
+  for (int w = lane; w < W; w += 64) out[row * W + w] = words[wave][w];
+}
+
+hipError_t launch_bitmap(const int32_t* idx, const int32_t* cnt, uint32_t* out, int64_t n_rows, int kmax, int n_cols,
+                         hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(bitmap_kernel, dim3((uint32_t)((n_rows + 3) / 4)), dim3(256), 0, stream, idx, cnt, out, n_rows,
+                     kmax, n_cols);
+  return hipGetLastError();
+}
+
 }  // namespace dsa

@@ -3,7 +3,12 @@
 //
 // Method: "dynamic sparse attention explainer" (zblog.xzdbk.com/559.html),
 // "基于Top-k选择的局部-全局混合": keep the k best-scoring blocks plus the
-// anchors (the sink block 0 and the row's own, last visible block).
+// anchors (the first blocks, the sink) and a local window (the last visible
+// blocks, ending at the row's own).  The budget k is fixed or a fraction of
+// the visible blocks, or comes from the row's block distribution (softmax of
+// its visible block scores): the number of candidates whose share reaches a
+// threshold (DeepSeek NSA article, section 2.2), or ceil(exp(entropy))
+// ("模型精度与稀疏度的动态平衡" and "工程实践建议" of the explainer).
 //
 // Lane l owns the contiguous run of R blocks starting at l * R (index order),
 // so the final compaction is an exclusive scan.  Each visible non-forced
@@ -23,8 +28,9 @@
 // m-th largest of the 256 group maxima, t0, is a lower bound of T (m distinct
 // keys are >= t0).  Only candidates >= t0 can be kept; when there are at most
 // 128 of them they are compacted in index order through 1 KiB of LDS, two per
-// lane, and the same search runs on those.  The forced blocks are the smallest (sink 0) and the largest (the
-// row's own block) visible indices, so they go first and last.
+// lane, and the same search runs on those.  The forced blocks are a prefix
+// (anchors) and a suffix (window) of the visible range, so they go first and
+// last around the candidates.
 #pragma once
 
 #include "dsa_internal.hpp"
@@ -81,6 +87,18 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
 // lanes below this one whose bit is set in mask
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
@@ -109,6 +127,55 @@ __device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&v)[C], int
   return T;
 }
 
+// Budget of a threshold- or entropy-mode row (wave-uniform), from the
+// row's block distribution p_j = exp(s_j - mx) / z over blocks 0 .. nv-1:
+// THRESHOLD keeps the candidates (na <= j < ws) with p_j >= tau, i.e.
+// s_j >= mx + ln(tau z), at most p.cand_cap of them; ENTROPY keeps
+// ceil(exp(H)) blocks, H = ln z - (sum_j e_j (s_j - mx)) / z, clamped to
+// [k_min, k_max].  All in fp32.
+template <int R, bool LDS_T>
+__device__ int64_t dist_budget(const float* srow, int nv, const TopkParams& p, int na, int ws) {
+  const int lane = threadIdx.x & 63;
+  const int j0 = lane * R;
+  float sv[R];
+#pragma unroll
+  for (int e = 0; e < R; ++e) {
+    const int j = j0 + e;
+    if constexpr (LDS_T) sv[e] = ((const __attribute__((address_space(3))) float*)srow)[e * 64 + lane];
+    else sv[e] = j < nv ? srow[j] : 0.f;
+  }
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int e = 0; e < R; ++e)
+    if (j0 + e < nv) mx = fmaxf(mx, sv[e]);
+  mx = wave_max_f32(mx);
+  float z = 0.f, a = 0.f;
+#pragma unroll
+  for (int e = 0; e < R; ++e)
+    if (j0 + e < nv) {
+      const float t = sv[e] - mx;
+      const float ex = expf(t);
+      z += ex;
+      a += ex * t;
+    }
+  z = wave_sum_f32(z);
+  a = wave_sum_f32(a);
+  const int nf = na + (nv - ws);
+  if (p.mode == DSA_SELECT_THRESHOLD) {
+    const float thr = mx + logf(p.threshold * z);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+      const int j = j0 + e;
+      c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(j >= na && j < ws && sv[e] >= thr));
+    }
+    return nf + min(c, p.cand_cap);
+  }
+  const float h = logf(z) - a / z;
+  const int k = (int)ceilf(expf(h));
+  return min(max(k, p.k_min), p.k_max);
+}
+
 // Select from the scores of blocks 0 .. nv-1, nv <= 64 * R.  Without LDS_T,
 // srow[j] is block j's score (global or LDS); with LDS_T, srow is an LDS
 // array of 64 * R scores laid out so that block j = l * R + e sits at
@@ -120,10 +187,13 @@ template <int R, bool LDS_T = false>
 __device__ int wave_select_row(const float* srow, int nv, TopkParams p, int32_t* out, int kmax, uint32_t* lds_key,
                                int32_t* lds_idx) {
   const int lane = threadIdx.x & 63;
-  const int f_sink = (p.flags & 1u) ? 0 : -1;
-  const int f_diag = (p.flags & 2u) ? nv - 1 : -1;
-  const int nf = (f_sink >= 0) + (f_diag >= 0) - (f_sink >= 0 && f_sink == f_diag);
-  int64_t budget = p.topk > 0 ? (int64_t)p.topk : ((int64_t)p.num * nv + p.den - 1) / p.den;
+  // forced: the prefix [0, na) (anchors) and the suffix [ws, nv) (window)
+  const int na = min(p.anchors, nv);
+  const int ws = max(nv - p.window, na);
+  const int nf = na + (nv - ws);
+  int64_t budget;
+  if (p.mode == DSA_SELECT_TOPK) budget = p.topk > 0 ? (int64_t)p.topk : ((int64_t)p.num * nv + p.den - 1) / p.den;
+  else budget = dist_budget<R, LDS_T>(srow, nv, p, na, ws);
   if (budget < nf) budget = nf;
   if (budget > nv) budget = nv;
   const int m = (int)budget - nf;  // candidates to keep
@@ -146,7 +216,7 @@ __device__ int wave_select_row(const float* srow, int nv, TopkParams p, int32_t*
   for (int e = 0; e < R; ++e) {
     const int j = j0 + e;
     key[e] = 0;
-    if (j < nv && j != f_sink && j != f_diag) {
+    if (j >= na && j < ws) {
       key[e] = order_key(LDS_T ? sv[e] : srow[j]);
       candbits[e / 32] |= 1u << (e % 32);
       kmx = max(kmx, key[e]);
@@ -197,15 +267,12 @@ __device__ int wave_select_row(const float* srow, int nv, TopkParams p, int32_t*
       const bool s0 = ok0 && (k0 > T || (k0 == T && lanes_below(eq0) < take_eq));
       const bool s1 = ok1 && (k1 > T || (k1 == T && __builtin_popcountll(eq0) + lanes_below(eq1) < take_eq));
       const uint64_t sm0 = __builtin_amdgcn_ballot_w64(s0), sm1 = __builtin_amdgcn_ballot_w64(s1);
-      const int base = f_sink >= 0 ? 1 : 0;
       const int nsel = __builtin_popcountll(sm0) + __builtin_popcountll(sm1);
-      if (s0) out[base + lanes_below(sm0)] = i0;
-      if (s1) out[base + __builtin_popcountll(sm0) + lanes_below(sm1)] = i1;
-      if (lane == 0) {
-        if (f_sink >= 0) out[0] = f_sink;
-        if (f_diag >= 0 && f_diag != f_sink) out[base + nsel] = f_diag;
-      }
-      const int total = base + nsel + (f_diag >= 0 && f_diag != f_sink ? 1 : 0);
+      if (s0) out[na + lanes_below(sm0)] = i0;
+      if (s1) out[na + __builtin_popcountll(sm0) + lanes_below(sm1)] = i1;
+      for (int e = lane; e < na; e += 64) out[e] = e;
+      for (int e = lane; e < nv - ws; e += 64) out[na + nsel + e] = ws + e;
+      const int total = na + nsel + (nv - ws);
       for (int e = total + lane; e < kmax; e += 64) out[e] = -1;
       return total;
     }

@@ -69,6 +69,13 @@ enum {
 #define DSA_FORCE_DIAG 2u /* the row's own block: the diagonal block in prefill,
                              the last cache block in decode */
 
+/* select_mode: how a row's budget is set (prefill; decode takes TOPK only) */
+#define DSA_SELECT_TOPK 0      /* topk or the fraction below */
+#define DSA_SELECT_THRESHOLD 1 /* every candidate whose share of the row's
+                                  block softmax is >= threshold */
+#define DSA_SELECT_ENTROPY 2   /* ceil(exp(H)) blocks, H the entropy of that
+                                  softmax, clamped to [k_min, k_max] */
+
 /* limits of the built kernels */
 #define DSA_MAX_BLOCKS 4096 /* nB = ceil(N / block) */
 
@@ -85,14 +92,39 @@ typedef struct dsa_shape {
   int32_t topk_num;   /* topk == 0: keep ceil(topk_num * visible / topk_den)  */
   int32_t topk_den;   /*   blocks (integer arithmetic), num >= 0, den >= 1    */
   uint32_t flags;     /* DSA_FORCE_SINK | DSA_FORCE_DIAG (or a subset) */
+  /* Selection variants.  All zero: DSA_SELECT_TOPK with a one-block sink and
+   * a one-block diagonal.  "dynamic sparse attention explainer", section
+   * "基于Top-k选择的局部-全局混合" (global tokens + a local window), DeepSeek
+   * NSA article section 2.2 (block-sparsify the fp32 scores with a
+   * threshold), explainer sections "模型精度与稀疏度的动态平衡" and
+   * "工程实践建议" (set k or the threshold from the attention entropy). */
+  int32_t select_mode; /* DSA_SELECT_* */
+  int32_t n_anchor;    /* with DSA_FORCE_SINK: blocks 0 .. n_anchor-1 forced
+                          (global anchors); 0 means 1 */
+  int32_t window;      /* with DSA_FORCE_DIAG: the last `window` visible blocks
+                          forced (a local window ending at the row's own
+                          block); 0 means 1 */
+  float threshold;     /* DSA_SELECT_THRESHOLD: tau in (0, 1] */
+  int32_t k_min;       /* DSA_SELECT_ENTROPY: 1 <= k_min <= k_max */
+  int32_t k_max;
 } dsa_shape;
 
-/* A row that sees `visible` blocks keeps
- *   min(max(k, |forced|), visible)  blocks, k = topk or the fraction above.
+/* The row's block distribution is p_j = softmax over its visible blocks of
+ * the block scores (forced blocks included).  A row that sees `visible`
+ * blocks and has F forced blocks keeps the forced blocks plus:
+ *   TOPK:       the best min(max(k, F), visible) - F candidates, k = topk or
+ *               the fraction above;
+ *   THRESHOLD:  every candidate with p_j >= threshold (at most
+ *               floor(1 / threshold) of them);
+ *   ENTROPY:    the best min(max(clamp(ceil(exp(H)), k_min, k_max), F),
+ *               visible) - F candidates, H = -sum p_j ln p_j.
  * Kept blocks are listed ascending; the rest of the row of idx is -1.
- * Ties in score go to the lower block index. */
+ * Ties in score go to the lower block index.  The decisions at a threshold
+ * or an integer exp(H) are taken in fp32. */
 
-/* Width of the prefill index array: the largest per-row budget.  Host only.
+/* Width of the prefill index array: the largest per-row budget (THRESHOLD:
+ * F + floor(1 / threshold); ENTROPY: max(k_max, F); both capped at the row's
+ * visible blocks).  Host only.
  * Returns DSA_OK and writes *kmax, or an error code. */
 int dsa_prefill_kmax(const dsa_shape* shape, int32_t* kmax);
 
@@ -177,6 +209,19 @@ size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape);
 int dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, const int32_t* idx, const int32_t* cnt, void* dq,
                         void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Selection as a bitmap ("dynamic sparse attention explainer", section
+ * "工程实践建议": store the sparse index as a compressed bitmap rather than a
+ * full index array).  idx [n_rows, kmax] int32 as written by the selection
+ * calls (entries outside [0, n_cols), such as the -1 padding, are skipped);
+ * cnt [n_rows] int32, or NULL when every row lists kmax blocks (decode).
+ * Writes every word of bitmap [n_rows, ceil(n_cols / 32)] uint32: bit j % 32
+ * of word j / 32 is set when block j is listed.  Prefill: n_rows =
+ * B * Hkv * nB, kmax = dsa_prefill_kmax, n_cols = nB; decode: n_rows =
+ * S * Hkv, kmax = dsa_decode_kmax, n_cols = nB, cnt = NULL.
+ * 0 <= n_rows < 2^31, kmax >= 1, 1 <= n_cols <= DSA_MAX_BLOCKS. */
+int dsa_indices_to_bitmap(const int32_t* idx, const int32_t* cnt, int64_t n_rows, int32_t kmax, int32_t n_cols,
+                          uint32_t* bitmap, void* stream);
 
 /* Static description of a status code. */
 const char* dsa_status_str(int status);

@@ -66,6 +66,15 @@ BAD = [
     (dict(topk=0, topk_num=0, flags=0), dsa.DSA_ERR_SHAPE),
     (dict(flags=4), dsa.DSA_ERR_SHAPE),
     (dict(seq_len=64 * 4096 + 1), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(select_mode=3), dsa.DSA_ERR_SHAPE),
+    (dict(n_anchor=-1), dsa.DSA_ERR_SHAPE),
+    (dict(window=-2), dsa.DSA_ERR_SHAPE),
+    (dict(select_mode=1, threshold=0.0), dsa.DSA_ERR_SHAPE),
+    (dict(select_mode=1, threshold=1.5), dsa.DSA_ERR_SHAPE),
+    (dict(select_mode=1, threshold=float("nan")), dsa.DSA_ERR_SHAPE),
+    (dict(select_mode=1, threshold=0.1, flags=0), dsa.DSA_ERR_SHAPE),
+    (dict(select_mode=2, k_min=0, k_max=4), dsa.DSA_ERR_SHAPE),
+    (dict(select_mode=2, k_min=5, k_max=4), dsa.DSA_ERR_SHAPE),
 ]
 
 
@@ -128,6 +137,31 @@ def test_decode_specific_checks(lib):
     assert lib.dsa_decode(ctypes.byref(z), p, p, p, p, p, None, p, p, 1 << 40, None) == dsa.DSA_ERR_SHAPE
 
 
+def test_decode_takes_top_k_only(lib):
+    """Threshold and entropy budgets vary per row; the decode kernels keep the
+    same count in every unit, so they refuse those modes (anchors and a window
+    are fine)."""
+    out = ctypes.c_int32()
+    for kw in (dict(select_mode=1, threshold=0.1), dict(select_mode=2, k_min=2, k_max=8)):
+        s = shape(**kw)
+        assert lib.dsa_prefill_kmax(ctypes.byref(s), ctypes.byref(out)) == 0
+        assert lib.dsa_decode_kmax(ctypes.byref(s), ctypes.byref(out)) == dsa.DSA_ERR_UNSUPPORTED
+    s = shape(n_anchor=3, window=4)
+    assert lib.dsa_decode_kmax(ctypes.byref(s), ctypes.byref(out)) == 0 and out.value == 7
+
+
+def test_bitmap_argument_checks(lib):
+    p = ctypes.c_void_p(16)
+    f = lib.dsa_indices_to_bitmap
+    assert f(p, None, -1, 4, 16, p, None) == dsa.DSA_ERR_SHAPE
+    assert f(p, None, 4, 0, 16, p, None) == dsa.DSA_ERR_SHAPE
+    assert f(p, None, 4, 4, 0, p, None) == dsa.DSA_ERR_SHAPE
+    assert f(p, None, 4, 4, 4097, p, None) == dsa.DSA_ERR_SHAPE
+    assert f(None, None, 4, 4, 16, p, None) == dsa.DSA_ERR_NULL
+    assert f(p, None, 4, 4, 16, None, None) == dsa.DSA_ERR_NULL
+    assert f(None, None, 0, 4, 16, None, None) == 0  # empty: nothing enqueued
+
+
 def test_empty_problems_are_no_ops(lib):
     """B == 0 or N == 0 returns OK without touching the (invalid) pointers."""
     p = ctypes.c_void_p(16)
@@ -147,6 +181,29 @@ def test_kmax_matches_the_oracle(lib, N, b, topk, num, den, flags):
     nb = -(-N // b)
     assert dsa.dsa_prefill_kmax(s) == O.kmax(nb, topk, num, den, flags, True, nb)
     assert dsa.dsa_decode_kmax(s) == O.kmax(1, topk, num, den, flags, False, nb)
+
+
+VARIANTS = [
+    dict(n_anchor=3, window=2), dict(n_anchor=5, window=1, flags=1), dict(window=7, flags=2, topk=3),
+    dict(select_mode=1, threshold=0.1), dict(select_mode=1, threshold=0.05, n_anchor=2, window=2),
+    dict(select_mode=1, threshold=0.25, flags=1), dict(select_mode=1, threshold=1.0),
+    dict(select_mode=2, k_min=2, k_max=32), dict(select_mode=2, k_min=1, k_max=1, n_anchor=2, window=3),
+    dict(select_mode=2, k_min=4, k_max=4000),
+]
+
+
+@pytest.mark.parametrize("N", [100, 1024, 20000])
+@pytest.mark.parametrize("kw", VARIANTS, ids=[str(v) for v in VARIANTS])
+def test_kmax_of_selection_variants_matches_the_oracle(lib, N, kw):
+    s = shape(seq_len=N, **kw)
+    nb = -(-N // 64)
+    spec = O.SelectSpec(mode=kw.get("select_mode", 0), anchors=max(1, kw.get("n_anchor", 0)),
+                        window=max(1, kw.get("window", 0)), threshold=kw.get("threshold", 0.0),
+                        k_min=kw.get("k_min", 0), k_max=kw.get("k_max", 0))
+    flags, topk = kw.get("flags", 3), kw.get("topk", 4)
+    assert dsa.dsa_prefill_kmax(s) == O.kmax(nb, topk, 0, 1, flags, True, nb, spec)
+    if kw.get("select_mode", 0) == 0:
+        assert dsa.dsa_decode_kmax(s) == O.kmax(1, topk, 0, 1, flags, False, nb, spec)
 
 
 def test_binding_rejects_host_tensors():

@@ -39,7 +39,9 @@ def shape_of(w: Workload, flags: int = 3):
 
 
 def check_rows(rows, gidx, gcnt):
-    """Every row's GPU set is accepted; returns (#flagged, #rows)."""
+    """Every row's GPU set is accepted; returns (#flagged, #rows).  A flagged
+    row's count may differ from the oracle's own pick (a threshold band, an
+    alternative entropy budget): ``accepts`` checks it."""
     flat_idx = gidx.reshape(-1, gidx.shape[-1])
     flat_cnt = gcnt.reshape(-1)
     assert len(rows) == flat_idx.shape[0]
@@ -47,9 +49,9 @@ def check_rows(rows, gidx, gcnt):
     for r, rs in enumerate(rows):
         c = int(flat_cnt[r])
         got = [int(x) for x in flat_idx[r, :c]]
-        assert c == len(rs.idx), (r, c, rs.idx)
         assert (flat_idx[r, c:] == -1).all(), r
         if not rs.flagged:
+            assert c == len(rs.idx), (r, c, rs.idx)
             assert got == rs.idx, (r, got, rs.idx)
         else:
             flagged += 1
