@@ -200,6 +200,68 @@ def bench_backward(args, dev, stream, inputs):
                               kernel="backward step: prep, invert, dq, dkdv", flops_per_step=flops))
 
 
+SELECT_VARIANTS = [
+    ("topk", {}),
+    ("anchors4_window4", dict(n_anchor=4, window=4)),
+    ("threshold_0.02", dict(select_mode=1, threshold=0.02)),
+    ("entropy_2_24", dict(select_mode=2, k_min=2, k_max=24)),
+]
+
+
+def bench_selection(args, dev, stream, inputs):
+    """dsa_select_topk for each selection variant on the prefill workload's
+    block scores, and dsa_indices_to_bitmap on the top-k selection; each
+    event-timed alone.  Bytes per launch: the visible (causal) scores read
+    plus the index rows and counts written; priced against HBM."""
+    import torch
+
+    import dynamic_block_sparse_dsa_amd as dsa
+
+    q, k, v, w = inputs
+    B, Hq, Hkv, N, d, nB = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_blocks
+    base = dsa.make_shape(B, Hq, Hkv, N, d, w.block, w.topk, w.topk_num, w.topk_den)
+    qbar = torch.empty((B, Hq, nB, d), dtype=torch.float32, device=dev)
+    kbar = torch.empty((B, Hkv, nB, d), dtype=torch.float32, device=dev)
+    sc = torch.empty((B, Hkv, nB, nB), dtype=torch.float32, device=dev)
+    dsa.dsa_block_means(base, Hq, q, qbar, stream=stream)
+    dsa.dsa_block_means(base, Hkv, k, kbar, stream=stream)
+    dsa.dsa_block_scores(base, qbar, kbar, sc, stream=stream)
+    rows = B * Hkv * nB
+    out = {}
+    for name, sel in SELECT_VARIANTS:
+        topk = w.topk if not sel.get("select_mode") else 0
+        shape = dsa.make_shape(B, Hq, Hkv, N, d, w.block, topk, w.topk_num, w.topk_den, **sel)
+        km = dsa.dsa_prefill_kmax(shape)
+        idx = torch.empty((B, Hkv, nB, km), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, Hkv, nB), dtype=torch.int32, device=dev)
+
+        def step():
+            dsa.dsa_select_topk(shape, sc, idx, cnt, stream=stream)
+
+        for _ in range(args.warmup):
+            step()
+        ms = time_events(step, args.steps, stream)
+        nbytes = B * Hkv * (nB * (nB + 1) // 2) * 4 + rows * (km + 1) * 4
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        c = cnt.float()
+        out[name] = dict(us=round(ms * 1e3, 2), kept_mean=round(float(c.mean()), 2), kept_max=int(c.max()),
+                         index_width=km, bytes_per_launch=nbytes, achieved_GBs=round(gbs, 1),
+                         frac_hbm=round(gbs / PEAK_HBM_GBS, 5))
+        if name == "topk":
+            bm = torch.empty((B, Hkv, nB, (nB + 31) // 32), dtype=torch.int32, device=dev)
+
+            def pack():
+                dsa.dsa_indices_to_bitmap(idx, cnt, nB, bm, stream=stream)
+
+            for _ in range(args.warmup):
+                pack()
+            ms_b = time_events(pack, args.steps, stream)
+            out["bitmap_us"] = round(ms_b * 1e3, 2)
+    out["config"] = dict(workload=w.name, rows=rows, kernel="select_topk_wave_kernel", bound="hbm (launch-bound at "
+                         "this size)")
+    return out
+
+
 def cpu_baseline(args, inputs):
     """The oracle, as it stands, on whole heads of the prefill workload until
     about --cpu-seconds have passed; scaled to tokens/s of the full problem."""
@@ -237,6 +299,7 @@ def main():
     ap.add_argument("--decode-workload", default="decode_s32_l65536")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-selection", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -274,6 +337,8 @@ def main():
         out["decode"] = bench_decode(args, dev, stream)
     if not args.no_backward:
         out["backward"] = bench_backward(args, dev, stream, inputs)
+    if not args.no_selection:
+        out["selection"] = bench_selection(args, dev, stream, inputs)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, inputs)
     print(json.dumps(out), flush=True)
