@@ -20,6 +20,14 @@ can be regenerated alone):
   * ``plain``: no structure.
 Target picks are drawn on the CPU with a generator of their own so that the
 values drawn on the device do not depend on them.
+
+Token-indexer workloads (``IndexWorkload``, ``make_index``; one generator per
+batch entry): index queries qi [B, N, HI, dI] and keys ki [B, N, dI] are
+N(0, 1); with ``clusters`` C > 0 every token s belongs to a cluster c(s)
+(uniform over C) whose random unit direction times the amplitude is added to
+ki[s], and every query token t aims all its index heads at one cluster drawn
+uniformly (the same direction times the amplitude added to qi[t, h]); head
+weights wi [B, N, HI] are U(0, 1) fp32; the attention Q, K, V are N(0, 1).
 """
 
 from __future__ import annotations
@@ -190,3 +198,68 @@ def make_decode(w: Workload, device="cpu", seed: int | None = None, units=None):
             kc[n] = ks.to(torch.bfloat16)
             vc[n] = vs.to(torch.bfloat16)
     return q, kc, vc
+
+
+@dataclass(frozen=True)
+class IndexWorkload:
+    """Token-level indexer + token-gather attention workload."""
+
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    seq_len: int
+    head_dim: int
+    n_index_heads: int
+    index_dim: int
+    topk: int
+    clusters: int = 0
+    amplitude: float = 0.0
+    seed: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+
+INDEX_WORKLOADS = {
+    w.name: w
+    for w in [
+        IndexWorkload("index_tiny_n512", 1, 4, 2, 512, 64, 16, 64, 64, clusters=16, amplitude=4.0, seed=10),
+        IndexWorkload("index_n8192", 1, 32, 8, 8192, 128, 16, 128, 64, clusters=128, amplitude=4.0, seed=11),
+    ]
+}
+
+
+def make_index(w: IndexWorkload, device="cpu", seed: int | None = None):
+    """qi [B, N, HI, dI] bf16, ki [B, N, dI] bf16, wi [B, N, HI] fp32, and
+    Q [B, Hq, N, d], K, V [B, Hkv, N, d] bf16, all contiguous."""
+    seed = w.seed if seed is None else seed
+    B, N, HI, dI = w.batch, w.seq_len, w.n_index_heads, w.index_dim
+    Hq, Hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
+    qi = torch.empty((B, N, HI, dI), dtype=torch.bfloat16, device=device)
+    ki = torch.empty((B, N, dI), dtype=torch.bfloat16, device=device)
+    wi = torch.empty((B, N, HI), dtype=torch.float32, device=device)
+    q = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=device)
+    k = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=device)
+    v = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=device)
+    for b in range(B):
+        gen = _gen(device, seed, b, 3)
+        qs = torch.randn((N, HI, dI), generator=gen, device=device, dtype=torch.float32)
+        ks = torch.randn((N, dI), generator=gen, device=device, dtype=torch.float32)
+        ws = torch.rand((N, HI), generator=gen, device=device, dtype=torch.float32)
+        if w.clusters > 0:
+            u = _directions(w.clusters, dI, gen, device)
+            cg = _gen("cpu", seed, b, 4)
+            member = torch.randint(0, w.clusters, (N,), generator=cg)
+            aim = torch.randint(0, w.clusters, (N,), generator=cg)
+            ks += w.amplitude * u[member.to(device)]
+            qs += w.amplitude * u[aim.to(device)][:, None, :]
+        qi[b] = qs.to(torch.bfloat16)
+        ki[b] = ks.to(torch.bfloat16)
+        wi[b] = ws
+        q[b] = torch.randn((Hq, N, d), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+        k[b] = torch.randn((Hkv, N, d), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+        v[b] = torch.randn((Hkv, N, d), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return qi, ki, wi, q, k, v
+

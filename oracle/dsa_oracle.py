@@ -20,6 +20,13 @@ What it computes, step by step, in the order the method runs:
   O4 ``attend``        softmax(s * q k^T) v over exactly the keys of the kept
                         blocks that are causally visible to each row.
   ``prefill`` / ``decode`` chain O1-O4.
+  I1 ``index_scores``  token-level lightning-indexer scores: for query token t
+                        and earlier token s, the sum over the index heads of
+                        head weight times ReLU(index query . index key).
+  I2 ``select_tokens`` per query token, the top-k earlier tokens by I1 (the
+                        same selection rule as O3, rows = tokens).
+  I3 ``token_attend``  attention of every head over its token's selected
+                        tokens.  ``index_prefill`` chains I1-I3.
   O5 ``attend_backward`` dQ, dK, dV of O4 with the selection held fixed (the
                         chain rule through O4's own definition, row by row).
 
@@ -36,6 +43,11 @@ Sources (the pages; cited by title and section):
         the pattern, softmax of logits / sqrt(d_k), weights times values).
   [NSA] DeepSeek NSA article, pnsm.cn/news/1939904.html -- section 2.2
         (routing scores in fp32, weighted sum in bf16).
+  [LC]  "低成本高性能大模型实现路径：从架构创新到工程优化"
+        (yunthe.com/news/806485.html), section 2.1 "轻量化索引器设计" (the
+        indexer: ReLU features, 16 index heads, each query token mapped to
+        its high-value key/value tokens with a top-k of 64) and section 2.2
+        (the indexer keeps its intermediates in FP8).
 
 Readings where the pages leave a point open (all listed in the design doc):
   * block statistic = mean(Q tile) . mean(K tile) / sqrt(d) (the workload
@@ -53,7 +65,12 @@ Readings where the pages leave a point open (all listed in the design doc):
     block); a row's block distribution is the softmax of its visible block
     scores; threshold mode keeps the candidates whose share is >= tau;
     entropy mode keeps ceil(exp(H)) blocks (H the Shannon entropy of that
-    distribution, nats), clamped to [k_min, k_max], then runs the top-k.
+    distribution, nats), clamped to [k_min, k_max], then runs the top-k;
+  * token indexer: the page's listing is garbled; from its text (ReLU
+    features, 16 index heads, top-64 per query token) the score of earlier
+    token s for query token t is sum_h w[t,h] * ReLU(qi[t,h] . ki[s]) with one
+    index key per token shared by the heads; one top-k per query token (sink
+    and self forced as in O3) is shared by every attention head.
 
 Parity status: every function here is pinned by tests in ``tests/`` that do
 not re-use this module's formulas (dense special case against a library
@@ -604,3 +621,71 @@ def _accepts_one(rs: RowSelection, got: list) -> tuple[bool, str]:
     if rs.need >= 0 and len(extra) != rs.need:
         return False, f"takes {len(extra)} from the tie band, needs {rs.need}"
     return True, ""
+
+
+# --------------------------------------------------------------------------
+# I1-I3 -- token-level lightning indexer and token-gather attention
+# --------------------------------------------------------------------------
+def index_score_row(qi_t: np.ndarray, ki: np.ndarray, wi_t: np.ndarray, t: int) -> np.ndarray:
+    """Scores of tokens 0..t for query token t: I[s] = sum_h wi_t[h] *
+    max(0, qi_t[h] . ki[s]).  qi_t [HI, dI], ki [N, dI], wi_t [HI].
+
+    [LC] section 2.1: ReLU feature heads (HI = 16) score where the query
+    token should look."""
+    dots = np.asarray(ki, dtype=np.float64)[: t + 1] @ np.asarray(qi_t, dtype=np.float64).T  # [t+1, HI]
+    return np.maximum(dots, 0.0) @ np.asarray(wi_t, dtype=np.float64)
+
+
+def index_scores(qi: np.ndarray, ki: np.ndarray, wi: np.ndarray) -> np.ndarray:
+    """I [B, N, N]: row t holds index_score_row for s <= t and -inf above.
+    qi [B, N, HI, dI], ki [B, N, dI], wi [B, N, HI]."""
+    B, N = qi.shape[:2]
+    out = np.full((B, N, N), -np.inf)
+    for b in range(B):
+        for t in range(N):
+            out[b, t, : t + 1] = index_score_row(qi[b, t], ki[b], wi[b, t], t)
+    return out
+
+
+def select_tokens(scores: np.ndarray, topk: int, flags: int = FORCE_SINK | FORCE_DIAG,
+                  spec: SelectSpec = DEFAULT_SPEC):
+    """Per query token t the forced tokens (the sink token 0 and t itself, per
+    ``flags``) and the best other tokens up to ``topk`` by index score (ties
+    to the lower position), ascending: the O3 rule with rows and columns
+    being tokens.  scores [B, N, N]; returns idx [B, N, kmax], cnt [B, N],
+    rows."""
+    idx, cnt, rows = select_topk(np.asarray(scores)[:, None], topk, 0, 1, flags, causal=True, spec=spec)
+    return idx[:, 0], cnt[:, 0], rows
+
+
+def token_attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, cnt: np.ndarray, units=None):
+    """Attention of query token t, head h over the tokens idx[b, t, :cnt]
+    (all <= t): softmax of s * q . k over them, times their values, s =
+    1/sqrt(d); query head h reads KV head h // G.  q [B, Hq, N, d]; k, v
+    [B, Hkv, N, d]; returns O [B, Hq, N, d] and LSE [B, Hq, N] (float64).
+    ``units`` restricts the rows to a list of (b, h, t)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    scale = 1.0 / math.sqrt(d)
+    if units is None:
+        units = [(b, h, t) for b in range(B) for h in range(Hq) for t in range(N)]
+    o = np.zeros((B, Hq, N, d))
+    lse = np.zeros((B, Hq, N))
+    for (b, h, t) in units:
+        keys = [int(s) for s in idx[b, t, : cnt[b, t]]]
+        logits = scale * (k[b, h // G, keys] @ q[b, h, t])
+        w, lse[b, h, t] = _softmax_row(logits)
+        o[b, h, t] = w @ v[b, h // G, keys]
+    return o, lse
+
+
+def index_prefill(qi, ki, wi, q, k, v, topk: int, flags: int = FORCE_SINK | FORCE_DIAG, attend_units=None):
+    """I1 -> I2 -> I3 for a causal prefill."""
+    sc = index_scores(qi, ki, wi)
+    idx, cnt, rows = select_tokens(sc, topk, flags)
+    o, lse = token_attend(q, k, v, idx, cnt, units=attend_units)
+    return dict(scores=sc, idx=idx, cnt=cnt, rows=rows, o=o, lse=lse)
+
