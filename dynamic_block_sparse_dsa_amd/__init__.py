@@ -36,6 +36,12 @@ EXPORTS = [
     "dsa_block_scores",
     "dsa_select_topk",
     "dsa_indices_to_bitmap",
+    "dsa_index_kmax",
+    "dsa_index_scores",
+    "dsa_select_tokens",
+    "dsa_token_attn_fwd",
+    "dsa_index_workspace_bytes",
+    "dsa_index_prefill",
     "dsa_sparse_attn_fwd",
     "dsa_prefill_workspace_bytes",
     "dsa_prefill",
@@ -83,6 +89,27 @@ def make_shape(batch, n_q_heads, n_kv_heads, seq_len, head_dim, block, topk=0, t
                  n_anchor, window, threshold, k_min, k_max)
 
 
+class IndexShape(ctypes.Structure):
+    """Mirror of ``dsa_index_shape``."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("n_index_heads", ctypes.c_int32),
+        ("index_dim", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+def make_index_shape(batch, n_q_heads, n_kv_heads, seq_len, head_dim, n_index_heads, index_dim, topk,
+                     flags=FORCE_SINK | FORCE_DIAG) -> IndexShape:
+    return IndexShape(batch, n_q_heads, n_kv_heads, seq_len, head_dim, n_index_heads, index_dim, topk, flags)
+
+
 class DsaError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"libdsa status {code}: {msg}")
@@ -101,6 +128,7 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m dynamic_block_sparse_dsa_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     P, S, I32, SZ = ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_size_t
+    X = ctypes.POINTER(IndexShape)
     sig = {
         "dsa_prefill_kmax": ([S, ctypes.POINTER(I32)], ctypes.c_int),
         "dsa_decode_kmax": ([S, ctypes.POINTER(I32)], ctypes.c_int),
@@ -108,6 +136,12 @@ def load() -> ctypes.CDLL:
         "dsa_block_scores": ([S, P, P, P, P], ctypes.c_int),
         "dsa_select_topk": ([S, P, P, P, P], ctypes.c_int),
         "dsa_indices_to_bitmap": ([P, P, ctypes.c_int64, I32, I32, P, P], ctypes.c_int),
+        "dsa_index_kmax": ([X, ctypes.POINTER(I32)], ctypes.c_int),
+        "dsa_index_scores": ([X, P, P, P, P, P], ctypes.c_int),
+        "dsa_select_tokens": ([X, P, P, P, P], ctypes.c_int),
+        "dsa_token_attn_fwd": ([X, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "dsa_index_workspace_bytes": ([X], SZ),
+        "dsa_index_prefill": ([X, P, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "dsa_sparse_attn_fwd": ([S, P, P, P, P, P, P, P, P], ctypes.c_int),
         "dsa_prefill_workspace_bytes": ([S], SZ),
         "dsa_prefill": ([S, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
@@ -211,6 +245,58 @@ def dsa_select_topk(shape: Shape, scores, idx, cnt, stream=None):
     _check(load().dsa_select_topk(ctypes.byref(shape), _ptr(scores, torch.float32, (B, Hkv, nB, nB), "scores"),
                                   _ptr(idx, torch.int32, (B, Hkv, nB, km), "idx"),
                                   _ptr(cnt, torch.int32, (B, Hkv, nB), "cnt"), _stream(stream)))
+
+
+def dsa_index_kmax(shape: IndexShape) -> int:
+    out = ctypes.c_int32(0)
+    _check(load().dsa_index_kmax(ctypes.byref(shape), ctypes.byref(out)))
+    return out.value
+
+
+def dsa_index_workspace_bytes(shape: IndexShape) -> int:
+    return int(load().dsa_index_workspace_bytes(ctypes.byref(shape)))
+
+
+def _index_dims(shape: IndexShape):
+    return (shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_len, shape.head_dim, shape.n_index_heads,
+            shape.index_dim)
+
+
+def dsa_index_scores(shape: IndexShape, qi, ki, wi, scores, stream=None):
+    B, _, _, N, _, HI, dI = _index_dims(shape)
+    _check(load().dsa_index_scores(ctypes.byref(shape), _ptr(qi, torch.bfloat16, (B, N, HI, dI), "qi"),
+                                   _ptr(ki, torch.bfloat16, (B, N, dI), "ki"), _ptr(wi, torch.float32, (B, N, HI), "wi"),
+                                   _ptr(scores, torch.float32, (B, N, N), "scores"), _stream(stream)))
+
+
+def dsa_select_tokens(shape: IndexShape, scores, idx, cnt, stream=None):
+    B, N = shape.batch, shape.seq_len
+    km = dsa_index_kmax(shape)
+    _check(load().dsa_select_tokens(ctypes.byref(shape), _ptr(scores, torch.float32, (B, N, N), "scores"),
+                                    _ptr(idx, torch.int32, (B, N, km), "idx"), _ptr(cnt, torch.int32, (B, N), "cnt"),
+                                    _stream(stream)))
+
+
+def dsa_token_attn_fwd(shape: IndexShape, q, k, v, idx, cnt, o, lse=None, stream=None):
+    B, Hq, Hkv, N, d, _, _ = _index_dims(shape)
+    km = dsa_index_kmax(shape)
+    _check(load().dsa_token_attn_fwd(
+        ctypes.byref(shape), _ptr(q, torch.bfloat16, (B, Hq, N, d), "q"), _ptr(k, torch.bfloat16, (B, Hkv, N, d), "k"),
+        _ptr(v, torch.bfloat16, (B, Hkv, N, d), "v"), _ptr(idx, torch.int32, (B, N, km), "idx"),
+        _ptr(cnt, torch.int32, (B, N), "cnt"), _ptr(o, torch.bfloat16, (B, Hq, N, d), "o"),
+        _ptr(lse, torch.float32, (B, Hq, N), "lse", optional=True), _stream(stream)))
+
+
+def dsa_index_prefill(shape: IndexShape, qi, ki, wi, q, k, v, o, lse, idx, cnt, ws, stream=None):
+    B, Hq, Hkv, N, d, HI, dI = _index_dims(shape)
+    km = dsa_index_kmax(shape)
+    wp, wb = _ws(ws, dsa_index_workspace_bytes(shape))
+    _check(load().dsa_index_prefill(
+        ctypes.byref(shape), _ptr(qi, torch.bfloat16, (B, N, HI, dI), "qi"), _ptr(ki, torch.bfloat16, (B, N, dI), "ki"),
+        _ptr(wi, torch.float32, (B, N, HI), "wi"), _ptr(q, torch.bfloat16, (B, Hq, N, d), "q"),
+        _ptr(k, torch.bfloat16, (B, Hkv, N, d), "k"), _ptr(v, torch.bfloat16, (B, Hkv, N, d), "v"),
+        _ptr(o, torch.bfloat16, (B, Hq, N, d), "o"), _ptr(lse, torch.float32, (B, Hq, N), "lse", optional=True),
+        _ptr(idx, torch.int32, (B, N, km), "idx"), _ptr(cnt, torch.int32, (B, N), "cnt"), wp, wb, _stream(stream)))
 
 
 def dsa_indices_to_bitmap(idx, cnt, n_cols: int, bitmap, stream=None):
@@ -342,6 +428,23 @@ def bitmap(idx, cnt, n_cols: int, stream=None):
     out = torch.empty(tuple(idx.shape[:-1]) + ((n_cols + 31) // 32,), dtype=torch.int32, device=idx.device)
     dsa_indices_to_bitmap(idx, cnt, n_cols, out, stream)
     return out
+
+
+def index_prefill(qi, ki, wi, q, k, v, topk: int, flags: int = FORCE_SINK | FORCE_DIAG, want_lse: bool = True,
+                  stream=None):
+    """Token-level indexer -> token selection -> token-gather attention;
+    allocates O, LSE, idx, cnt and the workspace."""
+    B, N, HI, dI = qi.shape
+    shape = make_index_shape(B, q.shape[1], k.shape[1], N, q.shape[3], HI, dI, topk, flags)
+    km = dsa_index_kmax(shape)
+    dev = q.device
+    o = torch.empty_like(q)
+    lse = torch.empty((B, q.shape[1], N), dtype=torch.float32, device=dev) if want_lse else None
+    idx = torch.empty((B, N, km), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, N), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, dsa_index_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
+    dsa_index_prefill(shape, qi, ki, wi, q, k, v, o, lse, idx, cnt, ws, stream)
+    return o, lse, idx, cnt
 
 
 def kv_block_means(k_cache, block: int, stream=None):

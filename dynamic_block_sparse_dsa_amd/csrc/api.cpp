@@ -123,6 +123,52 @@ dsa::TopkParams topk_params(const dsa_shape* s) {
 
 bool empty_prefill(const dsa_shape* s) { return s->batch == 0 || s->seq_len == 0; }
 
+int check_index(const dsa_index_shape* s) {
+  if (!s) return fail(DSA_ERR_NULL, "shape is NULL");
+  if (s->batch < 0) return fail(DSA_ERR_SHAPE, "batch %d < 0", s->batch);
+  if (s->seq_len < 0) return fail(DSA_ERR_SHAPE, "seq_len %d < 0", s->seq_len);
+  if (s->seq_len > DSA_MAX_TOKENS)
+    return fail(DSA_ERR_UNSUPPORTED, "seq_len %d > %d tokens", s->seq_len, DSA_MAX_TOKENS);
+  if (s->n_q_heads < 1 || s->n_kv_heads < 1 || s->n_q_heads % s->n_kv_heads != 0)
+    return fail(DSA_ERR_SHAPE, "head counts Hq %d, Hkv %d", s->n_q_heads, s->n_kv_heads);
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(DSA_ERR_UNSUPPORTED, "group size %d (built: 1, 2, 4, 8)", G);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", s->head_dim);
+  if (s->n_index_heads != DSA_INDEX_HEADS)
+    return fail(DSA_ERR_UNSUPPORTED, "n_index_heads %d (built: %d)", s->n_index_heads, DSA_INDEX_HEADS);
+  if (s->index_dim != 64 && s->index_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "index_dim %d (built: 64, 128)", s->index_dim);
+  if (s->topk < 1) return fail(DSA_ERR_SHAPE, "topk %d < 1", s->topk);
+  if (s->flags & ~(DSA_FORCE_SINK | DSA_FORCE_DIAG)) return fail(DSA_ERR_SHAPE, "unknown flags 0x%x", s->flags);
+  if ((int64_t)s->batch * s->seq_len * s->n_q_heads >= (1ll << 31))
+    return fail(DSA_ERR_UNSUPPORTED, "problem too large for one launch");
+  return DSA_OK;
+}
+
+int index_kmax(const dsa_index_shape* s) {
+  const int N = s->seq_len;
+  if (N == 0) return 0;
+  int nf = 0;
+  if (s->flags & DSA_FORCE_SINK) nf++;
+  if ((s->flags & DSA_FORCE_DIAG) && !((s->flags & DSA_FORCE_SINK) && N == 1)) nf++;
+  return std::min(N, std::max(s->topk, nf));
+}
+
+dsa::TopkParams token_params(const dsa_index_shape* s) {
+  return dsa::TopkParams{s->topk,
+                         0,
+                         1,
+                         s->flags,
+                         (s->flags & DSA_FORCE_SINK) ? 1 : 0,
+                         (s->flags & DSA_FORCE_DIAG) ? 1 : 0,
+                         DSA_SELECT_TOPK,
+                         0.f,
+                         0,
+                         0,
+                         0};
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,6 +248,91 @@ int dsa_select_topk(const dsa_shape* s, const float* scores, int32_t* idx, int32
   if (e != hipSuccess) return hip_fail(e, "select_topk launch");
   g_err[0] = 0;
   return DSA_OK;
+}
+
+int dsa_index_kmax(const dsa_index_shape* s, int32_t* kmax) {
+  int rc = check_index(s);
+  if (rc) return rc;
+  if (!kmax) return fail(DSA_ERR_NULL, "kmax is NULL");
+  *kmax = index_kmax(s);
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_index_scores(const dsa_index_shape* s, const void* qi, const void* ki, const float* wi, float* scores,
+                     void* stream) {
+  int rc = check_index(s);
+  if (rc) return rc;
+  if (s->batch == 0 || s->seq_len == 0) return DSA_OK;
+  if (!qi || !ki || !wi || !scores) return fail(DSA_ERR_NULL, "qi, ki, wi or scores is NULL");
+  hipError_t e = dsa::launch_index_scores(static_cast<const uint16_t*>(qi), static_cast<const uint16_t*>(ki), wi,
+                                          scores, s->batch, s->seq_len, s->index_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "index_scores launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_select_tokens(const dsa_index_shape* s, const float* scores, int32_t* idx, int32_t* cnt, void* stream) {
+  int rc = check_index(s);
+  if (rc) return rc;
+  if (s->batch == 0 || s->seq_len == 0) return DSA_OK;
+  if (!scores || !idx || !cnt) return fail(DSA_ERR_NULL, "scores, idx or cnt is NULL");
+  const int N = s->seq_len;
+  hipError_t e = dsa::launch_select_topk(scores, idx, cnt, (int64_t)s->batch * N, N, N, true, token_params(s),
+                                         index_kmax(s), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "select_tokens launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_token_attn_fwd(const dsa_index_shape* s, const void* q, const void* k, const void* v, const int32_t* idx,
+                       const int32_t* cnt, void* o, float* lse, void* stream) {
+  int rc = check_index(s);
+  if (rc) return rc;
+  if (s->batch == 0 || s->seq_len == 0) return DSA_OK;
+  if (!q || !k || !v || !idx || !cnt || !o) return fail(DSA_ERR_NULL, "q, k, v, idx, cnt or o is NULL");
+  dsa::TokenAttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.idx = idx;
+  a.cnt = cnt;
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.B = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.N = s->seq_len;
+  a.kmax = index_kmax(s);
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
+  hipError_t e = dsa::launch_token_attn(a, s->head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "token_attn launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+size_t dsa_index_workspace_bytes(const dsa_index_shape* s) {
+  if (check_index(s)) return 0;
+  return align256((size_t)s->batch * s->seq_len * s->seq_len * 4);
+}
+
+int dsa_index_prefill(const dsa_index_shape* s, const void* qi, const void* ki, const float* wi, const void* q,
+                      const void* k, const void* v, void* o, float* lse, int32_t* idx, int32_t* cnt, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc = check_index(s);
+  if (rc) return rc;
+  if (s->batch == 0 || s->seq_len == 0) return DSA_OK;
+  if (!qi || !ki || !wi || !q || !k || !v || !o || !idx || !cnt)
+    return fail(DSA_ERR_NULL, "qi, ki, wi, q, k, v, o, idx or cnt is NULL");
+  const size_t need = dsa_index_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
+  float* scores = static_cast<float*>(ws);
+  rc = dsa_index_scores(s, qi, ki, wi, scores, stream);
+  if (rc) return rc;
+  rc = dsa_select_tokens(s, scores, idx, cnt, stream);
+  if (rc) return rc;
+  return dsa_token_attn_fwd(s, q, k, v, idx, cnt, o, lse, stream);
 }
 
 int dsa_indices_to_bitmap(const int32_t* idx, const int32_t* cnt, int64_t n_rows, int32_t kmax, int32_t n_cols,

@@ -82,6 +82,23 @@ hipError_t launch_select_topk(const float* scores, int32_t* idx, int32_t* cnt, i
 hipError_t launch_bitmap(const int32_t* idx, const int32_t* cnt, uint32_t* out, int64_t n_rows, int kmax, int n_cols,
                          hipStream_t stream);
 
+// token-level indexer: scores [B, N, N] fp32 (row t written for s <= t)
+hipError_t launch_index_scores(const uint16_t* qi, const uint16_t* ki, const float* wi, float* scores, int B, int N,
+                               int di, hipStream_t stream);
+
+struct TokenAttnArgs {
+  const uint16_t* q;    // [B, Hq, N, d]
+  const uint16_t* k;    // [B, Hkv, N, d]
+  const uint16_t* v;
+  const int32_t* idx;   // [B, N, kmax] kept tokens per query token
+  const int32_t* cnt;   // [B, N]
+  uint16_t* o;          // [B, Hq, N, d]
+  float* lse;           // [B, Hq, N] or null
+  int B, Hq, Hkv, N, kmax;
+  float scale_log2;     // log2(e) / sqrt(d)
+};
+hipError_t launch_token_attn(const TokenAttnArgs& a, int d, hipStream_t stream);
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;

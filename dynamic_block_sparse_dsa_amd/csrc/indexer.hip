@@ -1,0 +1,307 @@
+// Token-level lightning indexer and token-gather attention (gfx950).
+//
+// Method: "低成本高性能大模型实现路径：从架构创新到工程优化"
+// (yunthe.com/news/806485.html), section 2.1 "轻量化索引器设计": an indexer of
+// ReLU feature heads (16 index heads) decides, per query token, which 64
+// key/value tokens matter; section 2.2 keeps the indexer's intermediates in
+// low precision.  Here the score of earlier token s for query token t is
+//   I[t, s] = sum_h w[t, h] * ReLU(qi[t, h] . ki[s])
+// (bf16 MFMA, fp32 accumulation), each query token keeps its top-k tokens
+// (the block path's one-wave top-k, rows = tokens, sink and self forced), and
+// every attention head attends over its token's kept key/value rows.
+//
+// index_scores_kernel: one workgroup per 16 query tokens, each wave 4 tokens
+//   = 2 column tiles of 32 (token, index head) pairs, so the 16 heads of a
+//   token are one 16-lane DPP row of the MFMA output.  Per 64-key tile
+//   (global -> LDS DMA, double-buffered, kswz rows): S^T = K_tile . Qi^T on
+//   v_mfma_f32_32x32x16_bf16 (key rows from LDS as A, the wave's index query
+//   rows as B in registers); then ReLU, times the head weight, and a
+//   reduce-scatter over each 16-lane row (four DPP steps) leaves lane i of the
+//   row with the head sum of its i-th output register, which it stores: one
+//   score per lane, causal part only.  Token tiles run latest first (they
+//   have the most key tiles).
+// token_attn_kernel: one wave per (batch, token, KV head): lane l gathers the
+//   l-th kept token's key row and computes the logits of the group's query
+//   heads (queries staged in LDS, read as broadcasts); softmax across the
+//   wave; P V streams the kept value rows (each row read by the whole wave,
+//   D / 64 dims per lane), 8 rows in flight.  More than 64 kept tokens are
+//   taken in chunks of 64 with an online softmax.
+#include "attn_common.hpp"
+#include "topk_row.hpp"
+
+namespace dsa {
+namespace {
+
+template <int DI>
+__device__ __forceinline__ void load_key_tile(const uint16_t* g, int row0, int n_rows, uint32_t lds_base, int wave,
+                                              int lane) {
+  constexpr int CH = DI / 8, RPI = 1024 / (2 * DI), LOADS = 64 * DI * 2 / 1024;
+  static_assert(LOADS % 4 == 0, "tile loads split over 4 waves");
+#pragma unroll
+  for (int n = 0; n < LOADS / 4; ++n) {
+    const int inst = wave + 4 * n;
+    const int r = inst * RPI + lane / CH;
+    const int c = (lane % CH) ^ kswz<DI>(r);
+    const int row = min(row0 + r, n_rows - 1);
+    dma16(g, (uint32_t)(row * DI + c * 8) * 2u, __builtin_amdgcn_readfirstlane(lds_base + inst * 1024));
+  }
+}
+
+template <int DI>
+__device__ __forceinline__ u32x4 key_frag(const LDS_AS uint16_t* tile, int r, int ks, int half) {
+  const int c = (2 * ks + half) ^ kswz<DI>(r);
+  return *reinterpret_cast<const LDS_AS u32x4*>(tile + r * DI + c * 8);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// v[0..15] per lane -> lane i of each 16-lane row gets sum over the row's
+// lanes of v[i].  Each step pairs lanes with a DPP mirror and halves the
+// registers: the lane keeps the half named by its bit and adds the partner's
+// copy of that half.
+__device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int i) {
+  float w8[8], w4[4], w2[2];
+  const bool u1 = i >= 8, u2 = (i & 7) >= 4, u3 = (i & 3) >= 2, u4 = (i & 1) != 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w8[j] = (u1 ? v[j + 8] : v[j]) + dppf<0x140>(u1 ? v[j] : v[j + 8]);  // row_mirror
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w4[j] = (u2 ? w8[j + 4] : w8[j]) + dppf<0x141>(u2 ? w8[j] : w8[j + 4]);  // row_half_mirror
+#pragma unroll
+  for (int j = 0; j < 2; ++j) w2[j] = (u3 ? w4[j + 2] : w4[j]) + dppf<0x1B>(u3 ? w4[j] : w4[j + 2]);  // quad [3,2,1,0]
+  return (u4 ? w2[1] : w2[0]) + dppf<0xB1>(u4 ? w2[0] : w2[1]);                                      // quad [1,0,3,2]
+}
+
+}  // namespace
+
+// ============================================================== index scores
+template <int DI>
+__global__ __launch_bounds__(256) void index_scores_kernel(const uint16_t* __restrict__ qi,
+                                                           const uint16_t* __restrict__ ki,
+                                                           const float* __restrict__ wi, float* __restrict__ scores,
+                                                           int N, int tiles_per_b) {
+  constexpr int HI = 16, NKS = DI / 16, KT = 64, TPW = 4, TPB = 4 * TPW;
+  __shared__ __align__(1024) uint16_t kt_lds[2][KT * DI];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, i16 = lane & 15;
+  const int64_t b = blockIdx.x / tiles_per_b;
+  const int tile = tiles_per_b - 1 - (int)(blockIdx.x % tiles_per_b);
+  const int t0 = tile * TPB;
+  const int n_kt = (min(t0 + TPB, N) - 1) / KT + 1;
+
+  // B operands: column (lane % 32) of column tile ct is token
+  // t0 + 4 wave + 2 ct + (lane % 32) / 16, index head lane % 16
+  u32x4 qf[2][NKS];
+  float wv[2];
+  int tok[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    tok[ct] = t0 + TPW * wave + 2 * ct + ((lane & 31) >> 4);
+    const int64_t trow = b * N + min(tok[ct], N - 1);
+    const uint16_t* qrow = qi + (trow * HI + i16) * DI;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ct][ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + 8 * half);
+    wv[ct] = wi[trow * HI + i16];
+  }
+  const uint16_t* kb = ki + b * (int64_t)N * DI;
+  const uint32_t base[2] = {(uint32_t)(uintptr_t)(LDS_AS uint16_t*)kt_lds[0],
+                            (uint32_t)(uintptr_t)(LDS_AS uint16_t*)kt_lds[1]};
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(qf[ct][ks]));
+  load_key_tile<DI>(kb, 0, N, base[0], wave, lane);
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    wait_vm<0>();
+    __syncthreads();  // tile kt resident; every wave is done with tile kt - 1
+    if (kt + 1 < n_kt) load_key_tile<DI>(kb, (kt + 1) * KT, N, base[(kt + 1) & 1], wave, lane);
+    const LDS_AS uint16_t* tl = (const LDS_AS uint16_t*)kt_lds[kt & 1];
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const u32x4 a = key_frag<DI>(tl, rt * 32 + (lane & 31), ks, half);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[ct][ks]), acc[rt][ct], 0,
+                                                                0, 0);
+      }
+    }
+    // ReLU, head weight, sum over the 16 heads of each token; lane i16 of the
+    // row ends with output register i16: key row 8 (i16 / 4) + 4 half + i16 % 4
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = fmaxf(acc[rt][ct][r], 0.f) * wv[ct];
+        const float sum = row_reduce_scatter16(v, i16);
+        const int key = kt * KT + rt * 32 + 8 * (i16 >> 2) + 4 * half + (i16 & 3);
+        if (tok[ct] < N && key <= tok[ct]) scores[(b * N + tok[ct]) * (int64_t)N + key] = sum;
+      }
+    }
+  }
+}
+
+// ============================================================== token attention
+template <int D, int G>
+__global__ __launch_bounds__(256) void token_attn_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ cnt, uint16_t* __restrict__ o,
+                                                         float* __restrict__ lse, int Hkv, int N, int kmax,
+                                                         float scale_log2, int64_t n_waves) {
+  constexpr int DPL = D / 64;  // output dims per lane
+  constexpr int QCH = D / 8;   // 16-byte chunks of a row
+  __shared__ __align__(16) uint16_t qs[4][G * D];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= n_waves) return;  // whole wave; no workgroup barrier below
+  const int g = (int)(w % Hkv);
+  const int64_t bt = w / Hkv;  // b * N + t
+  const int t = (int)(bt % N);
+  const int64_t b = bt / N;
+  const int Hq = Hkv * G;
+  const int n = min(max(cnt[bt], 0), kmax);
+  const int32_t* row = idx + bt * kmax;
+  const int64_t kvh = (b * Hkv + g) * (int64_t)N;
+
+  // the group's query rows -> LDS (G D bf16, 16 bytes per lane per step)
+  for (int c = lane; c < G * QCH; c += 64) {
+    const int hh = c / QCH, ch = c % QCH;
+    *reinterpret_cast<u32x4*>(&qs[wave][hh * D + ch * 8]) =
+        *reinterpret_cast<const u32x4*>(q + ((b * Hq + g * G + hh) * (int64_t)N + t) * D + ch * 8);
+  }
+  wave_lds_sync();
+
+  float m[G], l[G], acc[G][DPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -__builtin_inff();
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.f;
+  }
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int e = c0 + lane;
+    const bool ok = e < n;
+    const int s = ok ? min(max(row[e], 0), N - 1) : 0;
+    const uint16_t* krow = k + (kvh + s) * D;
+    float x[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) x[hh] = 0.f;
+#pragma unroll 4
+    for (int ch = 0; ch < QCH; ++ch) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + ch * 8);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(&qs[wave][hh * D + ch * 8]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          x[hh] = __builtin_fmaf(bf16_lo(qv[j]), bf16_lo(kv[j]), __builtin_fmaf(bf16_hi(qv[j]), bf16_hi(kv[j]), x[hh]));
+      }
+    }
+    float p[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float xl = ok ? x[hh] * scale_log2 : -__builtin_inff();
+      const float mn = fmaxf(m[hh], wave_max_f32(xl));
+      const float corr = __builtin_amdgcn_exp2f(m[hh] - mn);
+      p[hh] = ok ? __builtin_amdgcn_exp2f(xl - mn) : 0.f;
+      l[hh] = l[hh] * corr + wave_sum_f32(p[hh]);
+#pragma unroll
+      for (int e2 = 0; e2 < DPL; ++e2) acc[hh][e2] *= corr;
+      m[hh] = mn;
+    }
+    // P V: the chunk's kept rows, 8 in flight
+    const int nc = min(64, n - c0);
+    for (int j0 = 0; j0 < nc; j0 += 8) {
+      uint32_t vv[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = min(j0 + jj, nc - 1);
+        const int sj = __builtin_amdgcn_readlane(s, j);
+        const uint16_t* vrow = v + (kvh + sj) * D + lane * DPL;
+        vv[jj] = DPL == 2 ? *reinterpret_cast<const uint32_t*>(vrow) : (uint32_t)(*vrow) << 16;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj >= nc) break;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[hh]), j0 + jj));
+          if constexpr (DPL == 2) {
+            acc[hh][0] = __builtin_fmaf(pj, bf16_lo(vv[jj]), acc[hh][0]);
+            acc[hh][1] = __builtin_fmaf(pj, bf16_hi(vv[jj]), acc[hh][1]);
+          } else {
+            acc[hh][0] = __builtin_fmaf(pj, bf16_hi(vv[jj]), acc[hh][0]);
+          }
+        }
+      }
+    }
+  }
+  // O = acc / l (bf16), LSE = (m + log2 l) ln 2
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const float inv = l[hh] > 0.f ? 1.f / l[hh] : 0.f;
+    uint16_t* orow = o + ((b * Hq + g * G + hh) * (int64_t)N + t) * D + lane * DPL;
+    if constexpr (DPL == 2) {
+      const bf16x2_t pk = {(__bf16)(acc[hh][0] * inv), (__bf16)(acc[hh][1] * inv)};
+      *reinterpret_cast<bf16x2_t*>(orow) = pk;
+    } else {
+      *reinterpret_cast<__bf16*>(orow) = (__bf16)(acc[hh][0] * inv);
+    }
+    if (lse && lane == 0)
+      lse[(b * Hq + g * G + hh) * (int64_t)N + t] =
+          l[hh] > 0.f ? (m[hh] + __log2f(l[hh])) * 0.6931471805599453f : -__builtin_inff();
+  }
+}
+
+// ============================================================== launch
+hipError_t launch_index_scores(const uint16_t* qi, const uint16_t* ki, const float* wi, float* scores, int B, int N,
+                               int di, hipStream_t stream) {
+  if (B == 0 || N == 0) return hipSuccess;
+  const int tiles = (N + 15) / 16;
+  const dim3 grid((uint32_t)((int64_t)B * tiles)), blk(256);
+  if (di == 64) hipLaunchKernelGGL(index_scores_kernel<64>, grid, blk, 0, stream, qi, ki, wi, scores, N, tiles);
+  else hipLaunchKernelGGL(index_scores_kernel<128>, grid, blk, 0, stream, qi, ki, wi, scores, N, tiles);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_token_attn_d(const TokenAttnArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const int64_t n_waves = (int64_t)a.B * a.N * a.Hkv;
+  const dim3 grid((uint32_t)((n_waves + 3) / 4)), blk(256);
+#define DSA_TOKEN_ATTN(GG)                                                                                          \
+  hipLaunchKernelGGL((token_attn_kernel<D, GG>), grid, blk, 0, stream, a.q, a.k, a.v, a.idx, a.cnt, a.o, a.lse, a.Hkv, \
+                     a.N, a.kmax, a.scale_log2, n_waves)
+  switch (G) {
+    case 1: DSA_TOKEN_ATTN(1); break;
+    case 2: DSA_TOKEN_ATTN(2); break;
+    case 4: DSA_TOKEN_ATTN(4); break;
+    case 8: DSA_TOKEN_ATTN(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DSA_TOKEN_ATTN
+  return hipGetLastError();
+}
+
+hipError_t launch_token_attn(const TokenAttnArgs& a, int d, hipStream_t stream) {
+  if (a.B == 0 || a.N == 0) return hipSuccess;
+  return d == 64 ? launch_token_attn_d<64>(a, stream) : launch_token_attn_d<128>(a, stream);
+}
+
+}  // namespace dsa

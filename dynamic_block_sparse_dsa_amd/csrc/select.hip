@@ -189,9 +189,14 @@ hipError_t launch_select_topk(const float* scores, int32_t* idx, int32_t* cnt, i
   else if (longest <= 64 * 16)
     hipLaunchKernelGGL(select_topk_wave_kernel<16>, grid, block, 0, stream, scores, idx, cnt, n_rows, rows_per_unit,
                        n_cols, c, p, kmax);
-  else
+  else if (longest <= 64 * 64)
     hipLaunchKernelGGL(select_topk_wave_kernel<64>, grid, block, 0, stream, scores, idx, cnt, n_rows, rows_per_unit,
                        n_cols, c, p, kmax);
+  else if (longest <= 64 * 128)  // token rows
+    hipLaunchKernelGGL(select_topk_wave_kernel<128>, grid, block, 0, stream, scores, idx, cnt, n_rows, rows_per_unit,
+                       n_cols, c, p, kmax);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

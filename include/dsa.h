@@ -210,6 +210,62 @@ int dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void* k, co
                         const float* lse, const void* dout, const int32_t* idx, const int32_t* cnt, void* dq,
                         void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Token-level lightning indexer ("低成本高性能大模型实现路径：从架构创新
+ * 到工程优化", yunthe.com/news/806485.html, section 2.1 "轻量化索引器设计":
+ * ReLU feature heads, 16 index heads, every query token keeps its top 64
+ * key/value tokens; section 2.2: low-precision indexer intermediates).  For
+ * query token t and earlier token s (s <= t)
+ *     I[t, s] = sum_h wi[t, h] * max(0, qi[t, h] . ki[s])
+ * (bf16 inputs, fp32 products and sums).  Each query token keeps the forced
+ * tokens (DSA_FORCE_SINK: token 0; DSA_FORCE_DIAG: t itself) plus its best
+ * other tokens up to topk in all (ties to the lower position), listed
+ * ascending, and every attention head of the token attends over exactly
+ * those tokens (softmax of q . k / sqrt(d), times v; fp32).
+ * Layouts: qi [B, N, HI, dI] bf16; ki [B, N, dI] bf16; wi [B, N, HI] fp32;
+ * scores [B, N, N] fp32 (row t: entries 0..t are written, the rest is not
+ * touched); idx [B, N, kmax] int32 (-1 padded); cnt [B, N] int32; q, o
+ * [B, Hq, N, d] bf16; k, v [B, Hkv, N, d] bf16; lse [B, Hq, N] fp32
+ * (natural log, nullable).  Query head h reads KV head h / (Hq / Hkv). */
+#define DSA_INDEX_HEADS 16  /* HI, the only index head count built */
+#define DSA_MAX_TOKENS 8192 /* longest sequence the token selection takes */
+
+typedef struct dsa_index_shape {
+  int32_t batch;         /* B >= 0 */
+  int32_t n_q_heads;     /* Hq >= 1 */
+  int32_t n_kv_heads;    /* Hkv >= 1, Hq / Hkv in {1, 2, 4, 8} */
+  int32_t seq_len;       /* N, 0 <= N <= DSA_MAX_TOKENS */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t n_index_heads; /* HI: DSA_INDEX_HEADS */
+  int32_t index_dim;     /* dI: 64 or 128 */
+  int32_t topk;          /* tokens kept per query token, forced ones included, >= 1 */
+  uint32_t flags;        /* DSA_FORCE_SINK | DSA_FORCE_DIAG (or a subset) */
+} dsa_index_shape;
+
+/* Width of the token index array: the largest per-row count,
+ * min(N, max(topk, forced)).  Host only. */
+int dsa_index_kmax(const dsa_index_shape* shape, int32_t* kmax);
+
+/* Index scores I (above) into scores. */
+int dsa_index_scores(const dsa_index_shape* shape, const void* qi, const void* ki, const float* wi, float* scores,
+                     void* stream);
+
+/* Per query token, the kept tokens from a scores array as written by
+ * dsa_index_scores. */
+int dsa_select_tokens(const dsa_index_shape* shape, const float* scores, int32_t* idx, int32_t* cnt, void* stream);
+
+/* Attention of every head over its token's kept tokens.  idx entries are
+ * read for the first cnt of each row and must be positions <= t. */
+int dsa_token_attn_fwd(const dsa_index_shape* shape, const void* q, const void* k, const void* v, const int32_t* idx,
+                       const int32_t* cnt, void* o, float* lse, void* stream);
+
+/* Workspace of dsa_index_prefill in bytes: the scores, B * N * N * 4. */
+size_t dsa_index_workspace_bytes(const dsa_index_shape* shape);
+
+/* Scores -> selection -> attention in one call. */
+int dsa_index_prefill(const dsa_index_shape* shape, const void* qi, const void* ki, const float* wi, const void* q,
+                      const void* k, const void* v, void* o, float* lse, int32_t* idx, int32_t* cnt, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* ---- Selection as a bitmap ("dynamic sparse attention explainer", section
  * "工程实践建议": store the sparse index as a compressed bitmap rather than a
  * full index array).  idx [n_rows, kmax] int32 as written by the selection

@@ -1,0 +1,126 @@
+"""GPU parity of the token-level indexer (index scores, token selection,
+token-gather attention) through the C ABI against the fp64 oracle on the
+same seeded inputs.
+
+Bars: scores (fp32 sums of bf16 products) within 1e-4 relative of the
+oracle's plus 1e-4 of the row's largest magnitude; selections as for the
+block path (bit-exact except in near-tie rows, where the GPU's set must be
+an accepted one); attention over the GPU's sets within max-abs 2e-2,
+mean-abs 2e-3 and LSE 1e-3 (it runs in fp32, so the observed error is the
+bf16 rounding of O).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import dynamic_block_sparse_dsa_amd as dsa
+from dynamic_block_sparse_dsa_amd.inputs import INDEX_WORKLOADS, IndexWorkload, make_index
+from test_gpu_parity import check_out, check_rows, np64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run(w, flags, dev):
+    qi, ki, wi, q, k, v = make_index(w, device=dev)
+    shape = dsa.make_index_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_index_heads,
+                                 w.index_dim, w.topk, flags)
+    B, N = w.batch, w.seq_len
+    km = dsa.dsa_index_kmax(shape)
+    sc = torch.full((B, N, N), float("nan"), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, N, km), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, N), dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, w.n_q_heads, N), dtype=torch.float32, device=dev)
+    dsa.dsa_index_scores(shape, qi, ki, wi, sc)
+    dsa.dsa_select_tokens(shape, sc, idx, cnt)
+    dsa.dsa_token_attn_fwd(shape, q, k, v, idx, cnt, o, lse)
+    torch.cuda.synchronize()
+    return (qi, ki, wi, q, k, v), dict(scores=sc, idx=idx, cnt=cnt, o=o, lse=lse)
+
+
+def check_score_rows(got, ref_rows):
+    """got: {t: gpu row [t+1]}, ref_rows: {t: oracle row [t+1]}."""
+    worst = 0.0
+    for t, r in ref_rows.items():
+        g = got[t]
+        assert np.isfinite(g).all(), t
+        tol = 1e-4 * np.abs(r) + 1e-4 * np.abs(r).max()
+        assert (np.abs(g - r) <= tol).all(), (t, np.abs(g - r).max())
+        worst = max(worst, float((np.abs(g - r) / (np.abs(r).max() + 1e-30)).max()))
+    say(f"scores: {len(ref_rows)} rows, max |err| / row max {worst:.3g}")
+
+
+SMALL = [
+    ("tiny_n512_d64_dI64_g2", INDEX_WORKLOADS["index_tiny_n512"], 3),
+    ("n1000_ragged_dI128_g4", IndexWorkload("a", 1, 8, 2, 1000, 128, 16, 128, 64, clusters=32, amplitude=4.0,
+                                            seed=61), 3),
+    ("n100_rows_shorter_than_k", IndexWorkload("b", 1, 2, 1, 100, 64, 16, 64, 64, clusters=8, amplitude=4.0,
+                                               seed=62), 3),
+    ("b2_g8_k16_no_forcing", IndexWorkload("c", 2, 8, 1, 700, 128, 16, 64, 16, clusters=20, amplitude=4.0,
+                                           seed=63), 0),
+    ("g1_sink_only_k5", IndexWorkload("d", 1, 3, 3, 300, 64, 16, 128, 5, seed=64), 1),
+    ("self_only_k100", IndexWorkload("e", 1, 4, 4, 450, 128, 16, 128, 100, clusters=10, amplitude=4.0, seed=65), 2),
+    ("n1_single_token", IndexWorkload("f", 1, 2, 2, 1, 64, 16, 64, 64, seed=66), 3),
+    ("n17_short", IndexWorkload("g", 1, 2, 1, 17, 128, 16, 64, 4, seed=67), 3),
+]
+
+
+@pytest.mark.parametrize("name,w,flags", SMALL, ids=[c[0] for c in SMALL])
+def test_index_small(cuda_device, name, w, flags):
+    say(f"index {name}: B{w.batch} Hq{w.n_q_heads} Hkv{w.n_kv_heads} N{w.seq_len} d{w.head_dim} dI{w.index_dim} "
+        f"k{w.topk} flags{flags}")
+    x, g = run(w, flags, cuda_device)
+    qi, ki, wi, q, k, v = (np64(t) for t in x)
+    N = w.seq_len
+    ref_sc = O.index_scores(qi, ki, wi)
+    gsc = np64(g["scores"])
+    for b in range(w.batch):
+        check_score_rows({t: gsc[b, t, : t + 1] for t in range(N)}, {t: ref_sc[b, t, : t + 1] for t in range(N)})
+    _, _, rows = O.select_tokens(ref_sc, w.topk, flags)
+    gidx, gcnt = g["idx"].cpu().numpy(), g["cnt"].cpu().numpy()
+    check_rows(rows, gidx[:, None], gcnt[:, None])
+    o_ref, lse_ref = O.token_attend(q, k, v, gidx, gcnt)
+    check_out(np64(g["o"]), o_ref, np64(g["lse"]), lse_ref, name)
+    # the fused call runs the same kernels
+    o2, lse2, idx2, cnt2 = dsa.index_prefill(*x, w.topk, flags)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, g["idx"]) and torch.equal(cnt2, g["cnt"])
+    assert torch.equal(o2, g["o"]) and torch.equal(lse2, g["lse"])
+
+
+def test_index_full_n8192_sampled(cuda_device):
+    """The 8 192-token workload: scores, selection and attention on sampled
+    query tokens (the oracle computes those rows alone)."""
+    w = INDEX_WORKLOADS["index_n8192"]
+    say("index full n8192: running")
+    x, g = run(w, 3, cuda_device)
+    qi, ki, wi = x[0][0].float().cpu().numpy(), x[1][0].float().cpu().numpy(), x[2][0].cpu().numpy()
+    q, k, v = x[3], x[4], x[5]
+    gsc, gidx, gcnt = g["scores"][0], g["idx"].cpu().numpy(), g["cnt"].cpu().numpy()
+    rows = [0, 1, 63, 64, 65, 1000, 2047, 4095, 4096, 6000, 8100, 8190, 8191]
+    ref = {t: O.index_score_row(qi[t].astype(np.float64), ki.astype(np.float64), wi[t].astype(np.float64), t)
+           for t in rows}
+    check_score_rows({t: gsc[t, : t + 1].double().cpu().numpy() for t in rows}, ref)
+    flagged = 0
+    for t in rows:
+        f = O.forced_set(t + 1, 3)
+        rs = O.select_row(ref[t], t + 1, O.row_budget(t + 1, w.topk, 0, 1, len(f)), f)
+        c = int(gcnt[0, t])
+        got = [int(s) for s in gidx[0, t, :c]]
+        if rs.flagged:
+            flagged += 1
+            ok, why = O.accepts(rs, got)
+            assert ok, (t, why)
+        else:
+            assert got == rs.idx, (t, got, rs.idx)
+    say(f"index full n8192: {len(rows)} sampled rows, {flagged} flagged")
+    units = [(0, h, t) for t in rows for h in (0, 13, 31)]
+    o_ref, lse_ref = O.token_attend(np64(q), np64(k), np64(v), gidx, gcnt, units=units)
+    for (b, h, t) in units:
+        check_out(np64(g["o"][b, h, t])[None], o_ref[b, h, t][None], np64(g["lse"][b, h, t]).reshape(1),
+                  lse_ref[b, h, t].reshape(1), f"n8192 h{h} t{t}")
+    assert torch.isfinite(g["o"].float()).all()
