@@ -29,6 +29,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "attn_fwd.hip")
 DECODE_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "decode.hip")
 BWD_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "attn_bwd.hip")
+INDEX_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "indexer.hip")
 
 
 def src_hash(path):
@@ -262,6 +263,74 @@ def bench_selection(args, dev, stream, inputs):
     return out
 
 
+def bench_index(args, dev, stream):
+    """Token-level indexer workload: the chained step (wall clock) and each
+    of its three launches alone (HIP events).  Algorithmic work: index
+    scores 2 HI dI FLOP per causal (query token, token) pair (MFMA); token
+    selection reads the causal scores (4 bytes each); token attention reads
+    the kept tokens' K and V rows of every KV head (d * 2 bytes each) plus Q
+    and writes O."""
+    import torch
+
+    import dynamic_block_sparse_dsa_amd as dsa
+    from dynamic_block_sparse_dsa_amd.inputs import INDEX_WORKLOADS, make_index
+
+    w = INDEX_WORKLOADS[args.index_workload]
+    qi, ki, wi, q, k, v = make_index(w, device=dev)
+    B, Hq, Hkv, N, d, HI, dI = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_index_heads, w.index_dim
+    shape = dsa.make_index_shape(B, Hq, Hkv, N, d, HI, dI, w.topk)
+    km = dsa.dsa_index_kmax(shape)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, N, km), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, N), dtype=torch.int32, device=dev)
+    ws = torch.empty(dsa.dsa_index_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    sc = ws[: B * N * N * 4].view(torch.float32).view(B, N, N)
+    torch.cuda.synchronize()
+
+    def step():
+        dsa.dsa_index_prefill(shape, qi, ki, wi, q, k, v, o, lse, idx, cnt, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    parts = dict(
+        scores=lambda: dsa.dsa_index_scores(shape, qi, ki, wi, sc, stream=stream),
+        select=lambda: dsa.dsa_select_tokens(shape, sc, idx, cnt, stream=stream),
+        attention=lambda: dsa.dsa_token_attn_fwd(shape, q, k, v, idx, cnt, o, lse, stream=stream),
+    )
+    us = {}
+    for name, fn in parts.items():
+        for _ in range(args.warmup):
+            fn()
+        us[name] = time_events(fn, args.steps, stream) * 1e3
+    pairs = B * N * (N + 1) // 2
+    flops = 2 * HI * dI * pairs
+    kept = int(cnt.sum())
+    attn_bytes = kept * Hkv * d * 2 * 2 + 2 * B * Hq * N * d * 2
+    tf = flops / (us["scores"] * 1e-6) / 1e12
+    sel_gbs = pairs * 4 / (us["select"] * 1e-6) / 1e9
+    att_gbs = attn_bytes / (us["attention"] * 1e-6) / 1e9
+    return dict(
+        value=B * N / (ms_step * 1e-3), unit="tokens/s", ms_per_step=ms_step,
+        config=dict(workload=w.name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, seq_len=N, head_dim=d, index_heads=HI,
+                    index_dim=dI, topk=w.topk),
+        kernels_us={kk: round(vv, 2) for kk, vv in us.items()},
+        roofline=dict(bound="mfma", achieved=round(tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                      frac=round(tf / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic("index_" + w.name, INDEX_SRC),
+                      kernel="index_scores_kernel", flops_per_launch=flops),
+        select_roofline=dict(bound="hbm", achieved=round(sel_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                             frac=round(sel_gbs / PEAK_HBM_GBS, 4), bytes_per_launch=pairs * 4),
+        attention_roofline=dict(bound="hbm (gather)", achieved=round(att_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                                frac=round(att_gbs / PEAK_HBM_GBS, 4), bytes_per_launch=attn_bytes),
+    )
+
+
 def cpu_baseline(args, inputs):
     """The oracle, as it stands, on whole heads of the prefill workload until
     about --cpu-seconds have passed; scaled to tokens/s of the full problem."""
@@ -300,6 +369,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-selection", action="store_true")
+    ap.add_argument("--no-index", action="store_true")
+    ap.add_argument("--index-workload", default="index_n8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -339,6 +410,8 @@ def main():
         out["backward"] = bench_backward(args, dev, stream, inputs)
     if not args.no_selection:
         out["selection"] = bench_selection(args, dev, stream, inputs)
+    if not args.no_index:
+        out["indexer"] = bench_index(args, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, inputs)
     print(json.dumps(out), flush=True)

@@ -278,8 +278,8 @@ int dsa_select_tokens(const dsa_index_shape* s, const float* scores, int32_t* id
   if (s->batch == 0 || s->seq_len == 0) return DSA_OK;
   if (!scores || !idx || !cnt) return fail(DSA_ERR_NULL, "scores, idx or cnt is NULL");
   const int N = s->seq_len;
-  hipError_t e = dsa::launch_select_topk(scores, idx, cnt, (int64_t)s->batch * N, N, N, true, token_params(s),
-                                         index_kmax(s), static_cast<hipStream_t>(stream));
+  hipError_t e = dsa::launch_select_tokens(scores, idx, cnt, (int64_t)s->batch * N, N, token_params(s), index_kmax(s),
+                                           static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "select_tokens launch");
   g_err[0] = 0;
   return DSA_OK;

@@ -86,6 +86,13 @@ hipError_t launch_bitmap(const int32_t* idx, const int32_t* cnt, uint32_t* out, 
 hipError_t launch_index_scores(const uint16_t* qi, const uint16_t* ki, const float* wi, float* scores, int B, int N,
                                int di, hipStream_t stream);
 
+// token rows of up to 8192 scores: a streaming fast path, then the general
+// select for the rows it marks (cnt = -1)
+hipError_t launch_select_tokens(const float* scores, int32_t* idx, int32_t* cnt, int64_t n_rows, int N, TopkParams p,
+                                int kmax, hipStream_t stream);
+hipError_t launch_select_marked(const float* scores, int32_t* idx, int32_t* cnt, int64_t n_rows, int N, TopkParams p,
+                                int kmax, hipStream_t stream);
+
 struct TokenAttnArgs {
   const uint16_t* q;    // [B, Hq, N, d]
   const uint16_t* k;    // [B, Hkv, N, d]

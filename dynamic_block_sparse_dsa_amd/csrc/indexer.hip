@@ -26,6 +26,16 @@
 //   wave; P V streams the kept value rows (each row read by the whole wave,
 //   D / 64 dims per lane), 8 rows in flight.  More than 64 kept tokens are
 //   taken in chunks of 64 with an online softmax.
+// select_tokens_fast_kernel: one wave per query-token row of up to 8192
+//   scores.  Lane l owns tokens l + 64 e (so every load instruction reads 256
+//   consecutive bytes and ballots over e visit the candidates in index order).
+//   Pass 1 keeps 8 group maxima per lane; the m-th largest of them is a lower
+//   bound t0 of the m-th largest candidate (the groups are disjoint).  Pass 2
+//   re-reads the row (from L2) and compacts the candidates >= t0 -- usually
+//   about m -- into LDS in index order; the threshold search then runs on two
+//   keys per lane.  Rows it cannot finish (more than 64 to keep, or more than
+//   128 candidates at or above t0) get cnt = -1 and are completed by the
+//   general one-wave select.
 #include "attn_common.hpp"
 #include "topk_row.hpp"
 
@@ -269,6 +279,90 @@ __global__ __launch_bounds__(256) void token_attn_kernel(const uint16_t* __restr
   }
 }
 
+// ============================================================== token selection
+__global__ __launch_bounds__(256) void select_tokens_fast_kernel(const float* __restrict__ scores,
+                                                                 int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
+                                                                 int64_t n_rows, int N, TopkParams p, int kmax) {
+  constexpr int E = 128;  // tokens per lane: rows of up to 64 E
+  __shared__ uint32_t lds_key[4][128];
+  __shared__ int32_t lds_idx[4][128];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= n_rows) return;  // whole wave; no workgroup barrier below
+  const int nv = (int)(row % N) + 1;
+  const float* srow = scores + row * (int64_t)N;
+  int32_t* out = idx + row * (int64_t)kmax;
+  const int na = min(p.anchors, nv);
+  const int ws = max(nv - p.window, na);
+  const int nf = na + (nv - ws);
+  const int budget = min(max(p.topk, nf), nv);
+  const int m = budget - nf;
+  const int ncand = nv - nf;
+  if (m >= ncand || m <= 0) {  // every visible token, or the forced ones only
+    const int total = m <= 0 ? nf : nv;
+    for (int e = lane; e < total; e += 64) out[e] = m <= 0 ? (e < na ? e : ws + (e - na)) : e;
+    for (int e = total + lane; e < kmax; e += 64) out[e] = -1;
+    if (lane == 0) cnt[row] = total;
+    return;
+  }
+  if (m > 64) {
+    if (lane == 0) cnt[row] = -1;
+    return;
+  }
+  const int hi_e = (ws - 1) / 64;  // last e with a candidate in some lane
+  // pass 1: group maxima of the candidate keys (0 = no candidate)
+  uint32_t gmax[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) gmax[g] = 0u;
+  for (int e = na / 64; e <= hi_e; ++e) {
+    const int j = lane + 64 * e;
+    if (j >= na && j < ws) gmax[e >> 4] = max(gmax[e >> 4], order_key(srow[j]));
+  }
+  bool ex;
+  const uint32_t t0 = wave_kth_largest<8>(gmax, m, &ex);
+  // pass 2: compact the candidates >= t0 in index order
+  int ns = 0;
+  for (int e = na / 64; e <= hi_e; ++e) {
+    const int j = lane + 64 * e;
+    const bool c = j >= na && j < ws && t0 > 0u && order_key(srow[j]) >= t0;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(c);
+    const int pos = ns + lanes_below(bal);
+    if (c && pos < 128) {
+      lds_key[wave][pos] = order_key(srow[j]);
+      lds_idx[wave][pos] = j;
+    }
+    ns += __builtin_popcountll(bal);
+  }
+  if (t0 == 0u || ns > 128) {
+    if (lane == 0) cnt[row] = -1;
+    return;
+  }
+  wave_lds_sync();
+  const bool ok0 = lane < ns, ok1 = lane + 64 < ns;
+  const uint32_t k0 = ok0 ? lds_key[wave][lane] : 0u, k1 = ok1 ? lds_key[wave][64 + lane] : 0u;
+  const int i0 = ok0 ? lds_idx[wave][lane] : -1, i1 = ok1 ? lds_idx[wave][64 + lane] : -1;
+  bool exact;
+  const uint32_t kk[2] = {k0, k1};
+  const uint32_t T = wave_kth_largest<2>(kk, m, &exact);
+  const int n_gt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok0 && k0 > T)) +
+                   __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok1 && k1 > T));
+  const uint64_t eq0 = __builtin_amdgcn_ballot_w64(ok0 && k0 == T);
+  const uint64_t eq1 = __builtin_amdgcn_ballot_w64(ok1 && k1 == T);
+  const int take_eq = exact ? 128 : m - n_gt;
+  const bool s0 = ok0 && (k0 > T || (k0 == T && lanes_below(eq0) < take_eq));
+  const bool s1 = ok1 && (k1 > T || (k1 == T && __builtin_popcountll(eq0) + lanes_below(eq1) < take_eq));
+  const uint64_t sm0 = __builtin_amdgcn_ballot_w64(s0), sm1 = __builtin_amdgcn_ballot_w64(s1);
+  const int nsel = __builtin_popcountll(sm0) + __builtin_popcountll(sm1);
+  if (s0) out[na + lanes_below(sm0)] = i0;
+  if (s1) out[na + __builtin_popcountll(sm0) + lanes_below(sm1)] = i1;
+  for (int e = lane; e < na; e += 64) out[e] = e;
+  for (int e = lane; e < nv - ws; e += 64) out[na + nsel + e] = ws + e;
+  const int total = na + nsel + (nv - ws);
+  for (int e = total + lane; e < kmax; e += 64) out[e] = -1;
+  if (lane == 0) cnt[row] = total;
+}
+
 // ============================================================== launch
 hipError_t launch_index_scores(const uint16_t* qi, const uint16_t* ki, const float* wi, float* scores, int B, int N,
                                int di, hipStream_t stream) {
@@ -297,6 +391,17 @@ static hipError_t launch_token_attn_d(const TokenAttnArgs& a, hipStream_t stream
   }
 #undef DSA_TOKEN_ATTN
   return hipGetLastError();
+}
+
+hipError_t launch_select_tokens(const float* scores, int32_t* idx, int32_t* cnt, int64_t n_rows, int N, TopkParams p,
+                                int kmax, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  if (N > 64 * 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(select_tokens_fast_kernel, dim3((uint32_t)((n_rows + 3) / 4)), dim3(256), 0, stream, scores, idx,
+                     cnt, n_rows, N, p, kmax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_select_marked(scores, idx, cnt, n_rows, N, p, kmax, stream);
 }
 
 hipError_t launch_token_attn(const TokenAttnArgs& a, int d, hipStream_t stream) {

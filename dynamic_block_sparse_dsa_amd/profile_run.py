@@ -3,12 +3,14 @@
     python3 -m dynamic_block_sparse_dsa_amd.profile_run attn   --workload prefill_n8192_h32 --reps 3
     python3 -m dynamic_block_sparse_dsa_amd.profile_run decode --workload decode_s32_l65536 --reps 3
     python3 -m dynamic_block_sparse_dsa_amd.profile_run bwd    --workload prefill_n8192_h32 --reps 3
+    python3 -m dynamic_block_sparse_dsa_amd.profile_run index  --workload index_n8192 --reps 3
     python3 -m dynamic_block_sparse_dsa_amd.profile_run copy   --mib 256 --reps 3
 
 ``attn`` selects once (dsa_prefill) and then launches dsa_sparse_attn_fwd
 ``reps`` times on the same indices; ``bwd`` selects and attends once and then
 launches dsa_sparse_attn_bwd ``reps`` times (seeded output gradient);
-``decode`` runs ``reps`` decode steps;
+``decode`` runs ``reps`` decode steps; ``index`` runs ``reps`` token-indexer
+steps (dsa_index_prefill);
 ``copy`` copies a ``mib`` MiB device buffer into another ``reps`` times (a plain
 copy kernel of known size: it reads and writes exactly ``mib`` MiB), which
 calibrates the HBM byte counters.  Each launch is followed by a device
@@ -21,7 +23,7 @@ import sys
 import torch
 
 import dynamic_block_sparse_dsa_amd as dsa
-from dynamic_block_sparse_dsa_amd.inputs import WORKLOADS, make_decode, make_prefill
+from dynamic_block_sparse_dsa_amd.inputs import INDEX_WORKLOADS, WORKLOADS, make_decode, make_index, make_prefill
 
 
 def run_attn(w, reps, stream):
@@ -48,6 +50,13 @@ def run_bwd(w, reps, stream):
     torch.cuda.synchronize()
     for _ in range(reps):
         dsa.dsa_sparse_attn_bwd(shape, q, k, v, o, lse, dout, idx, cnt, dq, dk, dv, ws, stream=stream)
+        stream.synchronize()
+
+
+def run_index(w, reps, stream):
+    qi, ki, wi, q, k, v = make_index(w, device="cuda")
+    for _ in range(reps):
+        dsa.index_prefill(qi, ki, wi, q, k, v, w.topk, stream=stream)
         stream.synchronize()
 
 
@@ -80,7 +89,7 @@ def run_copy(mib, reps, stream):
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("what", choices=["attn", "bwd", "decode", "copy"])
+    ap.add_argument("what", choices=["attn", "bwd", "decode", "index", "copy"])
     ap.add_argument("--workload", default=None)
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--mib", type=int, default=256)
@@ -89,6 +98,8 @@ def main(argv=None):
     stream = torch.cuda.Stream()
     if a.what == "copy":
         run_copy(a.mib, a.reps, stream)
+    elif a.what == "index":
+        run_index(INDEX_WORKLOADS[a.workload or "index_n8192"], a.reps, stream)
     else:
         name = a.workload or ("decode_s32_l65536" if a.what == "decode" else "prefill_n8192_h32")
         w = WORKLOADS[name]
