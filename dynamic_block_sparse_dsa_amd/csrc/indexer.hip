@@ -29,8 +29,9 @@
 // select_tokens_fast_kernel: one wave per query-token row of up to 8192
 //   scores.  Lane l owns tokens l + 64 e (so every load instruction reads 256
 //   consecutive bytes and ballots over e visit the candidates in index order).
-//   Pass 1 keeps 8 group maxima per lane; the m-th largest of them is a lower
-//   bound t0 of the m-th largest candidate (the groups are disjoint).  Pass 2
+//   Pass 1 keeps 8 group maxima per lane (group = e mod 8); the m-th largest
+//   of them (found exactly, no early exit) is a lower bound t0 of the m-th
+//   largest candidate (the groups are disjoint).  Pass 2
 //   re-reads the row (from L2) and compacts the candidates >= t0 -- usually
 //   about m -- into LDS in index order; the threshold search then runs on two
 //   keys per lane.  Rows it cannot finish (more than 64 to keep, or more than
@@ -311,28 +312,51 @@ __global__ __launch_bounds__(256) void select_tokens_fast_kernel(const float* __
     return;
   }
   const int hi_e = (ws - 1) / 64;  // last e with a candidate in some lane
-  // pass 1: group maxima of the candidate keys (0 = no candidate)
+  // pass 1: group maxima of the candidate keys (0 = no candidate).  Group
+  // g of a lane holds its e = g mod 8, so every row -- short ones too --
+  // spreads over all 8 groups; 16 loads are issued together.
+  const int e_lo = (na / 64) & ~15;
   uint32_t gmax[8];
 #pragma unroll
   for (int g = 0; g < 8; ++g) gmax[g] = 0u;
-  for (int e = na / 64; e <= hi_e; ++e) {
-    const int j = lane + 64 * e;
-    if (j >= na && j < ws) gmax[e >> 4] = max(gmax[e >> 4], order_key(srow[j]));
+  for (int e0 = e_lo; e0 <= hi_e; e0 += 16) {
+    uint32_t kv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = lane + 64 * (e0 + u);
+      kv[u] = (j >= na && j < ws) ? order_key(srow[j]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) gmax[u & 7] = max(gmax[u & 7], kv[u]);
   }
   bool ex;
-  const uint32_t t0 = wave_kth_largest<8>(gmax, m, &ex);
-  // pass 2: compact the candidates >= t0 in index order
+  const uint32_t t0 = wave_kth_largest<8, false>(gmax, m, &ex);  // the m-th largest group maximum
+  // pass 2: compact the candidates >= t0 in index order; a lane reads an
+  // element again only when its group maximum reaches t0
   int ns = 0;
-  for (int e = na / 64; e <= hi_e; ++e) {
-    const int j = lane + 64 * e;
-    const bool c = j >= na && j < ws && t0 > 0u && order_key(srow[j]) >= t0;
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(c);
-    const int pos = ns + lanes_below(bal);
-    if (c && pos < 128) {
-      lds_key[wave][pos] = order_key(srow[j]);
-      lds_idx[wave][pos] = j;
+  if (t0 > 0u) {
+    bool need[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) need[g] = gmax[g] >= t0;
+    for (int e0 = e_lo; e0 <= hi_e; e0 += 16) {
+      uint32_t kv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int j = lane + 64 * (e0 + u);
+        kv[u] = (need[u & 7] && j >= na && j < ws) ? order_key(srow[j]) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const bool c = kv[u] >= t0;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(c);
+        const int pos = ns + lanes_below(bal);
+        if (c && pos < 128) {
+          lds_key[wave][pos] = kv[u];
+          lds_idx[wave][pos] = lane + 64 * (e0 + u);
+        }
+        ns += __builtin_popcountll(bal);
+      }
     }
-    ns += __builtin_popcountll(bal);
   }
   if (t0 == 0u || ns > 128) {
     if (lane == 0) cnt[row] = -1;
@@ -397,6 +421,9 @@ hipError_t launch_select_tokens(const float* scores, int32_t* idx, int32_t* cnt,
                                 int kmax, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   if (N > 64 * 128) return hipErrorInvalidValue;
+  const int nf = (p.anchors > 0 ? 1 : 0) + (p.window > 0 ? 1 : 0);
+  if (p.topk - nf > 64)  // the fast path cannot take these rows: general select for all
+    return launch_select_topk(scores, idx, cnt, n_rows, N, N, true, p, kmax, stream);
   hipLaunchKernelGGL(select_tokens_fast_kernel, dim3((uint32_t)((n_rows + 3) / 4)), dim3(256), 0, stream, scores, idx,
                      cnt, n_rows, N, p, kmax);
   hipError_t e = hipGetLastError();

@@ -202,26 +202,36 @@ hipError_t launch_select_topk(const float* scores, int32_t* idx, int32_t* cnt, i
 
 // ============================================================== marked token rows
 // The general one-wave select for the causal rows whose count is -1 (rows the
-// token fast path left); the others exit at once.
+// token fast path left).  Each wave scans 64 consecutive rows' counts at once
+// and selects only the marked ones, so the usual (no or few marked rows)
+// launch is short.
 __global__ __launch_bounds__(256) void select_marked_kernel(const float* __restrict__ scores, int32_t* __restrict__ idx,
                                                             int32_t* __restrict__ cnt, int64_t n_rows, int N,
                                                             TopkParams p, int kmax) {
   __shared__ uint32_t lds_key[4][128];
   __shared__ int32_t lds_idx[4][128];
+  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= n_rows) return;
-  if (__builtin_amdgcn_readfirstlane(cnt[row]) >= 0) return;
-  const int nv = (int)(row % N) + 1;
-  const int total = wave_select_row<128>(scores + row * (int64_t)N, nv, p, idx + row * (int64_t)kmax, kmax,
-                                         lds_key[wave], lds_idx[wave]);
-  if ((threadIdx.x & 63) == 0) cnt[row] = total;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
+  if (row0 >= n_rows) return;  // whole wave
+  const bool marked = row0 + lane < n_rows && cnt[row0 + lane] < 0;
+  uint64_t todo = __builtin_amdgcn_ballot_w64(marked);
+  while (todo) {
+    const int l = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int64_t row = row0 + l;
+    const int nv = (int)(row % N) + 1;
+    const int total = wave_select_row<128>(scores + row * (int64_t)N, nv, p, idx + row * (int64_t)kmax, kmax,
+                                           lds_key[wave], lds_idx[wave]);
+    if (lane == 0) cnt[row] = total;
+  }
 }
 
 hipError_t launch_select_marked(const float* scores, int32_t* idx, int32_t* cnt, int64_t n_rows, int N, TopkParams p,
                                 int kmax, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_marked_kernel, dim3((uint32_t)((n_rows + 3) / 4)), dim3(256), 0, stream, scores, idx, cnt,
+  const int64_t waves = (n_rows + 63) / 64;
+  hipLaunchKernelGGL(select_marked_kernel, dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0, stream, scores, idx, cnt,
                      n_rows, N, p, kmax);
   return hipGetLastError();
 }

@@ -106,8 +106,11 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 // Largest T >= 1 with at least m of the values v[0..C-1] of the 64 lanes
 // >= T (0 if fewer than m values are >= 1; a 0 never counts).  *exact is set
-// when exactly m values are >= T.
-template <int C>
+// when exactly m values are >= T.  With EARLY the search stops at the first
+// trial value with exactly m values at or above it (T then has only its
+// leading bits and can lie well below the m-th largest value); without it T
+// is the m-th largest value itself.
+template <int C, bool EARLY = true>
 __device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&v)[C], int m, bool* exact) {
   uint32_t T = 0;
   *exact = false;
@@ -118,7 +121,7 @@ __device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&v)[C], int
     for (int c = 0; c < C; ++c) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[c] >= trial));
     if (n >= m) {
       T = trial;
-      if (n == m) {
+      if (EARLY && n == m) {
         *exact = true;
         break;
       }

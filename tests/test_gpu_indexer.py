@@ -124,3 +124,25 @@ def test_index_full_n8192_sampled(cuda_device):
         check_out(np64(g["o"][b, h, t])[None], o_ref[b, h, t][None], np64(g["lse"][b, h, t]).reshape(1),
                   lse_ref[b, h, t].reshape(1), f"n8192 h{h} t{t}")
     assert torch.isfinite(g["o"].float()).all()
+
+
+def test_all_tied_scores_take_the_lowest_positions(cuda_device):
+    """Zero index queries give every score 0: a row keeps the sink, itself and
+    the lowest other positions (ties go to the lower position).  Every long row
+    has more than 128 tied candidates, so the fast path hands them all to the
+    general select."""
+    w = IndexWorkload("z", 1, 2, 1, 3000, 64, 16, 64, 64, seed=68)
+    qi, ki, wi, q, k, v = make_index(w, device=cuda_device)
+    qi.zero_()
+    o, lse, idx, cnt = dsa.index_prefill(qi, ki, wi, q, k, v, w.topk)
+    torch.cuda.synchronize()
+    gi, gc = idx.cpu().numpy()[0], cnt.cpu().numpy()[0]
+    for t in range(w.seq_len):
+        want = list(range(t + 1)) if t < 64 else list(range(63)) + [t]
+        assert gc[t] == len(want) and list(gi[t, : gc[t]]) == want, t
+    o_ref, lse_ref = O.token_attend(np64(q), np64(k), np64(v), idx.cpu().numpy(), cnt.cpu().numpy(),
+                                    units=[(0, h, t) for h in (0, 1) for t in (0, 70, 2999)])
+    for h in (0, 1):
+        for t in (0, 70, 2999):
+            check_out(np64(o[0, h, t])[None], o_ref[0, h, t][None], np64(lse[0, h, t]).reshape(1),
+                      lse_ref[0, h, t].reshape(1), f"tied h{h} t{t}")
