@@ -27,6 +27,11 @@ What it computes, step by step, in the order the method runs:
                         same selection rule as O3, rows = tokens).
   I3 ``token_attend``  attention of every head over its token's selected
                         tokens.  ``index_prefill`` chains I1-I3.
+  P1 ``paged_gather`` /  a paged KV cache (pages of one block, a block table
+     ``paged_decode``    per sequence, a length per sequence): the decode of
+                        each sequence over its own gathered cache.
+  P2 ``kv_append``     append one token per sequence: write it into its page
+                        and recompute that page's key block mean.
   O5 ``attend_backward`` dQ, dK, dV of O4 with the selection held fixed (the
                         chain rule through O4's own definition, row by row).
 
@@ -70,7 +75,11 @@ Readings where the pages leave a point open (all listed in the design doc):
     features, 16 index heads, top-64 per query token) the score of earlier
     token s for query token t is sum_h w[t,h] * ReLU(qi[t,h] . ki[s]) with one
     index key per token shared by the heads; one top-k per query token (sink
-    and self forced as in O3) is shared by every attention head.
+    and self forced as in O3) is shared by every attention head;
+  * production decode: a page holds one block of one sequence for every KV
+    head; sequence s sees its first lengths[s] tokens; the block means are
+    kept per page and recomputed from the page's rows when a token lands in
+    it (the index data is built when the cache is written).
 
 Parity status: every function here is pinned by tests in ``tests/`` that do
 not re-use this module's formulas (dense special case against a library
@@ -688,4 +697,88 @@ def index_prefill(qi, ki, wi, q, k, v, topk: int, flags: int = FORCE_SINK | FORC
     idx, cnt, rows = select_tokens(sc, topk, flags)
     o, lse = token_attend(q, k, v, idx, cnt, units=attend_units)
     return dict(scores=sc, idx=idx, cnt=cnt, rows=rows, o=o, lse=lse)
+
+
+# --------------------------------------------------------------------------
+# P1-P2 -- paged KV cache, per-sequence lengths, appends
+# --------------------------------------------------------------------------
+def paged_gather(pool: np.ndarray, table: np.ndarray, s: int, length: int, block: int) -> np.ndarray:
+    """The first ``length`` rows of sequence s from a paged pool [n_pages,
+    Hkv, block, d]: logical block j lives in page table[s, j].  Returns
+    [Hkv, length, d]."""
+    nb = n_blocks(length, block)
+    if nb == 0:
+        return np.zeros((pool.shape[1], 0, pool.shape[3]))
+    rows = [np.asarray(pool[int(table[s, j])], dtype=np.float64) for j in range(nb)]
+    return np.concatenate(rows, axis=1)[:, :length]
+
+
+def paged_decode(q, k_pool, v_pool, table, lengths, block: int, topk: int, num: int = 0, den: int = 1,
+                 flags: int = FORCE_SINK | FORCE_DIAG, spec: SelectSpec = DEFAULT_SPEC, units=None):
+    """One decode step over a paged cache with a length per sequence: for
+    every sequence the O1-O4 decode of its own gathered cache (its new token
+    is at position lengths[s] - 1; its last block may be partial).  [ZB]
+    "动态开销与计算收益的权衡" ties the index data to the KV cache.
+
+    q [S, Hq, d]; pools [n_pages, Hkv, block, d]; table [S, max_blocks];
+    lengths [S].  Returns o [S, Hq, d], lse [S, Hq], idx [S, Hkv, kmax] (-1
+    padded, kmax from the longest possible sequence, max_blocks * block),
+    cnt [S, Hkv] and rows (a list per (s, g), None for empty sequences).
+    ``units`` restricts the attention to a list of (s, g)."""
+    q = np.asarray(q, dtype=np.float64)
+    S, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    max_blocks = table.shape[1]
+    km = kmax(1, topk, num, den, flags, False, max_blocks, spec)
+    o = np.zeros((S, Hq, d))
+    lse = np.full((S, Hq), -np.inf)
+    idx = np.full((S, Hkv, km), -1, dtype=np.int32)
+    cnt = np.zeros((S, Hkv), dtype=np.int32)
+    rows = [None] * (S * Hkv)
+    for s in range(S):
+        L = int(lengths[s])
+        if L == 0:
+            continue
+        kc = paged_gather(k_pool, table, s, L, block)[None]
+        vc = paged_gather(v_pool, table, s, L, block)[None]
+        todo = [(0, g) for g in range(Hkv) if units is None or (s, g) in units]
+        r = decode(q[s : s + 1], kc, vc, block, topk, num, den, flags, units=todo, spec=spec)
+        for g in range(Hkv):
+            c = int(r["cnt"][0, g])
+            idx[s, g, :c] = r["idx"][0, g, :c]
+            cnt[s, g] = c
+            rows[s * Hkv + g] = r["rows"][g]
+            if units is None or (s, g) in units:
+                o[s, g * G : (g + 1) * G] = r["o"][0, g * G : (g + 1) * G]
+                lse[s, g * G : (g + 1) * G] = r["lse"][0, g * G : (g + 1) * G]
+    return dict(o=o, lse=lse, idx=idx, cnt=cnt, rows=rows)
+
+
+def kv_append(k_pool, v_pool, kbar_pool, table, lengths, k_new, v_new, block: int):
+    """Append one token per sequence, in place: sequence s writes k_new[s],
+    v_new[s] ([Hkv, d]) at position lengths[s] (page table[s, pos // block],
+    slot pos % block), recomputes that page's key mean over its rows 0 ..
+    pos % block, and advances lengths[s]."""
+    for s in range(len(lengths)):
+        pos = int(lengths[s])
+        page = int(table[s, pos // block])
+        slot = pos % block
+        k_pool[page, :, slot] = k_new[s]
+        v_pool[page, :, slot] = v_new[s]
+        kbar_pool[page] = np.asarray(k_pool[page, :, : slot + 1], dtype=np.float64).mean(axis=1)
+        lengths[s] = pos + 1
+
+
+def paged_block_means(k_pool, table, lengths, block: int, n_pages: int) -> np.ndarray:
+    """Key block means per page for the pages the sequences use: the mean of
+    the page's rows that lie below the sequence's length.  Unused pages stay
+    zero.  Returns [n_pages, Hkv, d]."""
+    out = np.zeros((n_pages, k_pool.shape[1], k_pool.shape[3]))
+    for s in range(len(lengths)):
+        L = int(lengths[s])
+        for j in range(n_blocks(L, block)):
+            rows = min(block, L - j * block)
+            out[int(table[s, j])] = np.asarray(k_pool[int(table[s, j]), :, :rows], dtype=np.float64).mean(axis=1)
+    return out
 
