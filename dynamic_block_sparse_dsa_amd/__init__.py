@@ -50,6 +50,9 @@ EXPORTS = [
     "dsa_kv_block_means",
     "dsa_decode_workspace_bytes",
     "dsa_decode",
+    "dsa_paged_decode",
+    "dsa_paged_kv_append",
+    "dsa_paged_kv_block_means",
     "dsa_status_str",
     "dsa_last_error",
 ]
@@ -150,6 +153,9 @@ def load() -> ctypes.CDLL:
         "dsa_kv_block_means": ([S, P, P, P], ctypes.c_int),
         "dsa_decode_workspace_bytes": ([S], SZ),
         "dsa_decode": ([S, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "dsa_paged_decode": ([S, P, P, P, P, I32, P, I32, P, P, P, P, P, P], ctypes.c_int),
+        "dsa_paged_kv_append": ([S, P, P, P, I32, P, P, P, P, I32, P], ctypes.c_int),
+        "dsa_paged_kv_block_means": ([S, P, P, I32, P, P, I32, P], ctypes.c_int),
         "dsa_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "dsa_last_error": ([], ctypes.c_char_p),
     }
@@ -375,6 +381,47 @@ def dsa_decode(shape: Shape, q, k_cache, v_cache, kbar, o, lse, idx, ws, stream=
         _ptr(idx, torch.int32, (S, Hkv, km), "idx"), wp, wb, _stream(stream)))
 
 
+def _paged_dims(shape: Shape, k_pool, table):
+    n_pages = int(k_pool.shape[0])
+    return n_pages, int(table.shape[1])
+
+
+def dsa_paged_decode(shape: Shape, q, k_pool, v_pool, kbar_pool, block_table, lengths, o, lse, idx, cnt=None,
+                     stream=None):
+    S, Hq, Hkv, d, b = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.block
+    n_pages, mb = _paged_dims(shape, k_pool, block_table)
+    km = dsa_decode_kmax(shape)
+    _check(load().dsa_paged_decode(
+        ctypes.byref(shape), _ptr(q, torch.bfloat16, (S, Hq, d), "q"),
+        _ptr(k_pool, torch.bfloat16, (n_pages, Hkv, b, d), "k_pool"),
+        _ptr(v_pool, torch.bfloat16, (n_pages, Hkv, b, d), "v_pool"),
+        _ptr(kbar_pool, torch.float32, (n_pages, Hkv, d), "kbar_pool"), n_pages,
+        _ptr(block_table, torch.int32, (S, mb), "block_table"), mb, _ptr(lengths, torch.int32, (S,), "lengths"),
+        _ptr(o, torch.bfloat16, (S, Hq, d), "o"), _ptr(lse, torch.float32, (S, Hq), "lse", optional=True),
+        _ptr(idx, torch.int32, (S, Hkv, km), "idx"), _ptr(cnt, torch.int32, (S, Hkv), "cnt", optional=True),
+        _stream(stream)))
+
+
+def dsa_paged_kv_append(shape: Shape, k_new, v_new, block_table, lengths, k_pool, v_pool, kbar_pool, stream=None):
+    S, Hkv, d, b = shape.batch, shape.n_kv_heads, shape.head_dim, shape.block
+    n_pages, mb = _paged_dims(shape, k_pool, block_table)
+    _check(load().dsa_paged_kv_append(
+        ctypes.byref(shape), _ptr(k_new, torch.bfloat16, (S, Hkv, d), "k_new"),
+        _ptr(v_new, torch.bfloat16, (S, Hkv, d), "v_new"), _ptr(block_table, torch.int32, (S, mb), "block_table"), mb,
+        _ptr(lengths, torch.int32, (S,), "lengths"), _ptr(k_pool, torch.bfloat16, (n_pages, Hkv, b, d), "k_pool"),
+        _ptr(v_pool, torch.bfloat16, (n_pages, Hkv, b, d), "v_pool"),
+        _ptr(kbar_pool, torch.float32, (n_pages, Hkv, d), "kbar_pool"), n_pages, _stream(stream)))
+
+
+def dsa_paged_kv_block_means(shape: Shape, k_pool, block_table, lengths, kbar_pool, stream=None):
+    S, Hkv, d, b = shape.batch, shape.n_kv_heads, shape.head_dim, shape.block
+    n_pages, mb = _paged_dims(shape, k_pool, block_table)
+    _check(load().dsa_paged_kv_block_means(
+        ctypes.byref(shape), _ptr(k_pool, torch.bfloat16, (n_pages, Hkv, b, d), "k_pool"),
+        _ptr(block_table, torch.int32, (S, mb), "block_table"), mb, _ptr(lengths, torch.int32, (S,), "lengths"),
+        _ptr(kbar_pool, torch.float32, (n_pages, Hkv, d), "kbar_pool"), n_pages, _stream(stream)))
+
+
 # ----------------------------------------------------------------- conveniences
 def prefill(q, k, v, block: int, topk: int = 0, topk_num: int = 0, topk_den: int = 1,
             flags: int = FORCE_SINK | FORCE_DIAG, want_lse: bool = True, stream=None, **select):
@@ -445,6 +492,33 @@ def index_prefill(qi, ki, wi, q, k, v, topk: int, flags: int = FORCE_SINK | FORC
     ws = torch.empty(max(1, dsa_index_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
     dsa_index_prefill(shape, qi, ki, wi, q, k, v, o, lse, idx, cnt, ws, stream)
     return o, lse, idx, cnt
+
+
+def paged_decode(q, k_pool, v_pool, kbar_pool, block_table, lengths, block: int, topk: int = 0, topk_num: int = 0,
+                 topk_den: int = 1, flags: int = FORCE_SINK | FORCE_DIAG, n_anchor: int = 0, window: int = 0,
+                 want_lse: bool = True, stream=None):
+    """One decode step over a paged cache (a length per sequence); allocates
+    o, lse, idx and cnt."""
+    S, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    mb = block_table.shape[1]
+    shape = make_shape(S, Hq, Hkv, mb * block, d, block, topk, topk_num, topk_den, flags, n_anchor=n_anchor,
+                       window=window)
+    km = dsa_decode_kmax(shape)
+    dev = q.device
+    o = torch.empty_like(q)
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=dev) if want_lse else None
+    idx = torch.empty((S, Hkv, km), dtype=torch.int32, device=dev)
+    cnt = torch.empty((S, Hkv), dtype=torch.int32, device=dev)
+    dsa_paged_decode(shape, q, k_pool, v_pool, kbar_pool, block_table, lengths, o, lse, idx, cnt, stream)
+    return o, lse, idx, cnt
+
+
+def paged_shape(k_pool, block_table, n_q_heads: int, batch: int | None = None) -> Shape:
+    """A shape for the paged cache calls that need no selection parameters."""
+    n_pages, Hkv, b, d = k_pool.shape
+    S = block_table.shape[0] if batch is None else batch
+    return make_shape(S, n_q_heads, Hkv, block_table.shape[1] * b, d, b, 1)
 
 
 def kv_block_means(k_cache, block: int, stream=None):

@@ -250,6 +250,82 @@ int dsa_select_topk(const dsa_shape* s, const float* scores, int32_t* idx, int32
   return DSA_OK;
 }
 
+static int check_paged(const dsa_shape* s, int32_t n_pages, int32_t max_blocks) {
+  int rc = check_decode(s);
+  if (rc) return rc;
+  if (n_pages < 1) return fail(DSA_ERR_SHAPE, "n_pages %d < 1", n_pages);
+  if (max_blocks != n_blocks(s))
+    return fail(DSA_ERR_SHAPE, "max_blocks %d != ceil(seq_len %d / block %d)", max_blocks, s->seq_len, s->block);
+  if ((int64_t)n_pages * s->n_kv_heads * s->block * s->head_dim >= (1ll << 40))
+    return fail(DSA_ERR_UNSUPPORTED, "page pool too large");
+  return DSA_OK;
+}
+
+int dsa_paged_decode(const dsa_shape* s, const void* q, const void* k_pool, const void* v_pool,
+                     const float* kbar_pool, int32_t n_pages, const int32_t* block_table, int32_t max_blocks,
+                     const int32_t* lengths, void* o, float* lse, int32_t* idx, int32_t* cnt, void* stream) {
+  int rc = check_paged(s, n_pages, max_blocks);
+  if (rc) return rc;
+  if (s->batch == 0) return DSA_OK;
+  if (!q || !k_pool || !v_pool || !kbar_pool || !block_table || !lengths || !o || !idx)
+    return fail(DSA_ERR_NULL, "q, k_pool, v_pool, kbar_pool, block_table, lengths, o or idx is NULL");
+  dsa::PagedArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kp = static_cast<const uint16_t*>(k_pool);
+  a.vp = static_cast<const uint16_t*>(v_pool);
+  a.kbar = kbar_pool;
+  a.table = block_table;
+  a.lengths = lengths;
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.S = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.max_blocks = max_blocks;
+  a.n_pages = n_pages;
+  a.kmax = row_budget(s, (int)n_blocks(s));
+  a.scale = (float)(1.0 / sqrt((double)s->head_dim));
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
+  hipError_t e = dsa::launch_paged_decode(a, s->head_dim, s->block, topk_params(s), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "paged decode launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_paged_kv_append(const dsa_shape* s, const void* k_new, const void* v_new, const int32_t* block_table,
+                        int32_t max_blocks, int32_t* lengths, void* k_pool, void* v_pool, float* kbar_pool,
+                        int32_t n_pages, void* stream) {
+  int rc = check_paged(s, n_pages, max_blocks);
+  if (rc) return rc;
+  if (s->batch == 0) return DSA_OK;
+  if (!k_new || !v_new || !block_table || !lengths || !k_pool || !v_pool || !kbar_pool)
+    return fail(DSA_ERR_NULL, "k_new, v_new, block_table, lengths, k_pool, v_pool or kbar_pool is NULL");
+  hipError_t e = dsa::launch_kv_append(static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                                       block_table, lengths, static_cast<uint16_t*>(k_pool),
+                                       static_cast<uint16_t*>(v_pool), kbar_pool, s->batch, s->n_kv_heads,
+                                       s->head_dim, s->block, max_blocks, n_pages, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv append launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_paged_kv_block_means(const dsa_shape* s, const void* k_pool, const int32_t* block_table, int32_t max_blocks,
+                             const int32_t* lengths, float* kbar_pool, int32_t n_pages, void* stream) {
+  int rc = check_paged(s, n_pages, max_blocks);
+  if (rc) return rc;
+  if (s->batch == 0) return DSA_OK;
+  if (!k_pool || !block_table || !lengths || !kbar_pool)
+    return fail(DSA_ERR_NULL, "k_pool, block_table, lengths or kbar_pool is NULL");
+  hipError_t e = dsa::launch_paged_means(static_cast<const uint16_t*>(k_pool), block_table, lengths, kbar_pool,
+                                         s->batch, s->n_kv_heads, s->head_dim, s->block, max_blocks, n_pages,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "paged block means launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
 int dsa_index_kmax(const dsa_index_shape* s, int32_t* kmax) {
   int rc = check_index(s);
   if (rc) return rc;

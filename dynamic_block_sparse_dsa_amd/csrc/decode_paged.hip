@@ -1,0 +1,341 @@
+// Decode over a paged KV cache with a length per sequence, and the cache-side
+// work that keeps its index data current (token appends, per-page block means).
+//
+// Method sources: "dynamic sparse attention explainer" (zblog.xzdbk.com/559.html),
+//   "动态开销与计算收益的权衡": build the index data when the cache is written
+//   (here: each page's key block mean, recomputed when a token lands in it);
+//   "硬件友好的稀疏计算实现": tie the block decision to the KV cache's blocks
+//   (here a page is one block); "基于Top-k选择的局部-全局混合": the best blocks
+//   plus anchors and a local window.  "稀疏注意力 vs Flash Attention v2"
+//   (pnsm.cn/news/1249548.html), section 1: softmax of the scaled logits over
+//   the kept keys, times V.
+//
+// Layout: pools [n_pages, Hkv, BLK, D] bf16 (one (page, head) tile is one
+// contiguous BLK * D * 2-byte run), block means [n_pages, Hkv, D] fp32,
+// block table [S, max_blocks] int32 (page of each logical block), lengths [S].
+//
+// decode_paged_kernel: one 512-thread workgroup per (sequence, KV head) unit.
+//   The unit's nB = ceil(L / BLK) block means are read through the block table
+//   (16-byte non-temporal loads, d/8 lanes per row, waves taking batches of
+//   rows from an LDS counter) and scored by the max over the group's heads of
+//   q . kbar / sqrt(d) into LDS; one wave selects; the 8 waves then walk the
+//   kept blocks' 32-key chunks (page base from the table, keys past the
+//   sequence's end masked) with WaveAttn and merge through LDS into o and lse.
+// kv_append_kernel: one workgroup per sequence: writes the new token's K and V
+//   rows into slot L % BLK of page table[L / BLK] for every KV head, recomputes
+//   that page's key mean over its rows 0 .. L % BLK, then advances the length.
+// paged_means_kernel: one wave per (sequence, logical block, KV head): the
+//   mean of the page's rows below the sequence's length.
+#include "decode_common.hpp"
+#include "topk_row.hpp"
+
+namespace dsa {
+
+template <int D, int BLK, int G, int R>
+__global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkParams p) {
+  using C = DecCfg<D, G>;
+  constexpr int NT = 512, NW = 8;
+  constexpr int CPB = BLK / C::CK;
+  constexpr int TPR = D / 8, WROWS = 64 / TPR, UNR = 8, BR = WROWS * UNR;
+  __shared__ float sc[64 * R];
+  __shared__ uint32_t lds_key[128];
+  __shared__ int32_t lds_idx[128];
+  __shared__ int next_batch, n_sel;
+  __shared__ int32_t sel[64 * R];
+  __shared__ float pbuf[NW][C::CK][G];
+  __shared__ float abuf[NW][G];
+  __shared__ float mw[NW][G], lw[NW][G];
+  __shared__ float accw[NW][G][D];
+  const int unit = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t s = unit / a.Hkv;
+  const int g = unit % a.Hkv;
+  const int L = min(max(a.lengths[s], 0), a.max_blocks * BLK);
+  const int nB = (L + BLK - 1) / BLK;
+  const int32_t* trow = a.table + s * (int64_t)a.max_blocks;
+  auto page_of = [&](int j) { return min(max(trow[j], 0), a.n_pages - 1); };
+  const int kmax = a.kmax;
+
+  if (L == 0) {  // an empty sequence: nothing kept, o = 0, lse = -inf
+    for (int e = tid; e < kmax; e += NT) a.idx[(int64_t)unit * kmax + e] = -1;
+    for (int e = tid; e < G * D; e += NT) a.o[((s * a.Hq + g * G) * (int64_t)D) + e] = 0;
+    if (tid < G && a.lse) a.lse[s * a.Hq + g * G + tid] = -__builtin_inff();
+    if (tid == 0 && a.cnt) a.cnt[unit] = 0;
+    return;
+  }
+
+  // ---- scores of the nB blocks (through the table), then one wave selects
+  {
+    const int c = lane % TPR, rl = lane / TPR;
+    const int nbatch = (nB + BR - 1) / BR;
+    if (tid == 0) next_batch = NW;
+    __syncthreads();
+    float qv[G][8];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(a.q + (s * a.Hq + g * G + hh) * (int64_t)D + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[hh][2 * e] = bf16_lo(w[e]);
+        qv[hh][2 * e + 1] = bf16_hi(w[e]);
+      }
+    }
+    auto load = [&](f32x4(&kv)[UNR][2], int b) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int row = min(b * BR + u * WROWS + rl, nB - 1);
+        const float* kr = a.kbar + ((int64_t)page_of(row) * a.Hkv + g) * D + 8 * c;
+        kv[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kr));
+        kv[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kr + 4));
+      }
+    };
+    auto score = [&](const f32x4(&kv)[UNR][2], int b) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        float best = -__builtin_inff();
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            part = __builtin_fmaf(qv[hh][e], kv[u][0][e], part);
+            part = __builtin_fmaf(qv[hh][4 + e], kv[u][1][e], part);
+          }
+          best = fmaxf(best, group_sum<TPR>(part) * a.scale);
+        }
+        const int row = b * BR + u * WROWS + rl;
+        if (c == 0 && row < nB) sc[(row % R) * 64 + row / R] = best;
+      }
+    };
+    auto grab = [&]() {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(&next_batch, 1);
+      return __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
+    };
+    f32x4 k0[UNR][2], k1[UNR][2];
+    int b0 = wave;
+    if (b0 < nbatch) load(k0, b0);
+    int b1 = grab();
+    while (b0 < nbatch) {
+      if (b1 < nbatch) load(k1, b1);
+      score(k0, b0);
+      b0 = grab();
+      if (b1 >= nbatch) break;
+      if (b0 < nbatch) load(k0, b0);
+      score(k1, b1);
+      b1 = grab();
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int n = wave_select_row<R, true>(sc, nB, p, sel, kmax, lds_key, lds_idx);
+      if (tid == 0) n_sel = n;
+    }
+    __syncthreads();
+  }
+  const int ns = n_sel;
+  for (int e = tid; e < kmax; e += NT) a.idx[(int64_t)unit * kmax + e] = sel[e];
+  if (tid == 0 && a.cnt) a.cnt[unit] = ns;
+  if (tid == 0) next_batch = NW;
+  __syncthreads();
+
+  // ---- attention over the kept blocks' chunks
+  WaveAttn<D, G> wa;
+  wa.init(a.q, a.Hq, s, g);
+  ChunkRegs<D, G> rA, rB;
+  const int nch = ns * CPB;
+  struct Ref {
+    const uint16_t* kb;
+    const uint16_t* vb;
+    int key0, lim;  // key0 < 0: nothing
+  };
+  auto ref_of = [&](int i) {
+    Ref r{nullptr, nullptr, -1, 0};
+    if (i >= nch) return r;
+    const int blk = sel[i / CPB];
+    const int key0 = (i % CPB) * C::CK;
+    const int lim = min(BLK, L - blk * BLK);
+    if (key0 >= lim) return r;
+    const int64_t tile = ((int64_t)page_of(blk) * a.Hkv + g) * BLK * D;
+    r.kb = a.kp + tile;
+    r.vb = a.vp + tile;
+    r.key0 = key0;
+    r.lim = lim;
+    return r;
+  };
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_batch, 1);
+    return __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
+  };
+  int iA = wave;
+  Ref fA = ref_of(iA);
+  if (fA.key0 >= 0) wa.load(rA, fA.kb, fA.vb, fA.key0, fA.lim);
+  int iB = grab();
+  while (iA < nch) {
+    const Ref fB = ref_of(iB);
+    if (fB.key0 >= 0) wa.load(rB, fB.kb, fB.vb, fB.key0, fB.lim);
+    if (fA.key0 >= 0) wa.step(rA, fA.key0, fA.lim, a.scale_log2, pbuf[wave], abuf[wave]);
+    if (iB >= nch) break;
+    iA = grab();
+    fA = ref_of(iA);
+    if (fA.key0 >= 0) wa.load(rA, fA.kb, fA.vb, fA.key0, fA.lim);
+    if (fB.key0 >= 0) wa.step(rB, fB.key0, fB.lim, a.scale_log2, pbuf[wave], abuf[wave]);
+    iB = grab();
+  }
+  wa.to_lds(mw[wave], lw[wave], accw[wave]);
+  __syncthreads();
+  for (int e = tid; e < G * D; e += NT) {
+    const int hh = e / D, dd = e % D;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w][hh]);
+    float l = 0.f, v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = __builtin_amdgcn_exp2f(mw[w][hh] - M);  // 0 for a wave with no chunk
+      l += f * lw[w][hh];
+      v += f * accw[w][hh][dd];
+    }
+    const int64_t oh = s * a.Hq + g * G + hh;
+    a.o[oh * D + dd] = (uint16_t)f32_to_bf16_rne(v / l);
+    if (a.lse && dd == 0) a.lse[oh] = (M + __log2f(l)) * 0.69314718055994531f;
+  }
+}
+
+// ============================================================== appends
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restrict__ k_new,
+                                                        const uint16_t* __restrict__ v_new,
+                                                        const int32_t* __restrict__ table, int32_t* lengths,
+                                                        uint16_t* __restrict__ kp, uint16_t* __restrict__ vp,
+                                                        float* __restrict__ kbar, int Hkv, int max_blocks,
+                                                        int n_pages) {
+  const int64_t s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int pos = lengths[s];
+  __syncthreads();  // every thread has read the length before it moves
+  if (pos < 0 || pos >= max_blocks * BLK) return;  // full (or invalid): nothing written
+  const int page = table[s * (int64_t)max_blocks + pos / BLK];
+  if (page < 0 || page >= n_pages) return;
+  const int slot = pos % BLK;
+  for (int e = tid; e < Hkv * D; e += 256) {
+    const int g = e / D, dd = e % D;
+    const int64_t tile = ((int64_t)page * Hkv + g) * BLK * D;
+    const uint16_t kv = k_new[(s * Hkv + g) * D + dd];
+    kp[tile + (int64_t)slot * D + dd] = kv;
+    vp[tile + (int64_t)slot * D + dd] = v_new[(s * Hkv + g) * D + dd];
+    // the page's mean over rows 0 .. slot, summed in row order (as
+    // paged_means_kernel does): earlier rows from the pool, the new row from
+    // the source (no read-after-write of the pool)
+    float sum = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < slot; ++r) sum += __uint_as_float((uint32_t)kp[tile + (int64_t)r * D + dd] << 16);
+    sum += __uint_as_float((uint32_t)kv << 16);
+    kbar[((int64_t)page * Hkv + g) * D + dd] = sum / (float)(slot + 1);
+  }
+  __syncthreads();
+  if (tid == 0) lengths[s] = pos + 1;
+}
+
+// ============================================================== per-page means
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void paged_means_kernel(const uint16_t* __restrict__ kp,
+                                                          const int32_t* __restrict__ table,
+                                                          const int32_t* __restrict__ lengths,
+                                                          float* __restrict__ kbar, int S, int Hkv, int max_blocks,
+                                                          int n_pages) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w >= (int64_t)S * max_blocks * Hkv) return;
+  const int g = (int)(w % Hkv);
+  const int64_t sj = w / Hkv;
+  const int j = (int)(sj % max_blocks);
+  const int64_t s = sj / max_blocks;
+  const int L = min(max(lengths[s], 0), max_blocks * BLK);
+  if (j * BLK >= L) return;
+  const int page = table[s * (int64_t)max_blocks + j];
+  if (page < 0 || page >= n_pages) return;
+  const int rows = min(BLK, L - j * BLK);
+  const uint16_t* tile = kp + ((int64_t)page * Hkv + g) * BLK * D + lane * DPL;
+  float acc[DPL] = {};
+  for (int r = 0; r < rows; ++r) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] += __uint_as_float((uint32_t)tile[(int64_t)r * D + e] << 16);
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) kbar[((int64_t)page * Hkv + g) * D + lane * DPL + e] = acc[e] / (float)rows;
+}
+
+// ============================================================== launch
+template <int D, int BLK>
+static hipError_t launch_paged_d(const PagedArgs& a, TopkParams p, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const dim3 grid((uint32_t)((int64_t)a.S * a.Hkv)), blk(512);
+#define DSA_PAGED(GG, RR) hipLaunchKernelGGL((decode_paged_kernel<D, BLK, GG, RR>), grid, blk, 0, stream, a, p)
+#define DSA_PAGED_G(RR)                 \
+  switch (G) {                          \
+    case 1: DSA_PAGED(1, RR); break;    \
+    case 2: DSA_PAGED(2, RR); break;    \
+    case 4: DSA_PAGED(4, RR); break;    \
+    case 8: DSA_PAGED(8, RR); break;    \
+    default: return hipErrorInvalidValue; \
+  }
+  if (a.max_blocks <= 64 * 16) {
+    DSA_PAGED_G(16)
+  } else {
+    DSA_PAGED_G(64)
+  }
+#undef DSA_PAGED_G
+#undef DSA_PAGED
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_decode(const PagedArgs& a, int d, int block, TopkParams p, hipStream_t stream) {
+  if ((int64_t)a.S * a.Hkv == 0) return hipSuccess;
+  if (d == 64) return block == 64 ? launch_paged_d<64, 64>(a, p, stream) : launch_paged_d<64, 128>(a, p, stream);
+  return block == 64 ? launch_paged_d<128, 64>(a, p, stream) : launch_paged_d<128, 128>(a, p, stream);
+}
+
+hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* table, int32_t* lengths,
+                            uint16_t* kp, uint16_t* vp, float* kbar, int S, int Hkv, int d, int block, int max_blocks,
+                            int n_pages, hipStream_t stream) {
+  if (S == 0) return hipSuccess;
+  const dim3 grid((uint32_t)S), blk(256);
+  if (d == 64 && block == 64)
+    hipLaunchKernelGGL((kv_append_kernel<64, 64>), grid, blk, 0, stream, k_new, v_new, table, lengths, kp, vp, kbar,
+                       Hkv, max_blocks, n_pages);
+  else if (d == 64)
+    hipLaunchKernelGGL((kv_append_kernel<64, 128>), grid, blk, 0, stream, k_new, v_new, table, lengths, kp, vp, kbar,
+                       Hkv, max_blocks, n_pages);
+  else if (block == 64)
+    hipLaunchKernelGGL((kv_append_kernel<128, 64>), grid, blk, 0, stream, k_new, v_new, table, lengths, kp, vp, kbar,
+                       Hkv, max_blocks, n_pages);
+  else
+    hipLaunchKernelGGL((kv_append_kernel<128, 128>), grid, blk, 0, stream, k_new, v_new, table, lengths, kp, vp, kbar,
+                       Hkv, max_blocks, n_pages);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_means(const uint16_t* kp, const int32_t* table, const int32_t* lengths, float* kbar, int S,
+                              int Hkv, int d, int block, int max_blocks, int n_pages, hipStream_t stream) {
+  const int64_t waves = (int64_t)S * max_blocks * Hkv;
+  if (waves == 0) return hipSuccess;
+  const dim3 grid((uint32_t)((waves + 3) / 4)), blk(256);
+  if (d == 64 && block == 64)
+    hipLaunchKernelGGL((paged_means_kernel<64, 64>), grid, blk, 0, stream, kp, table, lengths, kbar, S, Hkv,
+                       max_blocks, n_pages);
+  else if (d == 64)
+    hipLaunchKernelGGL((paged_means_kernel<64, 128>), grid, blk, 0, stream, kp, table, lengths, kbar, S, Hkv,
+                       max_blocks, n_pages);
+  else if (block == 64)
+    hipLaunchKernelGGL((paged_means_kernel<128, 64>), grid, blk, 0, stream, kp, table, lengths, kbar, S, Hkv,
+                       max_blocks, n_pages);
+  else
+    hipLaunchKernelGGL((paged_means_kernel<128, 128>), grid, blk, 0, stream, kp, table, lengths, kbar, S, Hkv,
+                       max_blocks, n_pages);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

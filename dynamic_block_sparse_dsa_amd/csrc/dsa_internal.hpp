@@ -142,6 +142,29 @@ hipError_t launch_bwd_invert(const int32_t* idx, const int32_t* cnt, int32_t* in
                              int64_t n_units, int nB, int kmax, hipStream_t stream);
 hipError_t launch_sparse_attn_bwd(const BwdArgs& a, int d, int block, hipStream_t stream);
 
+// paged cache: pools [n_pages, Hkv, block, d], means [n_pages, Hkv, d],
+// table [S, max_blocks], lengths [S]
+struct PagedArgs {
+  const uint16_t* q;        // [S, Hq, d]
+  const uint16_t* kp;
+  const uint16_t* vp;
+  const float* kbar;
+  const int32_t* table;
+  const int32_t* lengths;
+  uint16_t* o;              // [S, Hq, d]
+  float* lse;               // [S, Hq] or null
+  int32_t* idx;             // [S, Hkv, kmax]
+  int32_t* cnt;             // [S, Hkv] or null
+  int S, Hq, Hkv, max_blocks, n_pages, kmax;
+  float scale, scale_log2;  // 1/sqrt(d), log2(e)/sqrt(d)
+};
+hipError_t launch_paged_decode(const PagedArgs& a, int d, int block, TopkParams p, hipStream_t stream);
+hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* table, int32_t* lengths,
+                            uint16_t* kp, uint16_t* vp, float* kbar, int S, int Hkv, int d, int block, int max_blocks,
+                            int n_pages, hipStream_t stream);
+hipError_t launch_paged_means(const uint16_t* kp, const int32_t* table, const int32_t* lengths, float* kbar, int S,
+                              int Hkv, int d, int block, int max_blocks, int n_pages, hipStream_t stream);
+
 struct DecodeArgs {
   const uint16_t* q;   // [S, Hq, d]
   const uint16_t* kc;  // [S, Hkv, L, d]

@@ -210,6 +210,49 @@ int dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void* k, co
                         const float* lse, const void* dout, const int32_t* idx, const int32_t* cnt, void* dq,
                         void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Paged decode with a length per sequence ("dynamic sparse attention
+ * explainer": "硬件友好的稀疏计算实现" ties the block decision to the KV
+ * cache's blocks; "动态开销与计算收益的权衡" builds the index data when the
+ * cache is written).  A page holds one block (shape->block tokens) of one
+ * sequence for every KV head:
+ *   k_pool, v_pool [n_pages, Hkv, block, d] bf16;
+ *   kbar_pool [n_pages, Hkv, d] fp32, each page's key mean;
+ *   block_table [S, max_blocks] int32, the page of logical block j of s;
+ *   lengths [S] int32, the tokens in each sequence's cache (device memory).
+ * shape: batch = S, heads, head_dim, block, topk / fraction, flags,
+ * n_anchor, window as for dsa_decode (select_mode DSA_SELECT_TOPK), and
+ * seq_len = the capacity, with max_blocks == ceil(seq_len / block); idx is
+ * [S, Hkv, dsa_decode_kmax(shape)].
+ * Sequence s (0 <= lengths[s] <= seq_len) is decoded over its first
+ * lengths[s] tokens exactly as dsa_decode with L = lengths[s] (its last block
+ * may be partial; its new token is at lengths[s] - 1); cnt [S, Hkv]
+ * (nullable) gets the kept counts, idx rows are -1 padded; an empty
+ * sequence gives o = 0, lse = -inf, cnt = 0.  The table entries of a
+ * sequence's first ceil(lengths[s] / block) blocks must name pages in
+ * [0, n_pages) (other entries are never read; out-of-range ones are clamped,
+ * never dereferenced). */
+int dsa_paged_decode(const dsa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
+                     const float* kbar_pool, int32_t n_pages, const int32_t* block_table, int32_t max_blocks,
+                     const int32_t* lengths, void* o, float* lse, int32_t* idx, int32_t* cnt, void* stream);
+
+/* Append one token per sequence: k_new, v_new [S, Hkv, d] bf16 go to
+ * position lengths[s] (page block_table[s][lengths[s] / block], slot
+ * lengths[s] % block); that page's key mean is recomputed over its rows 0 ..
+ * slot (summed in row order, as dsa_paged_kv_block_means does, so both give
+ * the same bits); lengths[s] is then incremented in place.  A sequence
+ * already holding seq_len tokens, or whose page is out of range, is left
+ * unchanged. */
+int dsa_paged_kv_append(const dsa_shape* shape, const void* k_new, const void* v_new, const int32_t* block_table,
+                        int32_t max_blocks, int32_t* lengths, void* k_pool, void* v_pool, float* kbar_pool,
+                        int32_t n_pages, void* stream);
+
+/* Key means of the pages in use: for every sequence s and logical block
+ * j < ceil(lengths[s] / block), kbar_pool[block_table[s][j]] = the mean of
+ * that page's rows below lengths[s].  Other pages are not written. */
+int dsa_paged_kv_block_means(const dsa_shape* shape, const void* k_pool, const int32_t* block_table,
+                             int32_t max_blocks, const int32_t* lengths, float* kbar_pool, int32_t n_pages,
+                             void* stream);
+
 /* ---- Token-level lightning indexer ("低成本高性能大模型实现路径：从架构创新
  * 到工程优化", yunthe.com/news/806485.html, section 2.1 "轻量化索引器设计":
  * ReLU feature heads, 16 index heads, every query token keeps its top 64
