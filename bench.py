@@ -153,6 +153,7 @@ def bench_decode(args, dev, stream):
     ms = tot / args.steps
     nbytes = work.decode_bytes(S, Hq, Hkv, L, d, w.block, km)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    args._decode_inputs = (q, kc, vc, w, flush)  # reused by the paged bench
     return dict(
         value=S / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
         config=dict(workload=w.name, sequences=S, n_q_heads=Hq, n_kv_heads=Hkv, cache_len=L, head_dim=d,
@@ -162,6 +163,78 @@ def bench_decode(args, dev, stream):
                       kernel=("decode step: decode_fused_kernel, one launch" if S * Hkv >= 256 else
                               "decode step: select, split attention, combine"), bytes_per_step=nbytes),
     )
+
+
+def bench_paged(args, dev, stream):
+    """dsa_paged_decode on the decode workload's caches scattered into
+    shuffled pages: every sequence at full length, then lengths drawn in
+    [L/4, L]; each step timed alone with events after a read-based cache
+    flush, priced in algorithmic bytes (work.paged_decode_bytes).  Also one
+    dsa_paged_kv_append of a token per sequence."""
+    import torch
+
+    import dynamic_block_sparse_dsa_amd as dsa
+    from dynamic_block_sparse_dsa_amd import work
+
+    q, kc, vc, w, flush = args._decode_inputs
+    S, Hq, Hkv, L, d, b = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block
+    mb = -(-L // b)
+    n_pages = S * mb + 64  # room for appends
+    g = torch.Generator(device="cpu")
+    g.manual_seed(9)
+    table = torch.randperm(n_pages, generator=g)[: S * mb].view(S, mb).to(torch.int32).to(dev)
+    kp = torch.empty((n_pages, Hkv, b, d), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    flat = table.reshape(-1).long()
+    kp[flat] = kc.view(S, Hkv, mb, b, d).permute(0, 2, 1, 3, 4).reshape(S * mb, Hkv, b, d)
+    vp[flat] = vc.view(S, Hkv, mb, b, d).permute(0, 2, 1, 3, 4).reshape(S * mb, Hkv, b, d)
+    kbar = torch.zeros((n_pages, Hkv, d), dtype=torch.float32, device=dev)
+    shape = dsa.make_shape(S, Hq, Hkv, mb * b, d, b, w.topk, w.topk_num, w.topk_den)
+    km = dsa.dsa_decode_kmax(shape)
+    o = torch.empty_like(q)
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=dev)
+    idx = torch.empty((S, Hkv, km), dtype=torch.int32, device=dev)
+    cnt = torch.empty((S, Hkv), dtype=torch.int32, device=dev)
+    out = {}
+    gl = torch.Generator(device="cpu")
+    gl.manual_seed(10)
+    cases = [("full_length", [L] * S),
+             ("mixed_lengths", torch.randint(L // 4, L + 1, (S,), generator=gl).tolist())]
+    for name, lens_list in cases:
+        lens = torch.tensor(lens_list, dtype=torch.int32, device=dev)
+        dsa.dsa_paged_kv_block_means(shape, kp, table, lens, kbar, stream=stream)
+
+        def step():
+            dsa.dsa_paged_decode(shape, q, kp, vp, kbar, table, lens, o, lse, idx, cnt, stream=stream)
+
+        for _ in range(args.warmup):
+            step()
+        tot = 0.0
+        for _ in range(args.steps):
+            with torch.cuda.stream(stream):
+                flush.sum()
+            tot += time_events(step, 1, stream)
+        ms = tot / args.steps
+        nbytes = work.paged_decode_bytes(lens.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(), Hq, d, b)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = dict(value=S / (ms * 1e-3), unit="tokens/s", ms_per_step=ms, tokens_in_caches=int(sum(lens_list)),
+                         roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                                       frac=round(gbs / PEAK_HBM_GBS, 4), bytes_per_step=nbytes,
+                                       kernel="decode_paged_kernel"))
+    # one append of a token per sequence (the mixed lengths leave room)
+    kn = torch.randn((S, Hkv, d), device=dev).to(torch.bfloat16)
+    vn = torch.randn((S, Hkv, d), device=dev).to(torch.bfloat16)
+    lens = torch.tensor(cases[1][1], dtype=torch.int32, device=dev).clamp(max=L - args.steps - args.warmup - 1)
+
+    def app():
+        dsa.dsa_paged_kv_append(shape, kn, vn, table, lens, kp, vp, kbar, stream=stream)
+
+    for _ in range(args.warmup):
+        app()
+    out["append_us"] = round(time_events(app, args.steps, stream) * 1e3, 2)
+    out["config"] = dict(workload=w.name + "_paged", sequences=S, n_q_heads=Hq, n_kv_heads=Hkv, capacity=L, head_dim=d,
+                         block=b, topk=w.topk, pages=n_pages)
+    return out
 
 
 def bench_backward(args, dev, stream, inputs):
@@ -370,6 +443,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-selection", action="store_true")
     ap.add_argument("--no-index", action="store_true")
+    ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--index-workload", default="index_n8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -406,6 +480,9 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(args, dev, stream)
+        if not args.no_paged:
+            out["paged_decode"] = bench_paged(args, dev, stream)
+        del args._decode_inputs
     if not args.no_backward:
         out["backward"] = bench_backward(args, dev, stream, inputs)
     if not args.no_selection:

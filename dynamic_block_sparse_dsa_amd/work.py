@@ -53,3 +53,20 @@ def decode_bytes(n_seq: int, hq: int, hkv: int, cache_len: int, d: int, block: i
 def decode_flops(n_seq: int, hq: int, kept: int, block: int, d: int, n_blocks: int) -> int:
     """Score scan (2*d per block per head) plus attention (4*d per key per head)."""
     return n_seq * hq * (2 * d * n_blocks + 4 * d * kept * block)
+
+
+def paged_decode_bytes(lengths, idx, cnt, hq: int, d: int, block: int) -> int:
+    """Bytes one paged decode step must move with a length per sequence: per
+    (sequence, KV head) the fp32 means of its ceil(L / block) pages and the
+    valid rows of its kept pages (K and V, bf16), plus q, o and the indices.
+    lengths [S]; idx [S, Hkv, kmax]; cnt [S, Hkv] (numpy)."""
+    S, hkv = cnt.shape
+    total = 0
+    for s in range(S):
+        L = int(lengths[s])
+        nb = -(-L // block)
+        for g in range(hkv):
+            rows = sum(min(block, L - int(j) * block) for j in idx[s, g, : cnt[s, g]])
+            total += nb * d * 4 + rows * d * 2 * 2 + int(cnt[s, g]) * 4
+    return total + S * hq * d * 2 * 2
+
