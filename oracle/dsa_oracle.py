@@ -32,6 +32,9 @@ What it computes, step by step, in the order the method runs:
                         each sequence over its own gathered cache.
   P2 ``kv_append``     append one token per sequence: write it into its page
                         and recompute that page's key block mean.
+  P3 ``quantize_fp8`` / FP8 (E4M3) cache rows with one fp32 scale per
+     ``dequantize_fp8``  (token, KV head) row; the fp8 paged decode is the
+                        paged decode of the dequantized pools.
   O5 ``attend_backward`` dQ, dK, dV of O4 with the selection held fixed (the
                         chain rule through O4's own definition, row by row).
 
@@ -79,7 +82,12 @@ Readings where the pages leave a point open (all listed in the design doc):
   * production decode: a page holds one block of one sequence for every KV
     head; sequence s sees its first lengths[s] tokens; the block means are
     kept per page and recomputed from the page's rows when a token lands in
-    it (the index data is built when the cache is written).
+    it (the index data is built when the cache is written);
+  * FP8 cache ([ZB] "工程实践建议": combine the sparsity with an FP8/INT4 KV
+    cache): a row's scale is amax / 448 in fp32 (448 is E4M3's largest
+    finite value; 1 for an all-zero row), its codes are the E4M3 values
+    nearest to fp32(x / scale), ties to even; the block means and the
+    attention use the dequantized values, code * scale.
 
 Parity status: every function here is pinned by tests in ``tests/`` that do
 not re-use this module's formulas (dense special case against a library
@@ -781,4 +789,55 @@ def paged_block_means(k_pool, table, lengths, block: int, n_pages: int) -> np.nd
             rows = min(block, L - j * block)
             out[int(table[s, j])] = np.asarray(k_pool[int(table[s, j]), :, :rows], dtype=np.float64).mean(axis=1)
     return out
+
+
+# --------------------------------------------------------------------------
+# P3 -- FP8 (E4M3) cache rows
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def quantize_fp8(x: np.ndarray):
+    """Rows of x (last axis) -> (codes uint8 [..., d], scales float32 [...]).
+
+    scale = fp32(amax(|row|) / 448) (1 for an all-zero row); code = E4M3
+    (OCP, no infinities) value nearest to fp32(x / scale), ties to even --
+    the division is taken in fp32, the precision the decision is made in.
+    The rounding itself is torch's float8_e4m3fn cast (a library step)."""
+    import torch
+
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x32).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x32 / scale[..., None]).astype(np.float32)
+    codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
+
+
+def fp8_values(codes: np.ndarray) -> np.ndarray:
+    """The E4M3 value of each code (float64)."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def dequantize_fp8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """code value * row scale (float64, exact)."""
+    return fp8_values(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def kv_append_fp8(k8, v8, k_scale, v_scale, kbar_pool, table, lengths, k_new, v_new, block: int):
+    """``kv_append`` for an FP8 cache: the new rows are quantized (their own
+    scales) and written; the page mean is recomputed from the dequantized
+    rows 0 .. slot."""
+    for s in range(len(lengths)):
+        pos = int(lengths[s])
+        page = int(table[s, pos // block])
+        slot = pos % block
+        kc, ks = quantize_fp8(k_new[s])
+        vc, vs = quantize_fp8(v_new[s])
+        k8[page, :, slot], k_scale[page, :, slot] = kc, ks
+        v8[page, :, slot], v_scale[page, :, slot] = vc, vs
+        kbar_pool[page] = dequantize_fp8(k8[page, :, : slot + 1], k_scale[page, :, : slot + 1]).mean(axis=1)
+        lengths[s] = pos + 1
 
