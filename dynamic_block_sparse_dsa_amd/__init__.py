@@ -53,6 +53,10 @@ EXPORTS = [
     "dsa_paged_decode",
     "dsa_paged_kv_append",
     "dsa_paged_kv_block_means",
+    "dsa_paged_quantize_fp8",
+    "dsa_paged_decode_fp8",
+    "dsa_paged_kv_append_fp8",
+    "dsa_paged_kv_block_means_fp8",
     "dsa_status_str",
     "dsa_last_error",
 ]
@@ -156,6 +160,10 @@ def load() -> ctypes.CDLL:
         "dsa_paged_decode": ([S, P, P, P, P, I32, P, I32, P, P, P, P, P, P], ctypes.c_int),
         "dsa_paged_kv_append": ([S, P, P, P, I32, P, P, P, P, I32, P], ctypes.c_int),
         "dsa_paged_kv_block_means": ([S, P, P, I32, P, P, I32, P], ctypes.c_int),
+        "dsa_paged_quantize_fp8": ([S, P, P, I32, P, P, P, P, P], ctypes.c_int),
+        "dsa_paged_decode_fp8": ([S, P, P, P, P, P, P, I32, P, I32, P, P, P, P, P, P], ctypes.c_int),
+        "dsa_paged_kv_append_fp8": ([S, P, P, P, I32, P, P, P, P, P, P, I32, P], ctypes.c_int),
+        "dsa_paged_kv_block_means_fp8": ([S, P, P, P, I32, P, P, I32, P], ctypes.c_int),
         "dsa_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "dsa_last_error": ([], ctypes.c_char_p),
     }
@@ -418,6 +426,60 @@ def dsa_paged_kv_block_means(shape: Shape, k_pool, block_table, lengths, kbar_po
     n_pages, mb = _paged_dims(shape, k_pool, block_table)
     _check(load().dsa_paged_kv_block_means(
         ctypes.byref(shape), _ptr(k_pool, torch.bfloat16, (n_pages, Hkv, b, d), "k_pool"),
+        _ptr(block_table, torch.int32, (S, mb), "block_table"), mb, _ptr(lengths, torch.int32, (S,), "lengths"),
+        _ptr(kbar_pool, torch.float32, (n_pages, Hkv, d), "kbar_pool"), n_pages, _stream(stream)))
+
+
+def _fp8_pools(shape: Shape, k8, v8, k_scale, v_scale):
+    n_pages = int(k8.shape[0])
+    Hkv, d, b = shape.n_kv_heads, shape.head_dim, shape.block
+    return n_pages, [_ptr(k8, torch.uint8, (n_pages, Hkv, b, d), "k8"), _ptr(v8, torch.uint8, (n_pages, Hkv, b, d), "v8"),
+                     _ptr(k_scale, torch.float32, (n_pages, Hkv, b), "k_scale"),
+                     _ptr(v_scale, torch.float32, (n_pages, Hkv, b), "v_scale")]
+
+
+def dsa_paged_quantize_fp8(shape: Shape, k_pool, v_pool, k8, v8, k_scale, v_scale, stream=None):
+    Hkv, d, b = shape.n_kv_heads, shape.head_dim, shape.block
+    n_pages, ptrs = _fp8_pools(shape, k8, v8, k_scale, v_scale)
+    _check(load().dsa_paged_quantize_fp8(
+        ctypes.byref(shape), _ptr(k_pool, torch.bfloat16, (n_pages, Hkv, b, d), "k_pool"),
+        _ptr(v_pool, torch.bfloat16, (n_pages, Hkv, b, d), "v_pool"), n_pages, *ptrs, _stream(stream)))
+
+
+def dsa_paged_decode_fp8(shape: Shape, q, k8, v8, k_scale, v_scale, kbar_pool, block_table, lengths, o, lse, idx,
+                         cnt=None, stream=None):
+    S, Hq, Hkv, d = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    n_pages, ptrs = _fp8_pools(shape, k8, v8, k_scale, v_scale)
+    mb = int(block_table.shape[1])
+    km = dsa_decode_kmax(shape)
+    _check(load().dsa_paged_decode_fp8(
+        ctypes.byref(shape), _ptr(q, torch.bfloat16, (S, Hq, d), "q"), *ptrs,
+        _ptr(kbar_pool, torch.float32, (n_pages, Hkv, d), "kbar_pool"), n_pages,
+        _ptr(block_table, torch.int32, (S, mb), "block_table"), mb, _ptr(lengths, torch.int32, (S,), "lengths"),
+        _ptr(o, torch.bfloat16, (S, Hq, d), "o"), _ptr(lse, torch.float32, (S, Hq), "lse", optional=True),
+        _ptr(idx, torch.int32, (S, Hkv, km), "idx"), _ptr(cnt, torch.int32, (S, Hkv), "cnt", optional=True),
+        _stream(stream)))
+
+
+def dsa_paged_kv_append_fp8(shape: Shape, k_new, v_new, block_table, lengths, k8, v8, k_scale, v_scale, kbar_pool,
+                            stream=None):
+    S, Hkv, d = shape.batch, shape.n_kv_heads, shape.head_dim
+    n_pages, ptrs = _fp8_pools(shape, k8, v8, k_scale, v_scale)
+    mb = int(block_table.shape[1])
+    _check(load().dsa_paged_kv_append_fp8(
+        ctypes.byref(shape), _ptr(k_new, torch.bfloat16, (S, Hkv, d), "k_new"),
+        _ptr(v_new, torch.bfloat16, (S, Hkv, d), "v_new"), _ptr(block_table, torch.int32, (S, mb), "block_table"), mb,
+        _ptr(lengths, torch.int32, (S,), "lengths"), *ptrs,
+        _ptr(kbar_pool, torch.float32, (n_pages, Hkv, d), "kbar_pool"), n_pages, _stream(stream)))
+
+
+def dsa_paged_kv_block_means_fp8(shape: Shape, k8, k_scale, block_table, lengths, kbar_pool, stream=None):
+    S, Hkv, d, b = shape.batch, shape.n_kv_heads, shape.head_dim, shape.block
+    n_pages = int(k8.shape[0])
+    mb = int(block_table.shape[1])
+    _check(load().dsa_paged_kv_block_means_fp8(
+        ctypes.byref(shape), _ptr(k8, torch.uint8, (n_pages, Hkv, b, d), "k8"),
+        _ptr(k_scale, torch.float32, (n_pages, Hkv, b), "k_scale"),
         _ptr(block_table, torch.int32, (S, mb), "block_table"), mb, _ptr(lengths, torch.int32, (S,), "lengths"),
         _ptr(kbar_pool, torch.float32, (n_pages, Hkv, d), "kbar_pool"), n_pages, _stream(stream)))
 

@@ -269,7 +269,7 @@ int dsa_paged_decode(const dsa_shape* s, const void* q, const void* k_pool, cons
   if (s->batch == 0) return DSA_OK;
   if (!q || !k_pool || !v_pool || !kbar_pool || !block_table || !lengths || !o || !idx)
     return fail(DSA_ERR_NULL, "q, k_pool, v_pool, kbar_pool, block_table, lengths, o or idx is NULL");
-  dsa::PagedArgs a;
+  dsa::PagedArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.kp = static_cast<const uint16_t*>(k_pool);
   a.vp = static_cast<const uint16_t*>(v_pool);
@@ -290,6 +290,90 @@ int dsa_paged_decode(const dsa_shape* s, const void* q, const void* k_pool, cons
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
   hipError_t e = dsa::launch_paged_decode(a, s->head_dim, s->block, topk_params(s), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "paged decode launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_paged_decode_fp8(const dsa_shape* s, const void* q, const uint8_t* k8, const uint8_t* v8, const float* k_scale,
+                         const float* v_scale, const float* kbar_pool, int32_t n_pages, const int32_t* block_table,
+                         int32_t max_blocks, const int32_t* lengths, void* o, float* lse, int32_t* idx, int32_t* cnt,
+                         void* stream) {
+  int rc = check_paged(s, n_pages, max_blocks);
+  if (rc) return rc;
+  if (s->batch == 0) return DSA_OK;
+  if (!q || !k8 || !v8 || !k_scale || !v_scale || !kbar_pool || !block_table || !lengths || !o || !idx)
+    return fail(DSA_ERR_NULL, "q, k8, v8, k_scale, v_scale, kbar_pool, block_table, lengths, o or idx is NULL");
+  dsa::PagedArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k8 = k8;
+  a.v8 = v8;
+  a.ksc = k_scale;
+  a.vsc = v_scale;
+  a.kbar = kbar_pool;
+  a.table = block_table;
+  a.lengths = lengths;
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.S = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.max_blocks = max_blocks;
+  a.n_pages = n_pages;
+  a.kmax = row_budget(s, (int)n_blocks(s));
+  a.scale = (float)(1.0 / sqrt((double)s->head_dim));
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
+  hipError_t e = dsa::launch_paged_decode(a, s->head_dim, s->block, topk_params(s), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 paged decode launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_paged_quantize_fp8(const dsa_shape* s, const void* k_pool, const void* v_pool, int32_t n_pages, uint8_t* k8,
+                           uint8_t* v8, float* k_scale, float* v_scale, void* stream) {
+  int rc = check_decode(s);
+  if (rc) return rc;
+  if (n_pages < 1) return fail(DSA_ERR_SHAPE, "n_pages %d < 1", n_pages);
+  if (!k_pool || !v_pool || !k8 || !v8 || !k_scale || !v_scale)
+    return fail(DSA_ERR_NULL, "k_pool, v_pool, k8, v8, k_scale or v_scale is NULL");
+  hipError_t e = dsa::launch_paged_quantize(static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool),
+                                            k8, v8, k_scale, v_scale, n_pages, s->n_kv_heads, s->head_dim, s->block,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_paged_kv_append_fp8(const dsa_shape* s, const void* k_new, const void* v_new, const int32_t* block_table,
+                            int32_t max_blocks, int32_t* lengths, uint8_t* k8, uint8_t* v8, float* k_scale,
+                            float* v_scale, float* kbar_pool, int32_t n_pages, void* stream) {
+  int rc = check_paged(s, n_pages, max_blocks);
+  if (rc) return rc;
+  if (s->batch == 0) return DSA_OK;
+  if (!k_new || !v_new || !block_table || !lengths || !k8 || !v8 || !k_scale || !v_scale || !kbar_pool)
+    return fail(DSA_ERR_NULL, "k_new, v_new, block_table, lengths, k8, v8, k_scale, v_scale or kbar_pool is NULL");
+  hipError_t e = dsa::launch_kv_append_fp8(static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                                           block_table, lengths, k8, v8, k_scale, v_scale, kbar_pool, s->batch,
+                                           s->n_kv_heads, s->head_dim, s->block, max_blocks, n_pages,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 kv append launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_paged_kv_block_means_fp8(const dsa_shape* s, const uint8_t* k8, const float* k_scale, const int32_t* block_table,
+                                 int32_t max_blocks, const int32_t* lengths, float* kbar_pool, int32_t n_pages,
+                                 void* stream) {
+  int rc = check_paged(s, n_pages, max_blocks);
+  if (rc) return rc;
+  if (s->batch == 0) return DSA_OK;
+  if (!k8 || !k_scale || !block_table || !lengths || !kbar_pool)
+    return fail(DSA_ERR_NULL, "k8, k_scale, block_table, lengths or kbar_pool is NULL");
+  hipError_t e = dsa::launch_paged_means_fp8(k8, k_scale, block_table, lengths, kbar_pool, s->batch, s->n_kv_heads,
+                                             s->head_dim, s->block, max_blocks, n_pages,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 paged block means launch");
   g_err[0] = 0;
   return DSA_OK;
 }

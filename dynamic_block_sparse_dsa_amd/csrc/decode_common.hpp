@@ -34,6 +34,37 @@ struct ChunkRegs {
   using C = DecCfg<D, G>;
   u32x4 kf[C::SUB][D / 32];
   u32x4 vv[C::VPL];
+  __device__ __forceinline__ u32x4 kfrag(int sb, int ks) const { return kf[sb][ks]; }
+  __device__ __forceinline__ u32x4 vrow(int v) const { return vv[v]; }
+  __device__ __forceinline__ float kscale(int, int) const { return 1.f; }
+  __device__ __forceinline__ float vscale(int, int) const { return 1.f; }
+};
+
+// 8 E4M3 codes (OCP) -> 8 bf16, exactly (every E4M3 value is a bf16 value)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 w) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    r[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, false));
+    r[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, true));
+  }
+  return r;
+}
+
+// The same chunk from an FP8 cache: the codes (half the bytes of bf16) and
+// the fp32 row scales of the keys this lane's scores cover (keys sb * 16 +
+// 4 (lane / 16) + j).  Codes become bf16 MFMA operands as they are used; the
+// K scale multiplies the key's logit and the V scale its softmax weight.
+template <int D, int G>
+struct ChunkRegs8 {
+  using C = DecCfg<D, G>;
+  u32x2 kf[C::SUB][D / 32];
+  u32x2 vv[C::VPL];
+  f32x4 ks[C::SUB], vs[C::SUB];
+  __device__ __forceinline__ u32x4 kfrag(int sb, int k) const { return fp8x8_to_bf16x8(kf[sb][k]); }
+  __device__ __forceinline__ u32x4 vrow(int v) const { return fp8x8_to_bf16x8(vv[v]); }
+  __device__ __forceinline__ float kscale(int sb, int j) const { return ks[sb][j]; }
+  __device__ __forceinline__ float vscale(int sb, int j) const { return vs[sb][j]; }
 };
 
 // One wave's online-softmax state for the G query heads of a unit, and the
@@ -92,8 +123,39 @@ struct WaveAttn {
   }
 
   // fold the chunk into the state; pbuf / abuf are this wave's LDS rows
-  __device__ __forceinline__ void step(const ChunkRegs<D, G>& r, int key0, int L, float scale_log2,
-                                       float (*pbuf)[G], float* abuf) {
+  // the FP8 chunk: codes and the row scales of this lane's keys (ksb, vsb
+  // are the tile's BLK scales); scales of keys past L are 0
+  __device__ __forceinline__ void load8(ChunkRegs8<D, G>& r, const uint8_t* kb, const uint8_t* vb, const float* ksb,
+                                        const float* vsb, int key0, int L) const {
+#pragma unroll
+    for (int sb = 0; sb < C::SUB; ++sb) {
+      const int key = min(key0 + sb * 16 + (lane & 15), L - 1);
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        r.kf[sb][ks] =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kb + (int64_t)key * D + ks * 32 + 8 * lq));
+    }
+#pragma unroll
+    for (int v = 0; v < C::VPL; ++v) {
+      const int key = min(key0 + pk + C::KGR * v, L - 1);
+      r.vv[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vb + (int64_t)key * D + pc * 8));
+    }
+#pragma unroll
+    for (int sb = 0; sb < C::SUB; ++sb) {
+      const int k0 = key0 + sb * 16 + 4 * lq;  // 4 consecutive keys, 16-byte aligned in the tile
+      const f32x4 kv = *reinterpret_cast<const f32x4*>(ksb + k0);
+      const f32x4 vv = *reinterpret_cast<const f32x4*>(vsb + k0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        r.ks[sb][j] = k0 + j < L ? kv[j] : 0.f;
+        r.vs[sb][j] = k0 + j < L ? vv[j] : 0.f;
+      }
+    }
+  }
+
+  template <class Regs>
+  __device__ __forceinline__ void step(const Regs& r, int key0, int L, float scale_log2, float (*pbuf)[G],
+                                       float* abuf) {
     const float NEG_INF = -__builtin_inff();
     f32x4 sc[C::SUB];
 #pragma unroll
@@ -101,7 +163,7 @@ struct WaveAttn {
       sc[sb] = (f32x4){0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
-        sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.kf[sb][ks]), as_bf16x8(qf[ks]), sc[sb], 0, 0, 0);
+        sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.kfrag(sb, ks)), as_bf16x8(qf[ks]), sc[sb], 0, 0, 0);
     }
     // output: lane holds head column n, keys sb * 16 + 4 * lq + j (keys past L masked)
     float mloc = NEG_INF;
@@ -110,7 +172,7 @@ struct WaveAttn {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int key = key0 + sb * 16 + 4 * lq + j;
-        const float x = (key < L) ? sc[sb][j] * scale_log2 : NEG_INF;
+        const float x = (key < L) ? sc[sb][j] * r.kscale(sb, j) * scale_log2 : NEG_INF;
         sc[sb][j] = x;
         mloc = fmaxf(mloc, x);
       }
@@ -126,7 +188,7 @@ struct WaveAttn {
       for (int j = 0; j < 4; ++j) {
         const float pv = __builtin_amdgcn_exp2f(sc[sb][j] - m_run);
         lsum += pv;
-        if (n < G) pbuf[sb * 16 + 4 * lq + j][n] = pv;
+        if (n < G) pbuf[sb * 16 + 4 * lq + j][n] = pv * r.vscale(sb, j);  // V scale folded into the weight
       }
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
@@ -145,11 +207,12 @@ struct WaveAttn {
 #pragma unroll
     for (int v = 0; v < C::VPL; ++v) {
       const int kk = pk + C::KGR * v;
+      const u32x4 vr = r.vrow(v);
       float vf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vf[2 * e] = bf16_lo(r.vv[v][e]);
-        vf[2 * e + 1] = bf16_hi(r.vv[v][e]);
+        vf[2 * e] = bf16_lo(vr[e]);
+        vf[2 * e + 1] = bf16_hi(vr[e]);
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {

@@ -26,12 +26,14 @@
 //   that page's key mean over its rows 0 .. L % BLK, then advances the length.
 // paged_means_kernel: one wave per (sequence, logical block, KV head): the
 //   mean of the page's rows below the sequence's length.
+#include <type_traits>
+
 #include "decode_common.hpp"
 #include "topk_row.hpp"
 
 namespace dsa {
 
-template <int D, int BLK, int G, int R>
+template <int D, int BLK, int G, int R, bool F8>
 __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkParams p) {
   using C = DecCfg<D, G>;
   constexpr int NT = 512, NW = 8;
@@ -142,26 +144,30 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
   // ---- attention over the kept blocks' chunks
   WaveAttn<D, G> wa;
   wa.init(a.q, a.Hq, s, g);
-  ChunkRegs<D, G> rA, rB;
+  using Regs = typename std::conditional<F8, ChunkRegs8<D, G>, ChunkRegs<D, G>>::type;
+  Regs rA, rB;
   const int nch = ns * CPB;
   struct Ref {
-    const uint16_t* kb;
-    const uint16_t* vb;
+    int64_t tile;   // (page, head) tile: element offset into the pools
     int key0, lim;  // key0 < 0: nothing
   };
   auto ref_of = [&](int i) {
-    Ref r{nullptr, nullptr, -1, 0};
+    Ref r{0, -1, 0};
     if (i >= nch) return r;
     const int blk = sel[i / CPB];
     const int key0 = (i % CPB) * C::CK;
     const int lim = min(BLK, L - blk * BLK);
     if (key0 >= lim) return r;
-    const int64_t tile = ((int64_t)page_of(blk) * a.Hkv + g) * BLK * D;
-    r.kb = a.kp + tile;
-    r.vb = a.vp + tile;
+    r.tile = ((int64_t)page_of(blk) * a.Hkv + g) * BLK;
     r.key0 = key0;
     r.lim = lim;
     return r;
+  };
+  auto load = [&](Regs& rr, const Ref& f) {
+    if constexpr (F8)
+      wa.load8(rr, a.k8 + f.tile * D, a.v8 + f.tile * D, a.ksc + f.tile, a.vsc + f.tile, f.key0, f.lim);
+    else
+      wa.load(rr, a.kp + f.tile * D, a.vp + f.tile * D, f.key0, f.lim);
   };
   auto grab = [&]() {
     int v = 0;
@@ -170,16 +176,16 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
   };
   int iA = wave;
   Ref fA = ref_of(iA);
-  if (fA.key0 >= 0) wa.load(rA, fA.kb, fA.vb, fA.key0, fA.lim);
+  if (fA.key0 >= 0) load(rA, fA);
   int iB = grab();
   while (iA < nch) {
     const Ref fB = ref_of(iB);
-    if (fB.key0 >= 0) wa.load(rB, fB.kb, fB.vb, fB.key0, fB.lim);
+    if (fB.key0 >= 0) load(rB, fB);
     if (fA.key0 >= 0) wa.step(rA, fA.key0, fA.lim, a.scale_log2, pbuf[wave], abuf[wave]);
     if (iB >= nch) break;
     iA = grab();
     fA = ref_of(iA);
-    if (fA.key0 >= 0) wa.load(rA, fA.kb, fA.vb, fA.key0, fA.lim);
+    if (fA.key0 >= 0) load(rA, fA);
     if (fB.key0 >= 0) wa.step(rB, fB.key0, fB.lim, a.scale_log2, pbuf[wave], abuf[wave]);
     iB = grab();
   }
@@ -268,12 +274,156 @@ __global__ __launch_bounds__(256) void paged_means_kernel(const uint16_t* __rest
   for (int e = 0; e < DPL; ++e) kbar[((int64_t)page * Hkv + g) * D + lane * DPL + e] = acc[e] / (float)rows;
 }
 
-// ============================================================== launch
+// ============================================================== FP8 cache rows
+// One row (D values, D/64 per lane) -> E4M3 codes with scale = amax / 448
+// (1 for an all-zero row): codes = round-to-nearest-even of fp32(x / scale),
+// by the hardware conversion.  Returns the scale; writes the lane's codes.
+template <int D>
+__device__ __forceinline__ float quantize_row(const float (&x)[D / 64], uint8_t* out) {
+  constexpr int DPL = D / 64;
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = wave_max_f32(amax);
+  const float scale = amax > 0.f ? amax / 448.f : 1.f;
+  typedef short s2 __attribute__((ext_vector_type(2)));
+  const s2 c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((s2){0, 0}, x[0] / scale, DPL == 2 ? x[DPL - 1] / scale : 0.f,
+                                                        1.0f, false);
+  const uint32_t w = __builtin_bit_cast(uint32_t, c);
+  if constexpr (DPL == 2) *reinterpret_cast<uint16_t*>(out) = (uint16_t)(w & 0xffffu);
+  else *out = (uint8_t)(w & 0xffu);
+  return scale;
+}
+
+// the lane's D/64 dequantized values (code * scale) of a row
+template <int D>
+__device__ __forceinline__ void dequant_row(const uint8_t* codes, float scale, float (&v)[D / 64]) {
+  constexpr int DPL = D / 64;
+  const int w = DPL == 2 ? (int)*reinterpret_cast<const uint16_t*>(codes) : (int)*codes;
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) v[e] = b[e] * scale;
+}
+
+// every slot of every (page, head) tile: one wave per (page, head)
 template <int D, int BLK>
+__global__ __launch_bounds__(256) void paged_quantize_kernel(const uint16_t* __restrict__ kp,
+                                                             const uint16_t* __restrict__ vp, uint8_t* __restrict__ k8,
+                                                             uint8_t* __restrict__ v8, float* __restrict__ ksc,
+                                                             float* __restrict__ vsc, int64_t n_tiles) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= n_tiles) return;  // whole wave
+  for (int r = 0; r < BLK; ++r) {
+    const int64_t row = t * BLK + r;
+    float x[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) x[e] = __uint_as_float((uint32_t)kp[row * D + lane * DPL + e] << 16);
+    float sk = quantize_row<D>(x, k8 + row * D + lane * DPL);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) x[e] = __uint_as_float((uint32_t)vp[row * D + lane * DPL + e] << 16);
+    float sv = quantize_row<D>(x, v8 + row * D + lane * DPL);
+    if (lane == 0) {
+      ksc[row] = sk;
+      vsc[row] = sv;
+    }
+  }
+}
+
+// append to an FP8 cache: one workgroup per sequence, one wave per KV head
+// (4 waves, heads strided); the page mean is recomputed from the dequantized
+// rows in row order, as paged_means_fp8_kernel does
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(const uint16_t* __restrict__ k_new,
+                                                            const uint16_t* __restrict__ v_new,
+                                                            const int32_t* __restrict__ table, int32_t* lengths,
+                                                            uint8_t* __restrict__ k8, uint8_t* __restrict__ v8,
+                                                            float* __restrict__ ksc, float* __restrict__ vsc,
+                                                            float* __restrict__ kbar, int Hkv, int max_blocks,
+                                                            int n_pages) {
+  constexpr int DPL = D / 64;
+  const int64_t s = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pos = lengths[s];
+  __syncthreads();  // every thread has read the length before it moves
+  if (pos < 0 || pos >= max_blocks * BLK) return;
+  const int page = table[s * (int64_t)max_blocks + pos / BLK];
+  if (page < 0 || page >= n_pages) return;
+  const int slot = pos % BLK;
+  for (int g = wave; g < Hkv; g += 4) {
+    const int64_t tile = ((int64_t)page * Hkv + g) * BLK;  // row index of slot 0
+    float x[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) x[e] = __uint_as_float((uint32_t)k_new[(s * Hkv + g) * D + lane * DPL + e] << 16);
+    const float sk = quantize_row<D>(x, k8 + (tile + slot) * D + lane * DPL);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) x[e] = __uint_as_float((uint32_t)v_new[(s * Hkv + g) * D + lane * DPL + e] << 16);
+    const float sv = quantize_row<D>(x, v8 + (tile + slot) * D + lane * DPL);
+    if (lane == 0) {
+      ksc[tile + slot] = sk;
+      vsc[tile + slot] = sv;
+    }
+    // mean of rows 0 .. slot (the new row's codes are re-read by the lane that wrote them)
+    float acc[DPL] = {};
+    for (int r = 0; r < slot; ++r) {
+      float v[DPL];
+      dequant_row<D>(k8 + (tile + r) * D + lane * DPL, ksc[tile + r], v);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += v[e];
+    }
+    {
+      float v[DPL];
+      dequant_row<D>(k8 + (tile + slot) * D + lane * DPL, sk, v);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) kbar[((int64_t)page * Hkv + g) * D + lane * DPL + e] = acc[e] / (float)(slot + 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) lengths[s] = pos + 1;
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void paged_means_fp8_kernel(const uint8_t* __restrict__ k8,
+                                                              const float* __restrict__ ksc,
+                                                              const int32_t* __restrict__ table,
+                                                              const int32_t* __restrict__ lengths,
+                                                              float* __restrict__ kbar, int S, int Hkv, int max_blocks,
+                                                              int n_pages) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w >= (int64_t)S * max_blocks * Hkv) return;
+  const int g = (int)(w % Hkv);
+  const int64_t sj = w / Hkv;
+  const int j = (int)(sj % max_blocks);
+  const int64_t s = sj / max_blocks;
+  const int L = min(max(lengths[s], 0), max_blocks * BLK);
+  if (j * BLK >= L) return;
+  const int page = table[s * (int64_t)max_blocks + j];
+  if (page < 0 || page >= n_pages) return;
+  const int rows = min(BLK, L - j * BLK);
+  const int64_t tile = ((int64_t)page * Hkv + g) * BLK;
+  float acc[DPL] = {};
+  for (int r = 0; r < rows; ++r) {
+    float v[DPL];
+    dequant_row<D>(k8 + (tile + r) * D + lane * DPL, ksc[tile + r], v);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] += v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) kbar[((int64_t)page * Hkv + g) * D + lane * DPL + e] = acc[e] / (float)rows;
+}
+
+// ============================================================== launch
+template <int D, int BLK, bool F8>
 static hipError_t launch_paged_d(const PagedArgs& a, TopkParams p, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const dim3 grid((uint32_t)((int64_t)a.S * a.Hkv)), blk(512);
-#define DSA_PAGED(GG, RR) hipLaunchKernelGGL((decode_paged_kernel<D, BLK, GG, RR>), grid, blk, 0, stream, a, p)
+#define DSA_PAGED(GG, RR) hipLaunchKernelGGL((decode_paged_kernel<D, BLK, GG, RR, F8>), grid, blk, 0, stream, a, p)
 #define DSA_PAGED_G(RR)                 \
   switch (G) {                          \
     case 1: DSA_PAGED(1, RR); break;    \
@@ -292,10 +442,16 @@ static hipError_t launch_paged_d(const PagedArgs& a, TopkParams p, hipStream_t s
   return hipGetLastError();
 }
 
+template <bool F8>
+static hipError_t launch_paged_f(const PagedArgs& a, int d, int block, TopkParams p, hipStream_t stream) {
+  if (d == 64)
+    return block == 64 ? launch_paged_d<64, 64, F8>(a, p, stream) : launch_paged_d<64, 128, F8>(a, p, stream);
+  return block == 64 ? launch_paged_d<128, 64, F8>(a, p, stream) : launch_paged_d<128, 128, F8>(a, p, stream);
+}
+
 hipError_t launch_paged_decode(const PagedArgs& a, int d, int block, TopkParams p, hipStream_t stream) {
   if ((int64_t)a.S * a.Hkv == 0) return hipSuccess;
-  if (d == 64) return block == 64 ? launch_paged_d<64, 64>(a, p, stream) : launch_paged_d<64, 128>(a, p, stream);
-  return block == 64 ? launch_paged_d<128, 64>(a, p, stream) : launch_paged_d<128, 128>(a, p, stream);
+  return a.k8 ? launch_paged_f<true>(a, d, block, p, stream) : launch_paged_f<false>(a, d, block, p, stream);
 }
 
 hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* table, int32_t* lengths,
@@ -337,5 +493,41 @@ hipError_t launch_paged_means(const uint16_t* kp, const int32_t* table, const in
                        max_blocks, n_pages);
   return hipGetLastError();
 }
+
+#define DSA_DB(F, ...)                                                  \
+  if (d == 64 && block == 64) hipLaunchKernelGGL((F<64, 64>), __VA_ARGS__); \
+  else if (d == 64) hipLaunchKernelGGL((F<64, 128>), __VA_ARGS__);          \
+  else if (block == 64) hipLaunchKernelGGL((F<128, 64>), __VA_ARGS__);      \
+  else hipLaunchKernelGGL((F<128, 128>), __VA_ARGS__)
+
+hipError_t launch_paged_quantize(const uint16_t* kp, const uint16_t* vp, uint8_t* k8, uint8_t* v8, float* ksc,
+                                 float* vsc, int n_pages, int Hkv, int d, int block, hipStream_t stream) {
+  const int64_t tiles = (int64_t)n_pages * Hkv;
+  if (tiles == 0) return hipSuccess;
+  const dim3 grid((uint32_t)((tiles + 3) / 4)), blk(256);
+  DSA_DB(paged_quantize_kernel, grid, blk, 0, stream, kp, vp, k8, v8, ksc, vsc, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_fp8(const uint16_t* k_new, const uint16_t* v_new, const int32_t* table, int32_t* lengths,
+                                uint8_t* k8, uint8_t* v8, float* ksc, float* vsc, float* kbar, int S, int Hkv, int d,
+                                int block, int max_blocks, int n_pages, hipStream_t stream) {
+  if (S == 0) return hipSuccess;
+  const dim3 grid((uint32_t)S), blk(256);
+  DSA_DB(kv_append_fp8_kernel, grid, blk, 0, stream, k_new, v_new, table, lengths, k8, v8, ksc, vsc, kbar, Hkv,
+         max_blocks, n_pages);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_means_fp8(const uint8_t* k8, const float* ksc, const int32_t* table, const int32_t* lengths,
+                                  float* kbar, int S, int Hkv, int d, int block, int max_blocks, int n_pages,
+                                  hipStream_t stream) {
+  const int64_t waves = (int64_t)S * max_blocks * Hkv;
+  if (waves == 0) return hipSuccess;
+  const dim3 grid((uint32_t)((waves + 3) / 4)), blk(256);
+  DSA_DB(paged_means_fp8_kernel, grid, blk, 0, stream, k8, ksc, table, lengths, kbar, S, Hkv, max_blocks, n_pages);
+  return hipGetLastError();
+}
+#undef DSA_DB
 
 }  // namespace dsa

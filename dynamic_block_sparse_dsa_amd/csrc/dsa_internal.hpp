@@ -157,6 +157,12 @@ struct PagedArgs {
   int32_t* cnt;             // [S, Hkv] or null
   int S, Hq, Hkv, max_blocks, n_pages, kmax;
   float scale, scale_log2;  // 1/sqrt(d), log2(e)/sqrt(d)
+  // FP8 pools (E4M3 codes [n_pages, Hkv, block, d]) and their row scales
+  // [n_pages, Hkv, block]; used instead of kp / vp when set
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* ksc;
+  const float* vsc;
 };
 hipError_t launch_paged_decode(const PagedArgs& a, int d, int block, TopkParams p, hipStream_t stream);
 hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* table, int32_t* lengths,
@@ -164,6 +170,15 @@ hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, const 
                             int n_pages, hipStream_t stream);
 hipError_t launch_paged_means(const uint16_t* kp, const int32_t* table, const int32_t* lengths, float* kbar, int S,
                               int Hkv, int d, int block, int max_blocks, int n_pages, hipStream_t stream);
+// FP8 pools: quantize bf16 pools (every slot), append, page means
+hipError_t launch_paged_quantize(const uint16_t* kp, const uint16_t* vp, uint8_t* k8, uint8_t* v8, float* ksc,
+                                 float* vsc, int n_pages, int Hkv, int d, int block, hipStream_t stream);
+hipError_t launch_kv_append_fp8(const uint16_t* k_new, const uint16_t* v_new, const int32_t* table, int32_t* lengths,
+                                uint8_t* k8, uint8_t* v8, float* ksc, float* vsc, float* kbar, int S, int Hkv, int d,
+                                int block, int max_blocks, int n_pages, hipStream_t stream);
+hipError_t launch_paged_means_fp8(const uint8_t* k8, const float* ksc, const int32_t* table, const int32_t* lengths,
+                                  float* kbar, int S, int Hkv, int d, int block, int max_blocks, int n_pages,
+                                  hipStream_t stream);
 
 struct DecodeArgs {
   const uint16_t* q;   // [S, Hq, d]

@@ -253,6 +253,40 @@ int dsa_paged_kv_block_means(const dsa_shape* shape, const void* k_pool, const i
                              int32_t max_blocks, const int32_t* lengths, float* kbar_pool, int32_t n_pages,
                              void* stream);
 
+/* ---- FP8 paged cache ("dynamic sparse attention explainer", "工程实践建议":
+ * combine the sparsity with an FP8/INT4 KV cache to cut bandwidth).  The
+ * pools hold E4M3 (OCP) codes k8, v8 [n_pages, Hkv, block, d] uint8 with one
+ * fp32 scale per (token, KV head) row, k_scale, v_scale [n_pages, Hkv,
+ * block]: scale = amax(|row|) / 448 (1 for an all-zero row) and code = the
+ * E4M3 value nearest to fp32(x / scale), ties to even; a row's value is
+ * code * scale.  The page means, the selection and the attention use those
+ * values (attention: bf16 MFMA on the codes, the K scale applied to each
+ * logit and the V scale to each softmax weight, fp32 accumulation).  Same
+ * layouts and rules as the bf16 paged calls otherwise. */
+
+/* Quantize whole bf16 pools (every slot of every page) into an FP8 cache. */
+int dsa_paged_quantize_fp8(const dsa_shape* shape, const void* k_pool, const void* v_pool, int32_t n_pages,
+                           uint8_t* k8, uint8_t* v8, float* k_scale, float* v_scale, void* stream);
+
+/* dsa_paged_decode over an FP8 cache. */
+int dsa_paged_decode_fp8(const dsa_shape* shape, const void* q, const uint8_t* k8, const uint8_t* v8,
+                         const float* k_scale, const float* v_scale, const float* kbar_pool, int32_t n_pages,
+                         const int32_t* block_table, int32_t max_blocks, const int32_t* lengths, void* o, float* lse,
+                         int32_t* idx, int32_t* cnt, void* stream);
+
+/* dsa_paged_kv_append into an FP8 cache: k_new, v_new [S, Hkv, d] bf16 are
+ * quantized row by row; the page mean is recomputed from the page's
+ * dequantized rows in row order (the same bits as
+ * dsa_paged_kv_block_means_fp8). */
+int dsa_paged_kv_append_fp8(const dsa_shape* shape, const void* k_new, const void* v_new, const int32_t* block_table,
+                            int32_t max_blocks, int32_t* lengths, uint8_t* k8, uint8_t* v8, float* k_scale,
+                            float* v_scale, float* kbar_pool, int32_t n_pages, void* stream);
+
+/* dsa_paged_kv_block_means over an FP8 cache (means of the dequantized rows). */
+int dsa_paged_kv_block_means_fp8(const dsa_shape* shape, const uint8_t* k8, const float* k_scale,
+                                 const int32_t* block_table, int32_t max_blocks, const int32_t* lengths,
+                                 float* kbar_pool, int32_t n_pages, void* stream);
+
 /* ---- Token-level lightning indexer ("低成本高性能大模型实现路径：从架构创新
  * 到工程优化", yunthe.com/news/806485.html, section 2.1 "轻量化索引器设计":
  * ReLU feature heads, 16 index heads, every query token keeps its top 64

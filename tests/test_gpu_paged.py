@@ -65,7 +65,8 @@ def paged_case(dev, w, lengths, flags=3, n_anchor=0, window=0, units=None, seed=
 
 def check_against_oracle(name, w, q, kp, vp, kbar, table, lens, o, lse, idx, cnt, flags, spec, units):
     tb, ln = table.cpu().numpy(), lens.cpu().numpy()
-    kp64, vp64 = np64(kp), np64(vp)
+    as64 = lambda t: t.numpy() if t.dtype == torch.float64 else np64(t)
+    kp64, vp64 = as64(kp), as64(vp)
     # page means of the used pages
     ref_kb = O.paged_block_means(kp64, tb, ln, w.block, kp.shape[0])
     used = sorted({int(tb[s, j]) for s in range(w.batch) for j in range(-(-int(ln[s]) // w.block))})
@@ -208,3 +209,99 @@ def test_paged_decode_full_size_sampled(cuda_device):
             check_out(np64(o[s, g * G + hh])[None], ((wts / wts.sum()) @ vseq[keys])[None],
                       np.array([float(lse[s, g * G + hh])]), np.array([logits.max() + math.log(wts.sum())]),
                       f"paged full s{s} g{g} h{hh}")
+
+
+# ------------------------------------------------------------------ FP8 cache
+def quantize_pools(kp, vp, shape):
+    n_pages, Hkv, b, d = kp.shape
+    k8 = torch.empty((n_pages, Hkv, b, d), dtype=torch.uint8, device=kp.device)
+    v8 = torch.empty_like(k8)
+    ks = torch.empty((n_pages, Hkv, b), dtype=torch.float32, device=kp.device)
+    vs = torch.empty_like(ks)
+    dsa.dsa_paged_quantize_fp8(shape, kp, vp, k8, v8, ks, vs)
+    return k8, v8, ks, vs
+
+
+def test_fp8_quantization_is_bit_exact(cuda_device):
+    g = torch.Generator(device=cuda_device)
+    g.manual_seed(81)
+    for d, b in ((128, 64), (64, 128)):
+        kp = (torch.randn((5, 2, b, d), generator=g, device=cuda_device) * 3).to(torch.bfloat16)
+        vp = (torch.randn((5, 2, b, d), generator=g, device=cuda_device) * 1e-3).to(torch.bfloat16)
+        kp[1, 0, 3] = 0  # an all-zero row
+        kp[2, 1, 7] *= 1e4
+        shape = dsa.paged_shape(kp, torch.zeros((1, 4), dtype=torch.int32), 2)
+        k8, v8, ks, vs = quantize_pools(kp, vp, shape)
+        torch.cuda.synchronize()
+        for pool, codes, scales in ((kp, k8, ks), (vp, v8, vs)):
+            rc, rs = O.quantize_fp8(np64(pool))
+            np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+            np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+FP8_CASES = [CASES[0], CASES[1]]
+
+
+@pytest.mark.parametrize("name,w,lengths,flags,n_anchor,window", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_fp8_paged_decode_small(cuda_device, name, w, lengths, flags, n_anchor, window):
+    say(f"fp8 paged {name}: lengths {lengths}")
+    q, kc, vc = make_decode(w, device=cuda_device)
+    kp, vp, table, lens = to_paged(kc, vc, lengths, w.block, 5)
+    shape = dsa.paged_shape(kp, table, w.n_q_heads)
+    k8, v8, ks, vs = quantize_pools(kp, vp, shape)
+    kbar = torch.zeros((kp.shape[0], w.n_kv_heads, w.head_dim), dtype=torch.float32, device=cuda_device)
+    dsa.dsa_paged_kv_block_means_fp8(shape, k8, ks, table, lens, kbar)
+    dshape = dsa.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, shape.seq_len, w.head_dim, w.block, w.topk,
+                            w.topk_num, w.topk_den, flags, n_anchor=n_anchor, window=window)
+    km = dsa.dsa_decode_kmax(dshape)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.n_q_heads), dtype=torch.float32, device=cuda_device)
+    idx = torch.empty((w.batch, w.n_kv_heads, km), dtype=torch.int32, device=cuda_device)
+    cnt = torch.empty((w.batch, w.n_kv_heads), dtype=torch.int32, device=cuda_device)
+    dsa.dsa_paged_decode_fp8(dshape, q, k8, v8, ks, vs, kbar, table, lens, o, lse, idx, cnt)
+    torch.cuda.synchronize()
+    # the oracle sees the dequantized pools (as bf16-free float64 tensors)
+    kd = O.dequantize_fp8(k8.cpu().numpy(), ks.cpu().numpy())
+    vd = O.dequantize_fp8(v8.cpu().numpy(), vs.cpu().numpy())
+    spec = O.SelectSpec(anchors=max(1, n_anchor), window=max(1, window))
+    check_against_oracle(name + "_fp8", w, q, torch.from_numpy(kd), torch.from_numpy(vd), kbar, table, lens, o, lse,
+                         idx, cnt, flags, spec, None)
+
+
+def test_fp8_appends(cuda_device):
+    w = Workload("f8", "decode", 3, 4, 2, 64 * 4, 128, 64, 4, seed=82)
+    start = [0, 63, 256]
+    q, kc, vc = make_decode(w, device=cuda_device)
+    kp, vp, table, lens = to_paged(kc, vc, start, w.block, 6)
+    shape = dsa.paged_shape(kp, table, w.n_q_heads)
+    k8, v8, ks, vs = quantize_pools(kp, vp, shape)
+    kbar = torch.zeros((kp.shape[0], w.n_kv_heads, w.head_dim), dtype=torch.float32, device=cuda_device)
+    dsa.dsa_paged_kv_block_means_fp8(shape, k8, ks, table, lens, kbar)
+    o8, ov8, oks, ovs, okb = (x.cpu().numpy().copy() for x in (k8, v8, ks, vs, kbar))
+    okb = okb.astype(np.float64)
+    ln_o = lens.cpu().numpy().copy()
+    tb = table.cpu().numpy()
+    g = torch.Generator(device=cuda_device)
+    g.manual_seed(83)
+    for step in range(70):
+        kn = (torch.randn((w.batch, w.n_kv_heads, w.head_dim), generator=g, device=cuda_device) * 2).to(torch.bfloat16)
+        vn = torch.randn((w.batch, w.n_kv_heads, w.head_dim), generator=g, device=cuda_device).to(torch.bfloat16)
+        dsa.dsa_paged_kv_append_fp8(shape, kn, vn, table, lens, k8, v8, ks, vs, kbar)
+        for s in range(w.batch):
+            if ln_o[s] >= w.seq_len:
+                continue
+            one = np.array([ln_o[s]], dtype=np.int32)
+            O.kv_append_fp8(o8, ov8, oks, ovs, okb, tb[s : s + 1], one, np64(kn)[s : s + 1], np64(vn)[s : s + 1],
+                            w.block)
+            ln_o[s] = one[0]
+    torch.cuda.synchronize()
+    assert (lens.cpu().numpy() == ln_o).all()
+    np.testing.assert_array_equal(k8.cpu().numpy(), o8)
+    np.testing.assert_array_equal(v8.cpu().numpy(), ov8)
+    np.testing.assert_array_equal(ks.cpu().numpy(), oks)
+    np.testing.assert_array_equal(vs.cpu().numpy(), ovs)
+    np.testing.assert_allclose(np64(kbar), okb, rtol=1e-5, atol=1e-6)
+    kbar2 = kbar.clone()
+    dsa.dsa_paged_kv_block_means_fp8(shape, k8, ks, table, lens, kbar2)
+    torch.cuda.synchronize()
+    assert torch.equal(kbar2, kbar)
