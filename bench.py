@@ -221,6 +221,33 @@ def bench_paged(args, dev, stream):
                          roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                                        frac=round(gbs / PEAK_HBM_GBS, 4), bytes_per_step=nbytes,
                                        kernel="decode_paged_kernel"))
+    # the same caches in FP8 (E4M3 codes, a scale per row), full length
+    k8 = torch.empty((n_pages, Hkv, b, d), dtype=torch.uint8, device=dev)
+    v8 = torch.empty_like(k8)
+    ks = torch.empty((n_pages, Hkv, b), dtype=torch.float32, device=dev)
+    vs = torch.empty_like(ks)
+    dsa.dsa_paged_quantize_fp8(shape, kp, vp, k8, v8, ks, vs, stream=stream)
+    lens = torch.full((S,), L, dtype=torch.int32, device=dev)
+    dsa.dsa_paged_kv_block_means_fp8(shape, k8, ks, table, lens, kbar, stream=stream)
+
+    def step8():
+        dsa.dsa_paged_decode_fp8(shape, q, k8, v8, ks, vs, kbar, table, lens, o, lse, idx, cnt, stream=stream)
+
+    for _ in range(args.warmup):
+        step8()
+    tot = 0.0
+    for _ in range(args.steps):
+        with torch.cuda.stream(stream):
+            flush.sum()
+        tot += time_events(step8, 1, stream)
+    ms = tot / args.steps
+    nbytes = work.paged_decode_bytes(lens.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(), Hq, d, b, kv_bytes=1,
+                                     row_scales=True)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["fp8_full_length"] = dict(value=S / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
+                                  roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                                                frac=round(gbs / PEAK_HBM_GBS, 4), bytes_per_step=nbytes,
+                                                kernel="decode_paged_kernel (fp8)"))
     # one append of a token per sequence (the mixed lengths leave room)
     kn = torch.randn((S, Hkv, d), device=dev).to(torch.bfloat16)
     vn = torch.randn((S, Hkv, d), device=dev).to(torch.bfloat16)
@@ -232,6 +259,14 @@ def bench_paged(args, dev, stream):
     for _ in range(args.warmup):
         app()
     out["append_us"] = round(time_events(app, args.steps, stream) * 1e3, 2)
+
+    def app8():
+        dsa.dsa_paged_kv_append_fp8(shape, kn, vn, table, lens, k8, v8, ks, vs, kbar, stream=stream)
+
+    lens = torch.tensor(cases[1][1], dtype=torch.int32, device=dev).clamp(max=L - 2 * (args.steps + args.warmup) - 1)
+    for _ in range(args.warmup):
+        app8()
+    out["append_fp8_us"] = round(time_events(app8, args.steps, stream) * 1e3, 2)
     out["config"] = dict(workload=w.name + "_paged", sequences=S, n_q_heads=Hq, n_kv_heads=Hkv, capacity=L, head_dim=d,
                          block=b, topk=w.topk, pages=n_pages)
     return out

@@ -55,10 +55,12 @@ def decode_flops(n_seq: int, hq: int, kept: int, block: int, d: int, n_blocks: i
     return n_seq * hq * (2 * d * n_blocks + 4 * d * kept * block)
 
 
-def paged_decode_bytes(lengths, idx, cnt, hq: int, d: int, block: int) -> int:
+def paged_decode_bytes(lengths, idx, cnt, hq: int, d: int, block: int, kv_bytes: int = 2, row_scales: bool = False) -> int:
     """Bytes one paged decode step must move with a length per sequence: per
     (sequence, KV head) the fp32 means of its ceil(L / block) pages and the
-    valid rows of its kept pages (K and V, bf16), plus q, o and the indices.
+    valid rows of its kept pages (K and V: kv_bytes per element, bf16 = 2,
+    E4M3 = 1, plus a 4-byte scale per K and V row with row_scales), plus q, o
+    and the indices.
     lengths [S]; idx [S, Hkv, kmax]; cnt [S, Hkv] (numpy)."""
     S, hkv = cnt.shape
     total = 0
@@ -67,6 +69,8 @@ def paged_decode_bytes(lengths, idx, cnt, hq: int, d: int, block: int) -> int:
         nb = -(-L // block)
         for g in range(hkv):
             rows = sum(min(block, L - int(j) * block) for j in idx[s, g, : cnt[s, g]])
-            total += nb * d * 4 + rows * d * 2 * 2 + int(cnt[s, g]) * 4
+            total += nb * d * 4 + rows * d * kv_bytes * 2 + int(cnt[s, g]) * 4
+            if row_scales:
+                total += rows * 4 * 2
     return total + S * hq * d * 2 * 2
 
