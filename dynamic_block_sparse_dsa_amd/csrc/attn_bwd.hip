@@ -31,15 +31,15 @@
 //      K, V as B), P and dS in registers (already in B-operand order), then
 //      dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transposed LDS
 //      reads.
-// All tiles in LDS use the row swizzle kswz; the transposed reads of a kswz
-// tile see at most 2-way bank conflicts.
+// Tiles in LDS are read row-wise, and Q, dO and K also transposed; all use
+// qswz, which keeps both kinds of read free of bank conflicts.
 #include "attn_common.hpp"
 
 namespace dsa {
 
 // ============================================================== tile loads
 // A ROWS x D bf16 tile (rows row0 .. row0 + ROWS - 1 of a [*, D] matrix,
-// rows clamped to n_rows - 1) into LDS with the kswz layout, by WAVES waves.
+// rows clamped to n_rows - 1) into LDS with the qswz layout, by WAVES waves.
 template <int D, int ROWS, int WAVES>
 __device__ __forceinline__ void load_tile(const uint16_t* g, int row0, int n_rows, uint32_t lds_base, int wave,
                                           int lane) {
@@ -51,14 +51,14 @@ __device__ __forceinline__ void load_tile(const uint16_t* g, int row0, int n_row
   for (int n = 0; n < LOADS / WAVES; ++n) {
     const int inst = wave + n * WAVES;
     const int r = inst * RPI + lane / CH;
-    const int c = (lane % CH) ^ kswz<D>(r);
+    const int c = (lane % CH) ^ qswz<D>(r);
     const int row = min(row0 + r, n_rows - 1);
     dma16(g, (uint32_t)(row * D + c * 8) * 2u, __builtin_amdgcn_readfirstlane(lds_base + inst * 1024));
   }
 }
 
 // 8 bf16 of the transposed operand: rows t0 + {0..3} and t0 + 8 + {0..3} of
-// a kswz tile at column block `d` (lane layout of ds_read_b64_tr_b16: within
+// a qswz tile at column block `d` (lane layout of ds_read_b64_tr_b16: within
 // 16 lanes, out lane i slot j receives element i % 4 of source lane 4j + i/4;
 // source lane s reads row base + s / 4, columns dbase + 4 (s % 4) .. + 3).
 template <int D>
@@ -68,7 +68,7 @@ __device__ __forceinline__ u32x4 read_tr(const LDS_AS uint16_t* tile, int row_ba
 #pragma unroll
   for (int sg = 0; sg < 2; ++sg) {
     const int row = row_base + 8 * sg;
-    const int c = cbase ^ kswz<D>(row);
+    const int c = cbase ^ qswz<D>(row);
     const LDS_AS char* addr = reinterpret_cast<const LDS_AS char*>(tile + row * D + c * 8) + sub;
     const i16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)addr);
     const u32x2 w = __builtin_bit_cast(u32x2, v4);
@@ -81,7 +81,7 @@ __device__ __forceinline__ u32x4 read_tr(const LDS_AS uint16_t* tile, int row_ba
 // row-major operand fragment: row r, k-step ks (dims 16 ks + 8 half .. + 7)
 template <int D>
 __device__ __forceinline__ u32x4 read_row(const LDS_AS uint16_t* tile, int r, int ks, int half) {
-  const int c = (2 * ks + half) ^ kswz<D>(r);
+  const int c = (2 * ks + half) ^ qswz<D>(r);
   return *reinterpret_cast<const LDS_AS u32x4*>(tile + r * D + c * 8);
 }
 

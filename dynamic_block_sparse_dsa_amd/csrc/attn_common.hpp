@@ -24,6 +24,15 @@ template <int D>
 __device__ __forceinline__ int vswz(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
+// qswz serves tiles read both ways (the backward's Q, dO and K tiles): with
+// 64 four-byte banks, 16 consecutive rows at one chunk land in 16 distinct
+// chunk slots (a bijection of the row's low bits), and 4 consecutive rows x
+// 4 aligned chunks (one transposed read of 32 lanes) do as well, since the
+// swizzle's upper two bits follow the row within its group of 4.
+template <int D>
+__device__ __forceinline__ int qswz(int r) {
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 // wait until at most n vector-memory operations of this wave are in flight
 template <int n>
