@@ -67,25 +67,18 @@ __device__ __forceinline__ void score_and_select(const DecodeArgs& a, const Topk
 
   float qv[G][8];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(a.q + (s * a.Hq + g * G + hh) * (int64_t)D + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qv[hh][2 * e] = bf16_lo(w[e]);
-      qv[hh][2 * e + 1] = bf16_hi(w[e]);
-    }
-  }
+  for (int hh = 0; hh < G; ++hh) load_q_halves<D>(a.q + (s * a.Hq + g * G + hh) * (int64_t)D, c, qv[hh]);
   // A wave scores batches of BR consecutive rows; after its first batch it
   // takes the next free one from an LDS counter, so waves that see shorter
   // memory latency do more of them.  The next batch is in flight while one is
   // scored; rows past the end are clamped (loaded again, never stored).
-  const float* kb = a.kbar + (int64_t)unit * nB * D + 8 * c;
+  const float* kb = a.kbar + (int64_t)unit * nB * D + 4 * c;
   auto load = [&](f32x4(&kv)[UNR][2], int b) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int row = min(b * BR + u * WROWS + rl, nB - 1);
       kv[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kb + (int64_t)row * D));
-      kv[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kb + (int64_t)row * D + 4));
+      kv[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kb + (int64_t)row * D + D / 2));
     }
   };
   auto score = [&](const f32x4(&kv)[UNR][2], int b) {

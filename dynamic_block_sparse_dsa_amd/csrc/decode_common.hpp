@@ -18,6 +18,23 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Block-mean scans: the TPR = D/8 lanes of a row group hold dims 4c .. 4c+3
+// and D/2 + 4c .. + 3 (c = lane % TPR), so each 16-byte-per-lane load covers
+// whole 256-byte stretches of a row (full cache lines).  qv[0..3] and
+// qv[4..7] are this lane's query values for those dims.
+template <int D>
+__device__ __forceinline__ void load_q_halves(const uint16_t* qrow, int c, float (&qv)[8]) {
+  const u32x2 w0 = *reinterpret_cast<const u32x2*>(qrow + 4 * c);
+  const u32x2 w1 = *reinterpret_cast<const u32x2*>(qrow + D / 2 + 4 * c);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    qv[2 * e] = bf16_lo(w0[e]);
+    qv[2 * e + 1] = bf16_hi(w0[e]);
+    qv[4 + 2 * e] = bf16_lo(w1[e]);
+    qv[4 + 2 * e + 1] = bf16_hi(w1[e]);
+  }
+}
+
 // Work unit of a wave: a 32-key chunk of a kept block.
 template <int D, int G>
 struct DecCfg {

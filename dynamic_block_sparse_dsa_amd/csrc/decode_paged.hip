@@ -75,21 +75,14 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
     __syncthreads();
     float qv[G][8];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(a.q + (s * a.Hq + g * G + hh) * (int64_t)D + 8 * c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[hh][2 * e] = bf16_lo(w[e]);
-        qv[hh][2 * e + 1] = bf16_hi(w[e]);
-      }
-    }
+    for (int hh = 0; hh < G; ++hh) load_q_halves<D>(a.q + (s * a.Hq + g * G + hh) * (int64_t)D, c, qv[hh]);
     auto load = [&](f32x4(&kv)[UNR][2], int b) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int row = min(b * BR + u * WROWS + rl, nB - 1);
-        const float* kr = a.kbar + ((int64_t)page_of(row) * a.Hkv + g) * D + 8 * c;
+        const float* kr = a.kbar + ((int64_t)page_of(row) * a.Hkv + g) * D + 4 * c;
         kv[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kr));
-        kv[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kr + 4));
+        kv[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kr + D / 2));
       }
     };
     auto score = [&](const f32x4(&kv)[UNR][2], int b) {
