@@ -18,8 +18,10 @@
 // loads (d/8 lanes per block row; waves take batches of rows from an LDS
 // counter and keep the next batch in flight; row dot products reduced with
 // DPP), scores each block by the max over the group's heads of
-// q_h . kbar_j / sqrt(d) into LDS, then one wave runs the top-k on the LDS
-// scores -- no score round trip.
+// q_h . kbar_j / sqrt(d) into LDS, then selects on the LDS scores -- no
+// score round trip: the whole workgroup runs a plain top-k (a digit-wise
+// histogram search for the threshold, block_select_topk), one wave the
+// threshold and entropy variants (wave_select_row).
 //
 // Attention over the kept blocks works in 32-key chunks (WaveAttn): a wave
 // issues all K and V loads of a chunk together, then Q K^T on
@@ -45,12 +47,14 @@ namespace dsa {
 // Score every block of one (sequence, KV head) unit into LDS and select its
 // kept blocks (written ascending to out, -1 padded to kmax; out may be
 // global or LDS).  All NT = 512 threads of the workgroup take part.  Scores:
-// block l * R + e at sc[e * 64 + l].  Returns after a workgroup barrier; the
-// selection itself is complete only after the next barrier.
-template <int D, int G, int R>
+// block l * R + e at sc[e * 64 + l].  pre_select() runs in every thread
+// once the scores are complete, before the selection (a caller's prefetch
+// stays in flight through it).  The selection is complete only after the
+// caller's next barrier.
+template <int D, int G, int R, typename Pre>
 __device__ __forceinline__ void score_and_select(const DecodeArgs& a, const TopkParams& p, int unit, float* sc,
-                                                 uint32_t* lds_key, int32_t* lds_idx, int* next_batch,
-                                                 int32_t* out) {
+                                                 uint32_t* lds_key, int32_t* lds_idx, uint32_t* bsel,
+                                                 int* next_batch, int32_t* out, Pre&& pre_select) {
   constexpr int NT = 512, NW = NT / 64;
   constexpr int TPR = D / 8;       // lanes per block row (8 floats each)
   constexpr int WROWS = 64 / TPR;  // rows per wave per pass
@@ -118,7 +122,9 @@ __device__ __forceinline__ void score_and_select(const DecodeArgs& a, const Topk
     b1 = grab();
   }
   __syncthreads();
-  if (t < 64) wave_select_row<R, true>(sc, nB, p, out, a.kmax, lds_key, lds_idx);  // one wave selects
+  pre_select();
+  if (p.mode == DSA_SELECT_TOPK) block_select_topk<R, NT>(sc, nB, p, out, a.kmax, bsel);  // the workgroup selects
+  else if (t < 64) wave_select_row<R, true>(sc, nB, p, out, a.kmax, lds_key, lds_idx);  // one wave selects
 }
 
 template <int D, int G, int R>
@@ -126,9 +132,10 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a, TopkPa
   __shared__ float sc[64 * R];
   __shared__ uint32_t lds_key[128];
   __shared__ int32_t lds_idx[128];
+  __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS];
   __shared__ int next_batch;
-  score_and_select<D, G, R>(a, p, blockIdx.x, sc, lds_key, lds_idx, &next_batch,
-                            a.idx + (int64_t)blockIdx.x * a.kmax);
+  score_and_select<D, G, R>(a, p, blockIdx.x, sc, lds_key, lds_idx, bsel, &next_batch,
+                            a.idx + (int64_t)blockIdx.x * a.kmax, [] {});
 }
 
 // ============================================================== 2. attention
@@ -248,6 +255,7 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkPar
   __shared__ float sc[64 * R];
   __shared__ uint32_t lds_key[128];
   __shared__ int32_t lds_idx[128];
+  __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS];
   __shared__ int next_batch;
   __shared__ int32_t sel[64 * R];          // kept blocks (kmax <= nB <= 64 R)
   __shared__ float pbuf[NW][C::CK][G];
@@ -267,8 +275,8 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkPar
   const int nB = a.nB;
   // With the sink and the last block forced (and distinct) their chunks are
   // known before the selection: they are taken first (logical chunks
-  // 0 .. 2 CPB - 1), so waves 1 .. 2 CPB - 1 load theirs while wave 0 is still
-  // selecting.  Logical chunk j -> chunk of the ascending selection.
+  // 0 .. 2 CPB - 1), so waves 1 .. 2 CPB - 1 issue their loads before the
+  // selection runs.  Logical chunk j -> chunk of the ascending selection.
   const bool early = (p.flags & 3u) == 3u && nB >= 2 && kmax >= 2;
   auto phys = [&](int j) {
     if (!early || j < CPB) return j;
@@ -292,18 +300,20 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkPar
   WaveAttn<D, G> wa;
   ChunkRegs<D, G> rA, rB;
 
-  score_and_select<D, G, R>(a, p, unit, sc, lds_key, lds_idx, &next_batch, sel);
-  wa.init(a, s, g);  // lane mapping + q; every later load depends on it
   const bool pre = early && wave >= 1 && wave < 2 * CPB && wave < NW;
   int kA = -1;
-  if (pre) {
-    kA = forced_key(wave);
-    if (kA >= 0) wa.load(rA, kb, vb, kA, L);
-  }
-  __syncthreads();
+  score_and_select<D, G, R>(a, p, unit, sc, lds_key, lds_idx, bsel, &next_batch, sel, [&] {
+    wa.init(a, s, g);  // lane mapping + q; every later load depends on it
+    if (pre) {
+      kA = forced_key(wave);
+      if (kA >= 0) wa.load(rA, kb, vb, kA, L);
+    }
+  });
+  // LDS-only barriers from here to the walk, so the preloads stay in flight
+  lds_barrier();
   for (int e = tid; e < kmax; e += 512) a.idx[(int64_t)unit * kmax + e] = sel[e];
   if (tid == 0) next_batch = NW;
-  __syncthreads();
+  lds_barrier();
   // chunks 0 .. NW-1 go to the waves in order, then each wave takes the next
   // free chunk from an LDS counter (next_batch is free again: the selection
   // barrier is behind us), keeping one more chunk in flight than it computes

@@ -18,7 +18,8 @@
 //   The unit's nB = ceil(L / BLK) block means are read through the block table
 //   (16-byte non-temporal loads, d/8 lanes per row, waves taking batches of
 //   rows from an LDS counter) and scored by the max over the group's heads of
-//   q . kbar / sqrt(d) into LDS; one wave selects; the 8 waves then walk the
+//   q . kbar / sqrt(d) into LDS; the workgroup selects (one wave for the
+//   threshold and entropy variants); the 8 waves then walk the
 //   kept blocks' 32-key chunks (page base from the table, keys past the
 //   sequence's end masked) with WaveAttn and merge through LDS into o and lse.
 // kv_append_kernel: one workgroup per sequence: writes the new token's K and V
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
   __shared__ float sc[64 * R];
   __shared__ uint32_t lds_key[128];
   __shared__ int32_t lds_idx[128];
+  __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS];
   __shared__ int next_batch, n_sel;
   __shared__ int32_t sel[64 * R];
   __shared__ float pbuf[NW][C::CK][G];
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
     return;
   }
 
-  // ---- scores of the nB blocks (through the table), then one wave selects
+  // ---- scores of the nB blocks (through the table), then the selection
   {
     const int c = lane % TPR, rl = lane / TPR;
     const int nbatch = (nB + BR - 1) / BR;
@@ -122,7 +124,10 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
       b1 = grab();
     }
     __syncthreads();
-    if (tid < 64) {
+    if (p.mode == DSA_SELECT_TOPK) {  // the workgroup selects
+      const int n = block_select_topk<R, NT>(sc, nB, p, sel, kmax, bsel);
+      if (tid == 0) n_sel = n;
+    } else if (tid < 64) {  // one wave selects
       const int n = wave_select_row<R, true>(sc, nB, p, sel, kmax, lds_key, lds_idx);
       if (tid == 0) n_sel = n;
     }

@@ -350,4 +350,174 @@ __device__ int wave_select_row(const float* srow, int nv, TopkParams p, int32_t*
   return total;
 }
 
+// ---------------------------------------------------------------- workgroup top-k
+// Workgroup barrier that orders LDS only: global loads in flight (a caller's
+// prefetch into registers) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// LDS words block_select_topk needs as scratch (up to 16 waves): two 256-bin
+// histograms, per-wave maxima, minima and scan totals, broadcast slots.
+constexpr int BSEL_SCRATCH_WORDS = 2 * 256 + 3 * 16 + 4;
+
+// Plain top-k selection of one row by all NT threads of a workgroup, with the
+// result of wave_select_row<R, true> (same forced prefix and suffix, same
+// budget, the top m candidates by (score desc, index asc), kept blocks written
+// ascending to out and padded with -1 to kmax; returns the number kept).  For
+// DSA_SELECT_TOPK rows only.  srow is the LDS score row in the transposed
+// layout (block l R + e at srow[e * 64 + l]); out may be global or LDS and is
+// complete after the caller's next barrier.  The m-th largest order key is
+// found a digit at a time (at most 8 bits per pass, from the highest bit in
+// which the candidate keys differ): an LDS histogram of the digit over the
+// keys that match the digits fixed so far, one wave walks it from the top to
+// the bin holding the m-th key, and the search ends early when that bin holds
+// exactly the keys still needed.  Thread t owns blocks t E .. t E + E - 1, so
+// one packed prefix sum in thread order ranks the ties at the threshold and
+// places every kept block.  Contains LDS-only barriers: every thread must
+// call it, and global loads the caller has in flight stay in flight.
+template <int R, int NT>
+__device__ __forceinline__ int block_select_topk(const float* srow, int nv, const TopkParams& p, int32_t* out, int kmax,
+                                 uint32_t* scratch) {
+  constexpr int NW = NT / 64;
+  constexpr int E = 64 * R / NT;  // blocks per thread
+  static_assert(E >= 1 && E * NT == 64 * R && NW <= 16, "row split");
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint32_t* hist = scratch;             // [2][256]
+  uint32_t* wmx = scratch + 512;        // [NW] per-wave maxima of the candidate keys
+  uint32_t* wmn = scratch + 512 + 16;   // [NW] minima
+  uint32_t* wsc = scratch + 512 + 32;   // [NW] packed scan totals
+  uint32_t* bc = scratch + 512 + 48;    // broadcast: digit, need, exact
+  const int na = min(p.anchors, nv);
+  const int ws = max(nv - p.window, na);
+  const int nf = na + (nv - ws);
+  int64_t budget = p.topk > 0 ? (int64_t)p.topk : ((int64_t)p.num * nv + p.den - 1) / p.den;
+  if (budget < nf) budget = nf;
+  if (budget > nv) budget = nv;
+  const int m = (int)budget - nf;
+  const int ncand = nv - nf;
+  const int j0 = t * E;
+
+  if (m <= 0 || m >= ncand) {  // forced blocks only, or every visible block
+    const int total = m <= 0 ? nf : nv;
+    for (int e = t; e < total; e += NT) out[e] = (m <= 0 && e >= na) ? ws + (e - na) : e;
+    for (int e = total + t; e < kmax; e += NT) out[e] = -1;
+    return total;
+  }
+
+  const __attribute__((address_space(3))) float* st = (const __attribute__((address_space(3))) float*)srow;
+  uint32_t key[E];
+  bool cand[E];
+  uint32_t kmx = 0, kmn = 0xffffffffu;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = j0 + e;
+    cand[e] = j >= na && j < ws;
+    key[e] = cand[e] ? order_key(st[(j % R) * 64 + j / R]) : 0u;
+    if (cand[e]) {
+      kmx = max(kmx, key[e]);
+      kmn = min(kmn, key[e]);
+    }
+  }
+  kmx = wave_max_u32(kmx);
+  kmn = wave_min_u32(kmn);
+  if (lane == 0) {
+    wmx[wave] = kmx;
+    wmn[wave] = kmn;
+  }
+  hist[t % 512] = 0u;
+  if (NT < 512)
+    for (int e = t + NT; e < 512; e += NT) hist[e] = 0u;
+  lds_barrier();
+  uint32_t hi = 0, lo = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    hi = max(hi, wmx[w]);
+    lo = min(lo, wmn[w]);
+  }
+
+  // digits fixed so far: the keys with (key & M) == P hold the m-th largest,
+  // and `need` of them are kept
+  uint32_t P = hi, M = 0xffffffffu;
+  int need = m;
+  if (hi != lo) {
+    int top = 31 - __builtin_clz(hi ^ lo);  // highest bit in which candidate keys differ
+    M = top == 31 ? 0u : ~((2u << top) - 1u);
+    P = hi & M;
+    for (int pass = 0;; ++pass) {
+      const int shift = max(top - 7, 0);
+      const uint32_t dm = (2u << (top - shift)) - 1u;  // digit mask, at most 8 bits
+      uint32_t* h = hist + 256 * (pass & 1);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (cand[e] && (key[e] & M) == P) atomicAdd(&h[(key[e] >> shift) & dm], 1u);
+      lds_barrier();
+      if (wave == 0) {
+        // lane l holds digits dm - 4 l - i (i = 0..3): descending over the lanes
+        uint32_t c[4];
+        int tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = (int)dm - 4 * lane - i;
+          c[i] = d >= 0 ? h[d] : 0u;
+          tot += (int)c[i];
+        }
+        int run = wave_incl_scan(tot) - tot;  // keys in higher digits than this lane's
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (run < need && need <= run + (int)c[i]) {
+            bc[0] = (uint32_t)((int)dm - 4 * lane - i);
+            bc[1] = (uint32_t)(need - run);
+            bc[2] = (uint32_t)(need - run) == c[i];
+          }
+          run += (int)c[i];
+        }
+      }
+      lds_barrier();
+      const uint32_t d = bc[0];
+      need = (int)bc[1];
+      const bool exact = bc[2] != 0u;
+      if (t < 256) h[t] = 0u;  // free for the pass after next (a barrier lies between)
+      P |= d << shift;
+      M |= dm << shift;
+      if (exact || shift == 0) break;
+      top = shift - 1;
+    }
+  }
+
+  // kept: forced, (key & M) > P, or (key & M) == P among the first `need` in
+  // index order.  Packed counts (above << 16 | at) in thread order.
+  uint32_t v = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = j0 + e;
+    const bool forced = j < nv && !cand[e];
+    if (forced || (cand[e] && (key[e] & M) > P)) v += 1u << 16;
+    else if (cand[e] && (key[e] & M) == P) v += 1u;
+  }
+  const uint32_t incl = (uint32_t)wave_incl_scan((int)v);
+  if (lane == 63) wsc[wave] = incl;
+  lds_barrier();
+  uint32_t before = incl - v;
+  for (int w = 0; w < wave; ++w) before += wsc[w];
+  int above = (int)(before >> 16), at = (int)(before & 0xffffu);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = j0 + e;
+    const bool forced = j < nv && !cand[e];
+    if (forced || (cand[e] && (key[e] & M) > P)) {
+      out[above + min(at, need)] = j;
+      ++above;
+    } else if (cand[e] && (key[e] & M) == P) {
+      if (at < need) out[above + at] = j;
+      ++at;
+    }
+  }
+  const int total = nf + m;
+  for (int e = total + t; e < kmax; e += NT) out[e] = -1;
+  return total;
+}
+
 }  // namespace dsa
