@@ -305,3 +305,34 @@ def test_fp8_appends(cuda_device):
     dsa.dsa_paged_kv_block_means_fp8(shape, k8, ks, table, lens, kbar2)
     torch.cuda.synchronize()
     assert torch.equal(kbar2, kbar)
+
+
+@pytest.mark.parametrize("lengths,topk,flags", [([64 * 300 - 5, 64 * 120 + 1, 64, 0], 17, 3),
+                                                ([64 * 1100, 64 * 700, 64 * 5], 40, 1)])
+def test_paged_decode_exact_ties(cuda_device, lengths, topk, flags):
+    """Integer-valued block scores (many exact ties) through the page table:
+    each sequence's selection equals the oracle's exactly on its own
+    ceil(L_s / 64) blocks (ties go to the lower block)."""
+    from test_gpu_parity import tied_decode_inputs
+    S, Hkv, G, d = len(lengths), 2, 2, 128
+    nblk = -(-max(lengths) // 64)
+    say(f"paged exact ties lengths {lengths} k{topk} flags{flags}")
+    q, kc, vc, v = tied_decode_inputs(cuda_device, S, Hkv, G, nblk, d, seed=topk, tail=0)
+    kp, vp, table, lens = to_paged(kc, vc, lengths, 64, seed=topk)
+    shape = dsa.paged_shape(kp, table, Hkv * G)
+    kbar = torch.zeros((kp.shape[0], Hkv, d), dtype=torch.float32, device=cuda_device)
+    dsa.dsa_paged_kv_block_means(shape, kp, table, lens, kbar)
+    o, lse, idx, cnt = dsa.paged_decode(q, kp, vp, kbar, table, lens, 64, topk, 0, 1, flags)
+    torch.cuda.synchronize()
+    gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for s, L in enumerate(lengths):
+        nb = -(-L // 64)
+        if nb == 0:
+            assert (gcnt[s] == 0).all() and (gidx[s] == -1).all()
+            continue
+        scores = (v[s : s + 1, :, :nb].astype(np.float64) / math.sqrt(d))[:, :, None, :]
+        ref_idx, ref_cnt, _ = O.select_topk(scores, topk, 0, 1, flags, causal=False)
+        km = ref_idx.shape[-1]
+        assert np.array_equal(gcnt[s], ref_cnt[0, :, 0]), s
+        assert np.array_equal(gidx[s, :, :km], ref_idx[0, :, 0]), s
+        assert (gidx[s, :, km:] == -1).all(), s

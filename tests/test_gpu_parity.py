@@ -392,6 +392,49 @@ def test_decode_full(cuda_device):
     decode_check(cuda_device, w, 3, sample=units, o_units=units[:4])
 
 
+def tied_decode_inputs(dev, S, Hkv, G, nblk, d, seed, tail=5):
+    """Caches whose block b of unit (s, g) has every key equal to v e0 with v an
+    integer in [-6, 6) (many exact ties), q = e0 for every head: block means
+    and scores are exact, score = v / sqrt(d).  Returns q, kc, vc, v."""
+    rng = np.random.default_rng(seed)
+    L = nblk * 64 - tail
+    v = rng.integers(-6, 6, size=(S, Hkv, nblk)).astype(np.float32)
+    kc = torch.zeros((S, Hkv, nblk * 64, d), dtype=torch.bfloat16, device=dev)
+    kc[..., 0] = torch.from_numpy(v).to(dev).repeat_interleave(64, dim=2).to(torch.bfloat16)
+    kc = kc[:, :, :L].contiguous()
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    vc = torch.randn((S, Hkv, L, d), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.zeros((S, Hkv * G, d), dtype=torch.bfloat16, device=dev)
+    q[..., 0] = 1.0
+    return q, kc, vc, v
+
+
+@pytest.mark.parametrize("S,Hkv,G,nblk,topk,flags", [(2, 2, 2, 300, 17, 3), (64, 4, 2, 300, 17, 3),
+                                                     (32, 8, 1, 1100, 40, 1), (32, 8, 2, 200, 150, 0),
+                                                     (3, 2, 4, 50, 49, 3)])
+def test_decode_exact_ties(cuda_device, S, Hkv, G, nblk, topk, flags):
+    """Integer-valued block scores (many exact ties): the decode selection
+    equals the oracle's exactly (ties go to the lower block), on the split
+    path (few units) and the fused path (>= 256 units), rows of up to 1 100
+    blocks, with and without forcing."""
+    say(f"decode exact ties S{S} Hkv{Hkv} G{G} nB{nblk} k{topk} flags{flags}")
+    d = 128
+    # a ragged last block only where it is forced (its mean is a division by
+    # the row count, exact in the oracle but not necessarily on the GPU)
+    tail = 5 if flags & O.FORCE_DIAG else 0
+    q, kc, vc, v = tied_decode_inputs(cuda_device, S, Hkv, G, nblk, d, seed=nblk + topk, tail=tail)
+    kbar = dsa.kv_block_means(kc, 64)
+    o, lse, idx = dsa.decode(q, kc, vc, kbar, 64, topk, flags=flags)
+    torch.cuda.synchronize()
+    scores = (v.astype(np.float64) / math.sqrt(d))[:, :, None, :]
+    ref_idx, ref_cnt, _ = O.select_topk(scores, topk, 0, 1, flags, causal=False)
+    gidx = idx.cpu().numpy()
+    km = ref_idx.shape[-1]
+    assert np.array_equal(gidx[..., :km], ref_idx[:, :, 0]) and (gidx[..., km:] == -1).all()
+    assert torch.isfinite(o.float()).all()
+
+
 def test_decode_split_count_does_not_change_results(cuda_device):
     """One sequence alone (8 units: the split path, many splits per unit) and
     inside a batch of 32 (256 units: the fused one-workgroup-per-unit path)
