@@ -621,12 +621,10 @@ int dsa_prefill(const dsa_shape* s, const void* q, const void* k, const void* v,
   p += align256(B * s->n_kv_heads * nB * d * 4);
   float* scores = reinterpret_cast<float*>(p);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = dsa::launch_block_means(static_cast<const uint16_t*>(q), qbar, (int64_t)B * s->n_q_heads, s->seq_len,
-                                         s->head_dim, s->block, st);
-  if (e != hipSuccess) return hip_fail(e, "block_means(q) launch");
-  e = dsa::launch_block_means(static_cast<const uint16_t*>(k), kbar, (int64_t)B * s->n_kv_heads, s->seq_len,
-                              s->head_dim, s->block, st);
-  if (e != hipSuccess) return hip_fail(e, "block_means(k) launch");
+  hipError_t e = dsa::launch_block_means2(static_cast<const uint16_t*>(q), qbar, (int64_t)B * s->n_q_heads,
+                                          static_cast<const uint16_t*>(k), kbar, (int64_t)B * s->n_kv_heads,
+                                          s->seq_len, s->head_dim, s->block, st);
+  if (e != hipSuccess) return hip_fail(e, "block_means(q, k) launch");
   rc = dsa_block_scores(s, qbar, kbar, scores, stream);
   if (rc) return rc;
   rc = dsa_select_topk(s, scores, idx, cnt, stream);

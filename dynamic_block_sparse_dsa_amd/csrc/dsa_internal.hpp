@@ -56,6 +56,9 @@ __device__ __forceinline__ uint32_t xcd_logical_id(uint32_t w, uint32_t total) {
 // x [n_units, N, d] bf16 -> xbar [n_units, nB, d] fp32 (mean per block)
 hipError_t launch_block_means(const uint16_t* x, float* xbar, int64_t n_units, int N, int d, int block,
                               hipStream_t stream);
+// the means of two [*, N, d] tensors (n0 and n1 units) in one launch
+hipError_t launch_block_means2(const uint16_t* x0, float* xbar0, int64_t n0, const uint16_t* x1, float* xbar1,
+                               int64_t n1, int N, int d, int block, hipStream_t stream);
 
 // qbar [B, Hq, nB, d], kbar [B, Hkv, nB, d] -> scores [B, Hkv, nB, nB]
 hipError_t launch_block_scores(const float* qbar, const float* kbar, float* scores, int B, int Hq, int Hkv, int nB,

@@ -21,13 +21,22 @@ namespace dsa {
 // One workgroup per (unit, block): 256 threads read the block's rows as
 // 16-byte chunks (D/8 chunks per row, 256/(D/8) row groups), sum them in fp32,
 // reduce the row groups through LDS and divide by the number of real rows.
+// Two tensors in one launch: the first n0 units of x0, then those of x1.
 template <int D>
-__global__ __launch_bounds__(256) void block_means_kernel(const uint16_t* __restrict__ x, float* __restrict__ xbar,
-                                                          int N, int block, int nB) {
+__global__ __launch_bounds__(256) void block_means_kernel(const uint16_t* __restrict__ x0, float* __restrict__ xbar0,
+                                                          int64_t n0, const uint16_t* __restrict__ x1,
+                                                          float* __restrict__ xbar1, int N, int block, int nB) {
   constexpr int CH = D / 8;        // 16-byte chunks per row
   constexpr int RG = 256 / CH;     // row groups
   __shared__ float part[RG][D + 1];
-  const int64_t wg = blockIdx.x;
+  int64_t wg = blockIdx.x;
+  const uint16_t* x = x0;
+  float* xbar = xbar0;
+  if (wg >= n0 * nB) {
+    wg -= n0 * nB;
+    x = x1;
+    xbar = xbar1;
+  }
   const int64_t unit = wg / nB;
   const int j = (int)(wg % nB);
   const int t = threadIdx.x, c = t % CH, rg = t / CH;
@@ -54,16 +63,23 @@ __global__ __launch_bounds__(256) void block_means_kernel(const uint16_t* __rest
   }
 }
 
-hipError_t launch_block_means(const uint16_t* x, float* xbar, int64_t n_units, int N, int d, int block,
-                              hipStream_t stream) {
+hipError_t launch_block_means2(const uint16_t* x0, float* xbar0, int64_t n0, const uint16_t* x1, float* xbar1,
+                               int64_t n1, int N, int d, int block, hipStream_t stream) {
   const int nB = (N + block - 1) / block;
-  const int64_t n_wg = n_units * nB;
+  const int64_t n_wg = (n0 + n1) * nB;
   if (n_wg == 0) return hipSuccess;
   if (d == 64)
-    hipLaunchKernelGGL(block_means_kernel<64>, dim3((uint32_t)n_wg), dim3(256), 0, stream, x, xbar, N, block, nB);
+    hipLaunchKernelGGL(block_means_kernel<64>, dim3((uint32_t)n_wg), dim3(256), 0, stream, x0, xbar0, n0, x1, xbar1,
+                       N, block, nB);
   else
-    hipLaunchKernelGGL(block_means_kernel<128>, dim3((uint32_t)n_wg), dim3(256), 0, stream, x, xbar, N, block, nB);
+    hipLaunchKernelGGL(block_means_kernel<128>, dim3((uint32_t)n_wg), dim3(256), 0, stream, x0, xbar0, n0, x1, xbar1,
+                       N, block, nB);
   return hipGetLastError();
+}
+
+hipError_t launch_block_means(const uint16_t* x, float* xbar, int64_t n_units, int N, int d, int block,
+                              hipStream_t stream) {
+  return launch_block_means2(x, xbar, n_units, nullptr, nullptr, 0, N, d, block, stream);
 }
 
 // ============================================================== block scores
