@@ -27,7 +27,7 @@
 //      of every query tile, added at the end); the waves' K and V operands
 //      sit in registers, and for every (query block of the inverted list) x
 //      (query head of the group) the Q and dO tiles stream through
-//      double-buffered LDS: S = Q K^T, dP = dO V^T (Q, dO rows as A operands,
+//      a ring of LDS stages: S = Q K^T, dP = dO V^T (Q, dO rows as A operands,
 //      K, V as B), P and dS in registers (already in B-operand order), then
 //      dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transposed LDS
 //      reads.
@@ -313,7 +313,9 @@ struct BwdKVCfg {
   static constexpr int QB_PER_WAVE = (BLK / 32) / QS;  // 32-query sub-blocks per wave per tile
   static constexpr int TILE = BLK * D;                  // bf16 elements
   static constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * BLK * 4;
-  static constexpr int NBUF = 3 * STAGE_BYTES <= 100 * 1024 ? 3 : 2;
+  // as many stages (up to 4) as 136 KiB of LDS holds: one workgroup per CU
+  // either way, and a deeper ring keeps more item loads in flight
+  static constexpr int NBUF = 4 * STAGE_BYTES <= 136 * 1024 ? 4 : 3 * STAGE_BYTES <= 136 * 1024 ? 3 : 2;
   static constexpr int STAT_BYTES_PER_WAVE = 2 * BLK * 4 / WAVES;  // statistics DMA: one instruction per wave
   static constexpr int LOADS_PER_ITEM = 2 * (TILE * 2 / 1024) / WAVES + 1;  // DMA instructions per wave
   static_assert(STAT_BYTES_PER_WAVE % 16 == 0 && STAT_BYTES_PER_WAVE <= 1024, "statistics split");
