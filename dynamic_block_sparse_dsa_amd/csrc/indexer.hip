@@ -27,16 +27,18 @@
 //   D / 64 dims per lane), 8 rows in flight.  More than 64 kept tokens are
 //   taken in chunks of 64 with an online softmax.
 // select_tokens_fast_kernel: one wave per query-token row of up to 8192
-//   scores.  Lane l owns tokens l + 64 e (so every load instruction reads 256
-//   consecutive bytes and ballots over e visit the candidates in index order).
-//   Pass 1 keeps 8 group maxima per lane (group = e mod 8); the m-th largest
-//   of them (found exactly, no early exit) is a lower bound t0 of the m-th
-//   largest candidate (the groups are disjoint).  Pass 2
-//   re-reads the row (from L2) and compacts the candidates >= t0 -- usually
-//   about m -- into LDS in index order; the threshold search then runs on two
-//   keys per lane.  Rows it cannot finish (more than 64 to keep, or more than
-//   128 candidates at or above t0) get cnt = -1 and are completed by the
-//   general one-wave select.
+//   scores.  The row is read in 256-token chunks, lane l holding tokens
+//   4 l .. 4 l + 3 of each (one 16-byte load per lane, 1 KiB per wave
+//   instruction; four chunks in flight).  Pass 1 keeps 8 group maxima per
+//   lane, group k + 4 (c mod 2) for position k of chunk c, so a run of high
+//   scores lands in many groups; the m-th largest of them (found exactly, no
+//   early exit) is a lower bound t0 of the m-th largest candidate (the groups
+//   are disjoint).  Pass 2 re-reads the chunks whose groups reach t0 and
+//   compacts the candidates >= t0 -- usually about m -- into LDS in index
+//   order (a prefix sum of the per-lane counts within a chunk); the threshold
+//   search then runs on two keys per lane.  Rows it cannot finish (more than
+//   64 to keep, or more than 128 candidates at or above t0) get cnt = -1 and
+//   are completed by the general one-wave select.
 #include "attn_common.hpp"
 #include "topk_row.hpp"
 
@@ -284,7 +286,6 @@ __global__ __launch_bounds__(256) void token_attn_kernel(const uint16_t* __restr
 __global__ __launch_bounds__(256) void select_tokens_fast_kernel(const float* __restrict__ scores,
                                                                  int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
                                                                  int64_t n_rows, int N, TopkParams p, int kmax) {
-  constexpr int E = 128;  // tokens per lane: rows of up to 64 E
   __shared__ uint32_t lds_key[4][128];
   __shared__ int32_t lds_idx[4][128];
   const int lane = threadIdx.x & 63;
@@ -311,50 +312,65 @@ __global__ __launch_bounds__(256) void select_tokens_fast_kernel(const float* __
     if (lane == 0) cnt[row] = -1;
     return;
   }
-  const int hi_e = (ws - 1) / 64;  // last e with a candidate in some lane
-  // pass 1: group maxima of the candidate keys (0 = no candidate).  Group
-  // g of a lane holds its e = g mod 8, so every row -- short ones too --
-  // spreads over all 8 groups; 16 loads are issued together.
-  const int e_lo = (na / 64) & ~15;
+  // token j = 256 c + 4 lane + k; a 16-byte load when the four are
+  // candidates and the row is 16-byte aligned, else one load per candidate
+  constexpr int CB = 4;  // chunks per batch
+  const int c_lo = (na / 256) & ~(CB - 1), c_hi = (ws - 1) / 256;
+  const bool aligned = (N & 3) == 0;
+  auto load4 = [&](int c, uint32_t (&kv)[4], bool want) {
+    const int j0 = 256 * c + 4 * lane;
+    if (want && aligned && j0 >= na && j0 + 3 < ws) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(srow + j0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kv[k] = order_key(v[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kv[k] = (want && j0 + k >= na && j0 + k < ws) ? order_key(srow[j0 + k]) : 0u;
+    }
+  };
+  // pass 1: group maxima of the candidate keys (0 = no candidate)
   uint32_t gmax[8];
 #pragma unroll
   for (int g = 0; g < 8; ++g) gmax[g] = 0u;
-  for (int e0 = e_lo; e0 <= hi_e; e0 += 16) {
-    uint32_t kv[16];
+  for (int c0 = c_lo; c0 <= c_hi; c0 += CB) {
+    uint32_t kv[CB][4];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int j = lane + 64 * (e0 + u);
-      kv[u] = (j >= na && j < ws) ? order_key(srow[j]) : 0u;
-    }
+    for (int u = 0; u < CB; ++u) load4(c0 + u, kv[u], true);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) gmax[u & 7] = max(gmax[u & 7], kv[u]);
+    for (int u = 0; u < CB; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) gmax[k + 4 * (u & 1)] = max(gmax[k + 4 * (u & 1)], kv[u][k]);
   }
   bool ex;
   const uint32_t t0 = wave_kth_largest<8, false>(gmax, m, &ex);  // the m-th largest group maximum
-  // pass 2: compact the candidates >= t0 in index order; a lane reads an
-  // element again only when its group maximum reaches t0
+  // pass 2: compact the candidates >= t0 in index order; a lane reads a chunk
+  // again only when one of its groups there reaches t0
   int ns = 0;
   if (t0 > 0u) {
-    bool need[8];
+    for (int c0 = c_lo; c0 <= c_hi; c0 += CB) {
+      uint32_t kv[CB][4];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) need[g] = gmax[g] >= t0;
-    for (int e0 = e_lo; e0 <= hi_e; e0 += 16) {
-      uint32_t kv[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int j = lane + 64 * (e0 + u);
-        kv[u] = (need[u & 7] && j >= na && j < ws) ? order_key(srow[j]) : 0u;
+      for (int u = 0; u < CB; ++u) {
+        const int gb = 4 * (u & 1);
+        load4(c0 + u, kv[u], max(max(gmax[gb], gmax[gb + 1]), max(gmax[gb + 2], gmax[gb + 3])) >= t0);
       }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const bool c = kv[u] >= t0;
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(c);
-        const int pos = ns + lanes_below(bal);
-        if (c && pos < 128) {
-          lds_key[wave][pos] = kv[u];
-          lds_idx[wave][pos] = lane + 64 * (e0 + u);
-        }
-        ns += __builtin_popcountll(bal);
+      for (int u = 0; u < CB; ++u) {
+        int mine = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mine += kv[u][k] >= t0;
+        const int incl = wave_incl_scan(mine);
+        int pos = ns + incl - mine;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (kv[u][k] >= t0) {
+            if (pos < 128) {
+              lds_key[wave][pos] = kv[u][k];
+              lds_idx[wave][pos] = 256 * (c0 + u) + 4 * lane + k;
+            }
+            ++pos;
+          }
+        ns += __builtin_amdgcn_readlane(incl, 63);
       }
     }
   }
