@@ -85,16 +85,19 @@ hipError_t launch_block_means(const uint16_t* x, float* xbar, int64_t n_units, i
 // ============================================================== block scores
 // One 256-thread workgroup per 32x32 tile of the score matrix of one (batch,
 // KV head): thread (ty, tx) owns rows ty, ty+16 and columns tx, tx+16.  Both
-// tiles of means are staged whole in LDS (row pitch D+1 floats: the column
-// reads of the K tile hit distinct banks, the Q reads are broadcasts); every
-// head of the group is scored against the K tile and the max is kept.  Tiles
-// strictly above the diagonal are -inf.
+// tiles of means are staged whole in LDS (row pitch D+4 floats: the float4
+// reads of 16 K rows hit distinct bank groups, the Q reads are broadcasts);
+// the K tile and the first Q tile are fetched together; every head of the
+// group is scored against the K tile and the max is kept.  Tiles strictly
+// above the diagonal are -inf.
 template <int D>
 __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restrict__ qbar,
                                                            const float* __restrict__ kbar, float* __restrict__ scores,
                                                            int Hq, int Hkv, int nB, float scale, int n_tiles) {
-  __shared__ float qs[32][D + 1];
-  __shared__ float ks[32][D + 1];
+  constexpr int PITCH = D + 4;  // rows 16-byte aligned, one bank group apart: conflict-free float4 reads
+  constexpr int PER_T = 32 * D / 4 / 256;  // float4 pieces of a tile per thread
+  __shared__ __align__(16) float qs[32][PITCH];
+  __shared__ __align__(16) float ks[32][PITCH];
   const int per_unit = n_tiles * n_tiles;
   const int64_t unit = blockIdx.x / per_unit;  // b * Hkv + g
   const int tile = blockIdx.x % per_unit;
@@ -113,34 +116,51 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restri
   const int G = Hq / Hkv;
   const int64_t b = unit / Hkv, g = unit % Hkv;
   const float* kb = kbar + unit * (int64_t)nB * D;
-  for (int e = t; e < 32 * D / 4; e += 256) {
-    const int r = e / (D / 4), c = e % (D / 4);
-    f32x4 v = (f32x4){0, 0, 0, 0};
-    if (j0 + r < nB) v = *reinterpret_cast<const f32x4*>(kb + (int64_t)(j0 + r) * D + 4 * c);
+  // a 32-row tile of means: global -> registers (rows past nB read as 0), then LDS
+  auto fetch = [&](const float* src, int r0, f32x4 (&v)[PER_T]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ks[r][4 * c + q] = v[q];
-  }
+    for (int n = 0; n < PER_T; ++n) {
+      const int e = t + 256 * n, r = e / (D / 4), c = e % (D / 4);
+      v[n] = (f32x4){0, 0, 0, 0};
+      if (r0 + r < nB) v[n] = *reinterpret_cast<const f32x4*>(src + (int64_t)(r0 + r) * D + 4 * c);
+    }
+  };
+  auto stash = [&](float (*dst)[PITCH], const f32x4 (&v)[PER_T]) {
+#pragma unroll
+    for (int n = 0; n < PER_T; ++n) {
+      const int e = t + 256 * n, r = e / (D / 4), c = e % (D / 4);
+      *reinterpret_cast<f32x4*>(&dst[r][4 * c]) = v[n];
+    }
+  };
   float best[2][2];
   for (int hh = 0; hh < G; ++hh) {
     const float* qb = qbar + ((b * Hq) + g * G + hh) * (int64_t)nB * D;
-    __syncthreads();  // previous head's reads of qs are done
-    for (int e = t; e < 32 * D / 4; e += 256) {
-      const int r = e / (D / 4), c = e % (D / 4);
-      f32x4 v = (f32x4){0, 0, 0, 0};
-      if (i0 + r < nB) v = *reinterpret_cast<const f32x4*>(qb + (int64_t)(i0 + r) * D + 4 * c);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) qs[r][4 * c + q] = v[q];
+    f32x4 qv[PER_T];
+    if (hh == 0) {  // the K tile and the first head's Q tile are fetched together
+      f32x4 kv[PER_T];
+      fetch(kb, j0, kv);
+      fetch(qb, i0, qv);
+      stash(ks, kv);
+    } else {
+      fetch(qb, i0, qv);
+      __syncthreads();  // previous head's reads of qs are done
     }
+    stash(qs, qv);
     __syncthreads();
     float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-#pragma unroll 8
-    for (int dd = 0; dd < D; ++dd) {
-      const float a0 = qs[ty][dd], a1 = qs[ty + 16][dd];
-      const float b0 = ks[tx][dd], b1 = ks[tx + 16][dd];
-      acc[0][0] = __builtin_fmaf(a0, b0, acc[0][0]);
-      acc[0][1] = __builtin_fmaf(a0, b1, acc[0][1]);
-      acc[1][0] = __builtin_fmaf(a1, b0, acc[1][0]);
-      acc[1][1] = __builtin_fmaf(a1, b1, acc[1][1]);
+#pragma unroll 4
+    for (int dd = 0; dd < D; dd += 4) {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&qs[ty][dd]);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&qs[ty + 16][dd]);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(&ks[tx][dd]);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(&ks[tx + 16][dd]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[0][0] = __builtin_fmaf(a0[e], b0[e], acc[0][0]);
+        acc[0][1] = __builtin_fmaf(a0[e], b1[e], acc[0][1]);
+        acc[1][0] = __builtin_fmaf(a1[e], b0[e], acc[1][0]);
+        acc[1][1] = __builtin_fmaf(a1[e], b1[e], acc[1][1]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r)
