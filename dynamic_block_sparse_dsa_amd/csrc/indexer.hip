@@ -11,15 +11,14 @@
 // every attention head attends over its token's kept key/value rows.
 //
 // index_scores_kernel: one workgroup per 16 query tokens, each wave 4 tokens
-//   = 2 column tiles of 32 (token, index head) pairs, so the 16 heads of a
-//   token are one 16-lane DPP row of the MFMA output.  Per 64-key tile
-//   (global -> LDS DMA, double-buffered, kswz rows): S^T = K_tile . Qi^T on
-//   v_mfma_f32_32x32x16_bf16 (key rows from LDS as A, the wave's index query
-//   rows as B in registers); then ReLU, times the head weight, and a
-//   reduce-scatter over each 16-lane row (four DPP steps) leaves lane i of the
-//   row with the head sum of its i-th output register, which it stores: one
-//   score per lane, causal part only.  Token tiles run latest first (they
-//   have the most key tiles).
+//   = 2 tiles of 32 (token, index head) pairs.  Per 64-key tile (global ->
+//   LDS DMA, double-buffered, kswz rows): S = Qi . K_tile^T on
+//   v_mfma_f32_32x32x16_bf16 (the wave's index query rows as A in registers,
+//   key rows from LDS as B), so a lane's output holds one key and 8 heads of
+//   each of two tokens; ReLU times the head weight is summed over those in
+//   the lane, the other 8 heads come from lane l ^ 32, and each lane stores
+//   one score (32 consecutive keys of a token per half-wave), causal part
+//   only.  Token tiles run latest first (they have the most key tiles).
 // token_attn_kernel: one wave per (batch, token, KV head): lane l gathers the
 //   l-th kept token's key row and computes the logits of the group's query
 //   heads (queries staged in LDS, read as broadcasts); softmax across the
@@ -66,27 +65,6 @@ __device__ __forceinline__ u32x4 key_frag(const LDS_AS uint16_t* tile, int r, in
   return *reinterpret_cast<const LDS_AS u32x4*>(tile + r * DI + c * 8);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dppf(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// v[0..15] per lane -> lane i of each 16-lane row gets sum over the row's
-// lanes of v[i].  Each step pairs lanes with a DPP mirror and halves the
-// registers: the lane keeps the half named by its bit and adds the partner's
-// copy of that half.
-__device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int i) {
-  float w8[8], w4[4], w2[2];
-  const bool u1 = i >= 8, u2 = (i & 7) >= 4, u3 = (i & 3) >= 2, u4 = (i & 1) != 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w8[j] = (u1 ? v[j + 8] : v[j]) + dppf<0x140>(u1 ? v[j] : v[j + 8]);  // row_mirror
-#pragma unroll
-  for (int j = 0; j < 4; ++j) w4[j] = (u2 ? w8[j + 4] : w8[j]) + dppf<0x141>(u2 ? w8[j] : w8[j + 4]);  // row_half_mirror
-#pragma unroll
-  for (int j = 0; j < 2; ++j) w2[j] = (u3 ? w4[j + 2] : w4[j]) + dppf<0x1B>(u3 ? w4[j] : w4[j + 2]);  // quad [3,2,1,0]
-  return (u4 ? w2[1] : w2[0]) + dppf<0xB1>(u4 ? w2[0] : w2[1]);                                      // quad [1,0,3,2]
-}
-
 }  // namespace
 
 // ============================================================== index scores
@@ -105,19 +83,31 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const uint16_t* __res
   const int t0 = tile * TPB;
   const int n_kt = (min(t0 + TPB, N) - 1) / KT + 1;
 
-  // B operands: column (lane % 32) of column tile ct is token
-  // t0 + 4 wave + 2 ct + (lane % 32) / 16, index head lane % 16
+  // A operands: row (lane % 32) of pair tile ct is the (token, index head)
+  // pair (t0 + 4 wave + 2 ct + (lane % 32) / 16, lane % 16)
   u32x4 qf[2][NKS];
-  float wv[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int tk = t0 + TPW * wave + 2 * ct + ((lane & 31) >> 4);
+    const uint16_t* qrow = qi + ((b * N + min(tk, N - 1)) * HI + i16) * DI;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ct][ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + 8 * half);
+  }
+  // Output register r of lane l holds key l % 32 and pair row
+  // 8 (r / 4) + 4 half + r % 4: registers 0..7 are token 2 ct (heads
+  // 4 half + r % 4 and 8 + 4 half + r % 4), 8..15 token 2 ct + 1, same heads.
+  // wr: the head weight of each register; the lane stores token 2 ct + half.
+  float wr[2][16];
   int tok[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
-    tok[ct] = t0 + TPW * wave + 2 * ct + ((lane & 31) >> 4);
-    const int64_t trow = b * N + min(tok[ct], N - 1);
-    const uint16_t* qrow = qi + (trow * HI + i16) * DI;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ct][ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + 8 * half);
-    wv[ct] = wi[trow * HI + i16];
+    for (int r = 0; r < 16; ++r) {
+      const int tr = t0 + TPW * wave + 2 * ct + (r >> 3);
+      const int hd = 8 * ((r >> 2) & 1) + 4 * half + (r & 3);
+      wr[ct][r] = wi[(b * N + min(tr, N - 1)) * HI + hd];
+    }
+    tok[ct] = t0 + TPW * wave + 2 * ct + half;
   }
   const uint16_t* kb = ki + b * (int64_t)N * DI;
   const uint32_t base[2] = {(uint32_t)(uintptr_t)(LDS_AS uint16_t*)kt_lds[0],
@@ -145,21 +135,26 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const uint16_t* __res
         const u32x4 a = key_frag<DI>(tl, rt * 32 + (lane & 31), ks, half);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[ct][ks]), acc[rt][ct], 0,
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qf[ct][ks]), as_bf16x8(a), acc[rt][ct], 0,
                                                                 0, 0);
       }
     }
-    // ReLU, head weight, sum over the 16 heads of each token; lane i16 of the
-    // row ends with output register i16: key row 8 (i16 / 4) + 4 half + i16 % 4
+    // ReLU, head weight, sum over the heads: 8 of each token in the lane,
+    // the other 8 in lane l ^ 32, which gets this lane's partial of the token
+    // it stores and sends its own
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        float v[16];
+        float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = fmaxf(acc[rt][ct][r], 0.f) * wv[ct];
-        const float sum = row_reduce_scatter16(v, i16);
-        const int key = kt * KT + rt * 32 + 8 * (i16 >> 2) + 4 * half + (i16 & 3);
+        for (int r = 0; r < 8; ++r) {
+          p0 = __builtin_fmaf(fmaxf(acc[rt][ct][r], 0.f), wr[ct][r], p0);
+          p1 = __builtin_fmaf(fmaxf(acc[rt][ct][8 + r], 0.f), wr[ct][8 + r], p1);
+        }
+        const float give = half ? p0 : p1, keep = half ? p1 : p0;
+        const float sum = keep + __shfl_xor(give, 32, 64);
+        const int key = kt * KT + rt * 32 + (lane & 31);
         if (tok[ct] < N && key <= tok[ct]) scores[(b * N + tok[ct]) * (int64_t)N + key] = sum;
       }
     }
