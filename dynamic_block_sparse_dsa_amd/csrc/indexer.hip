@@ -19,7 +19,8 @@
 //   the lane, the other 8 heads come from lane l ^ 32, and each lane stores
 //   one score (32 consecutive keys of a token per half-wave), causal part
 //   only.  Token tiles run latest first (they have the most key tiles).
-// token_attn_kernel: one wave per (batch, token, KV head): lane l gathers the
+// token_attn_kernel: one wave per (batch, token, KV head), KV-head-major over
+//   XCD-contiguous workgroups (one KV head's rows per XCD L2): lane l gathers the
 //   l-th kept token's key row and computes the logits of the group's query
 //   heads (queries staged in LDS, read as broadcasts); softmax across the
 //   wave; P V streams the kept value rows (each row read by the whole wave,
@@ -175,10 +176,13 @@ __global__ __launch_bounds__(256) void token_attn_kernel(const uint16_t* __restr
   __shared__ __align__(16) uint16_t qs[4][G * D];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  // KV-head-major over XCD-contiguous workgroup ranges: the waves of one XCD
+  // gather from one KV head's rows, which then stay in that XCD's L2
+  const int64_t w = (int64_t)xcd_logical_id(blockIdx.x, gridDim.x) * 4 + wave;
   if (w >= n_waves) return;  // whole wave; no workgroup barrier below
-  const int g = (int)(w % Hkv);
-  const int64_t bt = w / Hkv;  // b * N + t
+  const int64_t BN = n_waves / Hkv;
+  const int g = (int)(w / BN);
+  const int64_t bt = w % BN;  // b * N + t
   const int t = (int)(bt % N);
   const int64_t b = bt / N;
   const int Hq = Hkv * G;
