@@ -48,6 +48,22 @@ def measured_traffic(workload, kernel_src):
     return t.get("bytes_per_launch")
 
 
+def launch_stats(fn, n, stream, before=None):
+    """Per-launch times (us) of n launches, each bracketed by its own HIP
+    events on `stream` (`before`, if given, runs untimed before each):
+    median, min and 90th percentile."""
+    import statistics
+
+    t = []
+    for _ in range(n):
+        if before is not None:
+            before()
+        t.append(time_events(fn, 1, stream) * 1e3)
+    t.sort()
+    return dict(median=round(statistics.median(t), 2), min=round(t[0], 2),
+                p90=round(t[min(len(t) - 1, int(0.9 * len(t)))], 2), n=n)
+
+
 def time_events(fn, n, stream):
     import torch
 
@@ -99,6 +115,7 @@ def bench_prefill(args, dev, stream):
     for _ in range(args.warmup):
         attn()
     ms_attn = time_events(attn, args.steps, stream)
+    attn_stats = launch_stats(attn, max(args.steps, 50), stream)
     flops = work.prefill_flops(cnt.cpu().numpy(), w.group, w.block, d)
     tflops = flops / (ms_attn * 1e-3) / 1e12
     tiles = work.prefill_tiles(cnt.cpu().numpy(), w.group)
@@ -110,7 +127,8 @@ def bench_prefill(args, dev, stream):
                     topk=w.topk, topk_num=w.topk_num, topk_den=w.topk_den, structure=w.structure),
         roofline=dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                       frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel="sparse_attn_fwd_kernel",
-                      avg_launch_us=round(ms_attn * 1e3, 2), flops_per_launch=flops, executed_tiles=tiles,
+                      avg_launch_us=round(ms_attn * 1e3, 2), launch_us=attn_stats, flops_per_launch=flops,
+                      executed_tiles=tiles,
                       step_frac=round(flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)),
     )
     return res, (q, k, v, w)
@@ -145,17 +163,25 @@ def bench_decode(args, dev, stream):
     for _ in range(args.warmup):
         step()
     # each step timed alone with events, the cache flushed in between
-    tot = 0.0
-    for _ in range(args.steps):
+    def flush_cache():
         with torch.cuda.stream(stream):
             flush.sum()
-        tot += time_events(step, 1, stream)
+
+    tot = 0.0
+    steps_us = []
+    for _ in range(args.steps):
+        flush_cache()
+        steps_us.append(time_events(step, 1, stream) * 1e3)
+        tot += steps_us[-1] * 1e-3
     ms = tot / args.steps
+    steps_us.sort()
+    step_stats = dict(median=round(steps_us[len(steps_us) // 2], 2), min=round(steps_us[0], 2),
+                      p90=round(steps_us[min(len(steps_us) - 1, int(0.9 * len(steps_us)))], 2), n=len(steps_us))
     nbytes = work.decode_bytes(S, Hq, Hkv, L, d, w.block, km)
     gbs = nbytes / (ms * 1e-3) / 1e9
     args._decode_inputs = (q, kc, vc, w, flush)  # reused by the paged bench
     return dict(
-        value=S / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
+        value=S / (ms * 1e-3), unit="tokens/s", ms_per_step=ms, step_us=step_stats,
         config=dict(workload=w.name, sequences=S, n_q_heads=Hq, n_kv_heads=Hkv, cache_len=L, head_dim=d,
                     block=w.block, topk=w.topk),
         roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
@@ -439,6 +465,41 @@ def bench_index(args, dev, stream):
     )
 
 
+def ceilings(dev, stream):
+    """Measured ceilings for context (library and torch code, not this
+    library's path): a bf16 GEMM through torch.matmul (hipBLASLt) and a plain
+    device-to-device copy, each timed with HIP events."""
+    import torch
+
+    n = 8192
+    with torch.cuda.stream(stream):
+        a = torch.randn((n, n), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        b = torch.randn((n, n), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+        src = torch.ones(1 << 28, device=dev, dtype=torch.float32)  # 1 GiB
+        dst = torch.empty_like(src)
+
+    def gemm():
+        with torch.cuda.stream(stream):
+            torch.matmul(a, b, out=c)
+
+    def copy():
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+
+    for _ in range(3):
+        gemm()
+        copy()
+    ms_g = time_events(gemm, 10, stream)
+    ms_c = time_events(copy, 5, stream)
+    return dict(gemm_bf16=dict(shape=[n, n, n], tflops=round(2 * n**3 / (ms_g * 1e-3) / 1e12, 1),
+                               frac_of_peak=round(2 * n**3 / (ms_g * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                               source="torch.matmul (hipBLASLt)"),
+                copy=dict(bytes=2 * src.numel() * 4, gbs=round(2 * src.numel() * 4 / (ms_c * 1e-3) / 1e9, 1),
+                          frac_of_peak=round(2 * src.numel() * 4 / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          source="torch copy_, 1 GiB read + 1 GiB written"))
+
+
 def cpu_baseline(args, inputs):
     """The oracle, as it stands, on whole heads of the prefill workload until
     about --cpu-seconds have passed; scaled to tokens/s of the full problem."""
@@ -481,6 +542,7 @@ def main():
     ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--index-workload", default="index_n8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -524,6 +586,8 @@ def main():
         out["selection"] = bench_selection(args, dev, stream, inputs)
     if not args.no_index:
         out["indexer"] = bench_index(args, dev, stream)
+    if not args.no_ceilings:
+        out["ceilings"] = ceilings(dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, inputs)
     print(json.dumps(out), flush=True)
