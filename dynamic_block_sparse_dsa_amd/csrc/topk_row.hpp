@@ -379,8 +379,8 @@ constexpr int BSEL_SCRATCH_WORDS = 2 * 256 + 3 * 16 + 4;
 // places every kept block.  Contains LDS-only barriers: every thread must
 // call it, and global loads the caller has in flight stay in flight.
 template <int R, int NT>
-__device__ __forceinline__ int block_select_topk(const float* srow, int nv, const TopkParams& p, int32_t* out, int kmax,
-                                 uint32_t* scratch) {
+__device__ __forceinline__ int block_select_topk(const float* srow, int nv, const TopkParams& p, int32_t* out,
+                                                 int kmax, uint32_t* scratch) {
   constexpr int NW = NT / 64;
   constexpr int E = 64 * R / NT;  // blocks per thread
   static_assert(E >= 1 && E * NT == 64 * R && NW <= 16, "row split");
