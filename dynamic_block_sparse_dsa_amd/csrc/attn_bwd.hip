@@ -93,32 +93,45 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // ============================================================== 1. row statistics
 // rowstat[bh][i][0][r] = lse * log2(e), rowstat[bh][i][1][r] = rowsum(dO * O)
 // for row i BLK + r of head bh; rows past N (the ragged last block) get zeros.
-// d/8 lanes per row, DPP sums.
+// d/8 lanes per row (cross-lane sums); each thread takes four rows, issuing
+// all their loads before any sum.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ lse, float* __restrict__ rowstat,
                                                        int64_t n_pad_rows, int N, int BLK, int nB) {
-  constexpr int TPR = D / 8, RPW = 256 / TPR;
-  const int64_t prow = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;  // bh * nB BLK + n
+  constexpr int TPR = D / 8, RPP = 256 / TPR;  // lanes per row, rows per pass
+  constexpr int PASSES = 4;                     // rows per thread, all loads issued first
   const int c = threadIdx.x % TPR;
   const int64_t npad = (int64_t)nB * BLK;
-  const int64_t bh = prow / npad;
-  const int n = (int)(prow % npad);
-  const bool real = prow < n_pad_rows && n < N;
-  const int64_t row = bh * N + n;
-  float acc = 0.f;
-  if (real) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(o + row * D + 8 * c);
-    const u32x4 y = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * c);
+  u32x4 x[PASSES], y[PASSES];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
+  for (int k = 0; k < PASSES; ++k) {
+    const int64_t prow = ((int64_t)blockIdx.x * PASSES + k) * RPP + threadIdx.x / TPR;  // bh * nB BLK + n
+    const int64_t bh = prow / npad;
+    const int n = (int)(prow % npad);
+    x[k] = y[k] = (u32x4){0u, 0u, 0u, 0u};
+    if (prow < n_pad_rows && n < N) {
+      const int64_t row = bh * N + n;
+      x[k] = *reinterpret_cast<const u32x4*>(o + row * D + 8 * c);
+      y[k] = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * c);
+    }
   }
 #pragma unroll
-  for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (prow < n_pad_rows && c == 0) {
-    float* st = rowstat + (bh * nB + n / BLK) * 2 * BLK + n % BLK;
-    st[0] = real ? lse[row] * 1.4426950408889634f : 0.f;
-    st[BLK] = acc;
+  for (int k = 0; k < PASSES; ++k) {
+    const int64_t prow = ((int64_t)blockIdx.x * PASSES + k) * RPP + threadIdx.x / TPR;
+    const int64_t bh = prow / npad;
+    const int n = (int)(prow % npad);
+    const bool real = prow < n_pad_rows && n < N;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += bf16_lo(x[k][e]) * bf16_lo(y[k][e]) + bf16_hi(x[k][e]) * bf16_hi(y[k][e]);
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
+    if (prow < n_pad_rows && c == 0) {
+      float* st = rowstat + (bh * nB + n / BLK) * 2 * BLK + n % BLK;
+      st[0] = real ? lse[bh * N + n] * 1.4426950408889634f : 0.f;
+      st[BLK] = acc;
+    }
   }
 }
 
@@ -520,8 +533,8 @@ hipError_t launch_bwd_prep(const uint16_t* o, const uint16_t* dout, const float*
                            int N, int d, int block, int nB, hipStream_t stream) {
   const int64_t n_pad_rows = n_heads * nB * (int64_t)block;
   if (n_pad_rows == 0) return hipSuccess;
-  const int rpw = 256 / (d / 8);
-  const dim3 grid((uint32_t)((n_pad_rows + rpw - 1) / rpw)), blk(256);
+  const int rows_per_wg = 4 * (256 / (d / 8));  // bwd_prep_kernel: 4 passes of 256 / (d / 8) rows
+  const dim3 grid((uint32_t)((n_pad_rows + rows_per_wg - 1) / rows_per_wg)), blk(256);
   if (d == 64)
     hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, blk, 0, stream, o, dout, lse, rowstat, n_pad_rows, N, block, nB);
   else
