@@ -100,6 +100,11 @@ struct WaveAttn {
 
   // q [S, Hq, D]: the group's heads of sequence s
   __device__ __forceinline__ void init(const uint16_t* q, int Hq, int64_t s, int g) {
+    init_rows(q + (s * Hq + g * G) * (int64_t)D, D);
+  }
+
+  // query row of the group's head hh at q0 + hh * head_stride
+  __device__ __forceinline__ void init_rows(const uint16_t* q0, int64_t head_stride) {
     lane = threadIdx.x & 63;
     n = lane & 15;
     lq = lane >> 4;
@@ -111,7 +116,7 @@ struct WaveAttn {
     for (int ks = 0; ks < D / 32; ++ks) {
       qf[ks] = (u32x4){0, 0, 0, 0};
       if (n < G)
-        qf[ks] = *reinterpret_cast<const u32x4*>(q + (s * Hq + g * G + n) * (int64_t)D + ks * 32 + 8 * lq);
+        qf[ks] = *reinterpret_cast<const u32x4*>(q0 + n * head_stride + ks * 32 + 8 * lq);
     }
     m_run = -__builtin_inff();
     l_run = 0.f;

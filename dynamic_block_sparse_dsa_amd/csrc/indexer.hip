@@ -20,12 +20,13 @@
 //   one score (32 consecutive keys of a token per half-wave), causal part
 //   only.  Token tiles run latest first (they have the most key tiles).
 // token_attn_kernel: one wave per (batch, token, KV head), KV-head-major over
-//   XCD-contiguous workgroups (one KV head's rows per XCD L2): lane l gathers the
-//   l-th kept token's key row and computes the logits of the group's query
-//   heads (queries staged in LDS, read as broadcasts); softmax across the
-//   wave; P V streams the kept value rows (each row read by the whole wave,
-//   D / 64 dims per lane), 8 rows in flight.  More than 64 kept tokens are
-//   taken in chunks of 64 with an online softmax.
+//   XCD-contiguous workgroups (one KV head's rows per XCD L2).  The kept
+//   positions arrive 64 at a time (one coalesced load, spread by lane
+//   shuffles); each 32-token chunk gathers its K rows in MFMA A-operand layout
+//   (16 rows x 64 bytes per wave load) and its V rows as 16-byte pieces of
+//   whole rows, two chunks in flight, and runs the decode path's chunk step:
+//   Q K^T on v_mfma_f32_16x16x32_bf16 (kept keys x the group's query heads),
+//   online softmax in fp32, P V in fp32 VALU.
 // select_tokens_fast_kernel: one wave per query-token row of up to 8192
 //   scores.  The row is read in 256-token chunks, lane l holding tokens
 //   4 l .. 4 l + 3 of each (one 16-byte load per lane, 1 KiB per wave
@@ -40,6 +41,7 @@
 //   64 to keep, or more than 128 candidates at or above t0) get cnt = -1 and
 //   are completed by the general one-wave select.
 #include "attn_common.hpp"
+#include "decode_common.hpp"
 #include "topk_row.hpp"
 
 namespace dsa {
@@ -163,17 +165,41 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const uint16_t* __res
 }
 
 // ============================================================== token attention
+// A 32-key chunk of kept tokens: its K rows in this wave's LDS tile (row-major,
+// 16-byte chunks XOR-swizzled by kswz, read back as MFMA A operands) and its V
+// rows in registers (lane owns 8 dims of a key group).
 template <int D, int G>
-__global__ __launch_bounds__(256) void token_attn_kernel(const uint16_t* __restrict__ q,
-                                                         const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ v,
-                                                         const int32_t* __restrict__ idx,
-                                                         const int32_t* __restrict__ cnt, uint16_t* __restrict__ o,
-                                                         float* __restrict__ lse, int Hkv, int N, int kmax,
-                                                         float scale_log2, int64_t n_waves) {
-  constexpr int DPL = D / 64;  // output dims per lane
-  constexpr int QCH = D / 8;   // 16-byte chunks of a row
-  __shared__ __align__(16) uint16_t qs[4][G * D];
+struct GatherChunk {
+  using C = DecCfg<D, G>;
+  const LDS_AS uint16_t* kt;
+  int lane;
+  u32x4 vv[C::VPL];
+  __device__ __forceinline__ u32x4 kfrag(int sb, int ks) const {
+    const int row = sb * 16 + (lane & 15);
+    const int c = (4 * ks + (lane >> 4)) ^ kswz<D>(row);
+    return *reinterpret_cast<const LDS_AS u32x4*>(kt + row * D + c * 8);
+  }
+  __device__ __forceinline__ u32x4 vrow(int v) const { return vv[v]; }
+  __device__ __forceinline__ float kscale(int, int) const { return 1.f; }
+  __device__ __forceinline__ float vscale(int, int) const { return 1.f; }
+};
+
+// Waves per SIMD, as many as fit without spills: 128 VGPRs (four) for small
+// groups, 168 (three) for four heads at d = 128, 256 (two) for eight heads.
+template <int D, int G>
+constexpr int token_attn_waves() { return G <= 2 || (G == 4 && D == 64) ? 4 : G == 4 ? 3 : 2; }
+
+template <int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(token_attn_waves<D, G>())))
+void token_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                       const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
+                       const int32_t* __restrict__ cnt, uint16_t* __restrict__ o, float* __restrict__ lse,
+                       int Hkv, int N, int kmax, float scale_log2, int64_t n_waves) {
+  using C = DecCfg<D, G>;
+  constexpr int CH = D / 8, RPI = 64 / CH, NL = C::CK / RPI;  // lanes per row, rows per DMA, DMAs per chunk
+  __shared__ __align__(1024) uint16_t ktile[4][C::CK * D];
+  __shared__ float pbuf[4][C::CK][G];
+  __shared__ float abuf[4][G];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // KV-head-major over XCD-contiguous workgroup ranges: the waves of one XCD
@@ -186,98 +212,81 @@ __global__ __launch_bounds__(256) void token_attn_kernel(const uint16_t* __restr
   const int t = (int)(bt % N);
   const int64_t b = bt / N;
   const int Hq = Hkv * G;
-  const int n = min(max(cnt[bt], 0), kmax);
+  const int nk = min(max(cnt[bt], 0), kmax);
   const int32_t* row = idx + bt * kmax;
-  const int64_t kvh = (b * Hkv + g) * (int64_t)N;
+  const uint16_t* kb = k + (b * Hkv + g) * (int64_t)N * D;
+  const uint16_t* vb = v + (b * Hkv + g) * (int64_t)N * D;
+  const LDS_AS uint16_t* kt = (const LDS_AS uint16_t*)(ktile[wave]);
+  const uint32_t kt_base = (uint32_t)(uintptr_t)kt;
 
-  // the group's query rows -> LDS (G D bf16, 16 bytes per lane per step)
-  for (int c = lane; c < G * QCH; c += 64) {
-    const int hh = c / QCH, ch = c % QCH;
-    *reinterpret_cast<u32x4*>(&qs[wave][hh * D + ch * 8]) =
-        *reinterpret_cast<const u32x4*>(q + ((b * Hq + g * G + hh) * (int64_t)N + t) * D + ch * 8);
+  WaveAttn<D, G> wa;
+  wa.init_rows(q + ((b * Hq + g * G) * (int64_t)N + t) * D, (int64_t)N * D);
+
+  // kept positions base .. base + 63, one per lane; positions past nk repeat
+  // the last kept token (a finite row whose weight the step masks to 0)
+  auto ids = [&](int base) {
+    const int p = min(base + lane, nk - 1);
+    return min(max(row[p], 0), N - 1);
+  };
+  // chunk cc (0 or 1) of the 64 positions in iv.  K: each DMA brings RPI whole
+  // rows (CH consecutive lanes per row, so every request covers full cache
+  // lines), lane l landing in slot l of the tile; V: 16-byte pieces of rows.
+  auto gather = [&](GatherChunk<D, G>& r, int iv, int cc) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int rr = i * RPI + lane / CH;
+      const int key = __shfl(iv, 32 * cc + rr, 64);
+      const int c = (lane % CH) ^ kswz<D>(rr);
+      dma16(kb, (uint32_t)(key * D + c * 8) * 2u, __builtin_amdgcn_readfirstlane(kt_base + i * 1024));
+    }
+#pragma unroll
+    for (int vi = 0; vi < C::VPL; ++vi) {
+      const int key = __shfl(iv, 32 * cc + wa.pk + C::KGR * vi, 64);
+      r.vv[vi] = *reinterpret_cast<const u32x4*>(vb + (int64_t)key * D + wa.pc * 8);
+    }
+  };
+
+  // one 32-key chunk at a time (a second tile and register set would cost
+  // more waves per SIMD than it hides)
+  const int nch = (nk + C::CK - 1) / C::CK;
+  GatherChunk<D, G> r;
+  r.kt = kt;
+  r.lane = lane;
+  int iv = 0;
+  for (int c = 0; c < nch; ++c) {
+    if ((c & 1) == 0) iv = ids(c * C::CK);
+    gather(r, iv, c & 1);
+    wait_vm<C::VPL>();  // the K DMAs (issued before the V loads) have landed
+    wa.step(r, c * C::CK, nk, scale_log2, pbuf[wave], abuf[wave]);
   }
-  wave_lds_sync();
 
-  float m[G], l[G], acc[G][DPL];
+  // sum the key groups: every lane of a dim slice ends with the totals
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = wa.acc[hh][e];
+#pragma unroll
+      for (int off = C::CHK; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+      wa.acc[hh][e] = x;
+    }
+  // O = acc / l (bf16), LSE = (m + log2 l) ln 2; head hh's state is in lane hh
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    m[hh] = -__builtin_inff();
-    l[hh] = 0.f;
+    const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wa.l_run), hh));
+    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wa.m_run), hh));
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (wa.pk == 0) {
+      u32x4 pkd;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.f;
-  }
-  for (int c0 = 0; c0 < n; c0 += 64) {
-    const int e = c0 + lane;
-    const bool ok = e < n;
-    const int s = ok ? min(max(row[e], 0), N - 1) : 0;
-    const uint16_t* krow = k + (kvh + s) * D;
-    float x[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) x[hh] = 0.f;
-#pragma unroll 4
-    for (int ch = 0; ch < QCH; ++ch) {
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + ch * 8);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const u32x4 qv = *reinterpret_cast<const u32x4*>(&qs[wave][hh * D + ch * 8]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          x[hh] = __builtin_fmaf(bf16_lo(qv[j]), bf16_lo(kv[j]), __builtin_fmaf(bf16_hi(qv[j]), bf16_hi(kv[j]), x[hh]));
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_t h2 = {(__bf16)(wa.acc[hh][2 * e] * inv), (__bf16)(wa.acc[hh][2 * e + 1] * inv)};
+        pkd[e] = __builtin_bit_cast(uint32_t, h2);
       }
-    }
-    float p[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float xl = ok ? x[hh] * scale_log2 : -__builtin_inff();
-      const float mn = fmaxf(m[hh], wave_max_f32(xl));
-      const float corr = __builtin_amdgcn_exp2f(m[hh] - mn);
-      p[hh] = ok ? __builtin_amdgcn_exp2f(xl - mn) : 0.f;
-      l[hh] = l[hh] * corr + wave_sum_f32(p[hh]);
-#pragma unroll
-      for (int e2 = 0; e2 < DPL; ++e2) acc[hh][e2] *= corr;
-      m[hh] = mn;
-    }
-    // P V: the chunk's kept rows, 8 in flight
-    const int nc = min(64, n - c0);
-    for (int j0 = 0; j0 < nc; j0 += 8) {
-      uint32_t vv[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int j = min(j0 + jj, nc - 1);
-        const int sj = __builtin_amdgcn_readlane(s, j);
-        const uint16_t* vrow = v + (kvh + sj) * D + lane * DPL;
-        vv[jj] = DPL == 2 ? *reinterpret_cast<const uint32_t*>(vrow) : (uint32_t)(*vrow) << 16;
-      }
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        if (j0 + jj >= nc) break;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[hh]), j0 + jj));
-          if constexpr (DPL == 2) {
-            acc[hh][0] = __builtin_fmaf(pj, bf16_lo(vv[jj]), acc[hh][0]);
-            acc[hh][1] = __builtin_fmaf(pj, bf16_hi(vv[jj]), acc[hh][1]);
-          } else {
-            acc[hh][0] = __builtin_fmaf(pj, bf16_hi(vv[jj]), acc[hh][0]);
-          }
-        }
-      }
-    }
-  }
-  // O = acc / l (bf16), LSE = (m + log2 l) ln 2
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const float inv = l[hh] > 0.f ? 1.f / l[hh] : 0.f;
-    uint16_t* orow = o + ((b * Hq + g * G + hh) * (int64_t)N + t) * D + lane * DPL;
-    if constexpr (DPL == 2) {
-      const bf16x2_t pk = {(__bf16)(acc[hh][0] * inv), (__bf16)(acc[hh][1] * inv)};
-      *reinterpret_cast<bf16x2_t*>(orow) = pk;
-    } else {
-      *reinterpret_cast<__bf16*>(orow) = (__bf16)(acc[hh][0] * inv);
+      *reinterpret_cast<u32x4*>(o + ((b * Hq + g * G + hh) * (int64_t)N + t) * D + wa.pc * 8) = pkd;
     }
     if (lse && lane == 0)
-      lse[(b * Hq + g * G + hh) * (int64_t)N + t] =
-          l[hh] > 0.f ? (m[hh] + __log2f(l[hh])) * 0.6931471805599453f : -__builtin_inff();
+      lse[(b * Hq + g * G + hh) * (int64_t)N + t] = l > 0.f ? (m + __log2f(l)) * 0.6931471805599453f : -__builtin_inff();
   }
 }
 
@@ -415,13 +424,13 @@ hipError_t launch_index_scores(const uint16_t* qi, const uint16_t* ki, const flo
 
 template <int D>
 static hipError_t launch_token_attn_d(const TokenAttnArgs& a, hipStream_t stream) {
-  const int G = a.Hq / a.Hkv;
   const int64_t n_waves = (int64_t)a.B * a.N * a.Hkv;
+  if (n_waves == 0) return hipSuccess;
   const dim3 grid((uint32_t)((n_waves + 3) / 4)), blk(256);
 #define DSA_TOKEN_ATTN(GG)                                                                                          \
   hipLaunchKernelGGL((token_attn_kernel<D, GG>), grid, blk, 0, stream, a.q, a.k, a.v, a.idx, a.cnt, a.o, a.lse, a.Hkv, \
                      a.N, a.kmax, a.scale_log2, n_waves)
-  switch (G) {
+  switch (a.Hq / a.Hkv) {
     case 1: DSA_TOKEN_ATTN(1); break;
     case 2: DSA_TOKEN_ATTN(2); break;
     case 4: DSA_TOKEN_ATTN(4); break;
