@@ -6,8 +6,9 @@ Bars: scores (fp32 sums of bf16 products) within 1e-4 relative of the
 oracle's plus 1e-4 of the row's largest magnitude; selections as for the
 block path (bit-exact except in near-tie rows, where the GPU's set must be
 an accepted one); attention over the GPU's sets within max-abs 2e-2,
-mean-abs 2e-3 and LSE 1e-3 (it runs in fp32, so the observed error is the
-bf16 rounding of O).
+mean-abs 2e-3 and LSE 1e-3 (logits are fp32 sums of exact bf16 products on
+the matrix cores, the softmax and P V run in fp32, so the observed error is
+mostly the bf16 rounding of O).
 """
 
 import math
