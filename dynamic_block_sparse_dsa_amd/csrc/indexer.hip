@@ -70,6 +70,12 @@ __device__ __forceinline__ u32x4 key_frag(const LDS_AS uint16_t* tile, int r, in
 
 }  // namespace
 
+// ReLU on the bit pattern: negative floats (and -0) have the sign bit set,
+// so an integer max with 0 gives +0 for them and leaves the rest unchanged
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // ============================================================== index scores
 template <int DI>
 __global__ __launch_bounds__(256) void index_scores_kernel(const uint16_t* __restrict__ qi,
@@ -152,8 +158,8 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const uint16_t* __res
         float p0 = 0.f, p1 = 0.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          p0 = __builtin_fmaf(fmaxf(acc[rt][ct][r], 0.f), wr[ct][r], p0);
-          p1 = __builtin_fmaf(fmaxf(acc[rt][ct][8 + r], 0.f), wr[ct][8 + r], p1);
+          p0 = __builtin_fmaf(relu_bits(acc[rt][ct][r]), wr[ct][r], p0);
+          p1 = __builtin_fmaf(relu_bits(acc[rt][ct][8 + r]), wr[ct][8 + r], p1);
         }
         const float give = half ? p0 : p1, keep = half ? p1 : p0;
         const float sum = keep + __shfl_xor(give, 32, 64);
