@@ -147,3 +147,39 @@ def test_all_tied_scores_take_the_lowest_positions(cuda_device):
         for t in (0, 70, 2999):
             check_out(np64(o[0, h, t])[None], o_ref[0, h, t][None], np64(lse[0, h, t]).reshape(1),
                       lse_ref[0, h, t].reshape(1), f"tied h{h} t{t}")
+
+
+def test_token_attention_on_given_rows(cuda_device):
+    """dsa_token_attn_fwd on index rows written here rather than by the
+    selection: counts 0, 1, 2, 63, 64, 65, 127, 128, 129 and 150 (so rows
+    span up to three 64-position groups and five 32-token chunks),
+    positions in any order and with repeats.  Rows with a count checked
+    against the oracle; empty rows give O = 0 and LSE = -inf (the empty
+    sequence of the paged decode follows the same convention)."""
+    w = IndexWorkload("h", 1, 8, 2, 300, 128, 16, 64, 150, seed=69)
+    qi, ki, wi, q, k, v = make_index(w, device=cuda_device)
+    shape = dsa.make_index_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_index_heads,
+                                 w.index_dim, w.topk, 3)
+    km = dsa.dsa_index_kmax(shape)
+    assert km == 150
+    N = w.seq_len
+    rng = np.random.default_rng(70)
+    counts = [0, 1, 2, 63, 64, 65, 127, 128, 129, 150]
+    idx = np.full((1, N, km), -1, dtype=np.int32)
+    cnt = np.zeros((1, N), dtype=np.int32)
+    for t in range(N):
+        c = counts[t % len(counts)]
+        cnt[0, t] = c
+        idx[0, t, :c] = rng.integers(0, t + 1, size=c)  # with replacement: repeats at small t
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, w.n_q_heads, N), float("nan"), dtype=torch.float32, device=cuda_device)
+    dsa.dsa_token_attn_fwd(shape, q, k, v, torch.from_numpy(idx).to(cuda_device),
+                           torch.from_numpy(cnt).to(cuda_device), o, lse)
+    torch.cuda.synchronize()
+    go, gl = np64(o), np64(lse)
+    empty = cnt[0] == 0
+    assert (go[0][:, empty] == 0).all() and np.isneginf(gl[0][:, empty]).all()
+    rows = [t for t in range(N) if cnt[0, t] > 0]
+    units = [(0, h, t) for h in range(w.n_q_heads) for t in rows]
+    o_ref, lse_ref = O.token_attend(np64(q), np64(k), np64(v), idx, cnt, units=units)
+    check_out(go[0][:, rows], o_ref[0][:, rows], gl[0][:, rows], lse_ref[0][:, rows], "given rows")
