@@ -331,7 +331,8 @@ int dsa_index_scores(const dsa_index_shape* shape, const void* qi, const void* k
 int dsa_select_tokens(const dsa_index_shape* shape, const float* scores, int32_t* idx, int32_t* cnt, void* stream);
 
 /* Attention of every head over its token's kept tokens.  idx entries are
- * read for the first cnt of each row and must be positions <= t. */
+ * read for the first cnt of each row and must be positions <= t (repeats
+ * count once per occurrence).  A row with cnt = 0 gives O = 0 and LSE = -inf. */
 int dsa_token_attn_fwd(const dsa_index_shape* shape, const void* q, const void* k, const void* v, const int32_t* idx,
                        const int32_t* cnt, void* o, float* lse, void* stream);
 
