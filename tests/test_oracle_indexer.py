@@ -137,3 +137,22 @@ def test_planted_clusters_are_found():
     align = ki[0, kept] @ qdir / np.linalg.norm(qdir)
     everyone = ki[0, : t + 1] @ qdir / np.linalg.norm(qdir)
     assert np.median(align) > np.percentile(everyone, 90)
+
+
+def test_a_repeated_position_counts_once_per_occurrence():
+    """idx rows may repeat a position: token a listed twice with token b
+    weighs like a with ln 2 added to its logit, written out here:
+    w_a = 2 e^A / (2 e^A + e^B), LSE = ln(2 e^A + e^B)."""
+    N, d = 9, 8
+    q, k, v = rnd((1, 1, N, d), 21), rnd((1, 1, N, d), 22), rnd((1, 1, N, d), 23)
+    s = 1.0 / math.sqrt(d)
+    t, a, b = 7, 2, 5
+    idx = np.full((1, N, 3), -1, dtype=np.int32)
+    cnt = np.zeros((1, N), dtype=np.int32)
+    idx[0, t] = [a, b, a]
+    cnt[0, t] = 3
+    o, lse = O.token_attend(q, k, v, idx, cnt, units=[(0, 0, t)])
+    A, B = s * q[0, 0, t] @ k[0, 0, a], s * q[0, 0, t] @ k[0, 0, b]
+    Z = 2 * math.exp(A) + math.exp(B)
+    np.testing.assert_allclose(o[0, 0, t], (2 * math.exp(A) * v[0, 0, a] + math.exp(B) * v[0, 0, b]) / Z, rtol=1e-12)
+    assert lse[0, 0, t] == pytest.approx(math.log(Z), rel=1e-13)
