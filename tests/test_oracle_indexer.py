@@ -5,8 +5,9 @@ Checked against: a different order of the same arithmetic where the ReLU is
 inactive (sum the weighted heads first, one library matmul after), a closed
 form where it is active (a head pair x, -x gives |x . k|), an invariant
 (future tokens never change a row), the dense special case (every token
-kept equals causal SDPA from torch), closed forms for one and two kept tokens,
-and brute-force subsets for the selection.  Runs on the CPU.
+kept equals causal SDPA from torch), closed forms for one and two kept tokens
+and for a repeated kept position, and brute-force subsets for the selection.
+Runs on the CPU.
 """
 
 import itertools
