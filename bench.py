@@ -9,7 +9,10 @@ bf16 MFMA peak using its algorithmic FLOPs (4*b*b*d per executed tile) over
 its average launch time from HIP events on the stream it runs on.  `decode`
 reports a single-token decode step of 32 sequences against the HBM peak.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
-prefill workload.
+prefill workload.  The headline workload is the 131 072-token prefill (the
+largest configuration); the 8 192-token and the grouped-query 32 768-token
+prefills are reported beside it under `prefill_workloads`.  Every timed
+prefill launch follows a 512 MiB read that evicts the last-level cache.
 """
 
 import argparse
@@ -51,22 +54,6 @@ def measured_traffic(workload, kernel_src):
     return t.get("bytes_per_launch")
 
 
-def launch_stats(fn, n, stream, before=None):
-    """Per-launch times (us) of n launches, each bracketed by its own HIP
-    events on `stream` (`before`, if given, runs untimed before each):
-    median, min and 90th percentile."""
-    import statistics
-
-    t = []
-    for _ in range(n):
-        if before is not None:
-            before()
-        t.append(time_events(fn, 1, stream) * 1e3)
-    t.sort()
-    return dict(median=round(statistics.median(t), 2), min=round(t[0], 2),
-                p90=round(t[min(len(t) - 1, int(0.9 * len(t)))], 2), n=n)
-
-
 def time_events(fn, n, stream):
     import torch
 
@@ -79,18 +66,41 @@ def time_events(fn, n, stream):
     return a.elapsed_time(b) / n  # ms per launch
 
 
-def bench_prefill(args, dev, stream):
+def read_flush(flush, stream):
+    """Evict the last-level cache by reading a buffer twice its size (a
+    write-based flush would leave dirty lines whose write-back is charged to
+    the next timed launch)."""
+    import torch
+
+    with torch.cuda.stream(stream):
+        flush.sum()
+
+
+def stats_us(t):
+    """median, min and 90th percentile of a list of times in us."""
+    import statistics
+
+    t = sorted(t)
+    return dict(median=round(statistics.median(t), 2), min=round(t[0], 2),
+                p90=round(t[min(len(t) - 1, int(0.9 * len(t)))], 2), n=len(t))
+
+
+def bench_prefill(args, dev, stream, flush, wname, n_steps):
+    """One prefill workload: the fused step (dsa_prefill: block means, block
+    scores, top-k, attention) timed alone n_steps times with HIP events after
+    a read-based cache flush each, then the attention kernel alone, also
+    flushed before each launch."""
     import torch
 
     import dynamic_block_sparse_dsa_amd as dsa
     from dynamic_block_sparse_dsa_amd import work
     from dynamic_block_sparse_dsa_amd.inputs import WORKLOADS, make_prefill
 
-    w = WORKLOADS[args.workload]
+    w = WORKLOADS[wname]
     q, k, v = make_prefill(w, device=dev)
     B, Hq, Hkv, N, d, nB = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_blocks
     shape = dsa.make_shape(B, Hq, Hkv, N, d, w.block, w.topk, w.topk_num, w.topk_den)
-    km = dsa.dsa_prefill_kmax(shape)
+    km = dsa.dsa_kmax(shape)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     idx = torch.empty((B, Hkv, nB, km), dtype=torch.int32, device=dev)
@@ -103,13 +113,11 @@ def bench_prefill(args, dev, stream):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    steps_us = []
+    for _ in range(n_steps):
+        read_flush(flush, stream)
+        steps_us.append(time_events(step, 1, stream) * 1e3)
+    ms_step = sum(steps_us) / len(steps_us) * 1e-3
 
     # the dominant kernel alone, same inputs and indices, HIP events on its stream
     def attn():
@@ -117,27 +125,32 @@ def bench_prefill(args, dev, stream):
 
     for _ in range(args.warmup):
         attn()
-    ms_attn = time_events(attn, args.steps, stream)
-    attn_stats = launch_stats(attn, max(args.steps, 50), stream)
-    flops = work.prefill_flops(cnt.cpu().numpy(), w.group, w.block, d)
+    attn_us = []
+    for _ in range(max(n_steps, 20)):
+        read_flush(flush, stream)
+        attn_us.append(time_events(attn, 1, stream) * 1e3)
+    ms_attn = sum(attn_us) / len(attn_us) * 1e-3
+    cnt_h = cnt.cpu().numpy()
+    flops = work.prefill_flops(cnt_h, w.group, w.block, d)
     tflops = flops / (ms_attn * 1e-3) / 1e12
-    tiles = work.prefill_tiles(cnt.cpu().numpy(), w.group)
+    tiles = work.prefill_tiles(cnt_h, w.group)
     traffic = measured_traffic(w.name, ATTN_SRC)
     res = dict(
         ms_per_step=ms_step,
+        step_us=stats_us(steps_us),
         value=B * N / (ms_step * 1e-3),
         config=dict(workload=w.name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, seq_len=N, head_dim=d, block=w.block,
                     topk=w.topk, topk_num=w.topk_num, topk_den=w.topk_den, structure=w.structure),
         roofline=dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                       frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel="sparse_attn_fwd_kernel",
-                      avg_launch_us=round(ms_attn * 1e3, 2), launch_us=attn_stats, flops_per_launch=flops,
+                      avg_launch_us=round(ms_attn * 1e3, 2), launch_us=stats_us(attn_us), flops_per_launch=flops,
                       executed_tiles=tiles,
                       step_frac=round(flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)),
     )
     return res, (q, k, v, w)
 
 
-def bench_decode(args, dev, stream):
+def bench_decode(args, dev, stream, flush):
     import torch
 
     import dynamic_block_sparse_dsa_amd as dsa
@@ -148,16 +161,13 @@ def bench_decode(args, dev, stream):
     q, kc, vc = make_decode(w, device=dev)
     S, Hq, Hkv, L, d, nB = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_blocks
     shape = dsa.make_shape(S, Hq, Hkv, L, d, w.block, w.topk, w.topk_num, w.topk_den)
-    km = dsa.dsa_decode_kmax(shape)
+    km = dsa.dsa_kmax(shape)
     kbar = torch.empty((S, Hkv, nB, d), dtype=torch.float32, device=dev)
     dsa.dsa_kv_block_means(shape, kc, kbar, stream=stream)  # cache-time work, outside the step
     o = torch.empty_like(q)
     lse = torch.empty((S, Hq), dtype=torch.float32, device=dev)
     idx = torch.empty((S, Hkv, km), dtype=torch.int32, device=dev)
     ws = torch.empty(dsa.dsa_decode_workspace_bytes(shape), dtype=torch.uint8, device=dev)
-    # 512 MiB, twice the last-level cache.  Flushed by reading it: a write-based
-    # flush leaves dirty lines whose write-back would be charged to the step.
-    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def step():
@@ -166,20 +176,12 @@ def bench_decode(args, dev, stream):
     for _ in range(args.warmup):
         step()
     # each step timed alone with events, the cache flushed in between
-    def flush_cache():
-        with torch.cuda.stream(stream):
-            flush.sum()
-
-    tot = 0.0
     steps_us = []
     for _ in range(args.steps):
-        flush_cache()
+        read_flush(flush, stream)
         steps_us.append(time_events(step, 1, stream) * 1e3)
-        tot += steps_us[-1] * 1e-3
-    ms = tot / args.steps
-    steps_us.sort()
-    step_stats = dict(median=round(steps_us[len(steps_us) // 2], 2), min=round(steps_us[0], 2),
-                      p90=round(steps_us[min(len(steps_us) - 1, int(0.9 * len(steps_us)))], 2), n=len(steps_us))
+    ms = sum(steps_us) / len(steps_us) * 1e-3
+    step_stats = stats_us(steps_us)
     nbytes = work.decode_bytes(S, Hq, Hkv, L, d, w.block, km)
     gbs = nbytes / (ms * 1e-3) / 1e9
     args._decode_inputs = (q, kc, vc, w, flush)  # reused by the paged bench
@@ -219,7 +221,7 @@ def bench_paged(args, dev, stream):
     vp[flat] = vc.view(S, Hkv, mb, b, d).permute(0, 2, 1, 3, 4).reshape(S * mb, Hkv, b, d)
     kbar = torch.zeros((n_pages, Hkv, d), dtype=torch.float32, device=dev)
     shape = dsa.make_shape(S, Hq, Hkv, mb * b, d, b, w.topk, w.topk_num, w.topk_den)
-    km = dsa.dsa_decode_kmax(shape)
+    km = dsa.dsa_kmax(shape)
     o = torch.empty_like(q)
     lse = torch.empty((S, Hq), dtype=torch.float32, device=dev)
     idx = torch.empty((S, Hkv, km), dtype=torch.int32, device=dev)
@@ -363,13 +365,13 @@ def bench_selection(args, dev, stream, inputs):
     sc = torch.empty((B, Hkv, nB, nB), dtype=torch.float32, device=dev)
     dsa.dsa_block_means(base, Hq, q, qbar, stream=stream)
     dsa.dsa_block_means(base, Hkv, k, kbar, stream=stream)
-    dsa.dsa_block_scores(base, qbar, kbar, sc, stream=stream)
+    dsa.dsa_block_scores_from_means(base, qbar, kbar, sc, stream=stream)
     rows = B * Hkv * nB
     out = {}
     for name, sel in SELECT_VARIANTS:
         topk = w.topk if not sel.get("select_mode") else 0
         shape = dsa.make_shape(B, Hq, Hkv, N, d, w.block, topk, w.topk_num, w.topk_den, **sel)
-        km = dsa.dsa_prefill_kmax(shape)
+        km = dsa.dsa_kmax(shape)
         idx = torch.empty((B, Hkv, nB, km), dtype=torch.int32, device=dev)
         cnt = torch.empty((B, Hkv, nB), dtype=torch.int32, device=dev)
 
@@ -507,31 +509,53 @@ def ceilings(dev, stream):
 
 
 def cpu_baseline(args, inputs):
-    """The oracle, as it stands, on whole heads of the prefill workload until
-    about --cpu-seconds have passed; scaled to tokens/s of the full problem."""
+    """The oracle, as it stands, on a seeded sample of the prefill workload,
+    with as many BLAS threads as the process has host cores.  For sampled KV
+    groups it runs the whole selection (block means, block scores, top-k) and
+    for sampled query blocks (drawn uniformly over heads and blocks) the
+    attention, each timed; the time of the full problem is extrapolated as
+    groups x selection time per group + query blocks x attention time per
+    block.  Host copies and the fp64 upcast of the inputs are not timed."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle as O
 
     q, k, v, w = inputs
-    G = w.group
-    done = 0
+    G, nB = w.group, w.n_blocks
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(12345)
+    groups = [int(x) for x in rng.permutation(w.n_kv_heads)][:2]
+    t_sel, t_att, n_att = 0.0, 0.0, 0
     t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        for g in range(w.n_kv_heads):
+    with threadpool_limits(limits=cores):
+        for n, g in enumerate(groups):
             qn = q[:, g * G : (g + 1) * G].float().cpu().numpy().astype(np.float64)
             kn = k[:, g : g + 1].float().cpu().numpy().astype(np.float64)
             vn = v[:, g : g + 1].float().cpu().numpy().astype(np.float64)
-            O.prefill(qn, kn, vn, w.block, w.topk, w.topk_num, w.topk_den)
-            done += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-    el = time.perf_counter() - t0
-    frac = done / w.n_kv_heads
-    return dict(value=w.batch * w.seq_len * frac / el, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{done} of {w.n_kv_heads} KV-head groups of {w.name} (all {w.seq_len} rows each: pool, "
-                       f"score, select, attend), {el:.1f} s, 1 thread")
+            s0 = time.perf_counter()
+            qbar, kbar = O.block_means(qn, w.block), O.block_means(kn, w.block)
+            sc = O.block_scores(qbar, kbar, 1.0 / (w.head_dim ** 0.5))
+            idx, cnt, _ = O.select_topk(sc, w.topk, w.topk_num, w.topk_den)
+            t_sel += time.perf_counter() - s0
+            # attention of query blocks of this group until its share of the budget is spent
+            deadline = t0 + args.cpu_seconds * (n + 1) / len(groups)
+            while True:
+                hh, i = int(rng.integers(G)), int(rng.integers(nB))
+                s0 = time.perf_counter()
+                O.attend(qn[:, hh : hh + 1], kn, vn, idx, cnt, w.block, units=[(0, 0, i)])
+                t_att += time.perf_counter() - s0
+                n_att += 1
+                if time.perf_counter() >= deadline:
+                    break
+    n_sel = len(groups)
+    blocks_total = w.batch * w.n_q_heads * nB
+    t_full = w.batch * w.n_kv_heads * (t_sel / n_sel) + blocks_total * (t_att / max(n_att, 1))
+    return dict(value=round(w.batch * w.seq_len / t_full, 2), unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{w.name}: selection (block means, scores, top-k) of {n_sel} of {w.batch * w.n_kv_heads} KV "
+                       f"groups ({t_sel:.1f} s), attention of {n_att} of {blocks_total} query blocks drawn uniformly, "
+                       f"seed 12345 ({t_att:.1f} s); extrapolated full-problem time {t_full:.0f} s; "
+                       f"{cores} BLAS threads")
 
 
 def main():
@@ -539,7 +563,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill_n8192_h32")
+    ap.add_argument("--workload", default="prefill_n131072_b128")
+    ap.add_argument("--extra-workloads", default="prefill_n8192_h32,prefill_gqa_n32768",
+                    help="comma-separated prefill workloads reported beside the headline ('' for none)")
     ap.add_argument("--decode-workload", default="decode_s32_l65536")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
@@ -549,7 +575,7 @@ def main():
     ap.add_argument("--index-workload", default="index_n8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -564,7 +590,9 @@ def main():
     dsa.load()
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
-    pre, inputs = bench_prefill(args, dev, stream)
+    # 512 MiB, twice the last-level cache, read between timed launches
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    pre, inputs = bench_prefill(args, dev, stream, flush, args.workload, args.steps)
     out = {
         "metric": METRIC,
         "value": round(pre["value"], 1),
@@ -573,6 +601,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(pre["ms_per_step"], 4),
+        "step_us": pre["step_us"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -581,8 +610,17 @@ def main():
         "config": pre["config"],
         "roofline": pre["roofline"],
     }
+    extra = [x for x in args.extra_workloads.split(",") if x and x != args.workload]
+    if extra:
+        out["prefill_workloads"] = {}
+        for name in extra:
+            r, _ = bench_prefill(args, dev, stream, flush, name, args.steps)
+            out["prefill_workloads"][name] = dict(value=round(r["value"], 1), unit="tokens/s",
+                                                  ms_per_step=round(r["ms_per_step"], 4), step_us=r["step_us"],
+                                                  config=r["config"], roofline=r["roofline"])
+            torch.cuda.empty_cache()
     if not args.no_decode:
-        out["decode"] = bench_decode(args, dev, stream)
+        out["decode"] = bench_decode(args, dev, stream, flush)
         if not args.no_paged:
             out["paged_decode"] = bench_paged(args, dev, stream)
         del args._decode_inputs

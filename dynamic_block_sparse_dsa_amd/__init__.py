@@ -30,10 +30,12 @@ MAX_BLOCKS = 4096
 DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4, -5
 
 EXPORTS = [
+    "dsa_kmax",
     "dsa_prefill_kmax",
     "dsa_decode_kmax",
     "dsa_block_means",
     "dsa_block_scores",
+    "dsa_block_scores_from_means",
     "dsa_select_topk",
     "dsa_indices_to_bitmap",
     "dsa_index_kmax",
@@ -137,10 +139,12 @@ def load() -> ctypes.CDLL:
     P, S, I32, SZ = ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_size_t
     X = ctypes.POINTER(IndexShape)
     sig = {
+        "dsa_kmax": ([S], ctypes.c_int32),
         "dsa_prefill_kmax": ([S, ctypes.POINTER(I32)], ctypes.c_int),
         "dsa_decode_kmax": ([S, ctypes.POINTER(I32)], ctypes.c_int),
         "dsa_block_means": ([S, I32, P, P, P], ctypes.c_int),
         "dsa_block_scores": ([S, P, P, P, P], ctypes.c_int),
+        "dsa_block_scores_from_means": ([S, P, P, P, P], ctypes.c_int),
         "dsa_select_topk": ([S, P, P, P, P], ctypes.c_int),
         "dsa_indices_to_bitmap": ([P, P, ctypes.c_int64, I32, I32, P, P], ctypes.c_int),
         "dsa_index_kmax": ([X, ctypes.POINTER(I32)], ctypes.c_int),
@@ -224,6 +228,10 @@ def _key(shape: Shape):
 def _query(name: str, key):
     s = Shape(*key)
     lib = load()
+    if name == "dsa_kmax":
+        rc = int(lib.dsa_kmax(ctypes.byref(s)))
+        _check(min(rc, 0))
+        return rc
     if name.endswith("kmax"):
         out = ctypes.c_int32(0)
         _check(getattr(lib, name)(ctypes.byref(s), ctypes.byref(out)))
@@ -232,6 +240,11 @@ def _query(name: str, key):
 
 
 # ----------------------------------------------------------------- C ABI mirrors
+def dsa_kmax(shape: Shape) -> int:
+    """Index width (last dimension of idx) of a prefill or decode of this shape."""
+    return _query("dsa_kmax", _key(shape))
+
+
 def dsa_prefill_kmax(shape: Shape) -> int:
     return _query("dsa_prefill_kmax", _key(shape))
 
@@ -246,11 +259,19 @@ def dsa_block_means(shape: Shape, n_heads: int, x, xbar, stream=None):
                                   _ptr(xbar, torch.float32, (B, n_heads, nB, d), "xbar"), _stream(stream)))
 
 
-def dsa_block_scores(shape: Shape, qbar, kbar, scores, stream=None):
-    B, Hq, Hkv, d, nB = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_blocks
-    _check(load().dsa_block_scores(ctypes.byref(shape), _ptr(qbar, torch.float32, (B, Hq, nB, d), "qbar"),
-                                   _ptr(kbar, torch.float32, (B, Hkv, nB, d), "kbar"),
+def dsa_block_scores(shape: Shape, q, k, scores, stream=None):
+    B, Hq, Hkv, N, d, nB = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_len, shape.head_dim, shape.n_blocks
+    _check(load().dsa_block_scores(ctypes.byref(shape), _ptr(q, torch.bfloat16, (B, Hq, N, d), "q"),
+                                   _ptr(k, torch.bfloat16, (B, Hkv, N, d), "k"),
                                    _ptr(scores, torch.float32, (B, Hkv, nB, nB), "scores"), _stream(stream)))
+
+
+def dsa_block_scores_from_means(shape: Shape, qbar, kbar, scores, stream=None):
+    B, Hq, Hkv, d, nB = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_blocks
+    _check(load().dsa_block_scores_from_means(ctypes.byref(shape), _ptr(qbar, torch.float32, (B, Hq, nB, d), "qbar"),
+                                              _ptr(kbar, torch.float32, (B, Hkv, nB, d), "kbar"),
+                                              _ptr(scores, torch.float32, (B, Hkv, nB, nB), "scores"),
+                                              _stream(stream)))
 
 
 def dsa_select_topk(shape: Shape, scores, idx, cnt, stream=None):

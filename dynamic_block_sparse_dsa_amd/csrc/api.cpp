@@ -196,6 +196,13 @@ int dsa_prefill_kmax(const dsa_shape* s, int32_t* kmax) {
   return DSA_OK;
 }
 
+int32_t dsa_kmax(const dsa_shape* s) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  g_err[0] = 0;
+  return s->seq_len > 0 ? row_budget(s, (int)n_blocks(s)) : 0;
+}
+
 int dsa_decode_kmax(const dsa_shape* s, int32_t* kmax) {
   int rc = check_decode(s);
   if (rc) return rc;
@@ -224,7 +231,8 @@ int dsa_kv_block_means(const dsa_shape* s, const void* k_cache, float* kbar, voi
   return dsa_block_means(s, s->n_kv_heads, k_cache, kbar, stream);
 }
 
-int dsa_block_scores(const dsa_shape* s, const float* qbar, const float* kbar, float* scores, void* stream) {
+int dsa_block_scores_from_means(const dsa_shape* s, const float* qbar, const float* kbar, float* scores,
+                                void* stream) {
   int rc = check_shape(s);
   if (rc) return rc;
   if (empty_prefill(s)) return DSA_OK;
@@ -233,6 +241,19 @@ int dsa_block_scores(const dsa_shape* s, const float* qbar, const float* kbar, f
                                           s->head_dim, 1.0f / sqrtf((float)s->head_dim),
                                           static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "block_scores launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_block_scores(const dsa_shape* s, const void* q, const void* k, float* scores, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (empty_prefill(s)) return DSA_OK;
+  if (!q || !k || !scores) return fail(DSA_ERR_NULL, "q, k or scores is NULL");
+  hipError_t e = dsa::launch_pooled_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), scores,
+                                           s->batch, s->n_q_heads, s->n_kv_heads, s->seq_len, s->head_dim, s->block,
+                                           1.0f / sqrtf((float)s->head_dim), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pooled block_scores launch");
   g_err[0] = 0;
   return DSA_OK;
 }
@@ -625,7 +646,7 @@ int dsa_prefill(const dsa_shape* s, const void* q, const void* k, const void* v,
                                           static_cast<const uint16_t*>(k), kbar, (int64_t)B * s->n_kv_heads,
                                           s->seq_len, s->head_dim, s->block, st);
   if (e != hipSuccess) return hip_fail(e, "block_means(q, k) launch");
-  rc = dsa_block_scores(s, qbar, kbar, scores, stream);
+  rc = dsa_block_scores_from_means(s, qbar, kbar, scores, stream);
   if (rc) return rc;
   rc = dsa_select_topk(s, scores, idx, cnt, stream);
   if (rc) return rc;

@@ -63,6 +63,10 @@ hipError_t launch_block_means2(const uint16_t* x0, float* xbar0, int64_t n0, con
 // qbar [B, Hq, nB, d], kbar [B, Hkv, nB, d] -> scores [B, Hkv, nB, nB]
 hipError_t launch_block_scores(const float* qbar, const float* kbar, float* scores, int B, int Hq, int Hkv, int nB,
                                int d, float scale, hipStream_t stream);
+// q [B, Hq, N, d], k [B, Hkv, N, d] bf16 -> scores [B, Hkv, nB, nB] (the same
+// bits as block means followed by launch_block_scores), no workspace
+hipError_t launch_pooled_scores(const uint16_t* q, const uint16_t* k, float* scores, int B, int Hq, int Hkv, int N,
+                                int d, int block, float scale, hipStream_t stream);
 
 // Selection of one row.  anchors / window are resolved (0 when the matching
 // flag is off, >= 1 when on); cand_cap = floor(1 / threshold).

@@ -18,32 +18,20 @@
 namespace dsa {
 
 // ============================================================== block means
-// One workgroup per (unit, block): 256 threads read the block's rows as
-// 16-byte chunks (D/8 chunks per row, 256/(D/8) row groups), sum them in fp32,
-// reduce the row groups through LDS and divide by the number of real rows.
-// Two tensors in one launch: the first n0 units of x0, then those of x1.
+// The mean of one block is computed by one 64-lane wave in a fixed order:
+// lane l owns the 16-byte chunk c = l % CH of the row (CH = D/8 chunks) and
+// the row group r = l / CH (RG = 64/CH groups); it sums the rows r, r + RG,
+// r + 2 RG, ... of the block in fp32, then lane (0, c) adds the RG partial
+// sums in group order and divides by the number of real rows.  Every kernel
+// that pools a block (the means kernel and the fused score kernel) uses this
+// function, so both give the same bits.
 template <int D>
-__global__ __launch_bounds__(256) void block_means_kernel(const uint16_t* __restrict__ x0, float* __restrict__ xbar0,
-                                                          int64_t n0, const uint16_t* __restrict__ x1,
-                                                          float* __restrict__ xbar1, int N, int block, int nB) {
-  constexpr int CH = D / 8;        // 16-byte chunks per row
-  constexpr int RG = 256 / CH;     // row groups
-  __shared__ float part[RG][D + 1];
-  int64_t wg = blockIdx.x;
-  const uint16_t* x = x0;
-  float* xbar = xbar0;
-  if (wg >= n0 * nB) {
-    wg -= n0 * nB;
-    x = x1;
-    xbar = xbar1;
-  }
-  const int64_t unit = wg / nB;
-  const int j = (int)(wg % nB);
-  const int t = threadIdx.x, c = t % CH, rg = t / CH;
-  const int r0 = j * block;
-  const int rows = min(block, N - r0);
-  const uint16_t* base = x + (unit * N + r0) * (int64_t)D + c * 8;
+__device__ __forceinline__ void wave_block_mean(const uint16_t* __restrict__ rows0, int rows, int lane, float* out8) {
+  constexpr int CH = D / 8, RG = 64 / CH;
+  const int c = lane % CH, rg = lane / CH;
+  const uint16_t* base = rows0 + c * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 8
   for (int r = rg; r < rows; r += RG) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(base + (int64_t)r * D);
 #pragma unroll
@@ -52,27 +40,57 @@ __global__ __launch_bounds__(256) void block_means_kernel(const uint16_t* __rest
       acc[2 * e + 1] += bf16_hi(w[e]);
     }
   }
+  const float rows_f = (float)rows;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) part[rg][c * 8 + e] = acc[e];
-  __syncthreads();
-  if (t < D) {
-    float s = 0.f;
+  for (int e = 0; e < 8; ++e) {
+    float s = __shfl(acc[e], c, 64);
 #pragma unroll
-    for (int g = 0; g < RG; ++g) s += part[g][t];
-    xbar[(unit * nB + j) * (int64_t)D + t] = s / (float)rows;
+    for (int g = 1; g < RG; ++g) s += __shfl(acc[e], c + g * CH, 64);
+    out8[e] = s / rows_f;
+  }
+}
+
+// One wave per (unit, block); four waves per workgroup.  Two tensors in one
+// launch: the n0 * nB blocks of x0, then those of x1.
+template <int D>
+__global__ __launch_bounds__(256) void block_means_kernel(const uint16_t* __restrict__ x0, float* __restrict__ xbar0,
+                                                          int64_t n0, const uint16_t* __restrict__ x1,
+                                                          float* __restrict__ xbar1, int64_t n_total, int N,
+                                                          int block, int nB) {
+  constexpr int CH = D / 8;
+  const int lane = threadIdx.x & 63;
+  int64_t wb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (unit, block) of this wave
+  if (wb >= n_total) return;
+  const uint16_t* x = x0;
+  float* xbar = xbar0;
+  if (wb >= n0 * nB) {
+    wb -= n0 * nB;
+    x = x1;
+    xbar = xbar1;
+  }
+  const int64_t unit = wb / nB;
+  const int j = (int)(wb % nB);
+  const int r0 = j * block;
+  float m[8];
+  wave_block_mean<D>(x + (unit * N + r0) * (int64_t)D, min(block, N - r0), lane, m);
+  if (lane < CH) {
+    float* dst = xbar + (unit * nB + j) * (int64_t)D + lane * 8;
+    *reinterpret_cast<f32x4*>(dst) = (f32x4){m[0], m[1], m[2], m[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = (f32x4){m[4], m[5], m[6], m[7]};
   }
 }
 
 hipError_t launch_block_means2(const uint16_t* x0, float* xbar0, int64_t n0, const uint16_t* x1, float* xbar1,
                                int64_t n1, int N, int d, int block, hipStream_t stream) {
   const int nB = (N + block - 1) / block;
-  const int64_t n_wg = (n0 + n1) * nB;
-  if (n_wg == 0) return hipSuccess;
+  const int64_t n_total = (n0 + n1) * nB;
+  if (n_total == 0) return hipSuccess;
+  const uint32_t n_wg = (uint32_t)((n_total + 3) / 4);
   if (d == 64)
-    hipLaunchKernelGGL(block_means_kernel<64>, dim3((uint32_t)n_wg), dim3(256), 0, stream, x0, xbar0, n0, x1, xbar1,
+    hipLaunchKernelGGL(block_means_kernel<64>, dim3(n_wg), dim3(256), 0, stream, x0, xbar0, n0, x1, xbar1, n_total,
                        N, block, nB);
   else
-    hipLaunchKernelGGL(block_means_kernel<128>, dim3((uint32_t)n_wg), dim3(256), 0, stream, x0, xbar0, n0, x1, xbar1,
+    hipLaunchKernelGGL(block_means_kernel<128>, dim3(n_wg), dim3(256), 0, stream, x0, xbar0, n0, x1, xbar1, n_total,
                        N, block, nB);
   return hipGetLastError();
 }
@@ -191,6 +209,168 @@ hipError_t launch_block_scores(const float* qbar, const float* kbar, float* scor
     hipLaunchKernelGGL(block_scores_kernel<128>, dim3((uint32_t)n_wg), dim3(256), 0, stream, qbar, kbar, scores, Hq,
                        Hkv, nB, scale, n_tiles);
   return hipGetLastError();
+}
+
+// ============================================================== scores from Q, K
+// Block scores straight from the bf16 Q and K, with no workspace.  One
+// 256-thread workgroup per (batch, KV head, strip of T query blocks, strip of
+// T key blocks), key strip <= query strip.  The workgroup pools its query
+// strip for up to HC heads at a time into LDS (wave_block_mean: the bits of
+// block_means_kernel), then for every 32-block tile of its key strip pools
+// those key blocks into LDS and scores each (query block, key block) pair with
+// the dot-product order of block_scores_kernel, keeping the max over the
+// heads.  So the result equals block_scores_kernel on the block means, bit for
+// bit.  A query strip of T blocks is re-pooled once per key strip and a key
+// tile once per query strip (and head chunk): about nB / T reads of Q and K
+// in all, against one read for the means + scores path, which dsa_prefill
+// takes since it has a workspace.
+template <int D, int HC>
+__global__ __launch_bounds__(256) void pooled_scores_kernel(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ k,
+                                                            float* __restrict__ scores, int Hq, int Hkv, int N,
+                                                            int block, int nB, int T, int n_strips, float scale) {
+  constexpr int PITCH = D + 4;
+  constexpr int CH = D / 8;
+  __shared__ __align__(16) float qs[256][PITCH];  // row hh * T + i: head hh of the chunk, query block qb0 + i
+  __shared__ __align__(16) float ks[32][PITCH];
+  const int n_pairs = n_strips * (n_strips + 1) / 2;
+  const int64_t unit = blockIdx.x / n_pairs;  // b * Hkv + g
+  const int pair = (int)(blockIdx.x % n_pairs);
+  int si = 0;
+  while ((si + 1) * (si + 2) / 2 <= pair) ++si;
+  const int sj = pair - si * (si + 1) / 2;
+  const int G = Hq / Hkv;
+  const int64_t b = unit / Hkv, g = unit % Hkv;
+  const int qb0 = si * T, kb0 = sj * T;
+  const int nq = min(T, nB - qb0);                  // query blocks of the strip
+  const int k_end = min(kb0 + T, qb0 + nq);        // key blocks kb0 .. k_end - 1 can be visible
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, tx = t % 16, ty = t / 16;
+  float* out = scores + unit * (int64_t)nB * nB;
+  const float NEG_INF = -__builtin_inff();
+  const uint16_t* kunit = k + unit * (int64_t)N * D;
+
+  // -inf where no tile below computes: key columns past the key strip's
+  // visible end (diagonal strip only) and 32x32 tiles wholly above the
+  // diagonal; disjoint from what the tiles write
+  if (si == sj) {
+    const int ncols = nB - qb0;
+    for (int64_t e = t; e < (int64_t)nq * ncols; e += 256) {
+      const int ii = (int)(e / ncols), j = qb0 + (int)(e % ncols);
+      const int qt = ii & ~31, i_hi = qb0 + min(qt + 32, nq) - 1;
+      const int kt = qb0 + ((j - qb0) & ~31);
+      if (j >= k_end || kt > i_hi) out[(int64_t)(qb0 + ii) * nB + j] = NEG_INF;
+    }
+  }
+
+  for (int hc = 0; hc < G; hc += HC) {
+    const int nh = min(HC, G - hc);
+    __syncthreads();  // the previous chunk is done reading qs
+    for (int e = wave; e < nh * nq; e += 4) {
+      const int hh = e / nq, i = e % nq;
+      const int64_t h = g * G + hc + hh;
+      const int r0 = (qb0 + i) * block;
+      float m[8];
+      wave_block_mean<D>(q + ((b * Hq + h) * N + r0) * (int64_t)D, min(block, N - r0), lane, m);
+      if (lane < CH) {
+        *reinterpret_cast<f32x4*>(&qs[hh * T + i][lane * 8]) = (f32x4){m[0], m[1], m[2], m[3]};
+        *reinterpret_cast<f32x4*>(&qs[hh * T + i][lane * 8 + 4]) = (f32x4){m[4], m[5], m[6], m[7]};
+      }
+    }
+    for (int kt = kb0; kt < k_end; kt += 32) {
+      const int nkt = min(32, k_end - kt);
+      __syncthreads();  // qs complete; the previous key tile is done being read
+      for (int e = wave; e < 32; e += 4) {
+        float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (e < nkt) {
+          const int r0 = (kt + e) * block;
+          wave_block_mean<D>(kunit + (int64_t)r0 * D, min(block, N - r0), lane, m);
+        }
+        if (lane < CH) {
+          *reinterpret_cast<f32x4*>(&ks[e][lane * 8]) = (f32x4){m[0], m[1], m[2], m[3]};
+          *reinterpret_cast<f32x4*>(&ks[e][lane * 8 + 4]) = (f32x4){m[4], m[5], m[6], m[7]};
+        }
+      }
+      __syncthreads();
+      for (int qt = 0; qt < nq; qt += 32) {
+        const int i_hi = qb0 + min(qt + 32, nq) - 1;
+        if (i_hi < kt) continue;  // wholly above the diagonal (filled above)
+        float best[2][2];
+        for (int hh = 0; hh < nh; ++hh) {
+          float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll 4
+          for (int dd = 0; dd < D; dd += 4) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(&qs[hh * T + qt + ty][dd]);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(&qs[hh * T + qt + ty + 16][dd]);
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(&ks[tx][dd]);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(&ks[tx + 16][dd]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[0][0] = __builtin_fmaf(a0[e], b0[e], acc[0][0]);
+              acc[0][1] = __builtin_fmaf(a0[e], b1[e], acc[0][1]);
+              acc[1][0] = __builtin_fmaf(a1[e], b0[e], acc[1][0]);
+              acc[1][1] = __builtin_fmaf(a1[e], b1[e], acc[1][1]);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const float sc = acc[r][c] * scale;
+              best[r][c] = (hh == 0) ? sc : fmaxf(best[r][c], sc);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int ii = qt + ty + 16 * r, j = kt + tx + 16 * c;
+            if (ii < nq && j < k_end) {
+              const int i = qb0 + ii;
+              float* dst = out + (int64_t)i * nB + j;
+              // an earlier head chunk wrote this element (same thread)
+              const float prev = hc > 0 ? *dst : NEG_INF;
+              *dst = (j <= i) ? (hc > 0 ? fmaxf(prev, best[r][c]) : best[r][c]) : NEG_INF;
+            }
+          }
+      }
+    }
+  }
+}
+
+template <int D, int HC>
+static hipError_t launch_pooled_scores_hc(const uint16_t* q, const uint16_t* k, float* scores, int B, int Hq, int Hkv,
+                                          int N, int block, int nB, float scale, hipStream_t stream) {
+  // strips as long as the LDS allows (256 rows of means), shortened while the
+  // grid would leave most CUs idle
+  int T = 256 / HC;
+  auto n_wg = [&](int t) {
+    const int64_t s = (nB + t - 1) / t;
+    return (int64_t)B * Hkv * (s * (s + 1) / 2);
+  };
+  while (T > 32 && n_wg(T) < 512) T /= 2;
+  const int n_strips = (nB + T - 1) / T;
+  const int64_t wgs = n_wg(T);
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL((pooled_scores_kernel<D, HC>), dim3((uint32_t)wgs), dim3(256), 0, stream, q, k, scores, Hq, Hkv,
+                     N, block, nB, T, n_strips, scale);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_pooled_scores_d(const uint16_t* q, const uint16_t* k, float* scores, int B, int Hq, int Hkv,
+                                         int N, int block, int nB, float scale, hipStream_t stream) {
+  const int G = Hq / Hkv;
+  if (G >= 8) return launch_pooled_scores_hc<D, 8>(q, k, scores, B, Hq, Hkv, N, block, nB, scale, stream);
+  if (G >= 4) return launch_pooled_scores_hc<D, 4>(q, k, scores, B, Hq, Hkv, N, block, nB, scale, stream);
+  if (G >= 2) return launch_pooled_scores_hc<D, 2>(q, k, scores, B, Hq, Hkv, N, block, nB, scale, stream);
+  return launch_pooled_scores_hc<D, 1>(q, k, scores, B, Hq, Hkv, N, block, nB, scale, stream);
+}
+
+hipError_t launch_pooled_scores(const uint16_t* q, const uint16_t* k, float* scores, int B, int Hq, int Hkv, int N,
+                                int d, int block, float scale, hipStream_t stream) {
+  const int nB = (N + block - 1) / block;
+  if (d == 64) return launch_pooled_scores_d<64>(q, k, scores, B, Hq, Hkv, N, block, nB, scale, stream);
+  return launch_pooled_scores_d<128>(q, k, scores, B, Hq, Hkv, N, block, nB, scale, stream);
 }
 
 // ============================================================== top-k select

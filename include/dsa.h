@@ -19,11 +19,14 @@
  *
  * One prefill call runs four steps:
  *   1. block means of Q and K (fp32)                 dsa_block_means
- *   2. block scores, causal, max over a GQA group     dsa_block_scores
+ *   2. block scores, causal, max over a GQA group     dsa_block_scores (from
+ *                                                    Q, K) or
+ *                                                    dsa_block_scores_from_means
  *   3. top-k blocks per query block, sink and
  *      diagonal forced                               dsa_select_topk
  *   4. attention over the kept tiles                  dsa_sparse_attn_fwd
- * dsa_prefill chains them; dsa_decode is the single-token variant.
+ * dsa_prefill chains them; dsa_decode is the single-token variant;
+ * dsa_kmax gives the index width both write.
  *
  * Conventions for every call below:
  *   - All tensor pointers are DEVICE pointers, contiguous, row-major.  bf16
@@ -122,57 +125,111 @@ typedef struct dsa_shape {
  * Ties in score go to the lower block index.  The decisions at a threshold
  * or an integer exp(H) are taken in fp32. */
 
-/* Width of the prefill index array: the largest per-row budget (THRESHOLD:
- * F + floor(1 / threshold); ENTROPY: max(k_max, F); both capped at the row's
- * visible blocks).  Host only.
- * Returns DSA_OK and writes *kmax, or an error code. */
-int dsa_prefill_kmax(const dsa_shape* shape, int32_t* kmax);
+/* Width of the index array idx (its last dimension) for a prefill or a
+ * decode of this shape: the largest per-row budget, min(max(k, F), nB) for
+ * top-k (k = topk or the fraction of nB), F + floor(1 / threshold) for
+ * THRESHOLD and max(k_max, F) for ENTROPY, each capped at nB (F = forced
+ * blocks of a row that sees all nB blocks; a row's budget never shrinks as it
+ * sees more blocks, so the last row's is the largest).  The index lives in
+ * caller-preallocated contiguous memory of this width ("低成本高性能大模型实现
+ * 路径", section 3.1 "内存访问优化": sparse indices in preallocated contiguous
+ * blocks).  Host only; reads nothing but *shape.
+ * Returns kmax >= 0 (0 when seq_len == 0), or a negative DSA_ERR_* code. */
+int32_t dsa_kmax(const dsa_shape* shape);
 
-/* Width of the decode index array [S, Hkv, kmax] (every row sees all nB
- * blocks, so every row keeps exactly kmax).  Host only. */
+/* The same width through an out-parameter, with the checks of the prefill
+ * (dsa_prefill_kmax) or decode (dsa_decode_kmax) entry points: the decode
+ * form also rejects what dsa_decode does not take (select_mode != TOPK, group
+ * sizes other than 1, 2, 4, 8).  Returns DSA_OK and writes *kmax. */
+int dsa_prefill_kmax(const dsa_shape* shape, int32_t* kmax);
 int dsa_decode_kmax(const dsa_shape* shape, int32_t* kmax);
 
-/* Step 1: block means.  x: [B, n_heads, N, d] bf16 -> xbar: [B, n_heads, nB, d]
- * fp32 (N = shape->seq_len, B = shape->batch).  Used for Q (n_heads = Hq),
- * for K (n_heads = Hkv), and for a decode key cache (see dsa_kv_block_means).
- * fp32 because the selection is made from these values. */
+/* Step 1 on its own: block means.  x: [B, n_heads, N, d] bf16 -> xbar:
+ * [B, n_heads, nB, d] fp32 (N = shape->seq_len, B = shape->batch): the mean
+ * of each block's rows (a ragged last block over its real rows), summed in
+ * fp32 in a fixed order.  Used for Q (n_heads = Hq), K (n_heads = Hkv) and
+ * a decode key cache (dsa_kv_block_means).  fp32 because the selection is
+ * made from these values (DeepSeek NSA article, section 2.2: routing in
+ * fp32).  The block statistic itself -- one summary per tile that the
+ * per-block decision compares -- follows "dynamic sparse attention
+ * explainer", section "硬件友好的稀疏计算实现" (decide per 64x64 or 128x128
+ * block).  Errors: NULL x/xbar, n_heads < 1, shape errors.  Async on stream. */
 int dsa_block_means(const dsa_shape* shape, int32_t n_heads, const void* x, float* xbar, void* stream);
 
-/* Step 2: block scores.  scores[b, g, i, j] = max over the query heads h of
- * group g of (1/sqrt(d)) * <qbar[b, h, i], kbar[b, g, j]> for j <= i, and
- * -inf for j > i.  qbar [B, Hq, nB, d], kbar [B, Hkv, nB, d], fp32. */
-int dsa_block_scores(const dsa_shape* shape, const float* qbar, const float* kbar, float* scores, void* stream);
+/* Step 2: block scores from Q and K.  q [B, Hq, N, d], k [B, Hkv, N, d]
+ * bf16 (device) -> scores [B, Hkv, nB, nB] fp32 (device, caller-owned):
+ *   scores[b, g, i, j] = max over the query heads h of group g of
+ *                        (1/sqrt(d)) * <mean(Q_h block i), mean(K_g block j)>
+ * for j <= i, and -inf for j > i.  The means are pooled inside the call
+ * (no workspace; they are the bits of dsa_block_means) and the result is
+ * bit-identical to dsa_block_means + dsa_block_scores_from_means.  Sources:
+ * "稀疏注意力 vs Flash Attention v2" section 1 (content-aware sparsity ranks
+ * keys by query-key similarity); "dynamic sparse attention explainer",
+ * "前沿方向" (a GQA group shares one KV cache, hence one selection: the max
+ * over its heads).  Reads Q and K about nB / 256 times over (a strip of
+ * block means is pooled per workgroup); dsa_prefill, which has a workspace,
+ * pools each block once.  Errors: NULL q/k/scores, shape errors. */
+int dsa_block_scores(const dsa_shape* shape, const void* q, const void* k, float* scores, void* stream);
 
-/* Step 3: per-row selection from a score matrix [B, Hkv, nB, nB] (only
- * j <= i is read).  Row i keeps the forced blocks {0, i} (per flags) plus
- * the best-scoring other blocks up to its budget.  idx [B, Hkv, nB, kmax]
- * with kmax from dsa_prefill_kmax; cnt [B, Hkv, nB]. */
+/* Step 2 from precomputed block means: qbar [B, Hq, nB, d], kbar
+ * [B, Hkv, nB, d] fp32 (dsa_block_means) -> scores as dsa_block_scores. */
+int dsa_block_scores_from_means(const dsa_shape* shape, const float* qbar, const float* kbar, float* scores,
+                                void* stream);
+
+/* Step 3: per-row selection from a score matrix [B, Hkv, nB, nB] fp32 (only
+ * j <= i is read).  Row i keeps the forced blocks (DSA_FORCE_SINK: block 0
+ * or the first n_anchor blocks; DSA_FORCE_DIAG: block i or the last `window`
+ * visible blocks) plus the best-scoring other blocks up to its budget (the
+ * rules above; exact ties to the lower block index).  Output idx
+ * [B, Hkv, nB, dsa_kmax(shape)] int32, ascending, -1 padded; cnt [B, Hkv, nB]
+ * int32, the number kept.  Sources: "dynamic sparse attention explainer",
+ * "基于Top-k选择的局部-全局混合" (keep each query's k best keys, drop the rest;
+ * global + local anchors) and "硬件友好的稀疏计算实现" (per-block decision).
+ * Errors: NULL scores/idx/cnt, shape errors. */
 int dsa_select_topk(const dsa_shape* shape, const float* scores, int32_t* idx, int32_t* cnt, void* stream);
 
-/* Step 4: causal attention over the listed blocks.  Row p of query block i
- * attends to the keys c <= p of the blocks idx[b, g, i, 0..cnt-1] (which
- * must be ascending, distinct, in 0..i); logits are (1/sqrt(d)) q_p . k_c;
- * P is rounded to bf16 for the P V product, accumulation is fp32.
- * o: [B, Hq, N, d] bf16.  lse: [B, Hq, N] fp32 natural-log normaliser, or
- * NULL to skip it. */
+/* Step 4: causal attention over the listed blocks.  q [B, Hq, N, d], k, v
+ * [B, Hkv, N, d] bf16; idx, cnt as dsa_select_topk writes them (entries
+ * 0..cnt-1 of a row must be ascending, distinct, in 0..i -- not checked).
+ * Row p of query block i attends to the keys c <= p of its kept blocks:
+ *   O[p] = sum_c softmax_c((1/sqrt(d)) q_p . k_c) v_c,  LSE[p] = log sum_c
+ *   exp((1/sqrt(d)) q_p . k_c)
+ * with bf16 MFMA products, fp32 accumulation and online softmax, P rounded to
+ * bf16 for the P V product.  o [B, Hq, N, d] bf16; lse [B, Hq, N] fp32
+ * natural log, or NULL to skip it.  Sources: "稀疏注意力 vs Flash Attention
+ * v2" section 1 (the sparse_attention definition: logits, apply the pattern,
+ * softmax of logits / sqrt(d_k), times V; FlashAttention-2's tiled
+ * incremental softmax); "dynamic sparse attention explainer", "硬件友好的稀疏
+ * 计算实现" and "工程实践建议" (kept 64x64 / 128x128 blocks stay dense); DeepSeek
+ * NSA article section 2.2 (weighted sum in bf16).  Errors: NULL q/k/v/idx/
+ * cnt/o, shape errors. */
 int dsa_sparse_attn_fwd(const dsa_shape* shape, const void* q, const void* k, const void* v, const int32_t* idx,
                         const int32_t* cnt, void* o, float* lse, void* stream);
 
-/* Workspace for dsa_prefill, in bytes (block means of Q and K + scores). */
+/* Workspace for dsa_prefill, in bytes (block means of Q and K + scores,
+ * each 256-byte aligned).  0 for an invalid shape.  Host only. */
 size_t dsa_prefill_workspace_bytes(const dsa_shape* shape);
 
-/* Steps 1-4 in one call.  idx, cnt: outputs as for dsa_select_topk.
- * ws: device workspace of at least dsa_prefill_workspace_bytes(shape)
- * bytes; after the call it holds Q means, K means, then the scores. */
+/* Steps 1-4 in one call: Q/K/V in, a block size and k (in *shape), output
+ * plus the selected block indices out ("稀疏注意力 vs Flash Attention v2"
+ * section 1: sparse_attention(query, key, value, pattern); "dynamic sparse
+ * attention explainer", "基于Top-k选择的局部-全局混合").  q, k, v, o, lse as
+ * dsa_sparse_attn_fwd; idx, cnt as dsa_select_topk.  ws: device workspace
+ * of at least dsa_prefill_workspace_bytes(shape) bytes (caller-owned); after
+ * the call it holds the Q means, the K means, then the scores.  Errors as
+ * the steps, plus DSA_ERR_WORKSPACE. */
 int dsa_prefill(const dsa_shape* shape, const void* q, const void* k, const void* v, void* o, float* lse,
                 int32_t* idx, int32_t* cnt, void* ws, size_t ws_bytes, void* stream);
 
 /* Cache-time block means of a decode key cache: k_cache [S, Hkv, L, d] bf16
- * -> kbar [S, Hkv, nB, d] fp32 (the index data precomputed when the cache
- * is written, so a decode step does not re-pool raw keys). */
+ * -> kbar [S, Hkv, nB, d] fp32 -- the index data built when the cache is
+ * written, so a decode step does not re-pool raw keys ("dynamic sparse
+ * attention explainer", "动态开销与计算收益的权衡": precompute at cache time).
+ * Errors: as dsa_block_means plus the decode shape checks. */
 int dsa_kv_block_means(const dsa_shape* shape, const void* k_cache, float* kbar, void* stream);
 
-/* Workspace for dsa_decode, in bytes. */
+/* Workspace for dsa_decode, in bytes (split partials; 0 when the step runs
+ * as one workgroup per (sequence, KV head), i.e. S * Hkv >= 256). */
 size_t dsa_decode_workspace_bytes(const dsa_shape* shape);
 
 /* One decode step for S sequences.  q: [S, Hq, d] bf16 (the new tokens, at
@@ -180,9 +237,14 @@ size_t dsa_decode_workspace_bytes(const dsa_shape* shape);
  * dsa_kv_block_means of k_cache.  Per (sequence, KV head) the blocks are
  * scored by max over the group's heads of (1/sqrt(d)) q_h . kbar_j, the
  * sink and the last block are forced (per flags), the best others fill the
- * budget, and every key of the kept blocks is attended to.
- * o: [S, Hq, d] bf16; lse: [S, Hq] fp32 or NULL; idx: [S, Hkv, kmax] with
- * kmax from dsa_decode_kmax.  ws: at least dsa_decode_workspace_bytes. */
+ * budget (ties to the lower block), and every key of the kept blocks is
+ * attended to (split over the kept blocks, partials merged).
+ * o: [S, Hq, d] bf16; lse: [S, Hq] fp32 or NULL; idx: [S, Hkv, dsa_kmax]
+ * int32.  ws: at least dsa_decode_workspace_bytes.  Sources: "dynamic sparse
+ * attention explainer", "动态开销与计算收益的权衡" (cache-time index data),
+ * "前沿方向" (one selection per GQA group), "硬件友好的稀疏计算实现" (whole
+ * blocks of the cache).  Errors: NULL pointers, shape errors (decode takes
+ * DSA_SELECT_TOPK only; group sizes 1, 2, 4, 8), DSA_ERR_WORKSPACE. */
 int dsa_decode(const dsa_shape* shape, const void* q, const void* k_cache, const void* v_cache, const float* kbar,
                void* o, float* lse, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 

@@ -105,9 +105,10 @@ import numpy as np
 FORCE_SINK = 1  # keep block 0 in every row
 FORCE_DIAG = 2  # keep the row's own (diagonal / last visible) block
 
-# near-tie rule for flagging rows (see ``near``)
+# near-tie rule for flagging rows (see ``near``): the acceptance rule's 1e-3
+# relative gap.  Token-indexer rows add an absolute floor (``TOKEN_TIE_ABS``).
 TIE_REL = 1e-3
-TIE_ABS = 1e-6
+TOKEN_TIE_ABS = 1e-6
 
 # selection modes (``SelectSpec.mode``)
 SELECT_TOPK = 0
@@ -291,16 +292,17 @@ def threshold_row(scores: np.ndarray, n_visible: int, tau: float, forced: list) 
                         flagged=bool(band))
 
 
-def near(a: float, b: float) -> bool:
-    """Near-tie test between two scores: relative gap below 1e-3 (the
-    acceptance rule), or an absolute gap below 1e-6, which bounds the fp32
-    rounding of a block score for the synthetic workloads."""
+def near(a: float, b: float, abs_floor: float = 0.0) -> bool:
+    """Near-tie test between two scores: a relative gap below 1e-3, the
+    acceptance rule for block indices (rel(a, b) = |a - b| / max(|a|, |b|),
+    0 when a == b).  ``abs_floor`` > 0 also counts gaps below it (the token
+    indexer, see ``select_tokens``)."""
     if a == b:
         return True
     if not (math.isfinite(a) and math.isfinite(b)):
         return False
     gap = abs(a - b)
-    return gap < TIE_REL * max(abs(a), abs(b)) or gap < TIE_ABS
+    return gap < TIE_REL * max(abs(a), abs(b)) or gap < abs_floor
 
 
 @dataclass
@@ -323,7 +325,8 @@ class RowSelection:
     alts: list = field(default_factory=list)
 
 
-def select_row(scores: np.ndarray, n_visible: int, k_budget: int, forced: list) -> RowSelection:
+def select_row(scores: np.ndarray, n_visible: int, k_budget: int, forced: list,
+               abs_floor: float = 0.0) -> RowSelection:
     """Keep ``k_budget`` of the ``n_visible`` blocks of one row.
 
     The forced blocks are kept; the remaining m = k_budget - |forced| are the
@@ -332,8 +335,8 @@ def select_row(scores: np.ndarray, n_visible: int, k_budget: int, forced: list) 
     k highest-scoring keys and drop the rest.
 
     A row is flagged when the m-th and (m+1)-th candidates are near-ties
-    (``near``); its band holds the ranks from the first to the last candidate
-    near either of those two scores.
+    (``near`` with ``abs_floor``); its band holds the ranks from the first to
+    the last candidate near either of those two scores.
     """
     fs = set(forced)
     cand = np.array([j for j in range(n_visible) if j not in fs], dtype=np.int64)
@@ -346,10 +349,11 @@ def select_row(scores: np.ndarray, n_visible: int, k_budget: int, forced: list) 
     rsc = sc[order]
     chosen = set(int(j) for j in ranked[:m])
     sel = sorted(fs | chosen)
-    if m >= ranked.size or not near(float(rsc[m - 1]), float(rsc[m])):
+    if m >= ranked.size or not near(float(rsc[m - 1]), float(rsc[m]), abs_floor):
         return RowSelection(idx=sel, forced=sorted(fs), must=chosen)
     a, b = float(rsc[m - 1]), float(rsc[m])
-    in_band = [r for r in range(ranked.size) if near(float(rsc[r]), a) or near(float(rsc[r]), b)]
+    in_band = [r for r in range(ranked.size)
+               if near(float(rsc[r]), a, abs_floor) or near(float(rsc[r]), b, abs_floor)]
     lo, hi = min(in_band), max(in_band)
     must = set(int(j) for j in ranked[:lo])
     band = set(int(j) for j in ranked[lo : hi + 1])
@@ -381,14 +385,14 @@ def kmax(n_rows: int, topk: int, num: int, den: int, flags: int, causal: bool, n
 
 
 def select_topk(scores: np.ndarray, topk: int, num: int = 0, den: int = 1, flags: int = FORCE_SINK | FORCE_DIAG,
-                causal: bool = True, spec: SelectSpec = DEFAULT_SPEC):
+                causal: bool = True, spec: SelectSpec = DEFAULT_SPEC, abs_floor: float = 0.0):
     """Row-wise selection over a score array [..., R, C].
 
     causal=True (prefill): row i sees blocks 0..i.  causal=False (decode):
     every row sees all C blocks.  ``spec`` picks the forced set and the mode
     (plain top-k by default).  Returns (idx, cnt, rows) where idx is int32
     [..., R, kmax] ascending and -1 padded, cnt is int32 [..., R] and rows is
-    a flat list of ``RowSelection`` in C order.
+    a flat list of ``RowSelection`` in C order.  ``abs_floor``: see ``near``.
     """
     lead = scores.shape[:-2]
     R, C = scores.shape[-2:]
@@ -406,12 +410,12 @@ def select_topk(scores: np.ndarray, topk: int, num: int = 0, den: int = 1, flags
                 rs = threshold_row(row, nv, spec_tau(spec), f)
             elif spec.mode == SELECT_ENTROPY:
                 ks = entropy_budgets(row, nv, spec.k_min, spec.k_max, len(f))
-                rs = select_row(row, nv, ks[0], f)
+                rs = select_row(row, nv, ks[0], f, abs_floor)
                 if len(ks) > 1:
-                    rs.alts = [select_row(row, nv, kb, f) for kb in ks[1:]]
+                    rs.alts = [select_row(row, nv, kb, f, abs_floor) for kb in ks[1:]]
                     rs.flagged = True
             else:
-                rs = select_row(row, nv, row_budget(nv, topk, num, den, len(f)), f)
+                rs = select_row(row, nv, row_budget(nv, topk, num, den, len(f)), f, abs_floor)
             idx[u, i, : len(rs.idx)] = rs.idx
             cnt[u, i] = len(rs.idx)
             rows.append(rs)
@@ -670,8 +674,17 @@ def select_tokens(scores: np.ndarray, topk: int, flags: int = FORCE_SINK | FORCE
     ``flags``) and the best other tokens up to ``topk`` by index score (ties
     to the lower position), ascending: the O3 rule with rows and columns
     being tokens.  scores [B, N, N]; returns idx [B, N, kmax], cnt [B, N],
-    rows."""
-    idx, cnt, rows = select_topk(np.asarray(scores)[:, None], topk, 0, 1, flags, causal=True, spec=spec)
+    rows.
+
+    Near ties: besides the 1e-3 relative gap, two token scores within
+    ``TOKEN_TIE_ABS`` (1e-6) of each other flag the row.  A token score is a
+    sum of ReLU(index query . index key) terms; a dot product that lies
+    within fp32 rounding of zero is clipped to zero in one evaluation and
+    kept as a tiny positive value in another, so scores that close to each
+    other near zero cannot be ordered in fp32.  Block scores pass through no
+    such clip and use the relative rule alone."""
+    idx, cnt, rows = select_topk(np.asarray(scores)[:, None], topk, 0, 1, flags, causal=True, spec=spec,
+                                 abs_floor=TOKEN_TIE_ABS)
     return idx[:, 0], cnt[:, 0], rows
 
 

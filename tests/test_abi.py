@@ -40,6 +40,51 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name)
 
 
+# The boundary's core calls: name, return type and parameter types in order
+# (parameter names are free).  dsa_decode also takes a nullable LSE output
+# after o, for callers that merge decodes.
+BOUNDARY = {
+    "dsa_kmax": ("int32_t", ["const dsa_shape*"]),
+    "dsa_block_scores": ("int", ["const dsa_shape*", "const void*", "const void*", "float*", "void*"]),
+    "dsa_select_topk": ("int", ["const dsa_shape*", "const float*", "int32_t*", "int32_t*", "void*"]),
+    "dsa_sparse_attn_fwd": ("int", ["const dsa_shape*", "const void*", "const void*", "const void*", "const int32_t*",
+                                    "const int32_t*", "void*", "float*", "void*"]),
+    "dsa_prefill_workspace_bytes": ("size_t", ["const dsa_shape*"]),
+    "dsa_prefill": ("int", ["const dsa_shape*", "const void*", "const void*", "const void*", "void*", "float*",
+                            "int32_t*", "int32_t*", "void*", "size_t", "void*"]),
+    "dsa_kv_block_means": ("int", ["const dsa_shape*", "const void*", "float*", "void*"]),
+    "dsa_decode_workspace_bytes": ("size_t", ["const dsa_shape*"]),
+    "dsa_decode": ("int", ["const dsa_shape*", "const void*", "const void*", "const void*", "const float*", "void*",
+                           "float*", "int32_t*", "void*", "size_t", "void*"]),
+    "dsa_status_str": ("const char*", ["int"]),
+    "dsa_last_error": ("const char*", ["void"]),
+}
+
+
+def prototypes():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"([A-Za-z_][\w \t*]*?)\b(dsa_\w+)\s*\(([^)]*)\)\s*;", text):
+        ret = " ".join(m.group(1).split())
+        params = []
+        for par in m.group(3).split(","):
+            par = " ".join(par.replace("*", " * ").split())
+            toks = par.split(" ")
+            if len(toks) > 1 and toks[-1] not in ("*",) and toks[-1] != "void" and not toks[-1].endswith("_t") \
+                    and toks[-1] not in ("int", "float", "dsa_shape"):
+                toks = toks[:-1]  # drop the parameter name
+            params.append(" ".join(toks).replace(" *", "*"))
+        out[m.group(2)] = (ret.replace(" *", "*"), params)
+    return out
+
+
+def test_boundary_calls_have_the_specified_signatures():
+    protos = prototypes()
+    for name, want in BOUNDARY.items():
+        assert name in protos, name
+        assert protos[name] == want, (name, protos[name], want)
+
+
 def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.dsa_status_str(code)
@@ -84,9 +129,11 @@ def test_bad_shapes_are_rejected_everywhere(lib, kw, code):
     p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     out = ctypes.c_int32()
     calls = [
+        lambda: lib.dsa_kmax(ctypes.byref(s)),
         lambda: lib.dsa_prefill_kmax(ctypes.byref(s), ctypes.byref(out)),
         lambda: lib.dsa_block_means(ctypes.byref(s), 2, p, p, None),
         lambda: lib.dsa_block_scores(ctypes.byref(s), p, p, p, None),
+        lambda: lib.dsa_block_scores_from_means(ctypes.byref(s), p, p, p, None),
         lambda: lib.dsa_select_topk(ctypes.byref(s), p, p, p, None),
         lambda: lib.dsa_sparse_attn_fwd(ctypes.byref(s), p, p, p, p, p, p, None, None),
         lambda: lib.dsa_prefill(ctypes.byref(s), p, p, p, p, None, p, p, p, 1 << 40, None),
@@ -105,6 +152,9 @@ def test_null_arguments(lib):
     assert lib.dsa_prefill_kmax(ctypes.byref(s), None) == dsa.DSA_ERR_NULL
     assert lib.dsa_block_means(ctypes.byref(s), 4, None, p, None) == dsa.DSA_ERR_NULL
     assert lib.dsa_block_scores(ctypes.byref(s), p, None, p, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_block_scores(ctypes.byref(s), p, p, None, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_block_scores_from_means(ctypes.byref(s), p, None, p, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_kmax(None) == dsa.DSA_ERR_NULL
     assert lib.dsa_select_topk(ctypes.byref(s), p, p, None, None) == dsa.DSA_ERR_NULL
     assert lib.dsa_sparse_attn_fwd(ctypes.byref(s), p, p, None, p, p, p, None, None) == dsa.DSA_ERR_NULL
     assert lib.dsa_prefill(ctypes.byref(s), p, p, p, None, None, p, p, p, 1 << 40, None) == dsa.DSA_ERR_NULL
@@ -181,6 +231,7 @@ def test_kmax_matches_the_oracle(lib, N, b, topk, num, den, flags):
     nb = -(-N // b)
     assert dsa.dsa_prefill_kmax(s) == O.kmax(nb, topk, num, den, flags, True, nb)
     assert dsa.dsa_decode_kmax(s) == O.kmax(1, topk, num, den, flags, False, nb)
+    assert dsa.dsa_kmax(s) == dsa.dsa_prefill_kmax(s) == dsa.dsa_decode_kmax(s)
 
 
 VARIANTS = [
@@ -202,6 +253,7 @@ def test_kmax_of_selection_variants_matches_the_oracle(lib, N, kw):
                         k_min=kw.get("k_min", 0), k_max=kw.get("k_max", 0))
     flags, topk = kw.get("flags", 3), kw.get("topk", 4)
     assert dsa.dsa_prefill_kmax(s) == O.kmax(nb, topk, 0, 1, flags, True, nb, spec)
+    assert dsa.dsa_kmax(s) == dsa.dsa_prefill_kmax(s)
     if kw.get("select_mode", 0) == 0:
         assert dsa.dsa_decode_kmax(s) == O.kmax(1, topk, 0, 1, flags, False, nb, spec)
 

@@ -109,7 +109,7 @@ def test_index_full_n8192_sampled(cuda_device):
     flagged = 0
     for t in rows:
         f = O.forced_set(t + 1, 3)
-        rs = O.select_row(ref[t], t + 1, O.row_budget(t + 1, w.topk, 0, 1, len(f)), f)
+        rs = O.select_row(ref[t], t + 1, O.row_budget(t + 1, w.topk, 0, 1, len(f)), f, O.TOKEN_TIE_ABS)
         c = int(gcnt[0, t])
         got = [int(s) for s in gidx[0, t, :c]]
         if rs.flagged:

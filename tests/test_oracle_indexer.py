@@ -157,3 +157,23 @@ def test_a_repeated_position_counts_once_per_occurrence():
     Z = 2 * math.exp(A) + math.exp(B)
     np.testing.assert_allclose(o[0, 0, t], (2 * math.exp(A) * v[0, 0, a] + math.exp(B) * v[0, 0, b]) / Z, rtol=1e-12)
     assert lse[0, 0, t] == pytest.approx(math.log(Z), rel=1e-13)
+
+
+def test_token_near_ties_have_an_absolute_floor():
+    """Token rows flag two scores within 1e-6 of each other (a ReLU'd dot
+    product within fp32 rounding of zero may be clipped on one side only):
+    at the budget boundary, 5e-7 against 0 is a near tie, 5e-6 against 0 is
+    not.  The block path (``select_topk`` without the floor) keeps the
+    relative rule alone."""
+    # query token 4 sees tokens 0..4; forced {0, 4}; topk 3 keeps one of {1, 2, 3}
+    sc = np.full((1, 5, 5), -np.inf)
+    sc[0, 4, :5] = [9.0, 5e-7, 0.0, 0.0, 9.0]
+    for t in range(4):
+        sc[0, t, : t + 1] = np.arange(t + 1, dtype=np.float64)
+    _, _, rows = O.select_tokens(sc, 3)
+    assert rows[4].flagged and rows[4].band == {1, 2, 3}
+    _, _, rows = O.select_topk(sc[:, None], 3)
+    assert not rows[4].flagged and rows[4].idx == [0, 1, 4]
+    sc[0, 4, 1] = 5e-6
+    _, _, rows = O.select_tokens(sc, 3)
+    assert not rows[4].flagged and rows[4].idx == [0, 1, 4]

@@ -382,6 +382,22 @@ def test_near_tie_band_and_acceptance():
     assert not O.accepts(clear, [0, 1, 3, 4])[0]
 
 
+def test_block_near_ties_are_relative_only():
+    """Block selection flags a row only on the acceptance rule's relative gap
+    (< 1e-3): two scores on either side of zero, 4e-7 apart, are distinct
+    (relative gap 2), while 1.0 and 1.0009 are a near tie and 1.0 and 1.0011
+    are not."""
+    forced = O.forced_set(5, BOTH)  # {0, 4}; one of {1, 2, 3} is kept (k = 3)
+    rs = O.select_row(np.array([0.0, 2e-7, -2e-7, -5.0, 0.0]), 5, 3, forced)
+    assert not rs.flagged and rs.idx == [0, 1, 4]
+    assert O.select_row(np.array([0.0, 1.0, 1.0009, -5.0, 0.0]), 5, 3, forced).flagged
+    rs = O.select_row(np.array([0.0, 1.0, 1.0011, -5.0, 0.0]), 5, 3, forced)
+    assert not rs.flagged and rs.idx == [0, 2, 4]
+    # exact ties are always flagged (rel = 0), whatever their value
+    assert O.select_row(np.array([0.0, 0.0, 0.0, -5.0, 0.0]), 5, 3, forced).flagged
+    assert O.near(0.0, 0.0) and not O.near(1e-9, -1e-9) and O.near(1e-9, -1e-9, abs_floor=1e-6)
+
+
 def test_generator_is_reproducible_per_unit():
     w = WORKLOADS["decode_s32_l65536"]
     small = Workload("dec_small", "decode", 2, 8, 2, 640, 32, 64, 4, structure="planted", amplitude=2.0, seed=5)
