@@ -38,6 +38,11 @@ BWD_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "attn_bwd.h
 INDEX_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "indexer.hip")
 
 
+def log(msg):
+    """Progress on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def src_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
@@ -97,6 +102,7 @@ def bench_prefill(args, dev, stream, flush, wname, n_steps):
     from dynamic_block_sparse_dsa_amd.inputs import WORKLOADS, make_prefill
 
     w = WORKLOADS[wname]
+    log(f"prefill {wname}: inputs")
     q, k, v = make_prefill(w, device=dev)
     B, Hq, Hkv, N, d, nB = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_blocks
     shape = dsa.make_shape(B, Hq, Hkv, N, d, w.block, w.topk, w.topk_num, w.topk_den)
@@ -130,6 +136,7 @@ def bench_prefill(args, dev, stream, flush, wname, n_steps):
         read_flush(flush, stream)
         attn_us.append(time_events(attn, 1, stream) * 1e3)
     ms_attn = sum(attn_us) / len(attn_us) * 1e-3
+    log(f"prefill {wname}: step {ms_step:.3f} ms, attention {ms_attn:.3f} ms")
     cnt_h = cnt.cpu().numpy()
     flops = work.prefill_flops(cnt_h, w.group, w.block, d)
     tflops = flops / (ms_attn * 1e-3) / 1e12
@@ -620,19 +627,26 @@ def main():
                                                   config=r["config"], roofline=r["roofline"])
             torch.cuda.empty_cache()
     if not args.no_decode:
+        log("decode")
         out["decode"] = bench_decode(args, dev, stream, flush)
         if not args.no_paged:
+            log("paged decode")
             out["paged_decode"] = bench_paged(args, dev, stream)
         del args._decode_inputs
     if not args.no_backward:
+        log("backward")
         out["backward"] = bench_backward(args, dev, stream, inputs)
     if not args.no_selection:
+        log("selection variants")
         out["selection"] = bench_selection(args, dev, stream, inputs)
     if not args.no_index:
+        log("token indexer")
         out["indexer"] = bench_index(args, dev, stream)
     if not args.no_ceilings:
+        log("ceilings")
         out["ceilings"] = ceilings(dev, stream)
     if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(args, inputs)
     print(json.dumps(out), flush=True)
 
