@@ -52,6 +52,7 @@ EXPORTS = [
     "dsa_kv_block_means",
     "dsa_decode_workspace_bytes",
     "dsa_decode",
+    "dsa_decode_noalloc",
     "dsa_paged_decode",
     "dsa_paged_kv_append",
     "dsa_paged_kv_block_means",
@@ -161,6 +162,7 @@ def load() -> ctypes.CDLL:
         "dsa_kv_block_means": ([S, P, P, P], ctypes.c_int),
         "dsa_decode_workspace_bytes": ([S], SZ),
         "dsa_decode": ([S, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "dsa_decode_noalloc": ([S, P, P, P, P, P, P, P, P], ctypes.c_int),
         "dsa_paged_decode": ([S, P, P, P, P, I32, P, I32, P, P, P, P, P, P], ctypes.c_int),
         "dsa_paged_kv_append": ([S, P, P, P, I32, P, P, P, P, I32, P], ctypes.c_int),
         "dsa_paged_kv_block_means": ([S, P, P, I32, P, P, I32, P], ctypes.c_int),
@@ -408,6 +410,17 @@ def dsa_decode(shape: Shape, q, k_cache, v_cache, kbar, o, lse, idx, ws, stream=
         _ptr(v_cache, torch.bfloat16, (S, Hkv, L, d), "v_cache"), _ptr(kbar, torch.float32, (S, Hkv, nB, d), "kbar"),
         _ptr(o, torch.bfloat16, (S, Hq, d), "o"), _ptr(lse, torch.float32, (S, Hq), "lse", optional=True),
         _ptr(idx, torch.int32, (S, Hkv, km), "idx"), wp, wb, _stream(stream)))
+
+
+def dsa_decode_noalloc(shape: Shape, q, k_cache, v_cache, kbar, o, lse, idx, stream=None):
+    S, Hq, Hkv, L, d, nB = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_len, shape.head_dim, shape.n_blocks
+    km = dsa_decode_kmax(shape)
+    _check(load().dsa_decode_noalloc(
+        ctypes.byref(shape), _ptr(q, torch.bfloat16, (S, Hq, d), "q"),
+        _ptr(k_cache, torch.bfloat16, (S, Hkv, L, d), "k_cache"),
+        _ptr(v_cache, torch.bfloat16, (S, Hkv, L, d), "v_cache"), _ptr(kbar, torch.float32, (S, Hkv, nB, d), "kbar"),
+        _ptr(o, torch.bfloat16, (S, Hq, d), "o"), _ptr(lse, torch.float32, (S, Hq), "lse", optional=True),
+        _ptr(idx, torch.int32, (S, Hkv, km), "idx"), _stream(stream)))
 
 
 def _paged_dims(shape: Shape, k_pool, table):

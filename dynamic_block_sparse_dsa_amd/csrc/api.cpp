@@ -664,16 +664,8 @@ size_t dsa_decode_workspace_bytes(const dsa_shape* s) {
   return align256(units * nsplit * G * (d + 2) * 4);
 }
 
-int dsa_decode(const dsa_shape* s, const void* q, const void* k_cache, const void* v_cache, const float* kbar,
-               void* o, float* lse, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_decode(s);
-  if (rc) return rc;
-  if (s->batch == 0) return DSA_OK;
-  if (!q || !k_cache || !v_cache || !kbar || !o || !idx)
-    return fail(DSA_ERR_NULL, "q, k_cache, v_cache, kbar, o or idx is NULL");
-  const size_t need = dsa_decode_workspace_bytes(s);
-  if (!ws || ws_bytes < need)
-    return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
+static int decode_impl(const dsa_shape* s, const void* q, const void* k_cache, const void* v_cache, const float* kbar,
+                       void* o, float* lse, int32_t* idx, float* partial, void* stream) {
   const int nB = (int)n_blocks(s);
   const int kmax = row_budget(s, nB);
   dsa::DecodeArgs a;
@@ -694,11 +686,41 @@ int dsa_decode(const dsa_shape* s, const void* q, const void* k_cache, const voi
   a.block = s->block;
   a.scale = 1.0f / sqrtf((float)s->head_dim);
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
-  a.partial = static_cast<float*>(ws);
+  a.partial = partial;
   hipError_t e = dsa::launch_decode(a, s->head_dim, topk_params(s), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   g_err[0] = 0;
   return DSA_OK;
+}
+
+int dsa_decode(const dsa_shape* s, const void* q, const void* k_cache, const void* v_cache, const float* kbar,
+               void* o, float* lse, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_decode(s);
+  if (rc) return rc;
+  if (s->batch == 0) return DSA_OK;
+  if (!q || !k_cache || !v_cache || !kbar || !o || !idx)
+    return fail(DSA_ERR_NULL, "q, k_cache, v_cache, kbar, o or idx is NULL");
+  const size_t need = dsa_decode_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
+  return decode_impl(s, q, k_cache, v_cache, kbar, o, lse, idx, static_cast<float*>(ws), stream);
+}
+
+int dsa_decode_noalloc(const dsa_shape* s, const void* q, const void* k_cache, const void* v_cache, const float* kbar,
+                       void* o, float* lse, int32_t* idx, void* stream) {
+  int rc = check_decode(s);
+  if (rc) return rc;
+  if (s->batch == 0) return DSA_OK;
+  if (!q || !k_cache || !v_cache || !kbar || !o || !idx)
+    return fail(DSA_ERR_NULL, "q, k_cache, v_cache, kbar, o or idx is NULL");
+  const size_t need = dsa_decode_workspace_bytes(s);
+  if (need > DSA_DECODE_NOALLOC_MAX_BYTES)
+    return fail(DSA_ERR_UNSUPPORTED, "decode needs %zu bytes of scratch, more than the %zu the library holds", need,
+                (size_t)DSA_DECODE_NOALLOC_MAX_BYTES);
+  void* scratch = nullptr;
+  hipError_t e = dsa::decode_noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "decode scratch lookup");
+  return decode_impl(s, q, k_cache, v_cache, kbar, o, lse, idx, static_cast<float*>(scratch), stream);
 }
 
 }  // extern "C"

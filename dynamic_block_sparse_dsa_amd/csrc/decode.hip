@@ -36,6 +36,8 @@
 //     runs split-K over the kept blocks (one 256-thread workgroup per (unit,
 //     split)) and writes a partial (max, sum, acc[d]) per head;
 //     decode_combine_kernel merges the partials.
+#include <mutex>
+
 #include "decode_common.hpp"
 #include "topk_row.hpp"
 
@@ -146,6 +148,34 @@ constexpr int DEC_MAX_SPLITS = 32;
 // Split count aims at about this many attention workgroups: fewer, longer
 // lived waves (each walks several chunks) beat one chunk per wave.
 constexpr int DEC_TARGET_WG = 1024;
+
+// Library-owned scratch for dsa_decode_noalloc (callers that cannot allocate):
+// the split partials [S * Hkv, nsplit, G, d + 2] fp32 of any shape the split
+// path takes fit in it (S * Hkv < 256 units, nsplit <= ceil(1024 / units):
+// under 1 280 (unit, split) pairs x 8 heads x 130 floats = 5.3 MB).  One copy
+// per GPU, held until the process ends.  Host code never uses the array's
+// name as an address: decode_noalloc_scratch() looks the device address up
+// once per device and passes that pointer to the kernels.
+static __device__ __align__(256) unsigned char scratch[DSA_DECODE_NOALLOC_MAX_BYTES];
+
+hipError_t decode_noalloc_scratch(void** out) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* ptr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
 
 template <int D, int BLK, int G>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {

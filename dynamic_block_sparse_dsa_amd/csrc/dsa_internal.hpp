@@ -201,6 +201,9 @@ struct DecodeArgs {
   float scale_log2;  // log2(e) / sqrt(d)
 };
 hipError_t launch_decode(const DecodeArgs& a, int d, TopkParams p, hipStream_t stream);
+// device address, on the current device, of the library-owned scratch of
+// DSA_DECODE_NOALLOC_MAX_BYTES (looked up once per device)
+hipError_t decode_noalloc_scratch(void** out);
 
 // number of key splits a decode step uses (also sizes its workspace)
 int decode_splits(int S, int Hkv, int kmax);

@@ -248,6 +248,22 @@ size_t dsa_decode_workspace_bytes(const dsa_shape* shape);
 int dsa_decode(const dsa_shape* shape, const void* q, const void* k_cache, const void* v_cache, const float* kbar,
                void* o, float* lse, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
+/* Size of the device scratch dsa_decode_noalloc uses on each GPU (bytes). */
+#define DSA_DECODE_NOALLOC_MAX_BYTES (8u << 20)
+
+/* dsa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as dsa_decode, minus the workspace: the split-path
+ * partials go to a device array the library owns, DSA_DECODE_NOALLOC_MAX_BYTES
+ * per GPU, held from the first call on that GPU until the process ends.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library call).
+ * Every shape dsa_decode takes fits; a shape whose dsa_decode_workspace_bytes
+ * exceeded the array would get DSA_ERR_UNSUPPORTED.  All calls on one GPU
+ * share the array: calls that overlap on one GPU (e.g. on two streams) race,
+ * so serialise them.  Nothing in the array needs to start at zero. */
+int dsa_decode_noalloc(const dsa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                       const float* kbar, void* o, float* lse, int32_t* idx, void* stream);
+
 /* ---- Backward of step 4 (gradients through the kept tiles; the selection
  * is a discrete choice and is held fixed).  The chain rule through the
  * attention definition of "稀疏注意力 vs Flash Attention v2" section 1, with P

@@ -138,6 +138,7 @@ def test_bad_shapes_are_rejected_everywhere(lib, kw, code):
         lambda: lib.dsa_sparse_attn_fwd(ctypes.byref(s), p, p, p, p, p, p, None, None),
         lambda: lib.dsa_prefill(ctypes.byref(s), p, p, p, p, None, p, p, p, 1 << 40, None),
         lambda: lib.dsa_decode(ctypes.byref(s), p, p, p, p, p, None, p, p, 1 << 40, None),
+        lambda: lib.dsa_decode_noalloc(ctypes.byref(s), p, p, p, p, p, None, p, None),
     ]
     for c in calls:
         assert c() == code
@@ -159,6 +160,8 @@ def test_null_arguments(lib):
     assert lib.dsa_sparse_attn_fwd(ctypes.byref(s), p, p, None, p, p, p, None, None) == dsa.DSA_ERR_NULL
     assert lib.dsa_prefill(ctypes.byref(s), p, p, p, None, None, p, p, p, 1 << 40, None) == dsa.DSA_ERR_NULL
     assert lib.dsa_decode(ctypes.byref(s), p, p, p, None, p, None, p, p, 1 << 40, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_decode_noalloc(ctypes.byref(s), p, p, p, None, p, None, p, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_decode_noalloc(ctypes.byref(s), p, p, p, p, p, None, None, None) == dsa.DSA_ERR_NULL
     assert lib.dsa_block_means(ctypes.byref(s), 0, p, p, None) == dsa.DSA_ERR_SHAPE
 
 
@@ -185,6 +188,21 @@ def test_decode_specific_checks(lib):
     assert lib.dsa_decode_kmax(ctypes.byref(s), ctypes.byref(out)) == dsa.DSA_ERR_UNSUPPORTED
     z = shape(seq_len=0)
     assert lib.dsa_decode(ctypes.byref(z), p, p, p, p, p, None, p, p, 1 << 40, None) == dsa.DSA_ERR_SHAPE
+
+
+def test_noalloc_decode_scratch_covers_every_split_shape(lib):
+    """The split partials of every decode shape the library takes fit the
+    library-owned scratch of dsa_decode_noalloc (the fused path, >= 256
+    units, needs none): the largest split workspace over group sizes, head
+    dims, unit counts and budgets stays within DSA_DECODE_NOALLOC_MAX_BYTES."""
+    worst = 0
+    for G in (1, 2, 4, 8):
+        for d in (64, 128):
+            for S, Hkv in ((1, 1), (1, 8), (3, 7), (31, 8), (255, 1), (127, 2), (300, 1)):
+                for topk, L in ((1, 64), (4, 4096), (32, 65536), (4096, 64 * 4096), (700, 64 * 1000)):
+                    s = shape(batch=S, n_q_heads=Hkv * G, n_kv_heads=Hkv, seq_len=L, head_dim=d, topk=topk)
+                    worst = max(worst, lib.dsa_decode_workspace_bytes(ctypes.byref(s)))
+    assert 0 < worst <= 8 << 20
 
 
 def test_decode_takes_top_k_only(lib):
@@ -221,6 +239,7 @@ def test_empty_problems_are_no_ops(lib):
         assert lib.dsa_block_means(ctypes.byref(s), 4, p, p, None) == 0
     d = shape(batch=0)
     assert lib.dsa_decode(ctypes.byref(d), p, p, p, p, p, None, p, None, 0, None) == 0
+    assert lib.dsa_decode_noalloc(ctypes.byref(d), p, p, p, p, p, None, p, None) == 0
 
 
 @pytest.mark.parametrize("N,b,topk,num,den,flags", [
