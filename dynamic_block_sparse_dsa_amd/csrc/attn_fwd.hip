@@ -22,7 +22,7 @@
 //     assigns to its LDS slot -- the swizzle spreads the MFMA operand reads
 //     over all banks;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows are the A operand
-//     (ds_read_b128, read four k-steps ahead for 64-key tiles), Q^T the B
+//     (ds_read_b128), Q^T the B
 //     operand (registers, for the whole workgroup).
 //     One query row per lane (lanes l and l+32 hold the two key halves), so
 //     the row max and sum are in-lane plus one cross-half exchange;
@@ -30,6 +30,10 @@
 //     order; the V^T A operand comes straight from the row-major V tile with
 //     ds_read_b64_tr_b16 (within 16 lanes, lane i slot j receives element
 //     i % 4 of the 8-byte chunk of source lane 4j + i / 4);
+//   * LDS reads run ahead of the MFMAs that use them: K fragments four
+//     k-steps ahead for 64-key tiles and one for 128-key tiles, the V^T
+//     fragment of the next product one step ahead (without this the compiler
+//     puts every read right before its MFMA and waits for it);
 //   * the max is kept in raw logit units and 1/sqrt(d) * log2(e) is folded
 //     into the single FMA that feeds exp2; the running max is only raised
 //     (and O rescaled) when it grows by more than 8 (log2 units), which keeps
@@ -174,10 +178,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
     {
       // K fragments are read KLOOK k-steps ahead of the MFMAs that use them
       // (LDS latency exceeds two MFMAs); the scheduling barriers keep the
-      // compiler from sinking each read next to its use.  128-key tiles have
-      // no registers to spare for it.
+      // compiler from sinking each read next to its use.  128-key tiles
+      // (four MFMAs per k-step) have registers for one step.
       constexpr int NKS = D / 16, NST = BLK / 32;
-      constexpr int KLOOK = BLK == 64 ? 4 : 0;
+      constexpr int KLOOK = BLK == 64 ? 4 : 1;
       auto kread = [&](int ks, u32x4* dst) {
 #pragma unroll
         for (int st = 0; st < NST; ++st) {
@@ -250,28 +254,36 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
     // ---- V(t) resident (K(t+1) may be in flight)
     if (more) wait_vm<NV>(); else wait_vm<0>();
     __syncthreads();
-    // ---- O^T += V^T P^T, A operand by transposed LDS reads
+    // ---- O^T += V^T P^T, A operand by transposed LDS reads: the (d-tile,
+    // key-step) products in one sequence with the next step's V^T fragment in
+    // flight (the scheduling barriers keep each read a step ahead of its use)
     {
+      constexpr int KK = BLK / 16, NPV = (D / 32) * KK;
       const int grp = (lane >> 4) & 1, si = lane & 15;  // 16-lane group within the half; source index
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
+      auto vread = [&](int step, u32x4& vf) {
+        const int dt = step / KK, kk = step % KK;
         const int d = dt * 32 + 16 * grp + 4 * (si & 3);
         const int cbase = d >> 3, sub = (d & 7) * 2;  // 16-byte chunk and byte offset (0 or 8)
 #pragma unroll
-        for (int kk = 0; kk < BLK / 16; ++kk) {
-          u32x4 vf;
-#pragma unroll
-          for (int sg = 0; sg < 2; ++sg) {
-            const int key = 16 * kk + 8 * sg + 4 * half + (si >> 2);
-            const int c = cbase ^ vswz<D>(key);
-            const LDS_AS char* addr = reinterpret_cast<const LDS_AS char*>(vs_l + key * D + c * 8) + sub;
-            const i16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)addr);
-            const u32x2 w = __builtin_bit_cast(u32x2, v4);
-            vf[2 * sg] = w[0];
-            vf[2 * sg + 1] = w[1];
-          }
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[kk]), oacc[dt], 0, 0, 0);
+        for (int sg = 0; sg < 2; ++sg) {
+          const int key = 16 * kk + 8 * sg + 4 * half + (si >> 2);
+          const int c = cbase ^ vswz<D>(key);
+          const LDS_AS char* addr = reinterpret_cast<const LDS_AS char*>(vs_l + key * D + c * 8) + sub;
+          const i16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)addr);
+          const u32x2 w = __builtin_bit_cast(u32x2, v4);
+          vf[2 * sg] = w[0];
+          vf[2 * sg + 1] = w[1];
         }
+      };
+      u32x4 vb[2];
+      vread(0, vb[0]);
+#pragma unroll
+      for (int step = 0; step < NPV; ++step) {
+        if (step + 1 < NPV) vread(step + 1, vb[(step + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        oacc[step / KK] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vb[step & 1]), as_bf16x8(pf[step % KK]),
+                                                                 oacc[step / KK], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();  // every wave is done reading V(t)
