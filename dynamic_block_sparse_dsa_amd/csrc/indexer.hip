@@ -22,11 +22,13 @@
 // token_attn_kernel: one wave per (batch, token, KV head), KV-head-major over
 //   XCD-contiguous workgroups (one KV head's rows per XCD L2).  The kept
 //   positions arrive 64 at a time (one coalesced load, spread by lane
-//   shuffles); each 32-token chunk gathers its K rows in MFMA A-operand layout
-//   (16 rows x 64 bytes per wave load) and its V rows as 16-byte pieces of
-//   whole rows, two chunks in flight, and runs the decode path's chunk step:
-//   Q K^T on v_mfma_f32_16x16x32_bf16 (kept keys x the group's query heads),
-//   online softmax in fp32, P V in fp32 VALU.
+//   shuffles); one 32-token chunk at a time, its K rows go by DMA into a
+//   per-wave LDS tile (16 consecutive lanes per row, XOR-swizzled like the
+//   forward's K tile) and its V rows load as 16-byte pieces of whole rows;
+//   the wave waits for the K DMAs only, then runs the decode path's chunk
+//   step: Q K^T on v_mfma_f32_16x16x32_bf16 (kept keys, read back from the
+//   tile, x the group's query heads), online softmax in fp32, P V in fp32
+//   VALU.
 // select_tokens_fast_kernel: one wave per query-token row of up to 8192
 //   scores.  The row is read in 256-token chunks, lane l holding tokens
 //   4 l .. 4 l + 3 of each (one 16-byte load per lane, 1 KiB per wave
