@@ -410,12 +410,14 @@ def bench_selection(args, dev, stream, inputs):
 
 
 def bench_index(args, dev, stream):
-    """Token-level indexer workload: the chained step (wall clock) and each
-    of its three launches alone (HIP events).  Algorithmic work: index
-    scores 2 HI dI FLOP per causal (query token, token) pair (MFMA); token
-    selection reads the causal scores (4 bytes each); token attention reads
-    the kept tokens' K and V rows of every KV head (d * 2 bytes each) plus Q
-    and writes O."""
+    """Token-level indexer workload: the chained step (wall clock) and its
+    launches alone (HIP events): the fused index scores + token selection
+    (index_topk_kernel, plus index_merge_kernel for rows longer than one chunk
+    of keys) and the token attention.  Algorithmic work: index scores 2 HI dI
+    FLOP per causal (query token, token) pair (MFMA); token attention reads Q
+    and every KV head's K and V rows once and writes O (unique bytes, priced
+    against HBM), and gathers the kept tokens' K and V rows of every KV head
+    (d * 2 bytes each, mostly L2 hits)."""
     import torch
 
     import dynamic_block_sparse_dsa_amd as dsa
@@ -430,8 +432,7 @@ def bench_index(args, dev, stream):
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     idx = torch.empty((B, N, km), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, N), dtype=torch.int32, device=dev)
-    ws = torch.empty(dsa.dsa_index_workspace_bytes(shape), dtype=torch.uint8, device=dev)
-    sc = ws[: B * N * N * 4].view(torch.float32).view(B, N, N)
+    ws = torch.empty(max(1, dsa.dsa_index_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step():
@@ -446,8 +447,7 @@ def bench_index(args, dev, stream):
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     parts = dict(
-        scores=lambda: dsa.dsa_index_scores(shape, qi, ki, wi, sc, stream=stream),
-        select=lambda: dsa.dsa_select_tokens(shape, sc, idx, cnt, stream=stream),
+        topk=lambda: dsa.dsa_index_topk(shape, qi, ki, wi, idx, cnt, ws, stream=stream),
         attention=lambda: dsa.dsa_token_attn_fwd(shape, q, k, v, idx, cnt, o, lse, stream=stream),
     )
     us = {}
@@ -458,10 +458,11 @@ def bench_index(args, dev, stream):
     pairs = B * N * (N + 1) // 2
     flops = 2 * HI * dI * pairs
     kept = int(cnt.sum())
-    attn_bytes = kept * Hkv * d * 2 * 2 + 2 * B * Hq * N * d * 2
-    tf = flops / (us["scores"] * 1e-6) / 1e12
-    sel_gbs = pairs * 4 / (us["select"] * 1e-6) / 1e9
-    att_gbs = attn_bytes / (us["attention"] * 1e-6) / 1e9
+    gather_bytes = kept * Hkv * d * 2 * 2 + 2 * B * Hq * N * d * 2
+    unique_bytes = 2 * B * Hq * N * d * 2 + 2 * B * Hkv * N * d * 2
+    tf = flops / (us["topk"] * 1e-6) / 1e12
+    att_gbs = unique_bytes / (us["attention"] * 1e-6) / 1e9
+    fill_gbs = gather_bytes / (us["attention"] * 1e-6) / 1e9
     return dict(
         value=B * N / (ms_step * 1e-3), unit="tokens/s", ms_per_step=ms_step,
         config=dict(workload=w.name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, seq_len=N, head_dim=d, index_heads=HI,
@@ -469,14 +470,15 @@ def bench_index(args, dev, stream):
         kernels_us={kk: round(vv, 2) for kk, vv in us.items()},
         roofline=dict(bound="mfma", achieved=round(tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                       frac=round(tf / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic("index_" + w.name, INDEX_SRC),
-                      kernel="index_scores_kernel", flops_per_launch=flops),
-        select_roofline=dict(bound="hbm", achieved=round(sel_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                             frac=round(sel_gbs / PEAK_HBM_GBS, 4), bytes_per_launch=pairs * 4),
-        # the gathered rows come mostly from the L2s (the K/V of one KV head fit
-        # one XCD's L2), so the gather is priced against the L2 -> CU fill path
-        attention_roofline=dict(bound="l2 fill (gather)", achieved=round(att_gbs, 1), peak=round(PEAK_FILL_GBS, 1),
-                                unit="GB/s", frac=round(att_gbs / PEAK_FILL_GBS, 4), bytes_per_launch=attn_bytes,
-                                hbm_frac=round(att_gbs / PEAK_HBM_GBS, 4)),
+                      kernel="index_topk_kernel + index_merge_kernel", flops_per_launch=flops),
+        attention_roofline=dict(bound="hbm", achieved=round(att_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                                frac=round(att_gbs / PEAK_HBM_GBS, 4), bytes_per_launch=unique_bytes,
+                                mfma_frac=round(4 * Hq * kept * d / (us["attention"] * 1e-6) / 1e12
+                                                / PEAK_BF16_TFLOPS, 4),
+                                # the gathered rows come mostly from the L2s (the K and V of
+                                # one KV head fit one XCD's L2): the L2 -> CU fill rate
+                                gather_bytes=gather_bytes, gather_gbs=round(fill_gbs, 1),
+                                gather_frac_of_l2_fill=round(fill_gbs / PEAK_FILL_GBS, 4)),
     )
 
 

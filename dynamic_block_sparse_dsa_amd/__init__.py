@@ -42,6 +42,7 @@ EXPORTS = [
     "dsa_index_scores",
     "dsa_select_tokens",
     "dsa_token_attn_fwd",
+    "dsa_index_topk",
     "dsa_index_workspace_bytes",
     "dsa_index_prefill",
     "dsa_sparse_attn_fwd",
@@ -152,6 +153,7 @@ def load() -> ctypes.CDLL:
         "dsa_index_scores": ([X, P, P, P, P, P], ctypes.c_int),
         "dsa_select_tokens": ([X, P, P, P, P], ctypes.c_int),
         "dsa_token_attn_fwd": ([X, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "dsa_index_topk": ([X, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "dsa_index_workspace_bytes": ([X], SZ),
         "dsa_index_prefill": ([X, P, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "dsa_sparse_attn_fwd": ([S, P, P, P, P, P, P, P, P], ctypes.c_int),
@@ -312,6 +314,16 @@ def dsa_select_tokens(shape: IndexShape, scores, idx, cnt, stream=None):
     _check(load().dsa_select_tokens(ctypes.byref(shape), _ptr(scores, torch.float32, (B, N, N), "scores"),
                                     _ptr(idx, torch.int32, (B, N, km), "idx"), _ptr(cnt, torch.int32, (B, N), "cnt"),
                                     _stream(stream)))
+
+
+def dsa_index_topk(shape: IndexShape, qi, ki, wi, idx, cnt, ws, stream=None):
+    B, _, _, N, _, HI, dI = _index_dims(shape)
+    km = dsa_index_kmax(shape)
+    wp, wb = _ws(ws, dsa_index_workspace_bytes(shape))
+    _check(load().dsa_index_topk(ctypes.byref(shape), _ptr(qi, torch.bfloat16, (B, N, HI, dI), "qi"),
+                                 _ptr(ki, torch.bfloat16, (B, N, dI), "ki"), _ptr(wi, torch.float32, (B, N, HI), "wi"),
+                                 _ptr(idx, torch.int32, (B, N, km), "idx"), _ptr(cnt, torch.int32, (B, N), "cnt"),
+                                 wp, wb, _stream(stream)))
 
 
 def dsa_token_attn_fwd(shape: IndexShape, q, k, v, idx, cnt, o, lse=None, stream=None):

@@ -127,8 +127,6 @@ int check_index(const dsa_index_shape* s) {
   if (!s) return fail(DSA_ERR_NULL, "shape is NULL");
   if (s->batch < 0) return fail(DSA_ERR_SHAPE, "batch %d < 0", s->batch);
   if (s->seq_len < 0) return fail(DSA_ERR_SHAPE, "seq_len %d < 0", s->seq_len);
-  if (s->seq_len > DSA_MAX_TOKENS)
-    return fail(DSA_ERR_UNSUPPORTED, "seq_len %d > %d tokens", s->seq_len, DSA_MAX_TOKENS);
   if (s->n_q_heads < 1 || s->n_kv_heads < 1 || s->n_q_heads % s->n_kv_heads != 0)
     return fail(DSA_ERR_SHAPE, "head counts Hq %d, Hkv %d", s->n_q_heads, s->n_kv_heads);
   const int G = s->n_q_heads / s->n_kv_heads;
@@ -459,6 +457,7 @@ int dsa_select_tokens(const dsa_index_shape* s, const float* scores, int32_t* id
   if (s->batch == 0 || s->seq_len == 0) return DSA_OK;
   if (!scores || !idx || !cnt) return fail(DSA_ERR_NULL, "scores, idx or cnt is NULL");
   const int N = s->seq_len;
+  if (N > DSA_MAX_TOKENS) return fail(DSA_ERR_UNSUPPORTED, "seq_len %d > %d tokens", N, DSA_MAX_TOKENS);
   hipError_t e = dsa::launch_select_tokens(scores, idx, cnt, (int64_t)s->batch * N, N, token_params(s), index_kmax(s),
                                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "select_tokens launch");
@@ -492,9 +491,34 @@ int dsa_token_attn_fwd(const dsa_index_shape* s, const void* q, const void* k, c
   return DSA_OK;
 }
 
+// the fused selection takes rows of up to INDEX_TOPK_MAX_KEEP kept tokens;
+// longer rows go through the scores array
+bool index_fused(const dsa_index_shape* s) { return index_kmax(s) <= dsa::INDEX_TOPK_MAX_KEEP; }
+
 size_t dsa_index_workspace_bytes(const dsa_index_shape* s) {
   if (check_index(s)) return 0;
+  if (index_fused(s)) return align256(dsa::plan_index_topk(s->batch, s->seq_len, index_kmax(s)).ws_bytes);
   return align256((size_t)s->batch * s->seq_len * s->seq_len * 4);
+}
+
+int dsa_index_topk(const dsa_index_shape* s, const void* qi, const void* ki, const float* wi, int32_t* idx,
+                   int32_t* cnt, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_index(s);
+  if (rc) return rc;
+  if (s->batch == 0 || s->seq_len == 0) return DSA_OK;
+  if (!qi || !ki || !wi || !idx || !cnt) return fail(DSA_ERR_NULL, "qi, ki, wi, idx or cnt is NULL");
+  const int kmax = index_kmax(s);
+  if (!index_fused(s))
+    return fail(DSA_ERR_UNSUPPORTED, "%d kept tokens per row > %d", kmax, dsa::INDEX_TOPK_MAX_KEEP);
+  const size_t need = align256(dsa::plan_index_topk(s->batch, s->seq_len, kmax).ws_bytes);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
+  hipError_t e = dsa::launch_index_topk(static_cast<const uint16_t*>(qi), static_cast<const uint16_t*>(ki), wi, idx,
+                                        cnt, ws, s->batch, s->seq_len, s->index_dim, token_params(s), kmax,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "index_topk launch");
+  g_err[0] = 0;
+  return DSA_OK;
 }
 
 int dsa_index_prefill(const dsa_index_shape* s, const void* qi, const void* ki, const float* wi, const void* q,
@@ -505,6 +529,14 @@ int dsa_index_prefill(const dsa_index_shape* s, const void* qi, const void* ki, 
   if (s->batch == 0 || s->seq_len == 0) return DSA_OK;
   if (!qi || !ki || !wi || !q || !k || !v || !o || !idx || !cnt)
     return fail(DSA_ERR_NULL, "qi, ki, wi, q, k, v, o, idx or cnt is NULL");
+  if (index_fused(s)) {
+    rc = dsa_index_topk(s, qi, ki, wi, idx, cnt, ws, ws_bytes, stream);
+    if (rc) return rc;
+    return dsa_token_attn_fwd(s, q, k, v, idx, cnt, o, lse, stream);
+  }
+  if (s->seq_len > DSA_MAX_TOKENS)
+    return fail(DSA_ERR_UNSUPPORTED, "seq_len %d > %d tokens with %d kept per row", s->seq_len, DSA_MAX_TOKENS,
+                index_kmax(s));
   const size_t need = dsa_index_workspace_bytes(s);
   if (!ws || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);

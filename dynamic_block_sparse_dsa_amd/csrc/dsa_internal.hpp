@@ -100,6 +100,31 @@ hipError_t launch_select_tokens(const float* scores, int32_t* idx, int32_t* cnt,
 hipError_t launch_select_marked(const float* scores, int32_t* idx, int32_t* cnt, int64_t n_rows, int N, TopkParams p,
                                 int kmax, hipStream_t stream);
 
+// fused index scores + token selection: token tiles of 16 x chunks of kct
+// key tiles of 64; rows whose keys span several chunks keep a list per chunk
+// (the best m of it) in the workspace, merged by a second kernel
+constexpr int INDEX_TOPK_MAX_KEEP = 128;  // kmax the candidate lists take
+constexpr int INDEX_TOPK_MAX_CHUNKS = 2;
+struct IndexTopkArgs {
+  const uint16_t* qi;  // [B, N, 16, dI]
+  const uint16_t* ki;  // [B, N, dI]
+  const float* wi;     // [B, N, 16]
+  int32_t* idx;        // [B, N, kmax]
+  int32_t* cnt;        // [B, N]
+  uint32_t* part_key;  // [B, N, nch, mw] order keys of a chunk's list
+  int32_t* part_idx;   // [B, N, nch, mw] their positions
+  int32_t* part_cnt;   // [B, N, nch]
+  int N, n_tt, kct, nch, mw, kmax;
+  TopkParams p;
+};
+struct IndexTopkPlan {
+  int kct, nch, mw;
+  size_t ws_bytes;
+};
+IndexTopkPlan plan_index_topk(int B, int N, int kmax);
+hipError_t launch_index_topk(const uint16_t* qi, const uint16_t* ki, const float* wi, int32_t* idx, int32_t* cnt,
+                             void* ws, int B, int N, int di, TopkParams p, int kmax, hipStream_t stream);
+
 struct TokenAttnArgs {
   const uint16_t* q;    // [B, Hq, N, d]
   const uint16_t* k;    // [B, Hkv, N, d]

@@ -79,61 +79,51 @@ __device__ __forceinline__ float relu_bits(float x) {
 }
 
 // ============================================================== index scores
+// The index query rows, head weights and token numbers of a wave's four query
+// tokens t0 + 4 wave .. t0 + 4 wave + 3, and the scores of a 64-key LDS tile
+// against them.  A operands: row (lane % 32) of pair tile ct is the (token,
+// index head) pair (t0 + 4 wave + 2 ct + (lane % 32) / 16, lane % 16).
 template <int DI>
-__global__ __launch_bounds__(256) void index_scores_kernel(const uint16_t* __restrict__ qi,
-                                                           const uint16_t* __restrict__ ki,
-                                                           const float* __restrict__ wi, float* __restrict__ scores,
-                                                           int N, int tiles_per_b) {
-  constexpr int HI = 16, NKS = DI / 16, KT = 64, TPW = 4, TPB = 4 * TPW;
-  __shared__ __align__(1024) uint16_t kt_lds[2][KT * DI];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int half = lane >> 5, i16 = lane & 15;
-  const int64_t b = blockIdx.x / tiles_per_b;
-  const int tile = tiles_per_b - 1 - (int)(blockIdx.x % tiles_per_b);
-  const int t0 = tile * TPB;
-  const int n_kt = (min(t0 + TPB, N) - 1) / KT + 1;
-
-  // A operands: row (lane % 32) of pair tile ct is the (token, index head)
-  // pair (t0 + 4 wave + 2 ct + (lane % 32) / 16, lane % 16)
+struct IndexRows {
+  static constexpr int HI = 16, NKS = DI / 16;
   u32x4 qf[2][NKS];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int tk = t0 + TPW * wave + 2 * ct + ((lane & 31) >> 4);
-    const uint16_t* qrow = qi + ((b * N + min(tk, N - 1)) * HI + i16) * DI;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ct][ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + 8 * half);
-  }
-  // Output register r of lane l holds key l % 32 and pair row
-  // 8 (r / 4) + 4 half + r % 4: registers 0..7 are token 2 ct (heads
-  // 4 half + r % 4 and 8 + 4 half + r % 4), 8..15 token 2 ct + 1, same heads.
-  // wr: the head weight of each register; the lane stores token 2 ct + half.
   float wr[2][16];
-  int tok[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = t0 + TPW * wave + 2 * ct + (r >> 3);
-      const int hd = 8 * ((r >> 2) & 1) + 4 * half + (r & 3);
-      wr[ct][r] = wi[(b * N + min(tr, N - 1)) * HI + hd];
-    }
-    tok[ct] = t0 + TPW * wave + 2 * ct + half;
-  }
-  const uint16_t* kb = ki + b * (int64_t)N * DI;
-  const uint32_t base[2] = {(uint32_t)(uintptr_t)(LDS_AS uint16_t*)kt_lds[0],
-                            (uint32_t)(uintptr_t)(LDS_AS uint16_t*)kt_lds[1]};
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(qf[ct][ks]));
-  load_key_tile<DI>(kb, 0, N, base[0], wave, lane);
+  int tok[2];  // the token whose scores the lane ends with, per pair tile
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    wait_vm<0>();
-    __syncthreads();  // tile kt resident; every wave is done with tile kt - 1
-    if (kt + 1 < n_kt) load_key_tile<DI>(kb, (kt + 1) * KT, N, base[(kt + 1) & 1], wave, lane);
-    const LDS_AS uint16_t* tl = (const LDS_AS uint16_t*)kt_lds[kt & 1];
+  __device__ __forceinline__ void load(const uint16_t* qi, const float* wi, int64_t b, int N, int t0, int wave,
+                                       int lane) {
+    const int half = lane >> 5, i16 = lane & 15;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int tk = t0 + 4 * wave + 2 * ct + ((lane & 31) >> 4);
+      const uint16_t* qrow = qi + ((b * N + min(tk, N - 1)) * HI + i16) * DI;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ct][ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + 8 * half);
+    }
+    // Output register r of lane l holds key l % 32 and pair row
+    // 8 (r / 4) + 4 half + r % 4: registers 0..7 are token 2 ct (heads
+    // 4 half + r % 4 and 8 + 4 half + r % 4), 8..15 token 2 ct + 1, same
+    // heads.  wr: the head weight of each register; the lane ends with the
+    // score of token 2 ct + half.
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tr = t0 + 4 * wave + 2 * ct + (r >> 3);
+        const int hd = 8 * ((r >> 2) & 1) + 4 * half + (r & 3);
+        wr[ct][r] = wi[(b * N + min(tr, N - 1)) * HI + hd];
+      }
+      tok[ct] = t0 + 4 * wave + 2 * ct + half;
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(qf[ct][ks]));
+  }
+
+  // s[rt][ct]: the score of key 32 rt + lane % 32 of the tile for token tok[ct]
+  __device__ __forceinline__ void tile(const LDS_AS uint16_t* tl, int lane, float (&s)[2][2]) const {
+    const int half = lane >> 5;
     f32x16 acc[2][2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -150,9 +140,10 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const uint16_t* __res
                                                                 0, 0);
       }
     }
-    // ReLU, head weight, sum over the heads: 8 of each token in the lane,
-    // the other 8 in lane l ^ 32, which gets this lane's partial of the token
-    // it stores and sends its own
+    // ReLU, head weight, sum over the heads: 8 of each token in the lane
+    // (p0: token 2 ct, p1: token 2 ct + 1), the other 8 in lane l ^ 32.  One
+    // swap of p0's upper 32 lanes with p1's lower 32 lanes leaves, in every
+    // lane, the two partials of the token the lane keeps (2 ct + half).
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
@@ -163,13 +154,359 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const uint16_t* __res
           p0 = __builtin_fmaf(relu_bits(acc[rt][ct][r]), wr[ct][r], p0);
           p1 = __builtin_fmaf(relu_bits(acc[rt][ct][8 + r]), wr[ct][8 + r], p1);
         }
-        const float give = half ? p0 : p1, keep = half ? p1 : p0;
-        const float sum = keep + __shfl_xor(give, 32, 64);
-        const int key = kt * KT + rt * 32 + (lane & 31);
-        if (tok[ct] < N && key <= tok[ct]) scores[(b * N + tok[ct]) * (int64_t)N + key] = sum;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+        s[rt][ct] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
     }
   }
+};
+
+template <int DI>
+__global__ __launch_bounds__(256) void index_scores_kernel(const uint16_t* __restrict__ qi,
+                                                           const uint16_t* __restrict__ ki,
+                                                           const float* __restrict__ wi, float* __restrict__ scores,
+                                                           int N, int tiles_per_b) {
+  constexpr int KT = 64, TPB = 16;
+  __shared__ __align__(1024) uint16_t kt_lds[2][KT * DI];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t b = blockIdx.x / tiles_per_b;
+  const int tile = tiles_per_b - 1 - (int)(blockIdx.x % tiles_per_b);
+  const int t0 = tile * TPB;
+  const int n_kt = (min(t0 + TPB, N) - 1) / KT + 1;
+
+  IndexRows<DI> rows;
+  rows.load(qi, wi, b, N, t0, wave, lane);
+  const uint16_t* kb = ki + b * (int64_t)N * DI;
+  const uint32_t base[2] = {(uint32_t)(uintptr_t)(LDS_AS uint16_t*)kt_lds[0],
+                            (uint32_t)(uintptr_t)(LDS_AS uint16_t*)kt_lds[1]};
+  load_key_tile<DI>(kb, 0, N, base[0], wave, lane);
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    wait_vm<0>();
+    __syncthreads();  // tile kt resident; every wave is done with tile kt - 1
+    if (kt + 1 < n_kt) load_key_tile<DI>(kb, (kt + 1) * KT, N, base[(kt + 1) & 1], wave, lane);
+    float s[2][2];
+    rows.tile((const LDS_AS uint16_t*)kt_lds[kt & 1], lane, s);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int key = kt * KT + rt * 32 + (lane & 31), t = rows.tok[ct];
+        if (t < N && key <= t) scores[(b * N + t) * (int64_t)N + key] = s[rt][ct];
+      }
+  }
+}
+
+// ============================================================== fused scores + token selection
+// Kept tokens of a row (ties to the lower position):
+//   nv = t + 1 visible, the first na = min(anchors, nv) (the sink) and the
+//   last nv - ws (ws = max(nv - window, na); the token itself) forced, and the
+//   best m = min(max(topk, nf), nv) - nf of the candidates na <= s < ws.
+struct TokenRow {
+  int nv, na, ws, m;
+  __device__ __forceinline__ TokenRow(int t, const TopkParams& p) {
+    nv = t + 1;
+    na = min(p.anchors, nv);
+    ws = max(nv - p.window, na);
+    const int nf = na + nv - ws;
+    m = min(max(p.topk, nf), nv) - nf;
+  }
+};
+
+// order_key's inverse: the float whose key is k (k > 0)
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Streaming top-m of one wave-held candidate list (CAP scores as fp32 bits
+// and their positions in LDS, index order; 4 per lane, lane l holding entries
+// 4 l .. 4 l + 3), ranked by their order keys.
+// Keeps every entry >= T for the T the search ends at: the search starts at
+// the common leading bits of the largest and smallest key and sets one more
+// bit at a time while at least m entries stay at or above it, stopping as
+// soon as at most `limit` remain.  If it runs out of bits first (T is then
+// the m-th largest key exactly), the entries equal to T are cut to the
+// lowest positions so that exactly m are kept.  Either way every dropped
+// entry has m better ones (larger, or equal at a lower position), and so has
+// every later (higher) position whose key does not exceed T: *thr becomes the
+// acceptance threshold of later keys.  Returns the new count.
+template <int CAP>
+__device__ int compact_candidates(LDS_AS uint32_t* vals, LDS_AS int32_t* ids, int cnum, int m, int limit,
+                                  uint32_t* thr, int lane) {
+  static_assert(CAP == 256, "four entries per lane");
+  const u32x4 fv = *reinterpret_cast<const LDS_AS u32x4*>(vals + 4 * lane);
+  const u32x4 iv = *reinterpret_cast<const LDS_AS u32x4*>(ids + 4 * lane);
+  uint32_t k[4];
+  uint32_t mx = 0u, mn = ~0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    k[e] = 4 * lane + e < cnum ? order_key(__uint_as_float(fv[e])) : 0u;
+    if (k[e]) {
+      mx = max(mx, k[e]);
+      mn = min(mn, k[e]);
+    }
+  }
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  const uint32_t x = mx ^ mn;
+  int bit = x ? 31 - __builtin_clz(x) : -1;
+  uint32_t T = x ? (mx & ~(uint32_t)(((uint64_t)2 << bit) - 1u)) : mx;
+  int nT = cnum;
+  for (; bit >= 0 && nT > limit; --bit) {
+    const uint32_t trial = T | (1u << bit);
+    const int c = wave_count_ge<4>(k, trial);
+    if (c >= m) {
+      T = trial;
+      nT = c;
+    }
+  }
+  const bool cut = nT > limit;
+  const int n_gt = cut ? (T == ~0u ? 0 : wave_count_ge<4>(k, T + 1u)) : 0;
+  int my_eq = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) my_eq += k[e] == T;
+  int r = wave_incl_scan(my_eq) - my_eq;  // entries equal to T before this lane's
+  bool keep[4];
+  int mine = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    keep[e] = k[e] > T || (k[e] == T && (!cut || r < m - n_gt));
+    r += k[e] == T;
+    mine += keep[e];
+  }
+  const int incl = wave_incl_scan(mine);
+  int pos = incl - mine;
+  wave_lds_sync();  // every lane holds its entries before any is overwritten
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (keep[e]) {
+      vals[pos] = fv[e];
+      ids[pos] = (int32_t)iv[e];
+      ++pos;
+    }
+  wave_lds_sync();
+  *thr = max(*thr, T);
+  return __builtin_amdgcn_readlane(incl, 63);
+}
+
+// One unit = 16 query tokens x one chunk of kct key tiles.  Chunk c of token
+// tile tt exists for tt >= 4 c kct (the tile's keys reach past c kct tiles);
+// units run chunk-major, latest tiles first.  Per 64-key tile the scores come
+// from IndexRows::tile; each lane then holds two scores of each of two
+// tokens (32 consecutive keys of a token per half-wave), and a key joins its
+// token's candidate list (LDS, index order, the score's bits) when it is a
+// candidate and its score exceeds the token's threshold (-inf until the first
+// compaction; compared as floats, which orders like the keys).  A list that
+// may overflow on the next tile is compacted (compact_candidates, at most
+// m + 32 left).  At the end each list is cut to its best m: a tile whose keys
+// fit one chunk writes its final rows; otherwise each chunk's list goes to
+// the workspace (as order keys) for index_merge_kernel.
+template <int DI>
+__global__ __launch_bounds__(256) void index_topk_kernel(const IndexTopkArgs a) {
+  constexpr int KT = 64, TPB = 16, CAP = 256;
+  __shared__ __align__(1024) uint16_t kt_lds[2][KT * DI];
+  __shared__ __align__(16) uint32_t ckey[4][4][CAP];
+  __shared__ __align__(16) int32_t cid[4][4][CAP];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int64_t b = blockIdx.y;
+  const int N = a.N;
+  int u = blockIdx.x, c = 0;
+  for (; c < a.nch; ++c) {
+    const int uc = a.n_tt - 4 * c * a.kct;
+    if (u < uc) break;
+    u -= uc;
+  }
+  if (c >= a.nch) return;  // whole workgroup, before any barrier
+  const int tt = a.n_tt - 1 - u;
+  const int t0 = tt * TPB;
+  const int n_kt = (min(t0 + TPB, N) - 1) / KT + 1;
+  const int n_c = (n_kt - 1) / a.kct + 1;
+  const int kt0 = c * a.kct, kt1 = min(kt0 + a.kct, n_kt);
+
+  IndexRows<DI> rows;
+  rows.load(a.qi, a.wi, b, N, t0, wave, lane);
+  // candidate range [lo, lo + span) of the lane's tokens (span 0: none),
+  // budget m, threshold as an order key and as a float
+  int lo[2], span[2], mr[2], n[2] = {0, 0};
+  uint32_t thr[2] = {0u, 0u};
+  float thf[2] = {-__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const TokenRow tr(rows.tok[ct], a.p);
+    lo[ct] = tr.na;
+    span[ct] = rows.tok[ct] < N && tr.m > 0 ? tr.ws - tr.na : 0;
+    mr[ct] = tr.m;
+  }
+  const uint16_t* kb = a.ki + b * (int64_t)N * DI;
+  const uint32_t base[2] = {(uint32_t)(uintptr_t)(LDS_AS uint16_t*)kt_lds[0],
+                            (uint32_t)(uintptr_t)(LDS_AS uint16_t*)kt_lds[1]};
+  load_key_tile<DI>(kb, kt0 * KT, N, base[0], wave, lane);
+
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int i = kt - kt0;
+    wait_vm<0>();
+    __syncthreads();  // tile i resident; every wave is done with tile i - 1
+    if (kt + 1 < kt1) load_key_tile<DI>(kb, (kt + 1) * KT, N, base[(i + 1) & 1], wave, lane);
+    float s[2][2];
+    rows.tile((const LDS_AS uint16_t*)kt_lds[i & 1], lane, s);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int key = kt * KT + rt * 32 + (lane & 31);
+        const bool take = (s[rt][ct] > thf[ct]) & ((uint32_t)(key - lo[ct]) < (uint32_t)span[ct]);
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
+        const uint32_t lo32 = (uint32_t)bal, hi32 = (uint32_t)(bal >> 32);
+        // slot position: the half's count so far plus its taken lanes below
+        const int pos = n[ct] + lanes_below(bal) - (half ? __builtin_popcount(lo32) : 0);
+        if (take) {
+          ckey[wave][2 * ct + half][pos] = __float_as_uint(s[rt][ct]);
+          cid[wave][2 * ct + half][pos] = key;
+        }
+        n[ct] += __builtin_popcount(half ? hi32 : lo32);
+      }
+    }
+    // a list past CAP - 64 could overflow on the next tile
+    if (__builtin_amdgcn_ballot_w64(max(n[0], n[1]) > CAP - 64)) {
+      wave_lds_sync();
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int ct = sl >> 1, src = 32 * (sl & 1);
+        const int cs = __builtin_amdgcn_readlane(n[ct], src);
+        if (cs > CAP - 64) {
+          const int ms = __builtin_amdgcn_readlane(mr[ct], src);
+          uint32_t th = (uint32_t)__builtin_amdgcn_readlane((int)thr[ct], src);
+          const int nn = compact_candidates<CAP>((LDS_AS uint32_t*)ckey[wave][sl], (LDS_AS int32_t*)cid[wave][sl], cs,
+                                                      ms, ms + 32, &th, lane);
+          if ((sl & 1) == half) {
+            n[ct] = nn;
+            thr[ct] = th;
+            thf[ct] = key_float(th);
+          }
+        }
+      }
+    }
+  }
+  wave_lds_sync();
+
+  // the best m of each list; then the final row or the chunk's list
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    const int t = t0 + 4 * wave + sl;
+    if (t >= N) break;
+    const int ct = sl >> 1, src = 32 * (sl & 1);
+    int cs = __builtin_amdgcn_readlane(n[ct], src);
+    const TokenRow tr(t, a.p);
+    if (cs > tr.m) {
+      uint32_t th = 0u;
+      cs = compact_candidates<CAP>((LDS_AS uint32_t*)ckey[wave][sl], (LDS_AS int32_t*)cid[wave][sl], cs, tr.m, tr.m,
+                                    &th, lane);
+    }
+    const int64_t row = b * N + t;
+    if (n_c == 1) {
+      int32_t* out = a.idx + row * a.kmax;
+      for (int e = lane; e < tr.na; e += 64) out[e] = e;
+      for (int e = lane; e < cs; e += 64) out[tr.na + e] = cid[wave][sl][e];
+      for (int e = lane; e < tr.nv - tr.ws; e += 64) out[tr.na + cs + e] = tr.ws + e;
+      const int total = tr.na + cs + (tr.nv - tr.ws);
+      for (int e = total + lane; e < a.kmax; e += 64) out[e] = -1;
+      if (lane == 0) a.cnt[row] = total;
+    } else {
+      const int64_t slab = row * a.nch + c;
+      for (int e = lane; e < cs; e += 64) {
+        a.part_key[slab * a.mw + e] = order_key(__uint_as_float(ckey[wave][sl][e]));
+        a.part_idx[slab * a.mw + e] = cid[wave][sl][e];
+      }
+      if (lane == 0) a.part_cnt[slab] = cs;
+    }
+  }
+}
+
+// One wave per row of a multi-chunk token tile (t >= t_first): the chunks'
+// lists (each the best m of its keys, index order) concatenated in chunk
+// order are in index order; lane l holds positions R l .. R l + R - 1 of the
+// padded [n_c, mw] array.  The best m of the union are those of the row.
+template <int R>
+__global__ __launch_bounds__(256) void index_merge_kernel(const IndexTopkArgs a, int t_first, int B) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int N = a.N;
+  const int64_t rows_per_b = N - t_first;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= B * rows_per_b) return;  // whole wave; no workgroup barrier below
+  const int64_t b = w / rows_per_b;
+  const int t = t_first + (int)(w % rows_per_b);
+  const int n_kt = (min((t / 16 + 1) * 16, N) - 1) / 64 + 1;
+  const int n_c = (n_kt - 1) / a.kct + 1;
+  const TokenRow tr(t, a.p);
+  const int64_t row = b * N + t;
+  const int64_t slab0 = row * a.nch;
+  uint32_t k[R];
+  int32_t id[R];
+#pragma unroll
+  for (int e = 0; e < R; ++e) {
+    const int p = R * lane + e;
+    const int sl = p / a.mw, j = p - sl * a.mw;
+    const bool ok = sl < n_c && j < a.part_cnt[slab0 + min(sl, n_c - 1)];
+    k[e] = ok ? a.part_key[(slab0 + sl) * a.mw + j] : 0u;
+    id[e] = ok ? a.part_idx[(slab0 + sl) * a.mw + j] : 0;
+  }
+  const int total = wave_count_ge<R>(k, 1u);
+  uint32_t T = 1u;
+  bool cut = false;
+  int n_gt = 0;
+  if (total > tr.m) {
+    uint32_t mx = 0u, mn = ~0u;
+#pragma unroll
+    for (int e = 0; e < R; ++e)
+      if (k[e]) {
+        mx = max(mx, k[e]);
+        mn = min(mn, k[e]);
+      }
+    mx = wave_max_u32(mx);
+    mn = wave_min_u32(mn);
+    const uint32_t x = mx ^ mn;
+    int bit = x ? 31 - __builtin_clz(x) : -1;
+    T = x ? (mx & ~(uint32_t)(((uint64_t)2 << bit) - 1u)) : mx;
+    int nT = total;
+    for (; bit >= 0 && nT > tr.m; --bit) {
+      const uint32_t trial = T | (1u << bit);
+      const int cc = wave_count_ge<R>(k, trial);
+      if (cc >= tr.m) {
+        T = trial;
+        nT = cc;
+      }
+    }
+    cut = nT > tr.m;
+    n_gt = cut ? (T == ~0u ? 0 : wave_count_ge<R>(k, T + 1u)) : 0;
+  }
+  int my_eq = 0;
+#pragma unroll
+  for (int e = 0; e < R; ++e) my_eq += k[e] == T;
+  int r = wave_incl_scan(my_eq) - my_eq;
+  bool keep[R];
+  int mine = 0;
+#pragma unroll
+  for (int e = 0; e < R; ++e) {
+    keep[e] = k[e] > T || (k[e] == T && (!cut || r < tr.m - n_gt));
+    r += k[e] == T;
+    mine += keep[e];
+  }
+  const int incl = wave_incl_scan(mine);
+  const int nsel = __builtin_amdgcn_readlane(incl, 63);
+  int32_t* out = a.idx + row * a.kmax;
+  int pos = tr.na + incl - mine;
+#pragma unroll
+  for (int e = 0; e < R; ++e)
+    if (keep[e]) out[pos++] = id[e];
+  for (int e = lane; e < tr.na; e += 64) out[e] = e;
+  for (int e = lane; e < tr.nv - tr.ws; e += 64) out[tr.na + nsel + e] = tr.ws + e;
+  const int tot = tr.na + nsel + (tr.nv - tr.ws);
+  for (int e = tot + lane; e < a.kmax; e += 64) out[e] = -1;
+  if (lane == 0) a.cnt[row] = tot;
 }
 
 // ============================================================== token attention
@@ -446,6 +783,56 @@ static hipError_t launch_token_attn_d(const TokenAttnArgs& a, hipStream_t stream
     default: return hipErrorInvalidValue;
   }
 #undef DSA_TOKEN_ATTN
+  return hipGetLastError();
+}
+
+IndexTopkPlan plan_index_topk(int B, int N, int kmax) {
+  IndexTopkPlan pl{};
+  const int n_kt = (N + 63) / 64;
+  pl.kct = max(64, (n_kt + INDEX_TOPK_MAX_CHUNKS - 1) / INDEX_TOPK_MAX_CHUNKS);
+  pl.nch = max(1, (n_kt + pl.kct - 1) / pl.kct);
+  pl.mw = max(kmax, 1);
+  pl.ws_bytes = pl.nch > 1 ? (size_t)B * N * pl.nch * (8 * (size_t)pl.mw + 4) : 0;
+  return pl;
+}
+
+hipError_t launch_index_topk(const uint16_t* qi, const uint16_t* ki, const float* wi, int32_t* idx, int32_t* cnt,
+                             void* ws, int B, int N, int di, TopkParams p, int kmax, hipStream_t stream) {
+  if (B == 0 || N == 0) return hipSuccess;
+  if (kmax > INDEX_TOPK_MAX_KEEP) return hipErrorInvalidValue;
+  const IndexTopkPlan pl = plan_index_topk(B, N, kmax);
+  IndexTopkArgs a{};
+  a.qi = qi;
+  a.ki = ki;
+  a.wi = wi;
+  a.idx = idx;
+  a.cnt = cnt;
+  const size_t n_slab = (size_t)B * N * pl.nch;
+  a.part_key = pl.nch > 1 ? static_cast<uint32_t*>(ws) : nullptr;
+  a.part_idx = pl.nch > 1 ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + n_slab * pl.mw * 4) : nullptr;
+  a.part_cnt = pl.nch > 1 ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + n_slab * pl.mw * 8) : nullptr;
+  a.N = N;
+  a.n_tt = (N + 15) / 16;
+  a.kct = pl.kct;
+  a.nch = pl.nch;
+  a.mw = pl.mw;
+  a.kmax = kmax;
+  a.p = p;
+  int64_t units = 0;
+  for (int c = 0; c < pl.nch; ++c) units += a.n_tt - 4 * c * pl.kct;
+  const dim3 grid((uint32_t)units, (uint32_t)B), blk(256);
+  if (di == 64) hipLaunchKernelGGL(index_topk_kernel<64>, grid, blk, 0, stream, a);
+  else hipLaunchKernelGGL(index_topk_kernel<128>, grid, blk, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.nch == 1) return e;
+  const int t_first = 64 * pl.kct;
+  const int64_t rows = (int64_t)B * (N - t_first);
+  const dim3 mgrid((uint32_t)((rows + 3) / 4));
+  const int pos = pl.nch * pl.mw;
+  if (pos <= 128) hipLaunchKernelGGL(index_merge_kernel<2>, mgrid, blk, 0, stream, a, t_first, B);
+  else if (pos <= 256) hipLaunchKernelGGL(index_merge_kernel<4>, mgrid, blk, 0, stream, a, t_first, B);
+  else if (pos <= 512) hipLaunchKernelGGL(index_merge_kernel<8>, mgrid, blk, 0, stream, a, t_first, B);
+  else hipLaunchKernelGGL(index_merge_kernel<16>, mgrid, blk, 0, stream, a, t_first, B);
   return hipGetLastError();
 }
 

@@ -227,6 +227,7 @@ INDEX_WORKLOADS = {
     for w in [
         IndexWorkload("index_tiny_n512", 1, 4, 2, 512, 64, 16, 64, 64, clusters=16, amplitude=4.0, seed=10),
         IndexWorkload("index_n8192", 1, 32, 8, 8192, 128, 16, 128, 64, clusters=128, amplitude=4.0, seed=11),
+        IndexWorkload("index_n32768", 1, 32, 8, 32768, 128, 16, 128, 64, clusters=512, amplitude=4.0, seed=12),
     ]
 }
 

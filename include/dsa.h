@@ -382,13 +382,14 @@ int dsa_paged_kv_block_means_fp8(const dsa_shape* shape, const uint8_t* k8, cons
  * [B, Hq, N, d] bf16; k, v [B, Hkv, N, d] bf16; lse [B, Hq, N] fp32
  * (natural log, nullable).  Query head h reads KV head h / (Hq / Hkv). */
 #define DSA_INDEX_HEADS 16  /* HI, the only index head count built */
-#define DSA_MAX_TOKENS 8192 /* longest sequence the token selection takes */
+#define DSA_MAX_TOKENS 8192 /* longest sequence dsa_select_tokens takes (rows of the scores array) */
+#define DSA_INDEX_TOPK_MAX_KEEP 128 /* longest kept row (kmax) dsa_index_topk takes */
 
 typedef struct dsa_index_shape {
   int32_t batch;         /* B >= 0 */
   int32_t n_q_heads;     /* Hq >= 1 */
   int32_t n_kv_heads;    /* Hkv >= 1, Hq / Hkv in {1, 2, 4, 8} */
-  int32_t seq_len;       /* N, 0 <= N <= DSA_MAX_TOKENS */
+  int32_t seq_len;       /* N >= 0 (B * N * Hq < 2^31) */
   int32_t head_dim;      /* d: 64 or 128 */
   int32_t n_index_heads; /* HI: DSA_INDEX_HEADS */
   int32_t index_dim;     /* dI: 64 or 128 */
@@ -405,7 +406,7 @@ int dsa_index_scores(const dsa_index_shape* shape, const void* qi, const void* k
                      void* stream);
 
 /* Per query token, the kept tokens from a scores array as written by
- * dsa_index_scores. */
+ * dsa_index_scores.  N <= DSA_MAX_TOKENS, else DSA_ERR_UNSUPPORTED. */
 int dsa_select_tokens(const dsa_index_shape* shape, const float* scores, int32_t* idx, int32_t* cnt, void* stream);
 
 /* Attention of every head over its token's kept tokens.  idx entries are
@@ -414,10 +415,26 @@ int dsa_select_tokens(const dsa_index_shape* shape, const float* scores, int32_t
 int dsa_token_attn_fwd(const dsa_index_shape* shape, const void* q, const void* k, const void* v, const int32_t* idx,
                        const int32_t* cnt, void* o, float* lse, void* stream);
 
-/* Workspace of dsa_index_prefill in bytes: the scores, B * N * N * 4. */
+/* Index scores and token selection in one pass (same definition and result
+ * as dsa_index_scores then dsa_select_tokens, without the scores array):
+ * each query token keeps its forced tokens and its best other tokens by I,
+ * ties to the lower position, written to idx [B, N, kmax] (ascending, -1
+ * padded) and cnt [B, N].  Takes kmax <= DSA_INDEX_TOPK_MAX_KEEP (else
+ * DSA_ERR_UNSUPPORTED) and any N.  ws: device memory of at least
+ * dsa_index_workspace_bytes(shape) bytes (the per-chunk candidate lists of
+ * rows longer than one chunk of keys; 0 bytes when N <= 4096, NULL then
+ * allowed), caller-owned, contents undefined afterwards; DSA_ERR_WORKSPACE
+ * if smaller. */
+int dsa_index_topk(const dsa_index_shape* shape, const void* qi, const void* ki, const float* wi, int32_t* idx,
+                   int32_t* cnt, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace of dsa_index_prefill and dsa_index_topk in bytes: the candidate
+ * lists of dsa_index_topk when kmax <= DSA_INDEX_TOPK_MAX_KEEP, else the
+ * scores array, B * N * N * 4 (those shapes need N <= DSA_MAX_TOKENS). */
 size_t dsa_index_workspace_bytes(const dsa_index_shape* shape);
 
-/* Scores -> selection -> attention in one call. */
+/* Selection (dsa_index_topk, or dsa_index_scores then dsa_select_tokens for
+ * kmax > DSA_INDEX_TOPK_MAX_KEEP) then dsa_token_attn_fwd. */
 int dsa_index_prefill(const dsa_index_shape* shape, const void* qi, const void* ki, const float* wi, const void* q,
                       const void* k, const void* v, void* o, float* lse, int32_t* idx, int32_t* cnt, void* ws,
                       size_t ws_bytes, void* stream);

@@ -39,8 +39,20 @@ def run(w, flags, dev):
     dsa.dsa_index_scores(shape, qi, ki, wi, sc)
     dsa.dsa_select_tokens(shape, sc, idx, cnt)
     dsa.dsa_token_attn_fwd(shape, q, k, v, idx, cnt, o, lse)
+    fidx, fcnt = run_fused(shape, qi, ki, wi, dev)
     torch.cuda.synchronize()
-    return (qi, ki, wi, q, k, v), dict(scores=sc, idx=idx, cnt=cnt, o=o, lse=lse)
+    return (qi, ki, wi, q, k, v), dict(scores=sc, idx=idx, cnt=cnt, o=o, lse=lse, fidx=fidx, fcnt=fcnt)
+
+
+def run_fused(shape, qi, ki, wi, dev):
+    """dsa_index_topk into buffers pre-filled with garbage."""
+    B, N = shape.batch, shape.seq_len
+    km = dsa.dsa_index_kmax(shape)
+    idx = torch.full((B, N, km), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((B, N), -7, dtype=torch.int32, device=dev)
+    ws = torch.full((max(1, dsa.dsa_index_workspace_bytes(shape)),), 0x5A, dtype=torch.uint8, device=dev)
+    dsa.dsa_index_topk(shape, qi, ki, wi, idx, cnt, ws)
+    return idx, cnt
 
 
 def check_score_rows(got, ref_rows):
@@ -84,6 +96,8 @@ def test_index_small(cuda_device, name, w, flags):
     _, _, rows = O.select_tokens(ref_sc, w.topk, flags)
     gidx, gcnt = g["idx"].cpu().numpy(), g["cnt"].cpu().numpy()
     check_rows(rows, gidx[:, None], gcnt[:, None])
+    # the fused selection (scores never stored) keeps the same tokens
+    assert torch.equal(g["fidx"], g["idx"]) and torch.equal(g["fcnt"], g["cnt"])
     o_ref, lse_ref = O.token_attend(q, k, v, gidx, gcnt)
     check_out(np64(g["o"]), o_ref, np64(g["lse"]), lse_ref, name)
     # the fused call runs the same kernels
@@ -91,6 +105,50 @@ def test_index_small(cuda_device, name, w, flags):
     torch.cuda.synchronize()
     assert torch.equal(idx2, g["idx"]) and torch.equal(cnt2, g["cnt"])
     assert torch.equal(o2, g["o"]) and torch.equal(lse2, g["lse"])
+
+
+# Rows longer than one chunk of keys (4096 tokens): per-chunk candidate
+# lists in the workspace, merged by a second kernel
+MULTI = [
+    ("n4097_first_multi_chunk_row", IndexWorkload("m1", 1, 2, 1, 4097, 64, 16, 64, 64, clusters=32, amplitude=4.0,
+                                                  seed=71), 3),
+    ("b2_n4200_k128_dI128_g2", IndexWorkload("m2", 2, 4, 2, 4200, 64, 16, 128, 128, clusters=40, amplitude=4.0,
+                                             seed=72), 3),
+    ("n5000_k16_no_forcing", IndexWorkload("m3", 1, 2, 2, 5000, 64, 16, 64, 16, clusters=64, amplitude=4.0,
+                                           seed=73), 0),
+    ("n4500_sink_only_k2", IndexWorkload("m4", 1, 2, 1, 4500, 64, 16, 64, 2, seed=74), 1),
+    ("n4300_self_only_k1", IndexWorkload("m5", 1, 2, 1, 4300, 64, 16, 64, 1, seed=75), 2),
+]
+
+
+@pytest.mark.parametrize("name,w,flags", MULTI, ids=[c[0] for c in MULTI])
+def test_index_topk_multi_chunk(cuda_device, name, w, flags):
+    say(f"index multi-chunk {name}: B{w.batch} N{w.seq_len} dI{w.index_dim} k{w.topk} flags{flags}")
+    x, g = run(w, flags, cuda_device)
+    qi, ki, wi = (np64(t) for t in x[:3])
+    ref_sc = O.index_scores(qi, ki, wi)
+    _, _, rows = O.select_tokens(ref_sc, w.topk, flags)
+    fidx, fcnt = g["fidx"].cpu().numpy(), g["fcnt"].cpu().numpy()
+    check_rows(rows, fidx[:, None], fcnt[:, None])
+    assert torch.equal(g["fidx"], g["idx"]) and torch.equal(g["fcnt"], g["cnt"])
+
+
+def test_index_topk_rejects_long_rows_and_prefill_falls_back(cuda_device):
+    """kmax > 128: dsa_index_topk refuses; dsa_index_prefill takes the scores
+    array path (N <= 8192) and matches the oracle's selection."""
+    w = IndexWorkload("lr", 1, 2, 1, 900, 64, 16, 64, 200, clusters=16, amplitude=4.0, seed=76)
+    qi, ki, wi, q, k, v = make_index(w, device=cuda_device)
+    shape = dsa.make_index_shape(1, 2, 1, 900, 64, 16, 64, 200, 3)
+    idx = torch.empty((1, 900, 200), dtype=torch.int32, device=cuda_device)
+    cnt = torch.empty((1, 900), dtype=torch.int32, device=cuda_device)
+    ws = torch.empty(dsa.dsa_index_workspace_bytes(shape), dtype=torch.uint8, device=cuda_device)
+    with pytest.raises(dsa.DsaError, match="kept tokens per row"):
+        dsa.dsa_index_topk(shape, qi, ki, wi, idx, cnt, ws)
+    o, lse, idx, cnt = dsa.index_prefill(qi, ki, wi, q, k, v, w.topk)
+    torch.cuda.synchronize()
+    ref_sc = O.index_scores(np64(qi), np64(ki), np64(wi))
+    _, _, rows = O.select_tokens(ref_sc, w.topk, 3)
+    check_rows(rows, idx.cpu().numpy()[:, None], cnt.cpu().numpy()[:, None])
 
 
 def test_index_full_n8192_sampled(cuda_device):
@@ -119,6 +177,8 @@ def test_index_full_n8192_sampled(cuda_device):
         else:
             assert got == rs.idx, (t, got, rs.idx)
     say(f"index full n8192: {len(rows)} sampled rows, {flagged} flagged")
+    # every row: the fused selection equals the scores-array selection
+    assert torch.equal(g["fidx"], g["idx"]) and torch.equal(g["fcnt"], g["cnt"])
     units = [(0, h, t) for t in rows for h in (0, 13, 31)]
     o_ref, lse_ref = O.token_attend(np64(q), np64(k), np64(v), gidx, gcnt, units=units)
     for (b, h, t) in units:
@@ -183,3 +243,44 @@ def test_token_attention_on_given_rows(cuda_device):
     units = [(0, h, t) for h in range(w.n_q_heads) for t in rows]
     o_ref, lse_ref = O.token_attend(np64(q), np64(k), np64(v), idx, cnt, units=units)
     check_out(go[0][:, rows], o_ref[0][:, rows], gl[0][:, rows], lse_ref[0][:, rows], "given rows")
+
+
+def test_index_n32768_sampled(cuda_device):
+    """The 32 768-token workload (past the scores array's 8 192 limit): the
+    fused selection and token attention; sampled rows against the oracle's
+    rows, and every row checked for structure (ascending, distinct, the
+    forced tokens present, the budget met)."""
+    w = INDEX_WORKLOADS["index_n32768"]
+    say("index n32768: running")
+    qi, ki, wi, q, k, v = make_index(w, device=cuda_device)
+    o, lse, idx, cnt = dsa.index_prefill(qi, ki, wi, q, k, v, w.topk)
+    torch.cuda.synchronize()
+    N = w.seq_len
+    gi, gc = idx.cpu().numpy()[0], cnt.cpu().numpy()[0]
+    want_cnt = np.minimum(np.arange(N) + 1, w.topk)
+    assert (gc == want_cnt).all()
+    body = gi[64:]
+    assert (body[:, 0] == 0).all() and (body[:, -1] == np.arange(64, N)).all()
+    assert (np.diff(body, axis=1) > 0).all()
+    qn, kn, wn = qi[0].float().cpu().numpy(), ki[0].float().cpu().numpy(), wi[0].cpu().numpy()
+    rows = [0, 5, 63, 64, 2047, 2048, 2063, 2064, 4096, 8191, 8192, 12345, 16383, 16384, 20000, 24576, 30001,
+            32700, 32766, 32767]
+    flagged = 0
+    for t in rows:
+        r = O.index_score_row(qn[t].astype(np.float64), kn.astype(np.float64), wn[t].astype(np.float64), t)
+        f = O.forced_set(t + 1, 3)
+        rs = O.select_row(r, t + 1, O.row_budget(t + 1, w.topk, 0, 1, len(f)), f, O.TOKEN_TIE_ABS)
+        got = [int(s) for s in gi[t, : gc[t]]]
+        if rs.flagged:
+            flagged += 1
+            ok, why = O.accepts(rs, got)
+            assert ok, (t, why)
+        else:
+            assert got == rs.idx, (t, got, rs.idx)
+    say(f"index n32768: {len(rows)} sampled rows, {flagged} flagged")
+    units = [(0, h, t) for t in rows[::4] for h in (0, 31)]
+    o_ref, lse_ref = O.token_attend(np64(q[:, :, :]), np64(k), np64(v), idx.cpu().numpy(), cnt.cpu().numpy(),
+                                    units=units)
+    for (b, h, t) in units:
+        check_out(np64(o[b, h, t])[None], o_ref[b, h, t][None], np64(lse[b, h, t]).reshape(1),
+                  lse_ref[b, h, t].reshape(1), f"n32768 h{h} t{t}")
