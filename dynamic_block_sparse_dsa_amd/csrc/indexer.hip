@@ -293,11 +293,12 @@ __device__ int compact_candidates(LDS_AS uint32_t* vals, LDS_AS int32_t* ids, in
 // One unit = 16 query tokens x one chunk of kct key tiles.  Chunk c of token
 // tile tt exists for tt >= 4 c kct (the tile's keys reach past c kct tiles);
 // units run chunk-major, latest tiles first.  Per 64-key tile the scores come
-// from IndexRows::tile; each lane then holds two scores of each of two
-// tokens (32 consecutive keys of a token per half-wave), and a key joins its
-// token's candidate list (LDS, index order, the score's bits) when it is a
-// candidate and its score exceeds the token's threshold (-inf until the first
-// compaction; compared as floats, which orders like the keys).  A list that
+// from IndexRows::tile, regrouped so that one register holds one token's 64
+// scores (key = lane); a key joins its token's candidate list (LDS, index
+// order, the score's bits) when it is a candidate and its score exceeds the
+// token's threshold (-inf until the first compaction; compared as floats,
+// which orders like the keys).  Token state (counts, thresholds) is
+// wave-uniform.  A list that
 // may overflow on the next tile is compacted (compact_candidates, at most
 // m + 32 left).  At the end each list is cut to its best m: a tile whose keys
 // fit one chunk writes its final rows; otherwise each chunk's list goes to
@@ -310,7 +311,6 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const IndexTopkArgs a) 
   __shared__ __align__(16) int32_t cid[4][4][CAP];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int half = lane >> 5;
   const int64_t b = blockIdx.y;
   const int N = a.N;
   int u = blockIdx.x, c = 0;
@@ -328,17 +328,22 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const IndexTopkArgs a) 
 
   IndexRows<DI> rows;
   rows.load(a.qi, a.wi, b, N, t0, wave, lane);
-  // candidate range [lo, lo + span) of the lane's tokens (span 0: none),
-  // budget m, threshold as an order key and as a float
-  int lo[2], span[2], mr[2], n[2] = {0, 0};
-  uint32_t thr[2] = {0u, 0u};
-  float thf[2] = {-__builtin_inff(), -__builtin_inff()};
+  // per token j of the wave (t0 + 4 wave + j), all wave-uniform: candidate
+  // range [lo, lo + span) (span 0: none), budget m, list length n, threshold
+  // as an order key and as a float
+  int lo[4], span[4], mr[4], n[4];
+  uint32_t thr[4];
+  float thf[4];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const TokenRow tr(rows.tok[ct], a.p);
-    lo[ct] = tr.na;
-    span[ct] = rows.tok[ct] < N && tr.m > 0 ? tr.ws - tr.na : 0;
-    mr[ct] = tr.m;
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + 4 * wave + j;
+    const TokenRow tr(t, a.p);
+    lo[j] = tr.na;
+    span[j] = t < N && tr.m > 0 ? tr.ws - tr.na : 0;
+    mr[j] = tr.m;
+    n[j] = 0;
+    thr[j] = 0u;
+    thf[j] = -__builtin_inff();
   }
   const uint16_t* kb = a.ki + b * (int64_t)N * DI;
   const uint32_t base[2] = {(uint32_t)(uintptr_t)(LDS_AS uint16_t*)kt_lds[0],
@@ -352,64 +357,60 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const IndexTopkArgs a) 
     if (kt + 1 < kt1) load_key_tile<DI>(kb, (kt + 1) * KT, N, base[(i + 1) & 1], wave, lane);
     float s[2][2];
     rows.tile((const LDS_AS uint16_t*)kt_lds[i & 1], lane, s);
+    // s[rt][ct] holds keys 32 rt + lane % 32 of token 2 ct + half; swapping
+    // s[0][ct]'s upper 32 lanes with s[1][ct]'s lower ones leaves token 2 ct's
+    // 64 keys in one register and token 2 ct + 1's in the other, key = lane
+    float v[4];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s[0][ct]), __float_as_uint(s[1][ct]), false,
+                                                       false);
+      v[2 * ct] = __uint_as_float(sw[0]);
+      v[2 * ct + 1] = __uint_as_float(sw[1]);
+    }
+    const int key = kt * KT + lane;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int key = kt * KT + rt * 32 + (lane & 31);
-        const bool take = (s[rt][ct] > thf[ct]) & ((uint32_t)(key - lo[ct]) < (uint32_t)span[ct]);
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
-        const uint32_t lo32 = (uint32_t)bal, hi32 = (uint32_t)(bal >> 32);
-        // slot position: the half's count so far plus its taken lanes below
-        const int pos = n[ct] + lanes_below(bal) - (half ? __builtin_popcount(lo32) : 0);
-        if (take) {
-          ckey[wave][2 * ct + half][pos] = __float_as_uint(s[rt][ct]);
-          cid[wave][2 * ct + half][pos] = key;
-        }
-        n[ct] += __builtin_popcount(half ? hi32 : lo32);
+    for (int j = 0; j < 4; ++j) {
+      const bool take = (v[j] > thf[j]) & ((uint32_t)(key - lo[j]) < (uint32_t)span[j]);
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
+      if (take) {
+        const int pos = n[j] + lanes_below(bal);
+        ckey[wave][j][pos] = __float_as_uint(v[j]);
+        cid[wave][j][pos] = key;
       }
+      n[j] += __builtin_popcountll(bal);
     }
     // a list past CAP - 64 could overflow on the next tile
-    if (__builtin_amdgcn_ballot_w64(max(n[0], n[1]) > CAP - 64)) {
+    if (max(max(n[0], n[1]), max(n[2], n[3])) > CAP - 64) {
       wave_lds_sync();
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const int ct = sl >> 1, src = 32 * (sl & 1);
-        const int cs = __builtin_amdgcn_readlane(n[ct], src);
-        if (cs > CAP - 64) {
-          const int ms = __builtin_amdgcn_readlane(mr[ct], src);
-          uint32_t th = (uint32_t)__builtin_amdgcn_readlane((int)thr[ct], src);
-          const int nn = compact_candidates<CAP>((LDS_AS uint32_t*)ckey[wave][sl], (LDS_AS int32_t*)cid[wave][sl], cs,
-                                                      ms, ms + 32, &th, lane);
-          if ((sl & 1) == half) {
-            n[ct] = nn;
-            thr[ct] = th;
-            thf[ct] = key_float(th);
-          }
+      for (int j = 0; j < 4; ++j)
+        if (n[j] > CAP - 64) {
+          n[j] = compact_candidates<CAP>((LDS_AS uint32_t*)ckey[wave][j], (LDS_AS int32_t*)cid[wave][j], n[j], mr[j],
+                                         mr[j] + 32, &thr[j], lane);
+          thf[j] = key_float(thr[j]);
         }
-      }
     }
   }
   wave_lds_sync();
 
   // the best m of each list; then the final row or the chunk's list
 #pragma unroll
-  for (int sl = 0; sl < 4; ++sl) {
-    const int t = t0 + 4 * wave + sl;
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + 4 * wave + j;
     if (t >= N) break;
-    const int ct = sl >> 1, src = 32 * (sl & 1);
-    int cs = __builtin_amdgcn_readlane(n[ct], src);
+    int cs = n[j];
     const TokenRow tr(t, a.p);
     if (cs > tr.m) {
       uint32_t th = 0u;
-      cs = compact_candidates<CAP>((LDS_AS uint32_t*)ckey[wave][sl], (LDS_AS int32_t*)cid[wave][sl], cs, tr.m, tr.m,
+      cs = compact_candidates<CAP>((LDS_AS uint32_t*)ckey[wave][j], (LDS_AS int32_t*)cid[wave][j], cs, tr.m, tr.m,
                                     &th, lane);
     }
     const int64_t row = b * N + t;
     if (n_c == 1) {
       int32_t* out = a.idx + row * a.kmax;
       for (int e = lane; e < tr.na; e += 64) out[e] = e;
-      for (int e = lane; e < cs; e += 64) out[tr.na + e] = cid[wave][sl][e];
+      for (int e = lane; e < cs; e += 64) out[tr.na + e] = cid[wave][j][e];
       for (int e = lane; e < tr.nv - tr.ws; e += 64) out[tr.na + cs + e] = tr.ws + e;
       const int total = tr.na + cs + (tr.nv - tr.ws);
       for (int e = total + lane; e < a.kmax; e += 64) out[e] = -1;
@@ -417,8 +418,8 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const IndexTopkArgs a) 
     } else {
       const int64_t slab = row * a.nch + c;
       for (int e = lane; e < cs; e += 64) {
-        a.part_key[slab * a.mw + e] = order_key(__uint_as_float(ckey[wave][sl][e]));
-        a.part_idx[slab * a.mw + e] = cid[wave][sl][e];
+        a.part_key[slab * a.mw + e] = order_key(__uint_as_float(ckey[wave][j][e]));
+        a.part_idx[slab * a.mw + e] = cid[wave][j][e];
       }
       if (lane == 0) a.part_cnt[slab] = cs;
     }
