@@ -15,13 +15,16 @@
 //
 // Scoring + selection (score_and_select): one 512-thread workgroup per
 // (sequence, KV head) unit streams the unit's fp32 block means with 16-byte
-// loads (d/8 lanes per block row; waves take batches of rows from an LDS
-// counter and keep the next batch in flight; row dot products reduced with
-// DPP), scores each block by the max over the group's heads of
+// loads (d/8 lanes per block row; each wave scores one contiguous eighth of
+// the blocks, batch by batch with the next batch in flight; row dot products
+// reduced with DPP), scores each block by the max over the group's heads of
 // q_h . kbar_j / sqrt(d) into LDS, then selects on the LDS scores -- no
-// score round trip: the whole workgroup runs a plain top-k (a digit-wise
-// histogram search for the threshold, block_select_topk), one wave the
-// threshold and entropy variants (wave_select_row).
+// score round trip: a plain top-k keeping at most 64 candidates runs in two
+// wave-level rounds (each wave keeps the best of its own eighth as soon as it
+// has scored it, then one wave the best of those lists: topk_round1 and
+// topk_round2), larger ones a workgroup digit-wise histogram search
+// (block_select_topk); one wave runs the threshold and entropy variants
+// (wave_select_row).
 //
 // Attention over the kept blocks works in 32-key chunks (WaveAttn): a wave
 // issues all K and V loads of a chunk together, then Q K^T on
@@ -49,35 +52,36 @@ namespace dsa {
 // Score every block of one (sequence, KV head) unit into LDS and select its
 // kept blocks (written ascending to out, -1 padded to kmax; out may be
 // global or LDS).  All NT = 512 threads of the workgroup take part.  Scores:
-// block l * R + e at sc[e * 64 + l].  pre_select() runs in every thread
-// once the scores are complete, before the selection (a caller's prefetch
-// stays in flight through it).  The selection is complete only after the
-// caller's next barrier.
+// block l * R + e at sc[e * 64 + l].  Wave w scores the blocks
+// w B .. w B + B - 1 (B = 64 R / 8), batch by batch with the next batch in
+// flight, and a plain top-k row keeping at most 64 candidates then runs its
+// first selection round on them at once (topk_round1: the wave's best m), so
+// waves that finish scoring early select while others still load.
+// pre_select() runs in every thread once every wave is done, before the
+// second round (a caller's prefetch stays in flight through it).  The
+// selection is complete only after the caller's next barrier.
 template <int D, int G, int R, typename Pre>
 __device__ __forceinline__ void score_and_select(const DecodeArgs& a, const TopkParams& p, int unit, float* sc,
                                                  uint32_t* lds_key, int32_t* lds_idx, uint32_t* bsel,
-                                                 int* next_batch, int32_t* out, Pre&& pre_select) {
+                                                 int32_t* out, Pre&& pre_select) {
   constexpr int NT = 512, NW = NT / 64;
   constexpr int TPR = D / 8;       // lanes per block row (8 floats each)
   constexpr int WROWS = 64 / TPR;  // rows per wave per pass
   constexpr int UNR = 8;           // passes per batch
   constexpr int BR = WROWS * UNR;  // rows per batch (16 KiB of fp32 means at d = 128)
+  constexpr int BPW = 64 * R / NW;  // blocks per wave
+  static_assert(BPW % BR == 0, "whole batches per wave");
   const int64_t s = unit / a.Hkv;
   const int g = unit % a.Hkv;
   const int t = threadIdx.x, lane = t & 63, c = lane % TPR, rl = lane / TPR;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int nB = a.nB;
   const int nbatch = (nB + BR - 1) / BR;
-  if (t == 0) *next_batch = NW;  // batches 0 .. NW-1 go to the waves in order
-  __syncthreads();
 
   float qv[G][8];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) load_q_halves<D>(a.q + (s * a.Hq + g * G + hh) * (int64_t)D, c, qv[hh]);
-  // A wave scores batches of BR consecutive rows; after its first batch it
-  // takes the next free one from an LDS counter, so waves that see shorter
-  // memory latency do more of them.  The next batch is in flight while one is
-  // scored; rows past the end are clamped (loaded again, never stored).
+  // rows past the end are clamped (loaded again, never stored)
   const float* kb = a.kbar + (int64_t)unit * nB * D + 4 * c;
   auto load = [&](f32x4(&kv)[UNR][2], int b) {
 #pragma unroll
@@ -105,28 +109,36 @@ __device__ __forceinline__ void score_and_select(const DecodeArgs& a, const Topk
       if (c == 0 && row < nB) sc[(row % R) * 64 + row / R] = best;
     }
   };
-  auto grab = [&]() {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(next_batch, 1);
-    return __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
-  };
+  const int b_lo = wave * (BPW / BR), b_hi = min(b_lo + BPW / BR, nbatch);
   f32x4 k0[UNR][2], k1[UNR][2];
-  int b0 = wave;
-  if (b0 < nbatch) load(k0, b0);
-  int b1 = grab();
-  while (b0 < nbatch) {
-    if (b1 < nbatch) load(k1, b1);
-    score(k0, b0);
-    b0 = grab();
-    if (b1 >= nbatch) break;
-    if (b0 < nbatch) load(k0, b0);
-    score(k1, b1);
-    b1 = grab();
+  if (b_lo < b_hi) load(k0, b_lo);
+  for (int b = b_lo; b < b_hi; b += 2) {
+    if (b + 1 < b_hi) load(k1, b + 1);
+    score(k0, b);
+    if (b + 1 >= b_hi) break;
+    if (b + 2 < b_hi) load(k0, b + 2);
+    score(k1, b + 1);
+  }
+  const TopkRow tr(nB, p);
+  const bool two = p.mode == DSA_SELECT_TOPK && tr.two_round(nB);
+  const int ls = tr.m <= 32 ? 32 : 64;
+  uint32_t* scratch2 = bsel + BSEL_SCRATCH_WORDS;
+  if (two) {
+    wave_lds_sync();  // the wave's own scores
+    topk_round1<R, NW>(sc, tr, ls, scratch2);
   }
   __syncthreads();
   pre_select();
-  if (p.mode == DSA_SELECT_TOPK) block_select_topk<R, NT>(sc, nB, p, out, a.kmax, bsel);  // the workgroup selects
-  else if (t < 64) wave_select_row<R, true>(sc, nB, p, out, a.kmax, lds_key, lds_idx);  // one wave selects
+  if (two) {
+    if (wave == 0) {
+      if (ls == 32) topk_round2<NW, NW / 2>(tr, nB, out, a.kmax, ls, scratch2);
+      else topk_round2<NW, NW>(tr, nB, out, a.kmax, ls, scratch2);
+    }
+  } else if (p.mode == DSA_SELECT_TOPK) {
+    block_select_topk<R, NT>(sc, nB, p, out, a.kmax, bsel);  // the workgroup selects
+  } else if (t < 64) {
+    wave_select_row<R, true>(sc, nB, p, out, a.kmax, lds_key, lds_idx);  // one wave selects
+  }
 }
 
 template <int D, int G, int R>
@@ -134,10 +146,9 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a, TopkPa
   __shared__ float sc[64 * R];
   __shared__ uint32_t lds_key[128];
   __shared__ int32_t lds_idx[128];
-  __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS];
-  __shared__ int next_batch;
-  score_and_select<D, G, R>(a, p, blockIdx.x, sc, lds_key, lds_idx, bsel, &next_batch,
-                            a.idx + (int64_t)blockIdx.x * a.kmax, [] {});
+  __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS + BSEL2_SCRATCH_WORDS];
+  score_and_select<D, G, R>(a, p, blockIdx.x, sc, lds_key, lds_idx, bsel, a.idx + (int64_t)blockIdx.x * a.kmax,
+                            [] {});
 }
 
 // ============================================================== 2. attention
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkPar
   __shared__ float sc[64 * R];
   __shared__ uint32_t lds_key[128];
   __shared__ int32_t lds_idx[128];
-  __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS];
+  __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS + BSEL2_SCRATCH_WORDS];
   __shared__ int next_batch;
   __shared__ int32_t sel[64 * R];          // kept blocks (kmax <= nB <= 64 R)
   __shared__ float pbuf[NW][C::CK][G];
@@ -332,7 +343,7 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkPar
 
   const bool pre = early && wave >= 1 && wave < 2 * CPB && wave < NW;
   int kA = -1;
-  score_and_select<D, G, R>(a, p, unit, sc, lds_key, lds_idx, bsel, &next_batch, sel, [&] {
+  score_and_select<D, G, R>(a, p, unit, sc, lds_key, lds_idx, bsel, sel, [&] {
     wa.init(a, s, g);  // lane mapping + q; every later load depends on it
     if (pre) {
       kA = forced_key(wave);

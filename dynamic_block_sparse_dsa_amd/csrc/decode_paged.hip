@@ -43,7 +43,7 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
   __shared__ float sc[64 * R];
   __shared__ uint32_t lds_key[128];
   __shared__ int32_t lds_idx[128];
-  __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS];
+  __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS + BSEL2_SCRATCH_WORDS];
   __shared__ int next_batch, n_sel;
   __shared__ int32_t sel[64 * R];
   __shared__ float pbuf[NW][C::CK][G];
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
     }
     __syncthreads();
     if (p.mode == DSA_SELECT_TOPK) {  // the workgroup selects
-      const int n = block_select_topk<R, NT>(sc, nB, p, sel, kmax, bsel);
+      const int n = block_select_topk_waves<R, NT>(sc, nB, p, sel, kmax, bsel, bsel + BSEL_SCRATCH_WORDS);
       if (tid == 0) n_sel = n;
     } else if (tid < 64) {  // one wave selects
       const int n = wave_select_row<R, true>(sc, nB, p, sel, kmax, lds_key, lds_idx);

@@ -520,4 +520,185 @@ __device__ __forceinline__ int block_select_topk(const float* srow, int nv, cons
   return total;
 }
 
+// Best m of the keys v[0..C-1] of each lane (0 = not a candidate; lane-major
+// runs, so position order is lane * C + c): sets keep[c] and returns the
+// number kept, exactly min(m, candidates).  The m-th largest key T comes from
+// an MSB-first search that starts at the common leading bits of the largest
+// and smallest candidate key and stops as soon as exactly m keys are >= the
+// trial value; otherwise T is the m-th largest key and the keys equal to it
+// are kept in position order until m are kept.  All lanes active.
+template <int C>
+__device__ __forceinline__ int wave_keep_best(const uint32_t (&v)[C], int m, bool (&keep)[C]) {
+  int n = 0;
+  uint32_t mx = 0u, mn = ~0u;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[c] != 0u));
+    if (v[c]) {
+      mx = max(mx, v[c]);
+      mn = min(mn, v[c]);
+    }
+  }
+  uint32_t T = 1u;
+  bool cut = false;
+  int take_eq = 0;
+  if (n > m) {
+    mx = wave_max_u32(mx);
+    mn = wave_min_u32(mn);
+    const uint32_t x = mx ^ mn;
+    int bit = x ? 31 - __builtin_clz(x) : -1;
+    T = x ? (mx & ~(uint32_t)(((uint64_t)2 << bit) - 1u)) : mx;
+    int nT = n;
+    // two bits per step: the three trial values are counted independently
+    for (; bit >= 1 && nT > m; bit -= 2) {
+      const uint32_t t1 = T | (1u << (bit - 1)), t2 = T | (2u << (bit - 1)), t3 = T | (3u << (bit - 1));
+      const int c1 = wave_count_ge<C>(v, t1), c2 = wave_count_ge<C>(v, t2), c3 = wave_count_ge<C>(v, t3);
+      if (c3 >= m) {
+        T = t3;
+        nT = c3;
+      } else if (c2 >= m) {
+        T = t2;
+        nT = c2;
+      } else if (c1 >= m) {
+        T = t1;
+        nT = c1;
+      }
+    }
+    if (bit == 0 && nT > m) {
+      const int c = wave_count_ge<C>(v, T | 1u);
+      if (c >= m) {
+        T |= 1u;
+        nT = c;
+      }
+    }
+    cut = nT > m;
+    if (cut) take_eq = m - (T == ~0u ? 0 : wave_count_ge<C>(v, T + 1u));
+  }
+  int my_eq = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) my_eq += v[c] == T;
+  int r = cut ? wave_incl_scan(my_eq) - my_eq : 0;
+  int kept = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    keep[c] = v[c] > T || (v[c] == T && (!cut || r < take_eq));
+    r += v[c] == T;
+    kept += keep[c];
+  }
+  return min(n, m);
+}
+
+// LDS words the two-round selection needs: a list of up to 64 (key, block)
+// per wave and a count per wave (up to 16 waves)
+constexpr int BSEL2_SCRATCH_WORDS = 16 * 64 * 2 + 16;
+
+// Budget split of a DSA_SELECT_TOPK row that sees nv blocks: forced prefix
+// [0, na), forced suffix [ws, nv), m candidates kept (wave-uniform)
+struct TopkRow {
+  int na, ws, nf, m;
+  __device__ __forceinline__ TopkRow(int nv, const TopkParams& p) {
+    na = min(p.anchors, nv);
+    ws = max(nv - p.window, na);
+    nf = na + (nv - ws);
+    int64_t budget = p.topk > 0 ? (int64_t)p.topk : ((int64_t)p.num * nv + p.den - 1) / p.den;
+    if (budget < nf) budget = nf;
+    if (budget > nv) budget = nv;
+    m = (int)budget - nf;
+  }
+  // rows the two rounds take: some candidates kept, not all, at most 64
+  __device__ __forceinline__ bool two_round(int nv) const { return m > 0 && m < nv - nf && m <= 64; }
+};
+
+// Round 1 of the two-round selection, run by one wave on its own range of
+// blocks w B .. w B + B - 1 (B = 64 R / NW, R / NW consecutive blocks per
+// lane): the wave keeps its best m candidates (wave_keep_best) and writes them
+// in index order as an LDS list of LS slots (LS >= m) with its count.  srow:
+// the LDS score row in the transposed layout (block l R + e at srow[e * 64 +
+// l]), already written by this wave for its range (the caller syncs).
+template <int R, int NW>
+__device__ __forceinline__ void topk_round1(const float* srow, const TopkRow& tr, int ls, uint32_t* scratch2) {
+  constexpr int C = R / NW;
+  static_assert(C >= 1 && C * NW == R && NW <= 16, "row split");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __attribute__((address_space(3))) float* st = (const __attribute__((address_space(3))) float*)srow;
+  uint32_t* lkey = scratch2;                // [NW][ls]
+  uint32_t* lblk = scratch2 + 16 * 64;      // [NW][ls]
+  uint32_t* lcnt = scratch2 + 2 * 16 * 64;  // [NW]
+  uint32_t v[C];
+  const int j0 = wave * 64 * C + lane * C;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int j = j0 + c;
+    v[c] = (j >= tr.na && j < tr.ws) ? order_key(st[(j % R) * 64 + j / R]) : 0u;
+  }
+  bool keep[C];
+  const int kw = wave_keep_best<C>(v, tr.m, keep);
+  int mine = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) mine += keep[c];
+  int pos = wave_incl_scan(mine) - mine;
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+    if (keep[c]) {
+      lkey[wave * ls + pos] = v[c];
+      lblk[wave * ls + pos] = (uint32_t)(j0 + c);
+      ++pos;
+    }
+  if (lane == 0) lcnt[wave] = (uint32_t)kw;
+}
+
+// Round 2, one wave, after a barrier behind every wave's round 1: the best m
+// of the concatenated lists (in index order, so ties again go to the lower
+// block), written to out with the forced blocks: anchors, kept ascending,
+// window, -1 padding to kmax.  C2 = NW * ls / 64 list slots per lane.
+template <int NW, int C2>
+__device__ __forceinline__ void topk_round2(const TopkRow& tr, int nv, int32_t* out, int kmax, int ls,
+                                            const uint32_t* scratch2) {
+  static_assert(C2 * 64 <= 16 * 64, "list slots");
+  const int lane = threadIdx.x & 63;
+  const uint32_t* lkey = scratch2;
+  const uint32_t* lblk = scratch2 + 16 * 64;
+  const uint32_t* lcnt = scratch2 + 2 * 16 * 64;
+  uint32_t u[C2], blk[C2];
+#pragma unroll
+  for (int c = 0; c < C2; ++c) {
+    const int q = lane * C2 + c, w = q / ls, i = q - w * ls;
+    const bool ok = w < NW && i < (int)lcnt[min(w, NW - 1)];
+    u[c] = ok ? lkey[q] : 0u;
+    blk[c] = ok ? lblk[q] : 0u;
+  }
+  bool k2[C2];
+  wave_keep_best<C2>(u, tr.m, k2);
+  int mine = 0;
+#pragma unroll
+  for (int c = 0; c < C2; ++c) mine += k2[c];
+  int o = tr.na + wave_incl_scan(mine) - mine;
+#pragma unroll
+  for (int c = 0; c < C2; ++c)
+    if (k2[c]) out[o++] = (int32_t)blk[c];
+  for (int e = lane; e < tr.na; e += 64) out[e] = e;
+  for (int e = lane; e < nv - tr.ws; e += 64) out[tr.na + tr.m + e] = tr.ws + e;
+  for (int e = tr.nf + tr.m + lane; e < kmax; e += 64) out[e] = -1;
+}
+
+// block_select_topk's result for rows that keep at most 64 candidates (and
+// see at most 64 R blocks), in two wave-level rounds instead of a workgroup
+// radix search (topk_round1 on every wave, a barrier, topk_round2 on wave 0).
+// Every thread must call it; out is complete after the caller's next barrier.
+template <int R, int NT>
+__device__ __forceinline__ int block_select_topk_waves(const float* srow, int nv, const TopkParams& p, int32_t* out,
+                                                       int kmax, uint32_t* scratch, uint32_t* scratch2) {
+  constexpr int NW = NT / 64;
+  const TopkRow tr(nv, p);
+  if (!tr.two_round(nv)) return block_select_topk<R, NT>(srow, nv, p, out, kmax, scratch);
+  const int ls = tr.m <= 32 ? 32 : 64;
+  topk_round1<R, NW>(srow, tr, ls, scratch2);
+  lds_barrier();
+  if ((threadIdx.x >> 6) == 0) {
+    if (ls == 32) topk_round2<NW, NW / 2>(tr, nv, out, kmax, ls, scratch2);
+    else topk_round2<NW, NW>(tr, nv, out, kmax, ls, scratch2);
+  }
+  return tr.nf + tr.m;
+}
+
 }  // namespace dsa
