@@ -409,7 +409,7 @@ def bench_selection(args, dev, stream, inputs):
     return out
 
 
-def bench_index(args, dev, stream):
+def bench_index(args, dev, stream, wname=None):
     """Token-level indexer workload: the chained step (wall clock) and its
     launches alone (HIP events): the fused index scores + token selection
     (index_topk_kernel, plus index_merge_kernel for rows longer than one chunk
@@ -423,7 +423,7 @@ def bench_index(args, dev, stream):
     import dynamic_block_sparse_dsa_amd as dsa
     from dynamic_block_sparse_dsa_amd.inputs import INDEX_WORKLOADS, make_index
 
-    w = INDEX_WORKLOADS[args.index_workload]
+    w = INDEX_WORKLOADS[wname or args.index_workload]
     qi, ki, wi, q, k, v = make_index(w, device=dev)
     B, Hq, Hkv, N, d, HI, dI = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_index_heads, w.index_dim
     shape = dsa.make_index_shape(B, Hq, Hkv, N, d, HI, dI, w.topk)
@@ -582,6 +582,8 @@ def main():
     ap.add_argument("--no-index", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--index-workload", default="index_n8192")
+    ap.add_argument("--extra-index-workloads", default="index_n32768",
+                    help="comma-separated token-indexer workloads reported beside it ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -644,6 +646,9 @@ def main():
     if not args.no_index:
         log("token indexer")
         out["indexer"] = bench_index(args, dev, stream)
+        extra = [x for x in args.extra_index_workloads.split(",") if x and x != args.index_workload]
+        if extra:
+            out["indexer_workloads"] = {x: bench_index(args, dev, stream, x) for x in extra}
     if not args.no_ceilings:
         log("ceilings")
         out["ceilings"] = ceilings(dev, stream)

@@ -522,13 +522,14 @@ __device__ __forceinline__ int block_select_topk(const float* srow, int nv, cons
 
 // Best m of the keys v[0..C-1] of each lane (0 = not a candidate; lane-major
 // runs, so position order is lane * C + c): sets keep[c] and returns the
-// number kept, exactly min(m, candidates).  The m-th largest key T comes from
+// number kept, exactly min(m, candidates).  With more than m candidates,
+// *lower (if given) receives a value that at least m keys reach.  The m-th largest key T comes from
 // an MSB-first search that starts at the common leading bits of the largest
 // and smallest candidate key and stops as soon as exactly m keys are >= the
 // trial value; otherwise T is the m-th largest key and the keys equal to it
 // are kept in position order until m are kept.  All lanes active.
 template <int C>
-__device__ __forceinline__ int wave_keep_best(const uint32_t (&v)[C], int m, bool (&keep)[C]) {
+__device__ __forceinline__ int wave_keep_best(const uint32_t (&v)[C], int m, bool (&keep)[C], uint32_t* lower = nullptr) {
   int n = 0;
   uint32_t mx = 0u, mn = ~0u;
 #pragma unroll
@@ -573,6 +574,7 @@ __device__ __forceinline__ int wave_keep_best(const uint32_t (&v)[C], int m, boo
     }
     cut = nT > m;
     if (cut) take_eq = m - (T == ~0u ? 0 : wave_count_ge<C>(v, T + 1u));
+    if (lower) *lower = T;  // at least m of the keys are >= T
   }
   int my_eq = 0;
 #pragma unroll
@@ -589,8 +591,8 @@ __device__ __forceinline__ int wave_keep_best(const uint32_t (&v)[C], int m, boo
 }
 
 // LDS words the two-round selection needs: a list of up to 64 (key, block)
-// per wave and a count per wave (up to 16 waves)
-constexpr int BSEL2_SCRATCH_WORDS = 16 * 64 * 2 + 16;
+// per wave, a count and a lower bound per wave (up to 16 waves)
+constexpr int BSEL2_SCRATCH_WORDS = 16 * 64 * 2 + 32;
 
 // Budget split of a DSA_SELECT_TOPK row that sees nv blocks: forced prefix
 // [0, na), forced suffix [ws, nv), m candidates kept (wave-uniform)
@@ -624,6 +626,7 @@ __device__ __forceinline__ void topk_round1(const float* srow, const TopkRow& tr
   uint32_t* lkey = scratch2;                // [NW][ls]
   uint32_t* lblk = scratch2 + 16 * 64;      // [NW][ls]
   uint32_t* lcnt = scratch2 + 2 * 16 * 64;  // [NW]
+  uint32_t* lbnd = lcnt + 16;               // [NW]
   uint32_t v[C];
   const int j0 = wave * 64 * C + lane * C;
 #pragma unroll
@@ -632,7 +635,8 @@ __device__ __forceinline__ void topk_round1(const float* srow, const TopkRow& tr
     v[c] = (j >= tr.na && j < tr.ws) ? order_key(st[(j % R) * 64 + j / R]) : 0u;
   }
   bool keep[C];
-  const int kw = wave_keep_best<C>(v, tr.m, keep);
+  uint32_t bound = 0u;
+  const int kw = wave_keep_best<C>(v, tr.m, keep, &bound);
   int mine = 0;
 #pragma unroll
   for (int c = 0; c < C; ++c) mine += keep[c];
@@ -644,7 +648,10 @@ __device__ __forceinline__ void topk_round1(const float* srow, const TopkRow& tr
       lblk[wave * ls + pos] = (uint32_t)(j0 + c);
       ++pos;
     }
-  if (lane == 0) lcnt[wave] = (uint32_t)kw;
+  if (lane == 0) {
+    lcnt[wave] = (uint32_t)kw;
+    lbnd[wave] = bound;
+  }
 }
 
 // Round 2, one wave, after a barrier behind every wave's round 1: the best m
@@ -659,12 +666,20 @@ __device__ __forceinline__ void topk_round2(const TopkRow& tr, int nv, int32_t* 
   const uint32_t* lkey = scratch2;
   const uint32_t* lblk = scratch2 + 16 * 64;
   const uint32_t* lcnt = scratch2 + 2 * 16 * 64;
+  const uint32_t* lbnd = lcnt + 16;
+  // a wave with more than m candidates has m keys >= its bound, so keys below
+  // the largest bound cannot be among the best m: dropping them shortens the
+  // threshold search
+  uint32_t lb = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) lb = max(lb, lbnd[w]);
   uint32_t u[C2], blk[C2];
 #pragma unroll
   for (int c = 0; c < C2; ++c) {
     const int q = lane * C2 + c, w = q / ls, i = q - w * ls;
     const bool ok = w < NW && i < (int)lcnt[min(w, NW - 1)];
-    u[c] = ok ? lkey[q] : 0u;
+    const uint32_t k = ok ? lkey[q] : 0u;
+    u[c] = k >= lb ? k : 0u;
     blk[c] = ok ? lblk[q] : 0u;
   }
   bool k2[C2];
