@@ -7,18 +7,27 @@
 // low precision.  Here the score of earlier token s for query token t is
 //   I[t, s] = sum_h w[t, h] * ReLU(qi[t, h] . ki[s])
 // (bf16 MFMA, fp32 accumulation), each query token keeps its top-k tokens
-// (the block path's one-wave top-k, rows = tokens, sink and self forced), and
-// every attention head attends over its token's kept key/value rows.
+// (sink and self forced, the best others by I, ties to the lower position),
+// and every attention head attends over its token's kept key/value rows.
 //
-// index_scores_kernel: one workgroup per 16 query tokens, each wave 4 tokens
-//   = 2 tiles of 32 (token, index head) pairs.  Per 64-key tile (global ->
-//   LDS DMA, double-buffered, kswz rows): S = Qi . K_tile^T on
-//   v_mfma_f32_32x32x16_bf16 (the wave's index query rows as A in registers,
-//   key rows from LDS as B), so a lane's output holds one key and 8 heads of
-//   each of two tokens; ReLU times the head weight is summed over those in
-//   the lane, the other 8 heads come from lane l ^ 32, and each lane stores
-//   one score (32 consecutive keys of a token per half-wave), causal part
-//   only.  Token tiles run latest first (they have the most key tiles).
+// Score tile (IndexRows, both score kernels): a workgroup holds 16 query
+//   tokens, each wave 4 tokens = 2 tiles of 32 (token, index head) pairs.
+//   Per 64-key tile (global -> LDS DMA, double-buffered, kswz rows): S =
+//   Qi . K_tile^T on v_mfma_f32_32x32x16_bf16 (the wave's index query rows as
+//   A in registers, key rows from LDS as B), so a lane's output holds one key
+//   and 8 heads of each of two tokens; ReLU times the head weight is summed
+//   over those in the lane and the other 8 heads' partial arrives by one
+//   v_permlane32_swap per token pair.
+// index_topk_kernel (fused scores + selection, no score array): units of 16
+//   tokens x one chunk of key tiles; after each tile the scores are regrouped
+//   so one register holds one token's 64 keys, and keys above the token's
+//   running threshold join its LDS candidate list, which is compacted to a
+//   new threshold when it fills (compact_candidates); at the end each list is
+//   cut to its best m and written as the final row, or, for rows longer than
+//   one chunk, as that chunk's list for index_merge_kernel.
+// index_scores_kernel: the same tiles, every causal score stored (32
+//   consecutive keys of a token per half-wave).  Token tiles run latest first
+//   (they have the most key tiles).
 // token_attn_kernel: one wave per (batch, token, KV head), KV-head-major over
 //   XCD-contiguous workgroups (one KV head's rows per XCD L2).  The kept
 //   positions arrive 64 at a time (one coalesced load, spread by lane
