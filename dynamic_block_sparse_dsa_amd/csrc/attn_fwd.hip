@@ -96,8 +96,13 @@ __device__ __forceinline__ void issue_tile(const uint16_t* g, uint32_t lds_base,
   }
 }
 
-template <int D, int BLK, int HG>
-__device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks_l, LDS_AS uint16_t* vs_l) {
+// NB = 1: single K and V buffers, four barriers per tile (K(t+1) streams in
+// while the softmax and P V of tile t run, V(t+1) while Q K^T of tile t+1
+// runs).  NB = 2: two of each, one barrier per tile (K(t+1) and V(t+1) go to
+// the other buffers while tile t runs), where the LDS holds them without
+// costing a workgroup per CU.
+template <int D, int BLK, int HG, int NB>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks_all, LDS_AS uint16_t* vs_all) {
   using C = AttnCfg<D, BLK, HG>;
   constexpr int NV = C::LOADS_PER_WAVE;  // loads per wave per tile (K or V)
 
@@ -127,7 +132,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
   // loads, counted by lgkmcnt, so they never wait on the tile DMA (vmcnt)
   const CONST_AS int32_t* irow = (const CONST_AS int32_t*)(a.idx + (bg * a.nB + i) * (int64_t)a.kmax);
   const int n_sel = ((const CONST_AS int32_t*)a.cnt)[bg * a.nB + i];
-  const uint32_t ks_base = (uint32_t)(uintptr_t)ks_l, vs_base = (uint32_t)(uintptr_t)vs_l;
+  const uint32_t ks_base0 = (uint32_t)(uintptr_t)ks_all, vs_base0 = (uint32_t)(uintptr_t)vs_all;
+  constexpr uint32_t TILE_BYTES = BLK * D * 2;
 
   uint32_t koff[C::LOADS_PER_WAVE], voff[C::LOADS_PER_WAVE];
 #pragma unroll
@@ -139,8 +145,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
 
   if (n_sel > 0) {
     const int j0 = irow[0];
-    issue_tile<D, BLK, HG>(kgp, ks_base, koff, j0 * BLK, N, wave, lane, false);
-    issue_tile<D, BLK, HG>(vgp, vs_base, voff, j0 * BLK, N, wave, lane, true);
+    issue_tile<D, BLK, HG>(kgp, ks_base0, koff, j0 * BLK, N, wave, lane, false);
+    issue_tile<D, BLK, HG>(vgp, vs_base0, voff, j0 * BLK, N, wave, lane, true);
   }
 
   // Q^T fragments (B operand): lane holds its row, dims ks*16 + 8*half .. +7.
@@ -168,10 +174,25 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
     const bool diag = (j == i);
     const bool more = t + 1 < n_sel;
     const int jn = more ? irow[t + 1] : 0;
+    const int buf = NB == 2 ? (t & 1) : 0;
+    const LDS_AS uint16_t* ks_l = ks_all + buf * (BLK * D);
+    const LDS_AS uint16_t* vs_l = vs_all + buf * (BLK * D);
 
-    // ---- K(t) resident (V(t) may still be in flight; Q loads are older)
-    wait_vm<NV>();
-    __syncthreads();
+    if constexpr (NB == 2) {
+      // ---- K(t), V(t) resident; every wave is done with tile t - 1, whose
+      // buffers take K(t+1), V(t+1) now
+      wait_vm<0>();
+      __syncthreads();
+      if (more) {
+        const uint32_t nb = (uint32_t)(buf ^ 1) * TILE_BYTES;
+        issue_tile<D, BLK, HG>(kgp, ks_base0 + nb, koff, jn * BLK, N, wave, lane, false);
+        issue_tile<D, BLK, HG>(vgp, vs_base0 + nb, voff, jn * BLK, N, wave, lane, true);
+      }
+    } else {
+      // ---- K(t) resident (V(t) may still be in flight; Q loads are older)
+      wait_vm<NV>();
+      __syncthreads();
+    }
     f32x16 s[BLK / 32];
 #pragma unroll
     for (int st = 0; st < BLK / 32; ++st) s[st] = (f32x16){};
@@ -205,8 +226,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
         if (KLOOK > 0) __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();  // every wave is done reading K(t)
-    if (more) issue_tile<D, BLK, HG>(kgp, ks_base, koff, jn * BLK, N, wave, lane, false);
+    if constexpr (NB == 1) {
+      __syncthreads();  // every wave is done reading K(t)
+      if (more) issue_tile<D, BLK, HG>(kgp, ks_base0, koff, jn * BLK, N, wave, lane, false);
+    }
 
     // ---- causal mask on the diagonal block, row max (raw units)
     if (diag) {
@@ -252,8 +275,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
     }
 
     // ---- V(t) resident (K(t+1) may be in flight)
-    if (more) wait_vm<NV>(); else wait_vm<0>();
-    __syncthreads();
+    if constexpr (NB == 1) {
+      if (more) wait_vm<NV>(); else wait_vm<0>();
+      __syncthreads();
+    }
     // ---- O^T += V^T P^T, A operand by transposed LDS reads: the (d-tile,
     // key-step) products in one sequence with the next step's V^T fragment in
     // flight (the scheduling barriers keep each read a step ahead of its use)
@@ -286,8 +311,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();  // every wave is done reading V(t)
-    if (more) issue_tile<D, BLK, HG>(vgp, vs_base, voff, jn * BLK, N, wave, lane, true);
+    if constexpr (NB == 1) {
+      __syncthreads();  // every wave is done reading V(t)
+      if (more) issue_tile<D, BLK, HG>(vgp, vs_base0, voff, jn * BLK, N, wave, lane, true);
+    }
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = ln(sum) + max
@@ -312,13 +339,19 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
   }
 }
 
-template <int D, int BLK, int HG>
+template <int D, int BLK, int HG, int NB>
 __global__ __launch_bounds__((AttnCfg<D, BLK, HG>::THREADS)) __attribute__((amdgpu_waves_per_eu(2)))
 void sparse_attn_fwd_kernel(AttnArgs a) {
-  __shared__ __align__(1024) uint16_t Ks[BLK * D];
-  __shared__ __align__(1024) uint16_t Vs[BLK * D];
-  attn_body<D, BLK, HG>(a, (LDS_AS uint16_t*)(Ks), (LDS_AS uint16_t*)(Vs));
+  __shared__ __align__(1024) uint16_t Ks[NB][BLK * D];
+  __shared__ __align__(1024) uint16_t Vs[NB][BLK * D];
+  attn_body<D, BLK, HG, NB>(a, (LDS_AS uint16_t*)(Ks[0]), (LDS_AS uint16_t*)(Vs[0]));
 }
+
+// Double buffers where they cost no workgroup per CU: a workgroup of 8 waves
+// (two per SIMD) is alone on its CU anyway, and 4-wave workgroups of 64-key
+// tiles still fit two per CU with 64 KiB each.
+template <int D, int BLK, int HG>
+constexpr int attn_buffers() { return AttnCfg<D, BLK, HG>::WAVES >= 4 && 2 * 2 * BLK * D * 2 <= 80 * 1024 ? 2 : AttnCfg<D, BLK, HG>::WAVES == 8 ? 2 : 1; }
 
 template <int D, int BLK, int HG>
 static hipError_t launch_attn_cfg(const AttnArgs& a, hipStream_t stream) {
@@ -326,7 +359,8 @@ static hipError_t launch_attn_cfg(const AttnArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int64_t n_wg = (int64_t)a.B * a.Hkv * (G / HG) * a.nB;
   if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BLK, HG>), dim3((uint32_t)n_wg), dim3(C::THREADS), 0, stream, a);
+  constexpr int NB = attn_buffers<D, BLK, HG>();
+  hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BLK, HG, NB>), dim3((uint32_t)n_wg), dim3(C::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
