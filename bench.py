@@ -192,8 +192,32 @@ def bench_decode(args, dev, stream, flush):
     nbytes = work.decode_bytes(S, Hq, Hkv, L, d, w.block, km)
     gbs = nbytes / (ms * 1e-3) / 1e9
     args._decode_inputs = (q, kc, vc, w, flush)  # reused by the paged bench
+
+    # the same step captured in a HIP graph and replayed (the library records
+    # no allocation or memset), timed the same way; its outputs must equal the
+    # eager step's
+    o_eager, lse_eager, idx_eager = o.clone(), lse.clone(), idx.clone()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        dsa.dsa_decode(shape, q, kc, vc, kbar, o, lse, idx, ws)
+
+    def replay():
+        with torch.cuda.stream(stream):
+            graph.replay()
+
+    for _ in range(args.warmup):
+        replay()
+    graph_us = []
+    for _ in range(args.steps):
+        read_flush(flush, stream)
+        graph_us.append(time_events(replay, 1, stream) * 1e3)
+    torch.cuda.synchronize()
+    graph_same = bool(torch.equal(o, o_eager) and torch.equal(lse, lse_eager) and torch.equal(idx, idx_eager))
+    del graph
     return dict(
         value=S / (ms * 1e-3), unit="tokens/s", ms_per_step=ms, step_us=step_stats,
+        graph_step_us=dict(stats_us(graph_us), outputs_equal_eager=graph_same),
         config=dict(workload=w.name, sequences=S, n_q_heads=Hq, n_kv_heads=Hkv, cache_len=L, head_dim=d,
                     block=w.block, topk=w.topk),
         roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",

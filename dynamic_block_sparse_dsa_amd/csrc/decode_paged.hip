@@ -20,8 +20,10 @@
 //   rows from an LDS counter) and scored by the max over the group's heads of
 //   q . kbar / sqrt(d) into LDS; the workgroup selects (one wave for the
 //   threshold and entropy variants); the 8 waves then walk the
-//   kept blocks' 32-key chunks (page base from the table, keys past the
-//   sequence's end masked) with WaveAttn and merge through LDS into o and lse.
+//   kept blocks' 32-key chunks (wave w takes chunks w, w + 8, ...: a fixed
+//   assignment, so every call merges the same partials in the same order;
+//   page base from the table, keys past the sequence's end masked) with
+//   WaveAttn and merge through LDS into o and lse.
 // kv_append_kernel: one workgroup per sequence: writes the new token's K and V
 //   rows into slot L % BLK of page table[L / BLK] for every KV head, recomputes
 //   that page's key mean over its rows 0 .. L % BLK, then advances the length.
@@ -136,8 +138,6 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
   const int ns = n_sel;
   for (int e = tid; e < kmax; e += NT) a.idx[(int64_t)unit * kmax + e] = sel[e];
   if (tid == 0 && a.cnt) a.cnt[unit] = ns;
-  if (tid == 0) next_batch = NW;
-  __syncthreads();
 
   // ---- attention over the kept blocks' chunks
   WaveAttn<D, G> wa;
@@ -167,10 +167,12 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
     else
       wa.load(rr, a.kp + f.tile * D, a.vp + f.tile * D, f.key0, f.lim);
   };
+  // wave w takes chunks w, w + NW, ... (fixed, so the merge is reproducible)
+  int next_chunk = wave + NW;
   auto grab = [&]() {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&next_batch, 1);
-    return __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
+    const int v = next_chunk;
+    next_chunk += NW;
+    return v;
   };
   int iA = wave;
   Ref fA = ref_of(iA);
