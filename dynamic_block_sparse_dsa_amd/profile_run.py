@@ -5,6 +5,7 @@
     python3 -m dynamic_block_sparse_dsa_amd.profile_run bwd    --workload prefill_n8192_h32 --reps 3
     python3 -m dynamic_block_sparse_dsa_amd.profile_run index  --workload index_n8192 --reps 3
     python3 -m dynamic_block_sparse_dsa_amd.profile_run copy   --mib 256 --reps 3
+    python3 -m dynamic_block_sparse_dsa_amd.profile_run gemm   --n 8192 --reps 3
 
 ``attn`` selects once (dsa_prefill) and then launches dsa_sparse_attn_fwd
 ``reps`` times on the same indices; ``bwd`` selects and attends once and then
@@ -13,8 +14,11 @@ launches dsa_sparse_attn_bwd ``reps`` times (seeded output gradient);
 steps (dsa_index_prefill);
 ``copy`` copies a ``mib`` MiB device buffer into another ``reps`` times (a plain
 copy kernel of known size: it reads and writes exactly ``mib`` MiB), which
-calibrates the HBM byte counters.  Each launch is followed by a device
-synchronisation so that counter samples are per dispatch.
+calibrates the HBM byte counters; ``gemm`` multiplies two n x n bf16 matrices
+``reps`` times with torch.matmul (the vendor library's dense GEMM: context for
+the MFMA counters of the attention kernels, not part of the library).  Each
+launch is followed by a device synchronisation so that counter samples are
+per dispatch.
 """
 
 import argparse
@@ -87,17 +91,32 @@ def run_copy(mib, reps, stream):
             stream.synchronize()
 
 
+def run_gemm(n, reps, stream):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    a = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            torch.matmul(a, b)
+            stream.synchronize()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("what", choices=["attn", "bwd", "decode", "index", "copy"])
+    ap.add_argument("what", choices=["attn", "bwd", "decode", "index", "copy", "gemm"])
     ap.add_argument("--workload", default=None)
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--mib", type=int, default=256)
+    ap.add_argument("--n", type=int, default=8192)
     a = ap.parse_args(argv)
     dsa.load()
     stream = torch.cuda.Stream()
     if a.what == "copy":
         run_copy(a.mib, a.reps, stream)
+    elif a.what == "gemm":
+        run_gemm(a.n, a.reps, stream)
     elif a.what == "index":
         run_index(INDEX_WORKLOADS[a.workload or "index_n8192"], a.reps, stream)
     else:
