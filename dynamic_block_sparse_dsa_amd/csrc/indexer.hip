@@ -31,13 +31,13 @@
 // token_attn_kernel: one wave per (batch, token, KV head), KV-head-major over
 //   XCD-contiguous workgroups (one KV head's rows per XCD L2).  The kept
 //   positions arrive 64 at a time (one coalesced load, spread by lane
-//   shuffles); one 32-token chunk at a time, its K rows go by DMA into a
-//   per-wave LDS tile (16 consecutive lanes per row, XOR-swizzled like the
-//   forward's K tile) and its V rows load as 16-byte pieces of whole rows;
-//   the wave waits for the K DMAs only, then runs the decode path's chunk
-//   step: Q K^T on v_mfma_f32_16x16x32_bf16 (kept keys, read back from the
-//   tile, x the group's query heads), online softmax in fp32, P V in fp32
-//   VALU.
+//   shuffles); per 32-token chunk the K rows load straight into registers as
+//   MFMA A operands and the V rows go by DMA into a per-wave LDS tile (16
+//   consecutive lanes per row, XOR-swizzled); Q K^T and P V both on
+//   v_mfma_f32_16x16x32_bf16 with the heads as columns, P (rounded to bf16,
+//   as in the block-sparse forward) passed from the S accumulators in
+//   registers and V^T read back from the tile with ds_read_b64_tr_b16;
+//   online softmax in fp32.
 // select_tokens_fast_kernel: one wave per query-token row of up to 8192
 //   scores.  The row is read in 256-token chunks, lane l holding tokens
 //   4 l .. 4 l + 3 of each (one 16-byte load per lane, 1 KiB per wave
@@ -520,43 +520,40 @@ __global__ __launch_bounds__(256) void index_merge_kernel(const IndexTopkArgs a,
 }
 
 // ============================================================== token attention
-// A 32-key chunk of kept tokens: its K rows in this wave's LDS tile (row-major,
-// 16-byte chunks XOR-swizzled by kswz, read back as MFMA A operands) and its V
-// rows in registers (lane owns 8 dims of a key group).
-template <int D, int G>
-struct GatherChunk {
-  using C = DecCfg<D, G>;
-  const LDS_AS uint16_t* kt;
-  int lane;
-  u32x4 vv[C::VPL];
-  __device__ __forceinline__ u32x4 kfrag(int sb, int ks) const {
-    const int row = sb * 16 + (lane & 15);
-    const int c = (4 * ks + (lane >> 4)) ^ kswz<D>(row);
-    return *reinterpret_cast<const LDS_AS u32x4*>(kt + row * D + c * 8);
-  }
-  __device__ __forceinline__ u32x4 vrow(int v) const { return vv[v]; }
-  __device__ __forceinline__ float kscale(int, int) const { return 1.f; }
-  __device__ __forceinline__ float vscale(int, int) const { return 1.f; }
-};
-
-// Waves per SIMD, as many as fit without spills: 128 VGPRs (four) for small
-// groups, 168 (three) for four heads at d = 128, 256 (two) for eight heads.
-template <int D, int G>
-constexpr int token_attn_waves() { return G <= 2 || (G == 4 && D == 64) ? 4 : G == 4 ? 3 : 2; }
+// One wave per (batch, token, KV head): the G query heads of the token attend
+// over its kept tokens in 32-key chunks (v_mfma_f32_16x16x32_bf16 for both
+// products, heads as the 16 N columns, zero past G).
+//   S = K Q^T: K rows are A operands loaded straight into registers (lane l:
+//     key l % 16 of a 16-key half, 16 bytes at dims ks * 32 + 8 (l / 16));
+//     the output puts head l % 16 in the lane and keys 16 sb + 4 (l / 16) + j
+//     in its slots, so row max and sum are in-lane plus two xor shuffles.
+//   O^T += V^T P^T: P leaves the S accumulators already in B-operand order
+//     (slot 4 sb + j <-> key 16 sb + 4 (l / 16) + j); the V rows go by DMA
+//     into this wave's LDS tile and come back as the V^T A operand through
+//     ds_read_b64_tr_b16 (within 16 lanes, lane i slot j receives element i % 4
+//     of the 8-byte piece of source lane 4 j + i / 4), the source lanes of
+//     16-lane group g reading keys 4 g + 16 sg + j, which is the same key order.
+// The V tile's 16-byte chunks are XOR-swizzled by row (vtsw) so that the 32
+// lanes of two groups read eight distinct 32-byte bank ranges.
+template <int D>
+__device__ __forceinline__ int vtsw(int r) {
+  return D == 128 ? 2 * ((r & 3) + 4 * ((r >> 2) & 1)) : 2 * (((r >> 1) & 1) + 2 * ((r >> 2) & 1));
+}
 
 template <int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(token_attn_waves<D, G>())))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void token_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                        const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
                        const int32_t* __restrict__ cnt, uint16_t* __restrict__ o, float* __restrict__ lse,
                        int Hkv, int N, int kmax, float scale_log2, int64_t n_waves) {
-  using C = DecCfg<D, G>;
-  constexpr int CH = D / 8, RPI = 64 / CH, NL = C::CK / RPI;  // lanes per row, rows per DMA, DMAs per chunk
-  __shared__ __align__(1024) uint16_t ktile[4][C::CK * D];
-  __shared__ float pbuf[4][C::CK][G];
-  __shared__ float abuf[4][G];
+  static_assert(G <= 16, "heads are the 16 MFMA columns");
+  constexpr int CK = 32;                                   // keys per chunk
+  constexpr int CH = D / 8, RPI = 64 / CH, NL = CK / RPI;  // V DMA: lanes per row, rows per DMA, DMAs per chunk
+  constexpr int NKS = D / 32, NDB = D / 16;                // k-steps of Q K^T, 16-dim blocks of O
+  __shared__ __align__(1024) uint16_t vtile[4][CK * D];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, lq = lane >> 4;
   // KV-head-major over XCD-contiguous workgroup ranges: the waves of one XCD
   // gather from one KV head's rows, which then stay in that XCD's L2
   const int64_t w = (int64_t)xcd_logical_id(blockIdx.x, gridDim.x) * 4 + wave;
@@ -571,77 +568,135 @@ void token_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
   const int32_t* row = idx + bt * kmax;
   const uint16_t* kb = k + (b * Hkv + g) * (int64_t)N * D;
   const uint16_t* vb = v + (b * Hkv + g) * (int64_t)N * D;
-  const LDS_AS uint16_t* kt = (const LDS_AS uint16_t*)(ktile[wave]);
-  const uint32_t kt_base = (uint32_t)(uintptr_t)kt;
+  const uint16_t* q0 = q + ((b * Hq + g * G) * (int64_t)N + t) * D;  // head hh's row at q0 + hh N D
+  const LDS_AS uint16_t* vt = (const LDS_AS uint16_t*)(vtile[wave]);
+  const uint32_t vt_base = (uint32_t)(uintptr_t)vt;
 
-  WaveAttn<D, G> wa;
-  wa.init_rows(q + ((b * Hq + g * G) * (int64_t)N + t) * D, (int64_t)N * D);
+  // B operand of S = K Q^T: column n is head n (zero past G), slots <-> dims
+  // ks * 32 + 8 lq + e
+  u32x4 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qf[ks] = (u32x4){0, 0, 0, 0};
+    if (n < G) qf[ks] = *reinterpret_cast<const u32x4*>(q0 + (int64_t)n * N * D + ks * 32 + 8 * lq);
+  }
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = (f32x4){0, 0, 0, 0};
+  const float NEG_INF = -__builtin_inff();
+  float m_run = NEG_INF, l_run = 0.f;  // head n's state, in log2 units
 
   // kept positions base .. base + 63, one per lane; positions past nk repeat
-  // the last kept token (a finite row whose weight the step masks to 0)
+  // the last kept token (a finite row whose weight is masked to 0)
   auto ids = [&](int base) {
     const int p = min(base + lane, nk - 1);
     return min(max(row[p], 0), N - 1);
   };
-  // chunk cc (0 or 1) of the 64 positions in iv.  K: each DMA brings RPI whole
-  // rows (CH consecutive lanes per row, so every request covers full cache
-  // lines), lane l landing in slot l of the tile; V: 16-byte pieces of rows.
-  auto gather = [&](GatherChunk<D, G>& r, int iv, int cc) {
+  const int nch = (nk + CK - 1) / CK;
+  int iv = 0;
+  for (int c = 0; c < nch; ++c) {
+    const int cc = c & 1;  // chunk within the 64 positions in iv
+    if (cc == 0) iv = ids(c * CK);
+    // V rows -> LDS: each DMA brings RPI whole rows (CH consecutive lanes per
+    // row, every request covering full cache lines), lane l landing in slot l
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int rr = i * RPI + lane / CH;
       const int key = __shfl(iv, 32 * cc + rr, 64);
-      const int c = (lane % CH) ^ kswz<D>(rr);
-      dma16(kb, (uint32_t)(key * D + c * 8) * 2u, __builtin_amdgcn_readfirstlane(kt_base + i * 1024));
+      const int ch = (lane % CH) ^ vtsw<D>(rr);
+      dma16(vb, (uint32_t)(key * D + ch * 8) * 2u, __builtin_amdgcn_readfirstlane(vt_base + i * 1024));
     }
+    // K rows as A operands
+    u32x4 kf[2][NKS];
 #pragma unroll
-    for (int vi = 0; vi < C::VPL; ++vi) {
-      const int key = __shfl(iv, 32 * cc + wa.pk + C::KGR * vi, 64);
-      r.vv[vi] = *reinterpret_cast<const u32x4*>(vb + (int64_t)key * D + wa.pc * 8);
+    for (int sb = 0; sb < 2; ++sb) {
+      const int key = __shfl(iv, 32 * cc + 16 * sb + n, 64);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        kf[sb][ks] = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * D + ks * 32 + 8 * lq);
     }
-  };
-
-  // one 32-key chunk at a time (a second tile and register set would cost
-  // more waves per SIMD than it hides)
-  const int nch = (nk + C::CK - 1) / C::CK;
-  GatherChunk<D, G> r;
-  r.kt = kt;
-  r.lane = lane;
-  int iv = 0;
-  for (int c = 0; c < nch; ++c) {
-    if ((c & 1) == 0) iv = ids(c * C::CK);
-    gather(r, iv, c & 1);
-    wait_vm<C::VPL>();  // the K DMAs (issued before the V loads) have landed
-    wa.step(r, c * C::CK, nk, scale_log2, pbuf[wave], abuf[wave]);
+    f32x4 sc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      sc[sb] = (f32x4){0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[sb][ks]), as_bf16x8(qf[ks]), sc[sb], 0, 0, 0);
+    }
+    // logits in log2 units, positions past nk masked; running max and sum
+    float mloc = NEG_INF;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pos = c * CK + 16 * sb + 4 * lq + j;
+        const float x = pos < nk ? sc[sb][j] * scale_log2 : NEG_INF;
+        sc[sb][j] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);  // finite: a chunk holds a position below nk
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.f;
+    u32x4 pf;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      float p4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p4[j] = __builtin_amdgcn_exp2f(sc[sb][j] - m_run);
+        lsum += p4[j];
+      }
+      const bf16x2_t lo = {(__bf16)p4[0], (__bf16)p4[1]};
+      const bf16x2_t hi = {(__bf16)p4[2], (__bf16)p4[3]};
+      pf[2 * sb] = __builtin_bit_cast(uint32_t, lo);
+      pf[2 * sb + 1] = __builtin_bit_cast(uint32_t, hi);
+    }
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    // ---- O^T += V^T P^T, the V^T operand by transposed reads of the tile
+    wait_vm<0>();  // this wave's V DMAs have landed
+    const int src = lane & 15;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      u32x4 va;
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        const int r = 4 * lq + 16 * sg + (src >> 2);  // key row of the chunk
+        const int d0 = db * 16 + 4 * (src & 3);       // first of this source lane's 4 dims
+        const int ch = (d0 >> 3) ^ vtsw<D>(r);
+        const LDS_AS char* addr = reinterpret_cast<const LDS_AS char*>(vt + r * D + ch * 8) + (d0 & 7) * 2;
+        const i16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)addr);
+        const u32x2 w2 = __builtin_bit_cast(u32x2, v4);
+        va[2 * sg] = w2[0];
+        va[2 * sg + 1] = w2[1];
+      }
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pf), acc[db], 0, 0, 0);
+    }
   }
 
-  // sum the key groups: every lane of a dim slice ends with the totals
+  // O = acc / l (bf16): lane (n, lq) holds head n's dims db * 16 + 4 lq + j;
+  // LSE = (m + log2 l) ln 2
+  if (n < G) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* orow = o + ((b * Hq + g * G + n) * (int64_t)N + t) * D;
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = wa.acc[hh][e];
-#pragma unroll
-      for (int off = C::CHK; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-      wa.acc[hh][e] = x;
+    for (int db = 0; db < NDB; ++db) {
+      const bf16x2_t lo = {(__bf16)(acc[db][0] * inv), (__bf16)(acc[db][1] * inv)};
+      const bf16x2_t hi = {(__bf16)(acc[db][2] * inv), (__bf16)(acc[db][3] * inv)};
+      u32x2 w2;
+      w2[0] = __builtin_bit_cast(uint32_t, lo);
+      w2[1] = __builtin_bit_cast(uint32_t, hi);
+      *reinterpret_cast<u32x2*>(orow + db * 16 + 4 * lq) = w2;
     }
-  // O = acc / l (bf16), LSE = (m + log2 l) ln 2; head hh's state is in lane hh
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wa.l_run), hh));
-    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wa.m_run), hh));
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (wa.pk == 0) {
-      u32x4 pkd;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2_t h2 = {(__bf16)(wa.acc[hh][2 * e] * inv), (__bf16)(wa.acc[hh][2 * e + 1] * inv)};
-        pkd[e] = __builtin_bit_cast(uint32_t, h2);
-      }
-      *reinterpret_cast<u32x4*>(o + ((b * Hq + g * G + hh) * (int64_t)N + t) * D + wa.pc * 8) = pkd;
-    }
-    if (lse && lane == 0)
-      lse[(b * Hq + g * G + hh) * (int64_t)N + t] = l > 0.f ? (m + __log2f(l)) * 0.6931471805599453f : -__builtin_inff();
+    if (lse && lq == 0)
+      lse[(b * Hq + g * G + n) * (int64_t)N + t] =
+          l_run > 0.f ? (m_run + __log2f(l_run)) * 0.6931471805599453f : -__builtin_inff();
   }
 }
 

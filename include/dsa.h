@@ -375,7 +375,9 @@ int dsa_paged_kv_block_means_fp8(const dsa_shape* shape, const uint8_t* k8, cons
  * tokens (DSA_FORCE_SINK: token 0; DSA_FORCE_DIAG: t itself) plus its best
  * other tokens up to topk in all (ties to the lower position), listed
  * ascending, and every attention head of the token attends over exactly
- * those tokens (softmax of q . k / sqrt(d), times v; fp32).
+ * those tokens (softmax of q . k / sqrt(d), times v: bf16 products with
+ * fp32 accumulation and an fp32 softmax whose weights are rounded to bf16
+ * for the product with v, as in dsa_sparse_attn_fwd).
  * Layouts: qi [B, N, HI, dI] bf16; ki [B, N, dI] bf16; wi [B, N, HI] fp32;
  * scores [B, N, N] fp32 (row t: entries 0..t are written, the rest is not
  * touched); idx [B, N, kmax] int32 (-1 padded); cnt [B, N] int32; q, o

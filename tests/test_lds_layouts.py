@@ -91,6 +91,50 @@ def test_forward_operand_reads_stay_in_the_tile(D, BLK):
             assert 0 <= byte and byte + 8 <= tile_elems * 2 and key < BLK
 
 
+def vtsw(D, r):
+    return 2 * ((r & 3) + 4 * ((r >> 2) & 1)) if D == 128 else 2 * (((r >> 1) & 1) + 2 * ((r >> 2) & 1))
+
+
+@pytest.mark.parametrize("D", DIMS)
+def test_token_attention_v_tile(D):
+    """Token attention (indexer.hip, token_attn_kernel): the V DMA of a
+    32-key chunk writes each byte of the wave's tile once; every transposed
+    read returns V[key][d] for the d and key order the MFMA expects (A operand
+    of O^T += V^T P^T: lane 16 g + i holds dim 16 db + i, slot 4 sg + j key
+    4 g + 16 sg + j -- the order P leaves the S accumulators in); and the 32
+    lanes of two groups read 64 distinct four-byte banks."""
+    CK, CH = 32, D // 8
+    rpi, nl = 64 // CH, 32 // (64 // CH)
+    tile = [None] * (CK * D)  # logical (row, d) held by each bf16 slot
+    for i, lane in itertools.product(range(nl), range(64)):
+        rr = i * rpi + lane // CH
+        ch = (lane % CH) ^ vtsw(D, rr)
+        dst = i * 1024 + 16 * lane
+        assert dst == rr * D * 2 + (lane % CH) * 16
+        for e in range(8):
+            assert tile[dst // 2 + e] is None
+            tile[dst // 2 + e] = (rr, ch * 8 + e)
+    assert all(x is not None for x in tile)
+    for db, sg in itertools.product(range(D // 16), range(2)):
+        banks = {0: [], 1: []}
+        got = {}
+        for lane in range(64):
+            g, s = lane >> 4, lane & 15
+            r = 4 * g + 16 * sg + (s >> 2)
+            d0 = db * 16 + 4 * (s & 3)
+            byte = r * D * 2 + ((d0 >> 3) ^ vtsw(D, r)) * 16 + (d0 & 7) * 2
+            assert byte % 8 == 0 and 0 <= byte and byte + 8 <= CK * D * 2
+            banks[lane >> 5] += [(byte // 4) % 64, (byte // 4 + 1) % 64]
+            for e in range(4):  # destination lane 16 g + 4 (s & 3) + e, slot s >> 2
+                got[(16 * g + 4 * (s & 3) + e, s >> 2)] = tile[byte // 2 + e]
+        for half in (0, 1):
+            assert sorted(banks[half]) == list(range(64)), (db, sg, half)
+        for lane in range(64):
+            g, i = lane >> 4, lane & 15
+            for j in range(4):
+                assert got[(lane, j)] == (4 * g + 16 * sg + j, 16 * db + i)
+
+
 def bwd_kv_cfg(D, BLK):
     kg = BLK // 32
     qs = 2 if BLK == 64 else 1
