@@ -194,8 +194,10 @@ def bench_decode(args, dev, stream, flush):
     args._decode_inputs = (q, kc, vc, w, flush)  # reused by the paged bench
 
     # the same step captured in a HIP graph and replayed (the library records
-    # no allocation or memset), timed the same way; its outputs must equal the
-    # eager step's
+    # no allocation or memset), timed the same way; its selection must equal
+    # the eager step's and its outputs agree to the rounding of the merge order
+    # (the one-launch path takes chunks first come first served unless the
+    # shape asks for DSA_DETERMINISTIC)
     o_eager, lse_eager, idx_eager = o.clone(), lse.clone(), idx.clone()
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
@@ -213,11 +215,13 @@ def bench_decode(args, dev, stream, flush):
         read_flush(flush, stream)
         graph_us.append(time_events(replay, 1, stream) * 1e3)
     torch.cuda.synchronize()
-    graph_same = bool(torch.equal(o, o_eager) and torch.equal(lse, lse_eager) and torch.equal(idx, idx_eager))
+    graph_check = dict(idx_equal=bool(torch.equal(idx, idx_eager)),
+                       o_max_abs_diff=float((o.float() - o_eager.float()).abs().max()),
+                       lse_max_abs_diff=float((lse - lse_eager).abs().max()))
     del graph
     return dict(
         value=S / (ms * 1e-3), unit="tokens/s", ms_per_step=ms, step_us=step_stats,
-        graph_step_us=dict(stats_us(graph_us), outputs_equal_eager=graph_same),
+        graph_step_us=dict(stats_us(graph_us), **graph_check),
         config=dict(workload=w.name, sequences=S, n_q_heads=Hq, n_kv_heads=Hkv, cache_len=L, head_dim=d,
                     block=w.block, topk=w.topk),
         roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 FORCE_SINK = 1
 FORCE_DIAG = 2
+DETERMINISTIC = 4  # decode: the same bits on every call (fixed work order)
 SELECT_TOPK, SELECT_THRESHOLD, SELECT_ENTROPY = 0, 1, 2
 MAX_BLOCKS = 4096
 

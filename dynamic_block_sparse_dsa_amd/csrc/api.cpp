@@ -44,7 +44,9 @@ int check_shape(const dsa_shape* s) {
     return fail(DSA_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", s->head_dim);
   if (s->block != 64 && s->block != 128) return fail(DSA_ERR_UNSUPPORTED, "block %d (built: 64, 128)", s->block);
   if (s->topk < 0) return fail(DSA_ERR_SHAPE, "topk %d < 0", s->topk);
-  if (s->flags & ~(DSA_FORCE_SINK | DSA_FORCE_DIAG)) return fail(DSA_ERR_SHAPE, "unknown flags 0x%x", s->flags);
+  if (s->flags & ~(DSA_FORCE_SINK | DSA_FORCE_DIAG | DSA_DETERMINISTIC))
+    return fail(DSA_ERR_SHAPE, "unknown flags 0x%x", s->flags);
+  const uint32_t forced = s->flags & (DSA_FORCE_SINK | DSA_FORCE_DIAG);
   if (s->select_mode != DSA_SELECT_TOPK && s->select_mode != DSA_SELECT_THRESHOLD &&
       s->select_mode != DSA_SELECT_ENTROPY)
     return fail(DSA_ERR_SHAPE, "unknown select_mode %d", s->select_mode);
@@ -52,14 +54,15 @@ int check_shape(const dsa_shape* s) {
     return fail(DSA_ERR_SHAPE, "n_anchor %d and window %d must be >= 0", s->n_anchor, s->window);
   if (s->select_mode == DSA_SELECT_THRESHOLD && !(s->threshold > 0.f && s->threshold <= 1.f))
     return fail(DSA_ERR_SHAPE, "threshold %g is not in (0, 1]", (double)s->threshold);
-  if (s->select_mode == DSA_SELECT_THRESHOLD && s->flags == 0)
+  if (s->select_mode == DSA_SELECT_THRESHOLD && forced == 0)
     return fail(DSA_ERR_SHAPE, "threshold selection needs a forced block (a row could keep none)");
   if (s->select_mode == DSA_SELECT_ENTROPY && !(s->k_min >= 1 && s->k_min <= s->k_max))
     return fail(DSA_ERR_SHAPE, "entropy budget needs 1 <= k_min (%d) <= k_max (%d)", s->k_min, s->k_max);
   if (s->select_mode == DSA_SELECT_TOPK && s->topk == 0) {
     if (s->topk_den < 1) return fail(DSA_ERR_SHAPE, "topk_den %d < 1", s->topk_den);
     if (s->topk_num < 0) return fail(DSA_ERR_SHAPE, "topk_num %d < 0", s->topk_num);
-    if (s->topk_num == 0 && s->flags == 0) return fail(DSA_ERR_SHAPE, "topk, topk_num and flags are all 0: no block kept");
+    if (s->topk_num == 0 && forced == 0)
+      return fail(DSA_ERR_SHAPE, "topk, topk_num and the forcing flags are all 0: no block kept");
   }
   if (n_blocks(s) > DSA_MAX_BLOCKS)
     return fail(DSA_ERR_UNSUPPORTED, "%lld blocks > %d", (long long)n_blocks(s), DSA_MAX_BLOCKS);
@@ -689,6 +692,7 @@ size_t dsa_decode_workspace_bytes(const dsa_shape* s) {
   if (check_decode(s)) return 0;
   const size_t nB = (size_t)n_blocks(s), d = (size_t)s->head_dim;
   const size_t units = (size_t)s->batch * s->n_kv_heads;
+  if ((int64_t)units >= dsa::DEC_FUSED_MIN_UNITS) return 0;  // one launch, no partials
   const int kmax = s->seq_len > 0 ? row_budget(s, (int)nB) : 0;
   const size_t G = (size_t)(s->n_q_heads / s->n_kv_heads);
   const size_t nsplit = (size_t)dsa::decode_splits(s->batch, s->n_kv_heads, kmax);
@@ -733,7 +737,7 @@ int dsa_decode(const dsa_shape* s, const void* q, const void* k_cache, const voi
   if (!q || !k_cache || !v_cache || !kbar || !o || !idx)
     return fail(DSA_ERR_NULL, "q, k_cache, v_cache, kbar, o or idx is NULL");
   const size_t need = dsa_decode_workspace_bytes(s);
-  if (!ws || ws_bytes < need)
+  if (need > 0 && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
   return decode_impl(s, q, k_cache, v_cache, kbar, o, lse, idx, static_cast<float*>(ws), stream);
 }

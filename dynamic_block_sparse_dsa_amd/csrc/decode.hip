@@ -33,9 +33,9 @@
 //
 // Two ways to run a step:
 //   * fused (>= 256 units, one per CU): decode_fused_kernel -- the unit's
-//     workgroup selects, then its 8 waves walk the unit's chunks (a fixed
-//     round-robin assignment: the same bits on every call) and merge through
-//     LDS into o and lse.  One launch, no workspace.
+//     workgroup selects, then its 8 waves walk the unit's chunks (first come
+//     first served, or in a fixed round-robin order under DSA_DETERMINISTIC)
+//     and merge through LDS into o and lse.  One launch, no workspace.
 //   * split (fewer units): decode_select_kernel writes idx; decode_attn_kernel
 //     runs split-K over the kept blocks (one 256-thread workgroup per (unit,
 //     split)) and writes a partial (max, sum, acc[d]) per head;
@@ -286,8 +286,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 // ------------------------------------------------------------ fused path
 // One 512-thread workgroup per unit does the whole step: score + select as
 // above (the selection goes to LDS and to idx), then its 8 waves walk the
-// unit's chunks (a fixed round-robin assignment, two chunks in flight per
-// wave) and merge through LDS straight into o and lse.  No workspace, one launch.  Used
+// unit's chunks (taken from an LDS counter, or round-robin under
+// DSA_DETERMINISTIC; two chunks in flight per wave) and merge through LDS
+// straight into o and lse.  No workspace, one launch.  Used
 // when there are enough units to give every CU one.
 template <int D, int BLK, int G, int R>
 __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkParams p) {
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkPar
   __shared__ uint32_t lds_key[128];
   __shared__ int32_t lds_idx[128];
   __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS + BSEL2_SCRATCH_WORDS];
+  __shared__ int next_batch;
   __shared__ int32_t sel[64 * R];          // kept blocks (kmax <= nB <= 64 R)
   __shared__ float pbuf[NW][C::CK][G];
   __shared__ float abuf[NW][G];
@@ -353,14 +355,25 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkPar
   // LDS-only barriers from here to the walk, so the preloads stay in flight
   lds_barrier();
   for (int e = tid; e < kmax; e += 512) a.idx[(int64_t)unit * kmax + e] = sel[e];
-  // wave w takes chunks w, w + NW, w + 2 NW, ... (a fixed assignment, so the
-  // merge below adds the same partials in the same order on every call),
-  // keeping one more chunk in flight than it computes
+  if (tid == 0) next_batch = NW;
+  lds_barrier();
+  // chunks 0 .. NW-1 go to the waves in order, then each wave takes the next
+  // free chunk from an LDS counter (next_batch is free again: the selection
+  // barrier is behind us), keeping one more chunk in flight than it computes.
+  // DSA_DETERMINISTIC: wave w takes chunks w, w + NW, w + 2 NW, ... instead,
+  // so the merge below adds the same partials in the same order on every call
+  // (first come first served balances the waves a little better).
+  const bool fixed = (p.flags & DSA_DETERMINISTIC) != 0u;
   int next_chunk = wave + NW;
   auto grab = [&]() {
-    const int v = next_chunk;
-    next_chunk += NW;
-    return v;
+    if (fixed) {
+      const int v = next_chunk;
+      next_chunk += NW;
+      return v;
+    }
+    int v = 0;
+    if ((tid & 63) == 0) v = atomicAdd(&next_batch, 1);
+    return __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
   };
   int iA = wave;
   if (!pre) {
@@ -428,10 +441,6 @@ static void launch_fused(const DecodeArgs& a, TopkParams p, hipStream_t stream) 
   else
     hipLaunchKernelGGL((decode_fused_kernel<D, BLK, G, 64>), grid, blk, 0, stream, a, p);
 }
-
-// With at least this many (sequence, KV head) units -- one per CU of an
-// MI355X -- the fused one-workgroup-per-unit kernel fills the chip by itself.
-constexpr int64_t DEC_FUSED_MIN_UNITS = 256;
 
 template <int D, int BLK>
 static hipError_t launch_decode_d(const DecodeArgs& a, TopkParams p, hipStream_t stream) {

@@ -232,5 +232,9 @@ hipError_t decode_noalloc_scratch(void** out);
 
 // number of key splits a decode step uses (also sizes its workspace)
 int decode_splits(int S, int Hkv, int kmax);
+// With at least this many (sequence, KV head) units -- one per CU of an
+// MI355X -- a decode step is one launch of the fused one-workgroup-per-unit
+// kernel, which fills the chip by itself and needs no workspace.
+constexpr int64_t DEC_FUSED_MIN_UNITS = 256;
 
 }  // namespace dsa

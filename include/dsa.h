@@ -71,6 +71,11 @@ enum {
 #define DSA_FORCE_SINK 1u /* block 0 */
 #define DSA_FORCE_DIAG 2u /* the row's own block: the diagonal block in prefill,
                              the last cache block in decode */
+/* and how the work is ordered: with DSA_DETERMINISTIC a decode step gives the
+ * same bits on every call (its one-launch path, S * Hkv >= 256, then hands the
+ * kept chunks to its waves in a fixed order instead of first come first
+ * served; every other call gives the same bits on every call regardless) */
+#define DSA_DETERMINISTIC 4u
 
 /* select_mode: how a row's budget is set (prefill; decode takes TOPK only) */
 #define DSA_SELECT_TOPK 0      /* topk or the fraction below */
@@ -94,7 +99,8 @@ typedef struct dsa_shape {
                          0: use the fraction below */
   int32_t topk_num;   /* topk == 0: keep ceil(topk_num * visible / topk_den)  */
   int32_t topk_den;   /*   blocks (integer arithmetic), num >= 0, den >= 1    */
-  uint32_t flags;     /* DSA_FORCE_SINK | DSA_FORCE_DIAG (or a subset) */
+  uint32_t flags;     /* DSA_FORCE_SINK | DSA_FORCE_DIAG (or a subset),
+                         | DSA_DETERMINISTIC */
   /* Selection variants.  All zero: DSA_SELECT_TOPK with a one-block sink and
    * a one-block diagonal.  "dynamic sparse attention explainer", section
    * "基于Top-k选择的局部-全局混合" (global tokens + a local window), DeepSeek
@@ -240,7 +246,8 @@ size_t dsa_decode_workspace_bytes(const dsa_shape* shape);
  * budget (ties to the lower block), and every key of the kept blocks is
  * attended to (split over the kept blocks, partials merged).
  * o: [S, Hq, d] bf16; lse: [S, Hq] fp32 or NULL; idx: [S, Hkv, dsa_kmax]
- * int32.  ws: at least dsa_decode_workspace_bytes.  Sources: "dynamic sparse
+ * int32.  ws: at least dsa_decode_workspace_bytes (NULL allowed when that is
+ * 0).  Sources: "dynamic sparse
  * attention explainer", "动态开销与计算收益的权衡" (cache-time index data),
  * "前沿方向" (one selection per GQA group), "硬件友好的稀疏计算实现" (whole
  * blocks of the cache).  Errors: NULL pointers, shape errors (decode takes

@@ -109,7 +109,7 @@ BAD = [
     (dict(topk=0, topk_num=1, topk_den=0), dsa.DSA_ERR_SHAPE),
     (dict(topk=0, topk_num=-1, topk_den=3), dsa.DSA_ERR_SHAPE),
     (dict(topk=0, topk_num=0, flags=0), dsa.DSA_ERR_SHAPE),
-    (dict(flags=4), dsa.DSA_ERR_SHAPE),
+    (dict(flags=8), dsa.DSA_ERR_SHAPE),
     (dict(seq_len=64 * 4096 + 1), dsa.DSA_ERR_UNSUPPORTED),
     (dict(select_mode=3), dsa.DSA_ERR_SHAPE),
     (dict(n_anchor=-1), dsa.DSA_ERR_SHAPE),

@@ -100,9 +100,11 @@ DECODES = [
 @pytest.mark.parametrize("noalloc", [False, True], ids=["workspace", "noalloc"])
 def test_decode_step_replays(cuda_device, w, noalloc):
     """dsa_decode (caller workspace) or dsa_decode_noalloc (library-owned
-    scratch) captured once; three replays with a new query each."""
+    scratch) captured once; three replays with a new query each.  With
+    DSA_DETERMINISTIC, so that the one-launch path's merge order is fixed."""
     S, Hq, Hkv, L, d, nB = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.n_blocks
-    shape = dsa.make_shape(S, Hq, Hkv, L, d, w.block, w.topk)
+    shape = dsa.make_shape(S, Hq, Hkv, L, d, w.block, w.topk,
+                           flags=dsa.FORCE_SINK | dsa.FORCE_DIAG | dsa.DETERMINISTIC)
     km = dsa.dsa_kmax(shape)
     q, kc, vc = make_decode(w, device=cuda_device)
     kbar = dsa.kv_block_means(kc, w.block)
@@ -196,3 +198,36 @@ def test_paged_serving_step_replays(cuda_device):
         assert_same(graphed, eager, f"paged state after step {rep}")
     assert graphed[3].tolist() == [705, 68, 69, 6, 768, 768]
     say("paged serving step: 5 replays identical to the eager steps (appends included)")
+
+
+def test_decode_deterministic_flag(cuda_device):
+    """The one-launch decode path (256 units) gives the same bits on every call
+    under DSA_DETERMINISTIC; without it the chunks are taken first come first
+    served, the selection is the same and the outputs agree to the rounding of
+    the merge order."""
+    w = DECODES[1]
+    S, Hq, Hkv, L, d = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim
+    q, kc, vc = make_decode(w, device=cuda_device)
+    kbar = dsa.kv_block_means(kc, w.block)
+    runs = {}
+    for name, fl in (("fixed", dsa.DETERMINISTIC), ("free", 0)):
+        shape = dsa.make_shape(S, Hq, Hkv, L, d, w.block, w.topk, flags=dsa.FORCE_SINK | dsa.FORCE_DIAG | fl)
+        km = dsa.dsa_kmax(shape)
+        assert dsa.dsa_decode_workspace_bytes(shape) == 0  # the one-launch path
+        outs = []
+        for _ in range(4):
+            o = torch.empty_like(q)
+            lse = torch.empty((S, Hq), dtype=torch.float32, device=cuda_device)
+            idx = torch.empty((S, Hkv, km), dtype=torch.int32, device=cuda_device)
+            dsa.dsa_decode(shape, q, kc, vc, kbar, o, lse, idx, torch.empty(1, dtype=torch.uint8, device=cuda_device))
+            outs.append((o, lse, idx))
+        torch.cuda.synchronize()
+        runs[name] = outs
+    for o, lse, idx in runs["fixed"][1:]:
+        assert_same((o, lse, idx), runs["fixed"][0], "deterministic decode")
+    ref = runs["fixed"][0]
+    for o, lse, idx in runs["free"]:
+        assert torch.equal(idx, ref[2])
+        assert (o.float() - ref[0].float()).abs().max() <= 2 ** -7 * ref[0].float().abs().max()
+        assert torch.allclose(lse, ref[1], rtol=1e-5, atol=1e-5)
+    say("decode: DSA_DETERMINISTIC gives identical bits; first come first served agrees to rounding")
