@@ -36,6 +36,7 @@ ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "attn_fwd.
 DECODE_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "decode.hip")
 BWD_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "attn_bwd.hip")
 INDEX_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "indexer.hip")
+PAGED_SRC = os.path.join(ROOT, "dynamic_block_sparse_dsa_amd", "csrc", "decode_paged.hip")
 
 
 def log(msg):
@@ -286,6 +287,8 @@ def bench_paged(args, dev, stream):
         out[name] = dict(value=S / (ms * 1e-3), unit="tokens/s", ms_per_step=ms, tokens_in_caches=int(sum(lens_list)),
                          roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                                        frac=round(gbs / PEAK_HBM_GBS, 4), bytes_per_step=nbytes,
+                                       traffic=(measured_traffic("paged_" + w.name, PAGED_SRC)
+                                                if name == "full_length" else None),
                                        kernel="decode_paged_kernel"))
     # the same caches in FP8 (E4M3 codes, a scale per row), full length
     k8 = torch.empty((n_pages, Hkv, b, d), dtype=torch.uint8, device=dev)
@@ -313,6 +316,7 @@ def bench_paged(args, dev, stream):
     out["fp8_full_length"] = dict(value=S / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
                                   roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                                                 frac=round(gbs / PEAK_HBM_GBS, 4), bytes_per_step=nbytes,
+                                                traffic=measured_traffic("paged8_" + w.name, PAGED_SRC),
                                                 kernel="decode_paged_kernel (fp8)"))
     # one append of a token per sequence (the mixed lengths leave room)
     kn = torch.randn((S, Hkv, d), device=dev).to(torch.bfloat16)

@@ -153,13 +153,14 @@ __global__ __launch_bounds__(256) void bwd_invert_kernel(const int32_t* __restri
     bool hit = false;
     if (i < nB) {
       const int32_t* row = idx + (unit * nB + i) * (int64_t)kmax;
-      int lo = 0, hi = cnt[unit * nB + i];  // ascending block ids
+      const int n = min(max(cnt[unit * nB + i], 0), kmax);  // clamped into range
+      int lo = 0, hi = n;  // ascending block ids
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (row[mid] < j) lo = mid + 1;
         else hi = mid;
       }
-      hit = lo < cnt[unit * nB + i] && row[lo] == j;
+      hit = lo < n && row[lo] == j;
     }
     const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
     const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
@@ -208,13 +209,15 @@ void bwd_dq_kernel(BwdArgs a) {
   const uint16_t* kgp = a.k + bg * (int64_t)N * D;
   const uint16_t* vgp = a.v + bg * (int64_t)N * D;
   const CONST_AS int32_t* irow = (const CONST_AS int32_t*)(a.idx + (bg * a.nB + i) * (int64_t)a.kmax);
-  const int n_sel = ((const CONST_AS int32_t*)a.cnt)[bg * a.nB + i];
+  // counts and block ids clamped into range (as in the forward)
+  const int n_sel = min(max(((const CONST_AS int32_t*)a.cnt)[bg * a.nB + i], 0), a.kmax);
+  auto blk_at = [&](int t) { return min(max(irow[t], 0), a.nB - 1); };
   const uint32_t kbase[2] = {(uint32_t)(uintptr_t)(LDS_AS uint16_t*)Ks[0], (uint32_t)(uintptr_t)(LDS_AS uint16_t*)Ks[1]};
   const uint32_t vbase = (uint32_t)(uintptr_t)(LDS_AS uint16_t*)Vs;
 
   if (n_sel > 0) {
-    load_tile<D, BLK, C::WAVES>(kgp, irow[0] * BLK, N, kbase[0], wave, lane);
-    load_tile<D, BLK, C::WAVES>(vgp, irow[0] * BLK, N, vbase, wave, lane);
+    load_tile<D, BLK, C::WAVES>(kgp, blk_at(0) * BLK, N, kbase[0], wave, lane);
+    load_tile<D, BLK, C::WAVES>(vgp, blk_at(0) * BLK, N, vbase, wave, lane);
   }
   // B operands: lane's row, dims 16 ks + 8 half .. + 7
   u32x4 qf[NKS], df[NKS];
@@ -236,9 +239,9 @@ void bwd_dq_kernel(BwdArgs a) {
   const float c2 = a.scale_log2;
 
   for (int t = 0; t < n_sel; ++t) {
-    const int j = irow[t];
+    const int j = blk_at(t);
     const bool more = t + 1 < n_sel;
-    const int jn = more ? irow[t + 1] : 0;
+    const int jn = more ? blk_at(t + 1) : 0;
     const LDS_AS uint16_t* ks_l = (const LDS_AS uint16_t*)Ks[t & 1];
     // ---- K(t), V(t) resident; every wave is done with tile t - 1
     wait_vm<0>();

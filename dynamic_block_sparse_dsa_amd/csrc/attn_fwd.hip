@@ -131,7 +131,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
   // the index row is read through the constant address space: uniform scalar
   // loads, counted by lgkmcnt, so they never wait on the tile DMA (vmcnt)
   const CONST_AS int32_t* irow = (const CONST_AS int32_t*)(a.idx + (bg * a.nB + i) * (int64_t)a.kmax);
-  const int n_sel = ((const CONST_AS int32_t*)a.cnt)[bg * a.nB + i];
+  // counts and block ids are clamped into range: an index array that did not
+  // come from a selection call gives wrong results, never an access outside
+  // the tensors
+  const int n_sel = min(max(((const CONST_AS int32_t*)a.cnt)[bg * a.nB + i], 0), a.kmax);
+  auto blk_at = [&](int t) { return min(max(irow[t], 0), a.nB - 1); };
   const uint32_t ks_base0 = (uint32_t)(uintptr_t)ks_all, vs_base0 = (uint32_t)(uintptr_t)vs_all;
   constexpr uint32_t TILE_BYTES = BLK * D * 2;
 
@@ -144,7 +148,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
   }
 
   if (n_sel > 0) {
-    const int j0 = irow[0];
+    const int j0 = blk_at(0);
     issue_tile<D, BLK, HG>(kgp, ks_base0, koff, j0 * BLK, N, wave, lane, false);
     issue_tile<D, BLK, HG>(vgp, vs_base0, voff, j0 * BLK, N, wave, lane, true);
   }
@@ -170,10 +174,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, LDS_AS uint16_t* ks
   float l_part = 0.f;             // this lane's share of the row sum
 
   for (int t = 0; t < n_sel; ++t) {
-    const int j = irow[t];
+    const int j = blk_at(t);
     const bool diag = (j == i);
     const bool more = t + 1 < n_sel;
-    const int jn = more ? irow[t + 1] : 0;
+    const int jn = more ? blk_at(t + 1) : 0;
     const int buf = NB == 2 ? (t & 1) : 0;
     const LDS_AS uint16_t* ks_l = ks_all + buf * (BLK * D);
     const LDS_AS uint16_t* vs_l = vs_all + buf * (BLK * D);

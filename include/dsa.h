@@ -196,7 +196,10 @@ int dsa_select_topk(const dsa_shape* shape, const float* scores, int32_t* idx, i
 
 /* Step 4: causal attention over the listed blocks.  q [B, Hq, N, d], k, v
  * [B, Hkv, N, d] bf16; idx, cnt as dsa_select_topk writes them (entries
- * 0..cnt-1 of a row must be ascending, distinct, in 0..i -- not checked).
+ * 0..cnt-1 of a row must be ascending, distinct, in 0..i -- not checked;
+ * counts outside [0, kmax] and block ids outside [0, nB) are clamped into
+ * range, so such input gives wrong results but no access outside the
+ * tensors).
  * Row p of query block i attends to the keys c <= p of its kept blocks:
  *   O[p] = sum_c softmax_c((1/sqrt(d)) q_p . k_c) v_c,  LSE[p] = log sum_c
  *   exp((1/sqrt(d)) q_p . k_c)
