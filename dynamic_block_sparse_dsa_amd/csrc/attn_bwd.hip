@@ -153,14 +153,17 @@ __global__ __launch_bounds__(256) void bwd_invert_kernel(const int32_t* __restri
     bool hit = false;
     if (i < nB) {
       const int32_t* row = idx + (unit * nB + i) * (int64_t)kmax;
-      const int n = min(max(cnt[unit * nB + i], 0), kmax);  // clamped into range
+      // count and block ids clamped into range, as where the forward and
+      // the dQ kernel read them (clamping keeps an ascending row ascending)
+      const int n = min(max(cnt[unit * nB + i], 0), kmax);
+      auto at = [&](int e) { return min(max(row[e], 0), nB - 1); };
       int lo = 0, hi = n;  // ascending block ids
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (row[mid] < j) lo = mid + 1;
+        if (at(mid) < j) lo = mid + 1;
         else hi = mid;
       }
-      hit = lo < n && row[lo] == j;
+      hit = lo < n && at(lo) == j;
     }
     const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
     const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
