@@ -283,3 +283,34 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros((1, 2, 128, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         dsa.dsa_block_means(s, 2, x, torch.zeros((1, 2, 2, 64)), stream=0)
+
+
+def test_decode_workspace_is_zero_on_the_one_launch_path(lib):
+    """From 256 (sequence, KV head) units on a decode step is one launch with
+    no partials: its workspace is 0 bytes and dsa_decode takes a NULL
+    workspace there (it still refuses one below that)."""
+    p = ctypes.c_void_p(16)
+    for S, Hkv in ((64, 4), (256, 1), (32, 8), (300, 1)):
+        s = shape(batch=S, n_q_heads=Hkv * 4, n_kv_heads=Hkv, seq_len=4096, topk=16)
+        assert lib.dsa_decode_workspace_bytes(ctypes.byref(s)) == 0
+    s = shape(batch=63, n_q_heads=16, n_kv_heads=4, seq_len=4096, topk=16)  # 252 units: split path
+    assert lib.dsa_decode_workspace_bytes(ctypes.byref(s)) > 0
+    assert lib.dsa_decode(ctypes.byref(s), p, p, p, p, p, None, p, None, 0, None) == dsa.DSA_ERR_WORKSPACE
+
+
+def test_deterministic_flag_is_a_shape_flag(lib):
+    """DSA_DETERMINISTIC is accepted next to the forcing flags (prefill and
+    decode shapes), does not count as a forced block, and the index shape,
+    whose calls are deterministic anyway, does not take it."""
+    out = ctypes.c_int32()
+    for fl in (dsa.DETERMINISTIC, 3 | dsa.DETERMINISTIC, 1 | dsa.DETERMINISTIC):
+        s = shape(flags=fl)
+        assert lib.dsa_prefill_kmax(ctypes.byref(s), ctypes.byref(out)) == 0
+        assert lib.dsa_decode_kmax(ctypes.byref(s), ctypes.byref(out)) == 0
+    # the flag forces nothing: a fraction of 0 with no forcing flag keeps no block
+    s = shape(topk=0, topk_num=0, topk_den=1, flags=dsa.DETERMINISTIC)
+    assert lib.dsa_prefill_kmax(ctypes.byref(s), ctypes.byref(out)) == dsa.DSA_ERR_SHAPE
+    s = shape(select_mode=1, threshold=0.1, flags=dsa.DETERMINISTIC)  # threshold needs a forced block
+    assert lib.dsa_prefill_kmax(ctypes.byref(s), ctypes.byref(out)) == dsa.DSA_ERR_SHAPE
+    i = dsa.make_index_shape(1, 4, 2, 1024, 128, 16, 128, 64, flags=3 | dsa.DETERMINISTIC)
+    assert lib.dsa_index_kmax(ctypes.byref(i), ctypes.byref(out)) == dsa.DSA_ERR_SHAPE
