@@ -155,11 +155,8 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a, TopkPa
 // ============================================================== 2. attention
 // ------------------------------------------------------------ split path
 // Split-K over the kept blocks, one 256-thread workgroup per (unit, split),
-// one chunk per wave at a time; the workgroup writes a partial per head.
-constexpr int DEC_MAX_SPLITS = 32;
-// Split count aims at about this many attention workgroups: fewer, longer
-// lived waves (each walks several chunks) beat one chunk per wave.
-constexpr int DEC_TARGET_WG = 1024;
+// one chunk per wave at a time; the workgroup writes a partial per head (the
+// split count: decode_splits, plan.cpp).
 
 // Library-owned scratch for dsa_decode_noalloc (callers that cannot allocate):
 // the split partials [S * Hkv, nsplit, G, d + 2] fp32 of any shape the split
@@ -413,17 +410,6 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkPar
 }
 
 // ============================================================== launch
-int decode_splits(int S, int Hkv, int kmax) {
-  const int64_t units = (int64_t)S * Hkv;
-  if (units == 0 || kmax == 0) return 1;
-  int64_t want = (DEC_TARGET_WG + units - 1) / units;
-  if (want < 1) want = 1;
-  if (want > kmax) want = kmax;
-  if (want > DEC_MAX_SPLITS) want = DEC_MAX_SPLITS;
-  const int bps = (int)((kmax + want - 1) / want);
-  return (kmax + bps - 1) / bps;  // every split gets at least one block
-}
-
 template <int D, int G>
 static void launch_select(const DecodeArgs& a, TopkParams p, hipStream_t stream) {
   const dim3 grid((uint32_t)((int64_t)a.S * a.Hkv)), blk(512);

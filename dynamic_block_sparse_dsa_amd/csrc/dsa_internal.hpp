@@ -230,7 +230,12 @@ hipError_t launch_decode(const DecodeArgs& a, int d, TopkParams p, hipStream_t s
 // DSA_DECODE_NOALLOC_MAX_BYTES (looked up once per device)
 hipError_t decode_noalloc_scratch(void** out);
 
-// number of key splits a decode step uses (also sizes its workspace)
+// Decode split path: at most DEC_MAX_SPLITS key splits per (sequence, KV
+// head); the split count aims at about DEC_TARGET_WG attention workgroups
+// (fewer, longer-lived waves that each walk several chunks beat one chunk per
+// wave).  decode_splits: the number a step uses (also sizes its workspace).
+constexpr int DEC_MAX_SPLITS = 32;
+constexpr int DEC_TARGET_WG = 1024;
 int decode_splits(int S, int Hkv, int kmax);
 // With at least this many (sequence, KV head) units -- one per CU of an
 // MI355X -- a decode step is one launch of the fused one-workgroup-per-unit

@@ -851,16 +851,6 @@ static hipError_t launch_token_attn_d(const TokenAttnArgs& a, hipStream_t stream
   return hipGetLastError();
 }
 
-IndexTopkPlan plan_index_topk(int B, int N, int kmax) {
-  IndexTopkPlan pl{};
-  const int n_kt = (N + 63) / 64;
-  pl.kct = max(64, (n_kt + INDEX_TOPK_MAX_CHUNKS - 1) / INDEX_TOPK_MAX_CHUNKS);
-  pl.nch = max(1, (n_kt + pl.kct - 1) / pl.kct);
-  pl.mw = max(kmax, 1);
-  pl.ws_bytes = pl.nch > 1 ? (size_t)B * N * pl.nch * (8 * (size_t)pl.mw + 4) : 0;
-  return pl;
-}
-
 hipError_t launch_index_topk(const uint16_t* qi, const uint16_t* ki, const float* wi, int32_t* idx, int32_t* cnt,
                              void* ws, int B, int N, int di, TopkParams p, int kmax, hipStream_t stream) {
   if (B == 0 || N == 0) return hipSuccess;
