@@ -28,6 +28,9 @@ DETERMINISTIC = 4  # decode: the same bits on every call (fixed work order)
 SELECT_TOPK, SELECT_THRESHOLD, SELECT_ENTROPY = 0, 1, 2
 MAX_BLOCKS = 4096
 
+LAYOUT_PREFILL, LAYOUT_DECODE, LAYOUT_PAGED = 0, 1, 2
+CHECK_SLOTS = ("rows", "count", "range", "order", "forced", "padding")  # report slots of the selection validator
+
 DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4, -5
 
 EXPORTS = [
@@ -39,6 +42,8 @@ EXPORTS = [
     "dsa_block_scores_from_means",
     "dsa_select_topk",
     "dsa_indices_to_bitmap",
+    "dsa_check_block_selection",
+    "dsa_check_token_selection",
     "dsa_index_kmax",
     "dsa_index_scores",
     "dsa_select_tokens",
@@ -150,6 +155,8 @@ def load() -> ctypes.CDLL:
         "dsa_block_scores_from_means": ([S, P, P, P, P], ctypes.c_int),
         "dsa_select_topk": ([S, P, P, P, P], ctypes.c_int),
         "dsa_indices_to_bitmap": ([P, P, ctypes.c_int64, I32, I32, P, P], ctypes.c_int),
+        "dsa_check_block_selection": ([S, I32, P, P, P, P, P], ctypes.c_int),
+        "dsa_check_token_selection": ([X, P, P, P, P], ctypes.c_int),
         "dsa_index_kmax": ([X, ctypes.POINTER(I32)], ctypes.c_int),
         "dsa_index_scores": ([X, P, P, P, P, P], ctypes.c_int),
         "dsa_select_tokens": ([X, P, P, P, P], ctypes.c_int),
@@ -359,6 +366,29 @@ def dsa_indices_to_bitmap(idx, cnt, n_cols: int, bitmap, stream=None):
     _check(load().dsa_indices_to_bitmap(
         _ptr(idx, torch.int32, lead + (km,), "idx"), _ptr(cnt, torch.int32, lead, "cnt", optional=True), n_rows, km,
         n_cols, _ptr(bitmap, torch.int32, lead + ((n_cols + 31) // 32,), "bitmap"), _stream(stream)))
+
+
+def dsa_check_block_selection(shape: Shape, layout: int, idx, cnt, lengths, report, stream=None):
+    """Selection validator (counts into report [6] int64); layouts LAYOUT_*."""
+    B, Hkv = shape.batch, shape.n_kv_heads
+    nB = -(-shape.seq_len // shape.block)
+    if layout == LAYOUT_PREFILL:
+        lead, km = (B, Hkv, nB), dsa_prefill_kmax(shape)
+    else:
+        lead, km = (B, Hkv), dsa_decode_kmax(shape)
+    _check(load().dsa_check_block_selection(
+        ctypes.byref(shape), layout, _ptr(idx, torch.int32, lead + (km,), "idx"),
+        _ptr(cnt, torch.int32, lead, "cnt", optional=True),
+        _ptr(lengths, torch.int32, (B,), "lengths", optional=True),
+        _ptr(report, torch.int64, (len(CHECK_SLOTS),), "report"), _stream(stream)))
+
+
+def dsa_check_token_selection(shape: IndexShape, idx, cnt, report, stream=None):
+    B, N = shape.batch, shape.seq_len
+    _check(load().dsa_check_token_selection(
+        ctypes.byref(shape), _ptr(idx, torch.int32, (B, N, dsa_index_kmax(shape)), "idx"),
+        _ptr(cnt, torch.int32, (B, N), "cnt", optional=True),
+        _ptr(report, torch.int64, (len(CHECK_SLOTS),), "report"), _stream(stream)))
 
 
 def dsa_sparse_attn_fwd(shape: Shape, q, k, v, idx, cnt, o, lse=None, stream=None):
@@ -584,6 +614,20 @@ def bitmap(idx, cnt, n_cols: int, stream=None):
     out = torch.empty(tuple(idx.shape[:-1]) + ((n_cols + 31) // 32,), dtype=torch.int32, device=idx.device)
     dsa_indices_to_bitmap(idx, cnt, n_cols, out, stream)
     return out
+
+
+def check_selection(shape, idx, cnt=None, lengths=None, layout: int = LAYOUT_PREFILL, stream=None) -> dict:
+    """Run the selection validator and return its report as a dict (waits for
+    the validator to read it).  shape: a Shape (block selection, `layout`) or an
+    IndexShape (token selection)."""
+    report = torch.empty(len(CHECK_SLOTS), dtype=torch.int64, device=idx.device)
+    if isinstance(shape, IndexShape):
+        dsa_check_token_selection(shape, idx, cnt, report, stream)
+    else:
+        dsa_check_block_selection(shape, layout, idx, cnt, lengths, report, stream)
+    if stream is not None:
+        torch.cuda.synchronize(idx.device)
+    return dict(zip(CHECK_SLOTS, report.tolist()))
 
 
 def index_prefill(qi, ki, wi, q, k, v, topk: int, flags: int = FORCE_SINK | FORCE_DIAG, want_lse: bool = True,

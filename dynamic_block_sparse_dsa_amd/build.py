@@ -19,8 +19,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["select.hip", "attn_fwd.hip", "attn_bwd.hip", "decode.hip", "decode_paged.hip", "indexer.hip", "plan.cpp",
-           "api.cpp"]
+SOURCES = ["select.hip", "attn_fwd.hip", "attn_bwd.hip", "decode.hip", "decode_paged.hip", "indexer.hip", "check.hip",
+           "plan.cpp", "api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

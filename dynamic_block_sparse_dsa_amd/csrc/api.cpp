@@ -759,4 +759,80 @@ int dsa_decode_noalloc(const dsa_shape* s, const void* q, const void* k_cache, c
   return decode_impl(s, q, k_cache, v_cache, kbar, o, lse, idx, static_cast<float*>(scratch), stream);
 }
 
+int dsa_check_block_selection(const dsa_shape* s, int32_t layout, const int32_t* idx, const int32_t* cnt,
+                              const int32_t* lengths, int64_t* report, void* stream) {
+  if (layout != DSA_LAYOUT_PREFILL && layout != DSA_LAYOUT_DECODE && layout != DSA_LAYOUT_PAGED)
+    return fail(DSA_ERR_SHAPE, "unknown layout %d", layout);
+  int rc = layout == DSA_LAYOUT_PREFILL ? check_shape(s) : check_decode(s);
+  if (rc) return rc;
+  if (!report) return fail(DSA_ERR_NULL, "report is NULL");
+  const int nB = (int)n_blocks(s);
+  dsa::CheckArgs a{};
+  a.report = reinterpret_cast<unsigned long long*>(report);
+  a.layout = layout;
+  if (layout == DSA_LAYOUT_PREFILL) {
+    a.n_rows = (int64_t)s->batch * s->n_kv_heads * nB;
+    a.kmax = prefill_kmax(s);
+    a.period = nB;
+  } else {
+    a.n_rows = (int64_t)s->batch * s->n_kv_heads;
+    a.kmax = s->seq_len > 0 ? row_budget(s, nB) : 0;
+    a.period = nB;
+    a.per_seq = s->n_kv_heads;
+    a.block = s->block;
+    a.capacity = s->seq_len;
+  }
+  if (a.n_rows > 0 && a.kmax > 0) {
+    if (!idx) return fail(DSA_ERR_NULL, "idx is NULL");
+    if (layout == DSA_LAYOUT_PREFILL && !cnt) return fail(DSA_ERR_NULL, "cnt is NULL (a prefill selection has one)");
+    if (layout == DSA_LAYOUT_PAGED && !lengths) return fail(DSA_ERR_NULL, "lengths is NULL");
+  } else {
+    a.n_rows = 0;  // nothing listed: the report is cleared and ROWS stays 0
+  }
+  a.idx = idx;
+  a.cnt = cnt;
+  a.lengths = lengths;
+  const dsa::TopkParams p = topk_params(s);
+  a.sel_mode = p.mode;
+  a.topk = p.topk;
+  a.topk_num = p.num;
+  a.topk_den = p.den;
+  a.anchors = p.anchors;
+  a.window = p.window;
+  a.cand_cap = p.cand_cap;
+  a.k_min = p.k_min;
+  a.k_max = p.k_max;
+  hipError_t e = dsa::launch_check(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "selection check launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
+int dsa_check_token_selection(const dsa_index_shape* s, const int32_t* idx, const int32_t* cnt, int64_t* report,
+                              void* stream) {
+  int rc = check_index(s);
+  if (rc) return rc;
+  if (!report) return fail(DSA_ERR_NULL, "report is NULL");
+  dsa::CheckArgs a{};
+  a.report = reinterpret_cast<unsigned long long*>(report);
+  a.layout = DSA_LAYOUT_PREFILL;  // the row of token t sees t + 1 positions
+  a.n_rows = (int64_t)s->batch * s->seq_len;
+  a.kmax = index_kmax(s);
+  a.period = s->seq_len;
+  if (a.n_rows > 0 && !idx) return fail(DSA_ERR_NULL, "idx is NULL");
+  a.idx = idx;
+  a.cnt = cnt;
+  const dsa::TopkParams p = token_params(s);
+  a.sel_mode = p.mode;
+  a.topk = p.topk;
+  a.topk_num = p.num;
+  a.topk_den = p.den;
+  a.anchors = p.anchors;
+  a.window = p.window;
+  hipError_t e = dsa::launch_check(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "selection check launch");
+  g_err[0] = 0;
+  return DSA_OK;
+}
+
 }  // extern "C"

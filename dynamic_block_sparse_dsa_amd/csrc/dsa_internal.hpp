@@ -243,3 +243,23 @@ int decode_splits(int S, int Hkv, int kmax);
 constexpr int64_t DEC_FUSED_MIN_UNITS = 256;
 
 }  // namespace dsa
+
+namespace dsa {
+
+// ---------------------------------------------------------------- selection validator
+// Rows r = 0 .. n_rows-1 of idx [n_rows, kmax]; a row sees `visible` ids:
+// PREFILL (r % period) + 1 (rows run over the query block / token fastest),
+// DECODE period, PAGED ceil(clamp(lengths[r / per_seq], 0, capacity) / block).
+// cnt null: a row's count is the length of its list before the first -1.
+struct CheckArgs {
+  const int32_t* idx;
+  const int32_t* cnt;      // [n_rows] or null
+  const int32_t* lengths;  // PAGED: [n_rows / per_seq]
+  unsigned long long* report;  // [DSA_CHECK_N]
+  int64_t n_rows;
+  int kmax, layout, period, per_seq, block, capacity;
+  int sel_mode, topk, topk_num, topk_den, anchors, window, cand_cap, k_min, k_max;
+};
+hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
+
+}  // namespace dsa

@@ -464,6 +464,59 @@ int dsa_index_prefill(const dsa_index_shape* shape, const void* qi, const void* 
 int dsa_indices_to_bitmap(const int32_t* idx, const int32_t* cnt, int64_t n_rows, int32_t kmax, int32_t n_cols,
                           uint32_t* bitmap, void* stream);
 
+/* ---- Selection validator (a debug check for index arrays that come from
+ * outside the library; the attention kernels only clamp what they read).
+ * Counts, without trapping, every way idx breaks the rules the selection
+ * calls above write it by, into report[DSA_CHECK_N] (device memory, int64,
+ * overwritten: the call clears it on the stream first, with a kernel):
+ *   ROWS     rows examined;
+ *   COUNT    rows whose count is outside what the selection rule allows for
+ *            the row's visible ids (TOPK: exactly min(max(k, F), visible);
+ *            THRESHOLD: F .. F + floor(1 / threshold); ENTROPY: between the
+ *            k_min and k_max budgets; F the row's forced count) or above kmax;
+ *   RANGE    listed ids outside 0 .. visible - 1 (the causal range);
+ *   ORDER    adjacent listed pairs that are not strictly ascending (repeats
+ *            included);
+ *   FORCED   forced ids (anchors and window of the flags) that are not
+ *            listed;
+ *   PADDING  entries past the count that are not -1.
+ * Every slot but ROWS is 0 for an array that a selection call wrote for the
+ * same shape.  The rules are those stated with dsa_shape and
+ * dsa_index_shape. */
+#define DSA_CHECK_N 6
+#define DSA_CHECK_ROWS 0
+#define DSA_CHECK_COUNT 1
+#define DSA_CHECK_RANGE 2
+#define DSA_CHECK_ORDER 3
+#define DSA_CHECK_FORCED 4
+#define DSA_CHECK_PADDING 5
+
+/* Index array layouts for dsa_check_block_selection.
+ *   PREFILL: idx [B, Hkv, nB, dsa_prefill_kmax] and cnt [B, Hkv, nB] as
+ *            dsa_select_topk writes them; row i sees blocks 0 .. i.
+ *   DECODE:  idx [S, Hkv, dsa_decode_kmax] as dsa_decode writes it; every
+ *            row sees the nB = ceil(seq_len / block) blocks; cnt NULL.
+ *   PAGED:   idx [S, Hkv, dsa_decode_kmax] and cnt [S, Hkv] (or NULL) as
+ *            dsa_paged_decode writes them, lengths [S] (device) the lengths
+ *            it decoded; a row of sequence s sees ceil(lengths[s] / block)
+ *            blocks (lengths clamped to 0 .. seq_len).
+ * cnt NULL: a row's count is the length of its list before the first -1. */
+#define DSA_LAYOUT_PREFILL 0
+#define DSA_LAYOUT_DECODE 1
+#define DSA_LAYOUT_PAGED 2
+
+/* Errors: NULL idx/report (or cnt for PREFILL, lengths for PAGED), shape
+ * errors (those of the call that wrote idx), an unknown layout. */
+int dsa_check_block_selection(const dsa_shape* shape, int32_t layout, const int32_t* idx, const int32_t* cnt,
+                              const int32_t* lengths, int64_t* report, void* stream);
+
+/* The same for a token selection: idx [B, N, dsa_index_kmax] and cnt [B, N]
+ * (or NULL) as dsa_index_topk or dsa_select_tokens write them; the row of
+ * token t sees positions 0 .. t, the forced ones are 0 (DSA_FORCE_SINK) and
+ * t (DSA_FORCE_DIAG), and its count is min(max(topk, F), t + 1). */
+int dsa_check_token_selection(const dsa_index_shape* shape, const int32_t* idx, const int32_t* cnt, int64_t* report,
+                              void* stream);
+
 /* Static description of a status code. */
 const char* dsa_status_str(int status);
 

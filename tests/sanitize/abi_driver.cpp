@@ -45,6 +45,7 @@ int main() {
   int32_t* I = reinterpret_cast<int32_t*>(fake);
   uint8_t* U = reinterpret_cast<uint8_t*>(fake);
   uint32_t* W = reinterpret_cast<uint32_t*>(fake);
+  int64_t* L = reinterpret_cast<int64_t*>(fake);
   const size_t BIG = (size_t)1 << 60;  // workspace sizes are only compared, never touched
   int32_t km = 0;
 
@@ -92,7 +93,14 @@ int main() {
       EXPECT(dsa_paged_decode_fp8(&s, P, U, U, F, F, F, 1000, I, mb, I, P, F, I, I, nullptr), DSA_OK);
       EXPECT(dsa_paged_kv_append_fp8(&s, P, P, I, mb, I, U, U, F, F, F, 1000, nullptr), DSA_OK);
       EXPECT(dsa_paged_kv_block_means_fp8(&s, U, F, I, mb, I, F, 1000, nullptr), DSA_OK);
+      EXPECT(dsa_check_block_selection(&s, DSA_LAYOUT_DECODE, I, nullptr, nullptr, L, nullptr), DSA_OK);
+      EXPECT(dsa_check_block_selection(&s, DSA_LAYOUT_PAGED, I, I, I, L, nullptr), DSA_OK);
+      EXPECT(dsa_check_block_selection(&s, DSA_LAYOUT_PAGED, I, I, nullptr, L, nullptr), DSA_ERR_NULL);
     }
+    EXPECT(dsa_check_block_selection(&s, DSA_LAYOUT_PREFILL, I, I, nullptr, L, nullptr), DSA_OK);
+    EXPECT(dsa_check_block_selection(&s, DSA_LAYOUT_PREFILL, I, nullptr, nullptr, L, nullptr), DSA_ERR_NULL);
+    EXPECT(dsa_check_block_selection(&s, DSA_LAYOUT_PREFILL, I, I, nullptr, nullptr, nullptr), DSA_ERR_NULL);
+    EXPECT(dsa_check_block_selection(&s, 3, I, I, I, L, nullptr), DSA_ERR_SHAPE);
   }
   EXPECT(dsa_indices_to_bitmap(I, I, 4096, 16, 128, W, nullptr), DSA_OK);
   EXPECT(dsa_indices_to_bitmap(I, nullptr, 4096, 16, 128, W, nullptr), DSA_OK);
@@ -141,6 +149,9 @@ int main() {
     EXPECT(dsa_token_attn_fwd(&s, P, P, P, I, I, P, F, nullptr), DSA_OK);
     const int rc = dsa_index_prefill(&s, P, P, F, P, P, P, P, F, I, I, P, BIG, nullptr);
     EXPECT(rc == DSA_OK || (!fused && s.seq_len > DSA_MAX_TOKENS), 1);
+    EXPECT(dsa_check_token_selection(&s, I, I, L, nullptr), DSA_OK);
+    EXPECT(dsa_check_token_selection(&s, I, nullptr, L, nullptr), DSA_OK);
+    EXPECT(dsa_check_token_selection(&s, I, I, nullptr, nullptr), DSA_ERR_NULL);
     if (s.seq_len <= DSA_MAX_TOKENS) {
       EXPECT(dsa_index_scores(&s, P, P, F, F, nullptr), DSA_OK);
       EXPECT(dsa_select_tokens(&s, F, I, I, nullptr), DSA_OK);

@@ -24,6 +24,7 @@ hipError_t launch_select_topk(const float*, int32_t*, int32_t*, int64_t, int, in
   return hit();
 }
 hipError_t launch_bitmap(const int32_t*, const int32_t*, uint32_t*, int64_t, int, int, hipStream_t) { return hit(); }
+hipError_t launch_check(const CheckArgs&, hipStream_t) { return hit(); }
 hipError_t launch_index_scores(const uint16_t*, const uint16_t*, const float*, float*, int, int, int, hipStream_t) {
   return hit();
 }
