@@ -52,9 +52,15 @@ struct ChunkRegs {
   u32x4 kf[C::SUB][D / 32];
   u32x4 vv[C::VPL];
   __device__ __forceinline__ u32x4 kfrag(int sb, int ks) const { return kf[sb][ks]; }
-  __device__ __forceinline__ u32x4 vrow(int v) const { return vv[v]; }
   __device__ __forceinline__ float kscale(int, int) const { return 1.f; }
   __device__ __forceinline__ float vscale(int, int) const { return 1.f; }
+  __device__ __forceinline__ void vrowf(int v, float (&vf)[8]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vf[2 * e] = bf16_lo(vv[v][e]);
+      vf[2 * e + 1] = bf16_hi(vv[v][e]);
+    }
+  }
 };
 
 // 8 E4M3 codes (OCP) -> 8 bf16, exactly (every E4M3 value is a bf16 value)
@@ -70,16 +76,34 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 w) {
 
 // The same chunk from an FP8 cache: the codes (half the bytes of bf16) and
 // the fp32 row scales of the keys this lane's scores cover (keys sb * 16 +
-// 4 (lane / 16) + j).  Codes become bf16 MFMA operands as they are used; the
-// K scale multiplies the key's logit and the V scale its softmax weight.
+// 4 (lane / 16) + j).  Key codes become bf16 MFMA operands as they are used,
+// V codes fp32 directly; the K scale multiplies the key's logit and the V
+// scale its softmax weight.  A lane's key codes are two 16-byte runs of its
+// key row, bytes 64 h + 16 (lane / 16) .. + 15 (h = 0, 1): fragment ks holds
+// dims 64 (ks / 2) + 16 (lane / 16) + 8 (ks % 2) .. + 7, a permutation of the
+// bf16 layout's dims ks * 32 + 8 (lane / 16) .. + 7 that the query fragments
+// follow (WaveAttn::init_rows with k16), so each load moves 16 bytes.
 template <int D, int G>
 struct ChunkRegs8 {
   using C = DecCfg<D, G>;
-  u32x2 kf[C::SUB][D / 32];
+  u32x4 kq[C::SUB][D / 64];
   u32x2 vv[C::VPL];
   f32x4 ks[C::SUB], vs[C::SUB];
-  __device__ __forceinline__ u32x4 kfrag(int sb, int k) const { return fp8x8_to_bf16x8(kf[sb][k]); }
-  __device__ __forceinline__ u32x4 vrow(int v) const { return fp8x8_to_bf16x8(vv[v]); }
+  __device__ __forceinline__ u32x4 kfrag(int sb, int k) const {
+    const u32x4 w = kq[sb][k >> 1];
+    return fp8x8_to_bf16x8((k & 1) ? (u32x2){w[2], w[3]} : (u32x2){w[0], w[1]});
+  }
+  __device__ __forceinline__ void vrowf(int v, float (&vf)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)vv[v][i], 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)vv[v][i], 1.0f, true);
+      vf[4 * i] = lo[0];
+      vf[4 * i + 1] = lo[1];
+      vf[4 * i + 2] = hi[0];
+      vf[4 * i + 3] = hi[1];
+    }
+  }
   __device__ __forceinline__ float kscale(int sb, int j) const { return ks[sb][j]; }
   __device__ __forceinline__ float vscale(int sb, int j) const { return vs[sb][j]; }
 };
@@ -99,12 +123,13 @@ struct WaveAttn {
   __device__ __forceinline__ void init(const DecodeArgs& a, int64_t s, int g) { init(a.q, a.Hq, s, g); }
 
   // q [S, Hq, D]: the group's heads of sequence s
-  __device__ __forceinline__ void init(const uint16_t* q, int Hq, int64_t s, int g) {
-    init_rows(q + (s * Hq + g * G) * (int64_t)D, D);
+  __device__ __forceinline__ void init(const uint16_t* q, int Hq, int64_t s, int g, bool k16 = false) {
+    init_rows(q + (s * Hq + g * G) * (int64_t)D, D, k16);
   }
 
-  // query row of the group's head hh at q0 + hh * head_stride
-  __device__ __forceinline__ void init_rows(const uint16_t* q0, int64_t head_stride) {
+  // query row of the group's head hh at q0 + hh * head_stride; k16: the
+  // fragment dims of ChunkRegs8 (16-byte FP8 key loads)
+  __device__ __forceinline__ void init_rows(const uint16_t* q0, int64_t head_stride, bool k16 = false) {
     lane = threadIdx.x & 63;
     n = lane & 15;
     lq = lane >> 4;
@@ -115,8 +140,8 @@ struct WaveAttn {
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       qf[ks] = (u32x4){0, 0, 0, 0};
-      if (n < G)
-        qf[ks] = *reinterpret_cast<const u32x4*>(q0 + n * head_stride + ks * 32 + 8 * lq);
+      const int d0 = k16 ? 64 * (ks >> 1) + 16 * lq + 8 * (ks & 1) : ks * 32 + 8 * lq;
+      if (n < G) qf[ks] = *reinterpret_cast<const u32x4*>(q0 + n * head_stride + d0);
     }
     m_run = -__builtin_inff();
     l_run = 0.f;
@@ -153,9 +178,9 @@ struct WaveAttn {
     for (int sb = 0; sb < C::SUB; ++sb) {
       const int key = min(key0 + sb * 16 + (lane & 15), L - 1);
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        r.kf[sb][ks] =
-            __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kb + (int64_t)key * D + ks * 32 + 8 * lq));
+      for (int h = 0; h < D / 64; ++h)
+        r.kq[sb][h] =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (int64_t)key * D + 64 * h + 16 * lq));
     }
 #pragma unroll
     for (int v = 0; v < C::VPL; ++v) {
@@ -229,13 +254,8 @@ struct WaveAttn {
 #pragma unroll
     for (int v = 0; v < C::VPL; ++v) {
       const int kk = pk + C::KGR * v;
-      const u32x4 vr = r.vrow(v);
       float vf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[2 * e] = bf16_lo(vr[e]);
-        vf[2 * e + 1] = bf16_hi(vr[e]);
-      }
+      r.vrowf(v, vf);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         const float pw = pbuf[kk][hh];  // 0 for keys past L

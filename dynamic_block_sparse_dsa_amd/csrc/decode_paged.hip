@@ -16,14 +16,18 @@
 //
 // decode_paged_kernel: one 512-thread workgroup per (sequence, KV head) unit.
 //   The unit's nB = ceil(L / BLK) block means are read through the block table
-//   (16-byte non-temporal loads, d/8 lanes per row, waves taking batches of
-//   rows from an LDS counter) and scored by the max over the group's heads of
-//   q . kbar / sqrt(d) into LDS; the workgroup selects (one wave for the
-//   threshold and entropy variants); the 8 waves then walk the
-//   kept blocks' 32-key chunks (wave w takes chunks w, w + 8, ...: a fixed
-//   assignment, so every call merges the same partials in the same order;
-//   page base from the table, keys past the sequence's end masked) with
-//   WaveAttn and merge through LDS into o and lse.
+//   (16-byte non-temporal loads, d/8 lanes per row, wave w scoring its own
+//   range of blocks) and scored by the max over the group's heads of
+//   q . kbar / sqrt(d) into LDS; each wave runs the first round of a top-k
+//   selection on its range as soon as it is scored, then one wave the second
+//   (the whole workgroup, or one wave, for rows the two rounds do not cover
+//   and for the threshold and entropy variants).  Meanwhile the waves whose
+//   first chunk lies in a forced block (sink, last block) load it.  The 8
+//   waves then walk the kept blocks' 32-key chunks with WaveAttn (page base
+//   from the table, keys past the sequence's end masked), taking chunks first
+//   come first served, or w, w + 8, ... under DSA_DETERMINISTIC so that every
+//   call merges the same partials in the same order, and merge through LDS
+//   into o and lse.
 // kv_append_kernel: one workgroup per sequence: writes the new token's K and V
 //   rows into slot L % BLK of page table[L / BLK] for every KV head, recomputes
 //   that page's key mean over its rows 0 .. L % BLK, then advances the length.
@@ -71,16 +75,52 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
     return;
   }
 
-  // ---- scores of the nB blocks (through the table), then the selection
+  // The attention's chunks: chunk i is part i % CPB of kept block i / CPB.
+  // With the sink and the last block forced (and distinct) their chunks are
+  // known before the selection: they are taken first (logical chunks 0 ..
+  // 2 CPB - 1), so waves 1 .. 2 CPB - 1 issue their loads while wave 0 runs
+  // the selection's second round.  Logical chunk j -> chunk of the ascending
+  // selection (ns kept blocks, ns * CPB chunks).
+  using Regs = typename std::conditional<F8, ChunkRegs8<D, G>, ChunkRegs<D, G>>::type;
+  const bool early = (p.flags & 3u) == 3u && nB >= 2;
+  struct Ref {
+    int64_t tile;   // (page, head) tile: element offset into the pools
+    int key0, lim;  // key0 < 0: nothing
+  };
+  auto ref_blk = [&](int blk, int part) {
+    Ref r{0, -1, 0};
+    const int key0 = part * C::CK;
+    const int lim = min(BLK, L - blk * BLK);
+    if (key0 >= lim) return r;
+    r.tile = ((int64_t)page_of(blk) * a.Hkv + g) * BLK;
+    r.key0 = key0;
+    r.lim = lim;
+    return r;
+  };
+  WaveAttn<D, G> wa;
+  Regs rA, rB;
+  auto load = [&](Regs& rr, const Ref& f) {
+    if constexpr (F8)
+      wa.load8(rr, a.k8 + f.tile * D, a.v8 + f.tile * D, a.ksc + f.tile, a.vsc + f.tile, f.key0, f.lim);
+    else
+      wa.load(rr, a.kp + f.tile * D, a.vp + f.tile * D, f.key0, f.lim);
+  };
+  const bool pre = early && wave >= 1 && wave < 2 * CPB && wave < NW;
+  Ref fA{0, -1, 0};
+
+  // ---- scores of the nB blocks (through the table), then the selection.
+  // Wave w scores blocks w BPW .. w BPW + BPW - 1 with its next batch in
+  // flight, then (a plain top-k row keeping at most 64 candidates) runs the
+  // selection's first round on them at once, while other waves still load.
   {
+    constexpr int BPW = 64 * R / NW;  // blocks per wave
+    static_assert(BPW % BR == 0, "whole batches per wave");
     const int c = lane % TPR, rl = lane / TPR;
     const int nbatch = (nB + BR - 1) / BR;
-    if (tid == 0) next_batch = NW;
-    __syncthreads();
     float qv[G][8];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) load_q_halves<D>(a.q + (s * a.Hq + g * G + hh) * (int64_t)D, c, qv[hh]);
-    auto load = [&](f32x4(&kv)[UNR][2], int b) {
+    auto load_means = [&](f32x4(&kv)[UNR][2], int b) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int row = min(b * BR + u * WROWS + rl, nB - 1);
@@ -107,76 +147,85 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
         if (c == 0 && row < nB) sc[(row % R) * 64 + row / R] = best;
       }
     };
-    auto grab = [&]() {
-      int v = 0;
-      if (lane == 0) v = atomicAdd(&next_batch, 1);
-      return __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
-    };
+    const int b_lo = wave * (BPW / BR), b_hi = min(b_lo + BPW / BR, nbatch);
     f32x4 k0[UNR][2], k1[UNR][2];
-    int b0 = wave;
-    if (b0 < nbatch) load(k0, b0);
-    int b1 = grab();
-    while (b0 < nbatch) {
-      if (b1 < nbatch) load(k1, b1);
-      score(k0, b0);
-      b0 = grab();
-      if (b1 >= nbatch) break;
-      if (b0 < nbatch) load(k0, b0);
-      score(k1, b1);
-      b1 = grab();
+    if (b_lo < b_hi) load_means(k0, b_lo);
+    for (int b = b_lo; b < b_hi; b += 2) {
+      if (b + 1 < b_hi) load_means(k1, b + 1);
+      score(k0, b);
+      if (b + 1 >= b_hi) break;
+      if (b + 2 < b_hi) load_means(k0, b + 2);
+      score(k1, b + 1);
+    }
+    const TopkRow tr(nB, p);
+    const bool two = p.mode == DSA_SELECT_TOPK && tr.two_round(nB);
+    const int ls = tr.m <= 32 ? 32 : 64;
+    uint32_t* scratch2 = bsel + BSEL_SCRATCH_WORDS;
+    if (two) {
+      wave_lds_sync();  // the wave's own scores
+      topk_round1<R, NW>(sc, tr, ls, scratch2);
     }
     __syncthreads();
-    if (p.mode == DSA_SELECT_TOPK) {  // the workgroup selects
-      const int n = block_select_topk_waves<R, NT>(sc, nB, p, sel, kmax, bsel, bsel + BSEL_SCRATCH_WORDS);
+    wa.init(a.q, a.Hq, s, g, F8);  // lane mapping + q; every later load depends on it
+    if (pre) {  // forced chunk `wave`: part of block 0 or of block nB - 1
+      fA = wave < CPB ? ref_blk(0, wave) : ref_blk(nB - 1, wave - CPB);
+      if (fA.key0 >= 0) load(rA, fA);
+    }
+    if (two) {
+      if (wave == 0) {
+        if (ls == 32) topk_round2<NW, NW / 2>(tr, nB, sel, kmax, ls, scratch2);
+        else topk_round2<NW, NW>(tr, nB, sel, kmax, ls, scratch2);
+      }
+      if (tid == 0) n_sel = tr.nf + tr.m;
+    } else if (p.mode == DSA_SELECT_TOPK) {  // the workgroup selects
+      const int n = block_select_topk<R, NT>(sc, nB, p, sel, kmax, bsel);
       if (tid == 0) n_sel = n;
     } else if (tid < 64) {  // one wave selects
       const int n = wave_select_row<R, true>(sc, nB, p, sel, kmax, lds_key, lds_idx);
       if (tid == 0) n_sel = n;
     }
-    __syncthreads();
+    // LDS-only barriers from here to the walk, so the preloads stay in flight
+    lds_barrier();
   }
   const int ns = n_sel;
   for (int e = tid; e < kmax; e += NT) a.idx[(int64_t)unit * kmax + e] = sel[e];
   if (tid == 0 && a.cnt) a.cnt[unit] = ns;
+  if (tid == 0) next_batch = NW;
+  lds_barrier();
 
   // ---- attention over the kept blocks' chunks
-  WaveAttn<D, G> wa;
-  wa.init(a.q, a.Hq, s, g);
-  using Regs = typename std::conditional<F8, ChunkRegs8<D, G>, ChunkRegs<D, G>>::type;
-  Regs rA, rB;
   const int nch = ns * CPB;
-  struct Ref {
-    int64_t tile;   // (page, head) tile: element offset into the pools
-    int key0, lim;  // key0 < 0: nothing
+  auto phys = [&](int j) {
+    if (!early || j < CPB) return j;
+    return j < 2 * CPB ? nch - 2 * CPB + j : j - CPB;
   };
-  auto ref_of = [&](int i) {
-    Ref r{0, -1, 0};
-    if (i >= nch) return r;
-    const int blk = sel[i / CPB];
-    const int key0 = (i % CPB) * C::CK;
-    const int lim = min(BLK, L - blk * BLK);
-    if (key0 >= lim) return r;
-    r.tile = ((int64_t)page_of(blk) * a.Hkv + g) * BLK;
-    r.key0 = key0;
-    r.lim = lim;
-    return r;
+  auto ref_of = [&](int j) {
+    if (j >= nch) return Ref{0, -1, 0};
+    const int i = phys(j);
+    return ref_blk(sel[i / CPB], i % CPB);
   };
-  auto load = [&](Regs& rr, const Ref& f) {
-    if constexpr (F8)
-      wa.load8(rr, a.k8 + f.tile * D, a.v8 + f.tile * D, a.ksc + f.tile, a.vsc + f.tile, f.key0, f.lim);
-    else
-      wa.load(rr, a.kp + f.tile * D, a.vp + f.tile * D, f.key0, f.lim);
-  };
-  // wave w takes chunks w, w + NW, ... (fixed, so the merge is reproducible)
+  // chunks 0 .. NW-1 go to the waves in order, then each wave takes the next
+  // free chunk from an LDS counter (next_batch is free again), keeping one
+  // more chunk in flight than it computes.  DSA_DETERMINISTIC: wave w takes
+  // chunks w, w + NW, w + 2 NW, ... instead, so the merge below adds the same
+  // partials in the same order on every call.
+  const bool fixed = (p.flags & DSA_DETERMINISTIC) != 0u;
   int next_chunk = wave + NW;
   auto grab = [&]() {
-    const int v = next_chunk;
-    next_chunk += NW;
-    return v;
+    if (fixed) {
+      const int v = next_chunk;
+      next_chunk += NW;
+      return v;
+    }
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_batch, 1);
+    return __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
   };
   int iA = wave;
-  Ref fA = ref_of(iA);
-  if (fA.key0 >= 0) load(rA, fA);
+  if (!pre) {
+    fA = ref_of(iA);
+    if (fA.key0 >= 0) load(rA, fA);
+  }
   int iB = grab();
   while (iA < nch) {
     const Ref fB = ref_of(iB);

@@ -72,9 +72,10 @@ enum {
 #define DSA_FORCE_DIAG 2u /* the row's own block: the diagonal block in prefill,
                              the last cache block in decode */
 /* and how the work is ordered: with DSA_DETERMINISTIC a decode step gives the
- * same bits on every call (its one-launch path, S * Hkv >= 256, then hands the
- * kept chunks to its waves in a fixed order instead of first come first
- * served; every other call gives the same bits on every call regardless) */
+ * same bits on every call (dsa_decode's one-launch path, S * Hkv >= 256, and
+ * every dsa_paged_decode / dsa_paged_decode_fp8 call then hand the kept
+ * chunks to their waves in a fixed order instead of first come first served;
+ * every other call gives the same bits on every call regardless) */
 #define DSA_DETERMINISTIC 4u
 
 /* select_mode: how a row's budget is set (prefill; decode takes TOPK only) */
@@ -318,7 +319,8 @@ int dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void* k, co
  * sequence gives o = 0, lse = -inf, cnt = 0.  The table entries of a
  * sequence's first ceil(lengths[s] / block) blocks must name pages in
  * [0, n_pages) (other entries are never read; out-of-range ones are clamped,
- * never dereferenced). */
+ * never dereferenced).  The same bits on every call with DSA_DETERMINISTIC;
+ * without it the merge order of the kept chunks varies (rounding only). */
 int dsa_paged_decode(const dsa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
                      const float* kbar_pool, int32_t n_pages, const int32_t* block_table, int32_t max_blocks,
                      const int32_t* lengths, void* o, float* lse, int32_t* idx, int32_t* cnt, void* stream);

@@ -142,8 +142,9 @@ def test_decode_step_replays(cuda_device, w, noalloc):
 
 def test_paged_serving_step_replays(cuda_device):
     """One serving step -- dsa_paged_kv_append of a token per sequence, then
-    dsa_paged_decode -- captured once and replayed for five steps: the
-    lengths advance on the device, so each replay appends at the next slot.
+    dsa_paged_decode (with DSA_DETERMINISTIC) -- captured once and replayed
+    for five steps: the lengths advance on the device, so each replay appends
+    at the next slot.
     The same five steps run eagerly on a copy of the initial pools."""
     w = Workload("g_paged", "decode", 6, 8, 2, 64 * 12, 128, 64, 5, structure="planted", amplitude=4.0, seed=95)
     S, Hq, Hkv, L, d, b = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block
@@ -158,7 +159,9 @@ def test_paged_serving_step_replays(cuda_device):
     kp[flat] = kc.view(S, Hkv, mb, b, d).permute(0, 2, 1, 3, 4).reshape(S * mb, Hkv, b, d)
     vp[flat] = vc.view(S, Hkv, mb, b, d).permute(0, 2, 1, 3, 4).reshape(S * mb, Hkv, b, d)
     lens = torch.tensor([700, 63, 64, 1, 765, 768], dtype=torch.int32, device=cuda_device)  # the last one is full
-    shape = dsa.make_shape(S, Hq, Hkv, mb * b, d, b, w.topk)
+    # DSA_DETERMINISTIC: the attention walk's merge order is fixed
+    shape = dsa.make_shape(S, Hq, Hkv, mb * b, d, b, w.topk,
+                           flags=dsa.FORCE_SINK | dsa.FORCE_DIAG | dsa.DETERMINISTIC)
     km = dsa.dsa_kmax(shape)
     kbar = torch.zeros((n_pages, Hkv, d), dtype=torch.float32, device=cuda_device)
     dsa.dsa_paged_kv_block_means(shape, kp, table, lens, kbar)
@@ -231,3 +234,37 @@ def test_decode_deterministic_flag(cuda_device):
         assert (o.float() - ref[0].float()).abs().max() <= 2 ** -7 * ref[0].float().abs().max()
         assert torch.allclose(lse, ref[1], rtol=1e-5, atol=1e-5)
     say("decode: DSA_DETERMINISTIC gives identical bits; first come first served agrees to rounding")
+
+
+def test_paged_deterministic_flag(cuda_device):
+    """dsa_paged_decode under DSA_DETERMINISTIC gives the same bits on every
+    call; without it the chunks are taken first come first served: the same
+    selection and outputs that agree to the rounding of the merge order."""
+    w = Workload("g_paged_det", "decode", 64, 16, 4, 64 * 40, 128, 64, 12, structure="planted", amplitude=3.0, seed=98)
+    S, Hq, Hkv, L, d, b = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block
+    mb = L // b
+    q, kc, vc = make_decode(w, device=cuda_device)
+    n_pages = S * mb
+    perm = torch.randperm(n_pages, generator=torch.Generator(device="cpu").manual_seed(99))
+    table = perm.view(S, mb).to(torch.int32).to(cuda_device)
+    kp = torch.empty((n_pages, Hkv, b, d), dtype=torch.bfloat16, device=cuda_device)
+    vp = torch.empty_like(kp)
+    flat = table.reshape(-1).long()
+    kp[flat] = kc.view(S, Hkv, mb, b, d).permute(0, 2, 1, 3, 4).reshape(S * mb, Hkv, b, d)
+    vp[flat] = vc.view(S, Hkv, mb, b, d).permute(0, 2, 1, 3, 4).reshape(S * mb, Hkv, b, d)
+    lens = torch.randint(1, L + 1, (S,), generator=torch.Generator(device="cpu").manual_seed(100))
+    lens = lens.to(torch.int32).to(cuda_device)
+    kbar = torch.zeros((n_pages, Hkv, d), dtype=torch.float32, device=cuda_device)
+    dsa.dsa_paged_kv_block_means(dsa.make_shape(S, Hq, Hkv, L, d, b, w.topk), kp, table, lens, kbar)
+    runs = {}
+    for name, fl in (("fixed", dsa.DETERMINISTIC), ("free", 0)):
+        runs[name] = [dsa.paged_decode(q, kp, vp, kbar, table, lens, b, w.topk, flags=3 | fl) for _ in range(3)]
+    torch.cuda.synchronize()
+    ref = runs["fixed"][0]
+    for r in runs["fixed"][1:]:
+        assert_same(r, ref, "deterministic paged decode")
+    for o, lse, idx, cnt in runs["free"]:
+        assert torch.equal(idx, ref[2]) and torch.equal(cnt, ref[3])
+        assert (o.float() - ref[0].float()).abs().max() <= 2 ** -7 * ref[0].float().abs().max()
+        assert torch.allclose(lse, ref[1], rtol=1e-5, atol=1e-5)
+    say("paged decode: DSA_DETERMINISTIC gives identical bits; first come first served agrees to rounding")
