@@ -191,8 +191,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   using C = DecCfg<D, G>;
   constexpr int WAVES = 4;
   constexpr int CPB = BLK / C::CK;         // chunks per block
-  __shared__ float pbuf[WAVES][C::CK][G];  // P of the wave's current chunk
-  __shared__ float abuf[WAVES][G];         // rescale factor of the wave's heads
+  __shared__ __align__(1024) uint16_t vtile[WAVES][C::CK * D];  // V rows of the wave's current chunk
   __shared__ float mw[WAVES][G], lw[WAVES][G];
   __shared__ float accw[WAVES][G][D];
 
@@ -219,7 +218,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
     const int key0 = blk * BLK + (ch % CPB) * C::CK;
     if (key0 >= L) continue;  // a chunk past the end of a ragged last block
     wa.load(r, kb, vb, key0, L);
-    wa.step(r, key0, L, a.scale_log2, pbuf[wave], abuf[wave]);
+    wa.step(r, key0, L, a.scale_log2, (LDS_AS uint16_t*)vtile[wave]);
   }
   wa.to_lds(mw[wave], lw[wave], accw[wave]);
   __syncthreads();
@@ -298,8 +297,7 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkPar
   __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS + BSEL2_SCRATCH_WORDS];
   __shared__ int next_batch;
   __shared__ int32_t sel[64 * R];          // kept blocks (kmax <= nB <= 64 R)
-  __shared__ float pbuf[NW][C::CK][G];
-  __shared__ float abuf[NW][G];
+  __shared__ __align__(1024) uint16_t vtile[NW][C::CK * D];
   __shared__ float mw[NW][G], lw[NW][G];
   __shared__ float accw[NW][G][D];
   const int unit = blockIdx.x;
@@ -381,12 +379,12 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(DecodeArgs a, TopkPar
   while (iA < nch) {
     const int kB = key_of(iB);
     if (kB >= 0) wa.load(rB, kb, vb, kB, L);
-    if (kA >= 0) wa.step(rA, kA, L, a.scale_log2, pbuf[wave], abuf[wave]);
+    if (kA >= 0) wa.step(rA, kA, L, a.scale_log2, (LDS_AS uint16_t*)vtile[wave]);
     if (iB >= nch) break;
     iA = grab();
     kA = key_of(iA);
     if (kA >= 0) wa.load(rA, kb, vb, kA, L);
-    if (kB >= 0) wa.step(rB, kB, L, a.scale_log2, pbuf[wave], abuf[wave]);
+    if (kB >= 0) wa.step(rB, kB, L, a.scale_log2, (LDS_AS uint16_t*)vtile[wave]);
     iB = grab();
   }
   wa.to_lds(mw[wave], lw[wave], accw[wave]);

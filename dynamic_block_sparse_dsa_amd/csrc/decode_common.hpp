@@ -3,7 +3,7 @@
 // and one wave's online-softmax attention over 32-key chunks (WaveAttn).
 #pragma once
 
-#include "dsa_internal.hpp"
+#include "attn_common.hpp"
 
 namespace dsa {
 
@@ -54,13 +54,7 @@ struct ChunkRegs {
   __device__ __forceinline__ u32x4 kfrag(int sb, int ks) const { return kf[sb][ks]; }
   __device__ __forceinline__ float kscale(int, int) const { return 1.f; }
   __device__ __forceinline__ float vscale(int, int) const { return 1.f; }
-  __device__ __forceinline__ void vrowf(int v, float (&vf)[8]) const {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vf[2 * e] = bf16_lo(vv[v][e]);
-      vf[2 * e + 1] = bf16_hi(vv[v][e]);
-    }
-  }
+  __device__ __forceinline__ u32x4 vrow(int v) const { return vv[v]; }
 };
 
 // 8 E4M3 codes (OCP) -> 8 bf16, exactly (every E4M3 value is a bf16 value)
@@ -76,9 +70,8 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 w) {
 
 // The same chunk from an FP8 cache: the codes (half the bytes of bf16) and
 // the fp32 row scales of the keys this lane's scores cover (keys sb * 16 +
-// 4 (lane / 16) + j).  Key codes become bf16 MFMA operands as they are used,
-// V codes fp32 directly; the K scale multiplies the key's logit and the V
-// scale its softmax weight.  A lane's key codes are two 16-byte runs of its
+// 4 (lane / 16) + j).  Codes become bf16 MFMA operands as they are used; the
+// K scale multiplies the key's logit and the V scale its softmax weight.  A lane's key codes are two 16-byte runs of its
 // key row, bytes 64 h + 16 (lane / 16) .. + 15 (h = 0, 1): fragment ks holds
 // dims 64 (ks / 2) + 16 (lane / 16) + 8 (ks % 2) .. + 7, a permutation of the
 // bf16 layout's dims ks * 32 + 8 (lane / 16) .. + 7 that the query fragments
@@ -93,31 +86,37 @@ struct ChunkRegs8 {
     const u32x4 w = kq[sb][k >> 1];
     return fp8x8_to_bf16x8((k & 1) ? (u32x2){w[2], w[3]} : (u32x2){w[0], w[1]});
   }
-  __device__ __forceinline__ void vrowf(int v, float (&vf)[8]) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)vv[v][i], 1.0f, false);
-      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)vv[v][i], 1.0f, true);
-      vf[4 * i] = lo[0];
-      vf[4 * i + 1] = lo[1];
-      vf[4 * i + 2] = hi[0];
-      vf[4 * i + 3] = hi[1];
-    }
-  }
+  __device__ __forceinline__ u32x4 vrow(int v) const { return fp8x8_to_bf16x8(vv[v]); }
   __device__ __forceinline__ float kscale(int sb, int j) const { return ks[sb][j]; }
   __device__ __forceinline__ float vscale(int sb, int j) const { return vs[sb][j]; }
 };
 
+// Row swizzle of a wave's V tile in LDS ([32 keys][D] bf16): the 16-byte
+// chunk index is XORed with vsw(row), so that the 32 lanes of two 16-lane
+// groups of a transposed read (4 consecutive rows x 4 dims each) hit 64
+// distinct four-byte banks.
+template <int D>
+__device__ __forceinline__ int dec_vsw(int r) {
+  return D == 128 ? 2 * ((r & 3) + 4 * ((r >> 2) & 1)) : 2 * (((r >> 1) & 1) + 2 * ((r >> 2) & 1));
+}
+
 // One wave's online-softmax state for the G query heads of a unit, and the
-// per-chunk work.  Q K^T on v_mfma_f32_16x16x32_bf16 (key rows as the A
-// operand, heads as B columns); P goes through a per-wave LDS row to the
-// P V layout (lane owns 8 dims of a key group), P V in fp32 VALU.
+// per-chunk work, both products on v_mfma_f32_16x16x32_bf16 with the group's
+// heads as the 16 columns.  S = K Q^T (key rows as the A operand) leaves head
+// n = lane % 16 in the lane and keys 16 sb + 4 (lane / 16) + j in its slots,
+// which is already the B operand order of O^T += V^T P^T.  The V rows go from
+// registers into the wave's LDS tile and come back transposed
+// (ds_read_b64_tr_b16) as the A operand, in the same key order.  The weights
+// enter as two bf16 terms, P = hi + lo (hi the bf16 rounding of P, lo that of
+// the remainder), so P V keeps about 16 bits of each weight; accumulation is
+// fp32.
 template <int D, int G>
 struct WaveAttn {
   using C = DecCfg<D, G>;
+  static constexpr int NDB = D / 16;  // 16-dim blocks of O
   u32x4 qf[D / 32];
   float m_run, l_run;  // head n's state (lanes with n < G)
-  float acc[G][8];
+  f32x4 acc[NDB];      // head n's dims 16 db + 4 (lane / 16) + j
   int lane, n, lq, pc, pk;
 
   __device__ __forceinline__ void init(const DecodeArgs& a, int64_t s, int g) { init(a.q, a.Hq, s, g); }
@@ -146,9 +145,7 @@ struct WaveAttn {
     m_run = -__builtin_inff();
     l_run = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+    for (int db = 0; db < NDB; ++db) acc[db] = (f32x4){0, 0, 0, 0};
   }
 
   // issue every load of the chunk starting at key0 (keys clamped to L-1)
@@ -169,7 +166,6 @@ struct WaveAttn {
     }
   }
 
-  // fold the chunk into the state; pbuf / abuf are this wave's LDS rows
   // the FP8 chunk: codes and the row scales of this lane's keys (ksb, vsb
   // are the tile's BLK scales); scales of keys past L are 0
   __device__ __forceinline__ void load8(ChunkRegs8<D, G>& r, const uint8_t* kb, const uint8_t* vb, const float* ksb,
@@ -200,10 +196,16 @@ struct WaveAttn {
     }
   }
 
+  // fold the chunk into the state; vt is this wave's LDS tile
   template <class Regs>
-  __device__ __forceinline__ void step(const Regs& r, int key0, int L, float scale_log2, float (*pbuf)[G],
-                                       float* abuf) {
+  __device__ __forceinline__ void step(const Regs& r, int key0, int L, float scale_log2, LDS_AS uint16_t* vt) {
     const float NEG_INF = -__builtin_inff();
+    // V rows into the tile: lane (pk, pc) holds dims 8 pc .. of rows pk + KGR v
+#pragma unroll
+    for (int v = 0; v < C::VPL; ++v) {
+      const int rr = pk + C::KGR * v;
+      *reinterpret_cast<LDS_AS u32x4*>(vt + rr * D + (pc ^ dec_vsw<D>(rr)) * 8) = r.vrow(v);
+    }
     f32x4 sc[C::SUB];
 #pragma unroll
     for (int sb = 0; sb < C::SUB; ++sb) {
@@ -229,65 +231,68 @@ struct WaveAttn {
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float lsum = 0.f;
+    u32x4 ph, pl;  // B operands: the weights' bf16 rounding and that of the rest
 #pragma unroll
-    for (int sb = 0; sb < C::SUB; ++sb)
+    for (int sb = 0; sb < C::SUB; ++sb) {
+      float w[4];
+      __bf16 h[4], l[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float pv = __builtin_amdgcn_exp2f(sc[sb][j] - m_run);
         lsum += pv;
-        if (n < G) pbuf[sb * 16 + 4 * lq + j][n] = pv * r.vscale(sb, j);  // V scale folded into the weight
+        w[j] = pv * r.vscale(sb, j);  // V scale folded into the weight
+        h[j] = (__bf16)w[j];
+        l[j] = (__bf16)(w[j] - (float)h[j]);
       }
+      ph[2 * sb] = __builtin_bit_cast(uint32_t, (bf16x2_t){h[0], h[1]});
+      ph[2 * sb + 1] = __builtin_bit_cast(uint32_t, (bf16x2_t){h[2], h[3]});
+      pl[2 * sb] = __builtin_bit_cast(uint32_t, (bf16x2_t){l[0], l[1]});
+      pl[2 * sb + 1] = __builtin_bit_cast(uint32_t, (bf16x2_t){l[2], l[3]});
+    }
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
     l_run = l_run * alpha + lsum;
-    if (lane < G) abuf[lane] = alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    // the tile writes above come before the transposed reads (one wave's LDS
+    // operations complete in order; the fence keeps the compiler's order)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- acc = alpha * acc + P V
+    const int src = lane & 15;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float al = abuf[hh];
+    for (int db = 0; db < NDB; ++db) {
+      u32x4 va;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] *= al;
-    }
-#pragma unroll
-    for (int v = 0; v < C::VPL; ++v) {
-      const int kk = pk + C::KGR * v;
-      float vf[8];
-      r.vrowf(v, vf);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float pw = pbuf[kk][hh];  // 0 for keys past L
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(pw, vf[e], acc[hh][e]);
+      for (int sg = 0; sg < 2; ++sg) {
+        const int rr = 4 * lq + 16 * sg + (src >> 2);  // key row of the chunk
+        const int d0 = db * 16 + 4 * (src & 3);        // first of this source lane's 4 dims
+        const int ch = (d0 >> 3) ^ dec_vsw<D>(rr);
+        const LDS_AS char* addr = reinterpret_cast<const LDS_AS char*>(vt + rr * D + ch * 8) + (d0 & 7) * 2;
+        const u32x2 w2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)addr));
+        va[2 * sg] = w2[0];
+        va[2 * sg + 1] = w2[1];
       }
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(ph), acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pl), acc[db], 0, 0, 0);
     }
+    // the next chunk's tile writes come after these reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // reduce the wave's key groups and leave (max, sum, acc[d]) per head in LDS
+  // leave (max, sum, acc[d]) per head in LDS
   __device__ __forceinline__ void to_lds(float* mw, float* lw, float (*accw)[D]) {
+    if (n < G) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[hh][e];
-#pragma unroll
-        for (int off = C::CHK; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-        acc[hh][e] = v;
+        for (int j = 0; j < 4; ++j) accw[n][db * 16 + 4 * lq + j] = acc[db][j];
+      if (lq == 0) {
+        mw[n] = m_run;
+        lw[n] = l_run;
       }
-    if (lane < G) {
-      mw[lane] = m_run;
-      lw[lane] = l_run;
-    }
-    if (pk == 0) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) accw[hh][pc * 8 + e] = acc[hh][e];
     }
   }
 };

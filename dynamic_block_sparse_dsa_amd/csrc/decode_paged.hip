@@ -52,8 +52,7 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
   __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS + BSEL2_SCRATCH_WORDS];
   __shared__ int next_batch, n_sel;
   __shared__ int32_t sel[64 * R];
-  __shared__ float pbuf[NW][C::CK][G];
-  __shared__ float abuf[NW][G];
+  __shared__ __align__(1024) uint16_t vtile[NW][C::CK * D];
   __shared__ float mw[NW][G], lw[NW][G];
   __shared__ float accw[NW][G][D];
   const int unit = blockIdx.x;
@@ -230,12 +229,12 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
   while (iA < nch) {
     const Ref fB = ref_of(iB);
     if (fB.key0 >= 0) load(rB, fB);
-    if (fA.key0 >= 0) wa.step(rA, fA.key0, fA.lim, a.scale_log2, pbuf[wave], abuf[wave]);
+    if (fA.key0 >= 0) wa.step(rA, fA.key0, fA.lim, a.scale_log2, (LDS_AS uint16_t*)vtile[wave]);
     if (iB >= nch) break;
     iA = grab();
     fA = ref_of(iA);
     if (fA.key0 >= 0) load(rA, fA);
-    if (fB.key0 >= 0) wa.step(rB, fB.key0, fB.lim, a.scale_log2, pbuf[wave], abuf[wave]);
+    if (fB.key0 >= 0) wa.step(rB, fB.key0, fB.lim, a.scale_log2, (LDS_AS uint16_t*)vtile[wave]);
     iB = grab();
   }
   wa.to_lds(mw[wave], lw[wave], accw[wave]);

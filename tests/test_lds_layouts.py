@@ -135,6 +135,42 @@ def test_token_attention_v_tile(D):
                 assert got[(lane, j)] == (4 * g + 16 * sg + j, 16 * db + i)
 
 
+@pytest.mark.parametrize("D", DIMS)
+def test_decode_v_tile(D):
+    """Decode (decode_common.hpp, WaveAttn::step): the wave's V rows go from
+    registers into its LDS tile -- lane (pk, pc) = (lane / (D/8), lane % (D/8))
+    writes dims 8 pc .. 8 pc + 7 of rows pk + (64 / (D/8)) v at chunk
+    pc ^ dec_vsw(row) -- covering each bf16 slot of the tile once; the
+    transposed reads (the same addressing as the token attention's) then return
+    V[key][d] in the MFMA A-operand order that matches the P layout (lane
+    16 g + i: dim 16 db + i, slot 4 sg + j: key 4 g + 16 sg + j)."""
+    CK, CHK = 32, D // 8
+    KGR = 64 // CHK
+    VPL = CK // KGR
+    tile = [None] * (CK * D)
+    for lane, v in itertools.product(range(64), range(VPL)):
+        pk, pc = lane // CHK, lane % CHK
+        rr = pk + KGR * v
+        ch = pc ^ vtsw(D, rr)
+        assert 0 <= ch < CHK
+        for e in range(8):
+            slot = rr * D + ch * 8 + e
+            assert tile[slot] is None
+            tile[slot] = (rr, pc * 8 + e)
+    assert all(x is not None for x in tile)
+    for db, sg in itertools.product(range(D // 16), range(2)):
+        for lane in range(64):
+            g, s_ = lane >> 4, lane & 15
+            r = 4 * g + 16 * sg + (s_ >> 2)
+            d0 = db * 16 + 4 * (s_ & 3)
+            byte = r * D * 2 + ((d0 >> 3) ^ vtsw(D, r)) * 16 + (d0 & 7) * 2
+            assert byte % 8 == 0 and 0 <= byte and byte + 8 <= CK * D * 2
+            for e in range(4):  # destination lane 16 g + 4 (s & 3) + e, slot 4 sg + (s >> 2)
+                dst_lane, slot = 16 * g + 4 * (s_ & 3) + e, s_ >> 2
+                key, d = tile[byte // 2 + e]
+                assert (key, d) == (4 * g + 16 * sg + slot, 16 * db + (dst_lane & 15))
+
+
 def bwd_kv_cfg(D, BLK):
     kg = BLK // 32
     qs = 2 if BLK == 64 else 1
