@@ -52,6 +52,7 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
   __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS + BSEL2_SCRATCH_WORDS];
   __shared__ int next_batch, n_sel;
   __shared__ int32_t sel[64 * R];
+  __shared__ int32_t psel[64 * R];  // page of each kept block
   __shared__ __align__(1024) uint16_t vtile[NW][C::CK * D];
   __shared__ float mw[NW][G], lw[NW][G];
   __shared__ float accw[NW][G][D];
@@ -86,16 +87,17 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
     int64_t tile;   // (page, head) tile: element offset into the pools
     int key0, lim;  // key0 < 0: nothing
   };
-  auto ref_blk = [&](int blk, int part) {
+  auto ref_page = [&](int blk, int page, int part) {
     Ref r{0, -1, 0};
     const int key0 = part * C::CK;
     const int lim = min(BLK, L - blk * BLK);
     if (key0 >= lim) return r;
-    r.tile = ((int64_t)page_of(blk) * a.Hkv + g) * BLK;
+    r.tile = ((int64_t)page * a.Hkv + g) * BLK;
     r.key0 = key0;
     r.lim = lim;
     return r;
   };
+  auto ref_blk = [&](int blk, int part) { return ref_page(blk, page_of(blk), part); };
   WaveAttn<D, G> wa;
   Regs rA, rB;
   auto load = [&](Regs& rr, const Ref& f) {
@@ -187,6 +189,11 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
     lds_barrier();
   }
   const int ns = n_sel;
+  // the kept blocks' pages, looked up once (by wave 0, which has no forced-chunk
+  // loads in flight to wait behind): a table read inside the walk would make
+  // each new chunk wait for the loads issued before it (vmcnt is in order)
+  if (wave == 0)
+    for (int e = lane; e < ns; e += 64) psel[e] = page_of(sel[e]);
   for (int e = tid; e < kmax; e += NT) a.idx[(int64_t)unit * kmax + e] = sel[e];
   if (tid == 0 && a.cnt) a.cnt[unit] = ns;
   if (tid == 0) next_batch = NW;
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
   auto ref_of = [&](int j) {
     if (j >= nch) return Ref{0, -1, 0};
     const int i = phys(j);
-    return ref_blk(sel[i / CPB], i % CPB);
+    return ref_page(sel[i / CPB], psel[i / CPB], i % CPB);
   };
   // chunks 0 .. NW-1 go to the waves in order, then each wave takes the next
   // free chunk from an LDS counter (next_batch is free again), keeping one
