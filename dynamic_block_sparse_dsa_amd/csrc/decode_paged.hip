@@ -52,7 +52,7 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
   __shared__ uint32_t bsel[BSEL_SCRATCH_WORDS + BSEL2_SCRATCH_WORDS];
   __shared__ int next_batch, n_sel;
   __shared__ int32_t sel[64 * R];
-  __shared__ int32_t psel[64 * R];  // page of each kept block
+  __shared__ int32_t psel[64 * R];  // pages: of the scanned rows, then of the kept blocks
   __shared__ __align__(1024) uint16_t vtile[NW][C::CK * D];
   __shared__ float mw[NW][G], lw[NW][G];
   __shared__ float accw[NW][G][D];
@@ -121,11 +121,18 @@ __global__ __launch_bounds__(512) void decode_paged_kernel(PagedArgs a, TopkPara
     float qv[G][8];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) load_q_halves<D>(a.q + (s * a.Hq + g * G + hh) * (int64_t)D, c, qv[hh]);
+    // the pages of the wave's own rows into LDS first (psel, free until the
+    // selection), so that no table read waits behind the mean loads in flight
+    for (int e = lane; e < BPW; e += 64) {
+      const int row = wave * BPW + e;
+      if (row < nB) psel[row] = page_of(row);
+    }
+    wave_lds_sync();
     auto load_means = [&](f32x4(&kv)[UNR][2], int b) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int row = min(b * BR + u * WROWS + rl, nB - 1);
-        const float* kr = a.kbar + ((int64_t)page_of(row) * a.Hkv + g) * D + 4 * c;
+        const int row = min(b * BR + u * WROWS + rl, nB - 1);  // in the wave's range
+        const float* kr = a.kbar + ((int64_t)psel[row] * a.Hkv + g) * D + 4 * c;
         kv[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kr));
         kv[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kr + D / 2));
       }
