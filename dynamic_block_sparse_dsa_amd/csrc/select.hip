@@ -101,32 +101,37 @@ hipError_t launch_block_means(const uint16_t* x, float* xbar, int64_t n_units, i
 }
 
 // ============================================================== block scores
-// One 256-thread workgroup per 32x32 tile of the score matrix of one (batch,
-// KV head): thread (ty, tx) owns rows ty, ty+16 and columns tx, tx+16.  Both
-// tiles of means are staged whole in LDS (row pitch D+4 floats: the float4
-// reads of 16 K rows hit distinct bank groups, the Q reads are broadcasts);
-// the K tile and the first Q tile are fetched together; every head of the
-// group is scored against the K tile and the max is kept.  Tiles strictly
-// above the diagonal are -inf.
-template <int D>
+// One 256-thread workgroup per TS x TS tile of the score matrix of one (batch,
+// KV head): thread (ty, tx) owns rows ty + 16 r and columns tx + 16 c
+// (r, c < TS / 16).  Both tiles of means are staged whole in LDS (row pitch
+// D+4 floats: the float4 reads of 16 K rows hit distinct bank groups, the Q
+// reads are broadcasts); the K tile and the first Q tile are fetched together;
+// every head of the group is scored against the K tile and the max is kept.
+// Tiles strictly above the diagonal are -inf.  Each score is one fp32 FMA
+// chain over the dims in order, so the tile size changes no bit; 64-row tiles
+// (4 x 4 scores per thread) read half the LDS bytes per score of 32-row ones
+// and serve the large score matrices, 32-row tiles the small ones (more
+// workgroups).
+template <int D, int TS>
 __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restrict__ qbar,
                                                            const float* __restrict__ kbar, float* __restrict__ scores,
                                                            int Hq, int Hkv, int nB, float scale, int n_tiles) {
   constexpr int PITCH = D + 4;  // rows 16-byte aligned, one bank group apart: conflict-free float4 reads
-  constexpr int PER_T = 32 * D / 4 / 256;  // float4 pieces of a tile per thread
-  __shared__ __align__(16) float qs[32][PITCH];
-  __shared__ __align__(16) float ks[32][PITCH];
+  constexpr int RT = TS / 16;   // rows (and columns) per thread
+  constexpr int PER_T = TS * D / 4 / 256;  // float4 pieces of a tile per thread
+  __shared__ __align__(16) float qs[TS][PITCH];
+  __shared__ __align__(16) float ks[TS][PITCH];
   const int per_unit = n_tiles * n_tiles;
   const int64_t unit = blockIdx.x / per_unit;  // b * Hkv + g
   const int tile = blockIdx.x % per_unit;
   const int ti = tile / n_tiles, tj = tile % n_tiles;
   const int t = threadIdx.x, tx = t % 16, ty = t / 16;
-  const int i0 = ti * 32, j0 = tj * 32;
+  const int i0 = ti * TS, j0 = tj * TS;
   float* out = scores + unit * (int64_t)nB * nB;
   const float NEG_INF = -__builtin_inff();
   if (tj > ti) {
-    for (int e = t; e < 32 * 32; e += 256) {
-      const int i = i0 + e / 32, j = j0 + e % 32;
+    for (int e = t; e < TS * TS; e += 256) {
+      const int i = i0 + e / TS, j = j0 + e % TS;
       if (i < nB && j < nB) out[(int64_t)i * nB + j] = NEG_INF;
     }
     return;
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restri
   const int G = Hq / Hkv;
   const int64_t b = unit / Hkv, g = unit % Hkv;
   const float* kb = kbar + unit * (int64_t)nB * D;
-  // a 32-row tile of means: global -> registers (rows past nB read as 0), then LDS
+  // a TS-row tile of means: global -> registers (rows past nB read as 0), then LDS
   auto fetch = [&](const float* src, int r0, f32x4 (&v)[PER_T]) {
 #pragma unroll
     for (int n = 0; n < PER_T; ++n) {
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restri
       *reinterpret_cast<f32x4*>(&dst[r][4 * c]) = v[n];
     }
   };
-  float best[2][2];
+  float best[RT][RT];
   for (int hh = 0; hh < G; ++hh) {
     const float* qb = qbar + ((b * Hq) + g * G + hh) * (int64_t)nB * D;
     f32x4 qv[PER_T];
@@ -165,49 +170,61 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restri
     }
     stash(qs, qv);
     __syncthreads();
-    float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    float acc[RT][RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int c = 0; c < RT; ++c) acc[r][c] = 0.f;
 #pragma unroll 4
     for (int dd = 0; dd < D; dd += 4) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&qs[ty][dd]);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&qs[ty + 16][dd]);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(&ks[tx][dd]);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(&ks[tx + 16][dd]);
+      f32x4 av[RT], bv[RT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[0][0] = __builtin_fmaf(a0[e], b0[e], acc[0][0]);
-        acc[0][1] = __builtin_fmaf(a0[e], b1[e], acc[0][1]);
-        acc[1][0] = __builtin_fmaf(a1[e], b0[e], acc[1][0]);
-        acc[1][1] = __builtin_fmaf(a1[e], b1[e], acc[1][1]);
-      }
+      for (int r = 0; r < RT; ++r) av[r] = *reinterpret_cast<const f32x4*>(&qs[ty + 16 * r][dd]);
+#pragma unroll
+      for (int c = 0; c < RT; ++c) bv[c] = *reinterpret_cast<const f32x4*>(&ks[tx + 16 * c][dd]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+          for (int c = 0; c < RT; ++c) acc[r][c] = __builtin_fmaf(av[r][e], bv[c][e], acc[r][c]);
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < RT; ++c) {
         const float sc = acc[r][c] * scale;
         best[r][c] = (hh == 0) ? sc : fmaxf(best[r][c], sc);
       }
   }
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+  for (int r = 0; r < RT; ++r)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < RT; ++c) {
       const int i = i0 + ty + 16 * r, j = j0 + tx + 16 * c;
       if (i < nB && j < nB) out[(int64_t)i * nB + j] = (j <= i) ? best[r][c] : NEG_INF;
     }
 }
 
+// 64-row tiles once the matrix has at least 8 of them per side
 hipError_t launch_block_scores(const float* qbar, const float* kbar, float* scores, int B, int Hq, int Hkv, int nB,
                                int d, float scale, hipStream_t stream) {
-  const int n_tiles = (nB + 31) / 32;
+  const bool big = nB >= 512;
+  const int ts = big ? 64 : 32;
+  const int n_tiles = (nB + ts - 1) / ts;
   const int64_t n_wg = (int64_t)B * Hkv * n_tiles * n_tiles;
   if (n_wg == 0) return hipSuccess;
-  if (d == 64)
-    hipLaunchKernelGGL(block_scores_kernel<64>, dim3((uint32_t)n_wg), dim3(256), 0, stream, qbar, kbar, scores, Hq,
-                       Hkv, nB, scale, n_tiles);
-  else
-    hipLaunchKernelGGL(block_scores_kernel<128>, dim3((uint32_t)n_wg), dim3(256), 0, stream, qbar, kbar, scores, Hq,
-                       Hkv, nB, scale, n_tiles);
+#define DSA_SCORES(DD, TT)                                                                                        \
+  hipLaunchKernelGGL((block_scores_kernel<DD, TT>), dim3((uint32_t)n_wg), dim3(256), 0, stream, qbar, kbar, scores, \
+                     Hq, Hkv, nB, scale, n_tiles)
+  if (d == 64) {
+    if (big) DSA_SCORES(64, 64);
+    else DSA_SCORES(64, 32);
+  } else {
+    if (big) DSA_SCORES(128, 64);
+    else DSA_SCORES(128, 32);
+  }
+#undef DSA_SCORES
   return hipGetLastError();
 }
 
