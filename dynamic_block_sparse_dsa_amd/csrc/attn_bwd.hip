@@ -337,6 +337,9 @@ struct BwdKVCfg {
   static constexpr int NBUF = 4 * STAGE_BYTES <= 136 * 1024 ? 4 : 3 * STAGE_BYTES <= 136 * 1024 ? 3 : 2;
   static constexpr int STAT_BYTES_PER_WAVE = 2 * BLK * 4 / WAVES;  // statistics DMA: one instruction per wave
   static constexpr int LOADS_PER_ITEM = 2 * (TILE * 2 / 1024) / WAVES + 1;  // DMA instructions per wave
+  // dV/dK steps (one dO^T and one Q^T fragment each) read ahead of their
+  // MFMAs; 128-key blocks already use every VGPR, so they look less far
+  static constexpr int DVK_LOOK = BLK == 64 ? 4 : 2;
   static_assert(STAT_BYTES_PER_WAVE % 16 == 0 && STAT_BYTES_PER_WAVE <= 1024, "statistics split");
 };
 
@@ -448,6 +451,25 @@ __global__ __launch_bounds__((BwdKVCfg<D, BLK>::THREADS)) void bwd_dkdv_kernel(B
         qa = qn;
         oa = on;
       }
+      // dV/dK step st = (kk, dt) multiplies transposed dO and Q fragments;
+      // they are read DVK_LOOK steps ahead, the first ones before P and dS
+      // are formed so that their latency hides behind that arithmetic (at
+      // one wave per SIMD nothing else hides it)
+      constexpr int NST = 2 * (D / 32), LOOK = C::DVK_LOOK < NST ? C::DVK_LOOK : NST;
+      const int grp = (lane >> 4) & 1, si = lane & 15;
+      u32x4 fo[NST], fq[NST];
+      auto fetch = [&](int st) {
+        const int d = (st % (D / 32)) * 32 + 16 * grp + 4 * (si & 3);
+        const int rb = qb * 32 + 16 * (st / (D / 32)) + 4 * half + (si >> 2);
+        fo[st] = read_tr<D>(os_l, rb, d);
+        fq[st] = read_tr<D>(qs_l, rb, d);
+      };
+      // LDS reads and MFMAs stay on their side of these fences; VALU, SALU
+      // and exp may cross
+      __builtin_amdgcn_sched_barrier(0x0406);
+#pragma unroll
+      for (int st = 0; st < LOOK; ++st) fetch(st);
+      __builtin_amdgcn_sched_barrier(0x0406);
       // element r: query qb 32 + 8 (r / 4) + 4 half + r % 4, this lane's key.
       // P and dS packed to bf16 in B-operand order (k-chunk kk: elements 8 kk .. 8 kk + 7)
       u32x4 pf[2], sf[2];
@@ -470,18 +492,13 @@ __global__ __launch_bounds__((BwdKVCfg<D, BLK>::THREADS)) void bwd_dkdv_kernel(B
         }
       }
       // dV^T += dO^T P, dK^T += Q^T dS (M = d, N = keys, K = these 32 queries)
-      const int grp = (lane >> 4) & 1, si = lane & 15;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int d = dt * 32 + 16 * grp + 4 * (si & 3);
-          const int rb = qb * 32 + 16 * kk + 4 * half + (si >> 2);
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_tr<D>(os_l, rb, d)), as_bf16x8(pf[kk]),
-                                                           dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(read_tr<D>(qs_l, rb, d)), as_bf16x8(sf[kk]),
-                                                           dk[dt], 0, 0, 0);
-        }
+      for (int st = 0; st < NST; ++st) {
+        if (st + LOOK < NST) fetch(st + LOOK);
+        const int kk = st / (D / 32), dt = st % (D / 32);
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fo[st]), as_bf16x8(pf[kk]), dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fq[st]), as_bf16x8(sf[kk]), dk[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0x0406);
       }
     }
   }
