@@ -424,7 +424,9 @@ __global__ __launch_bounds__((BwdKVCfg<D, BLK>::THREADS)) void bwd_dkdv_kernel(B
     // kept: query >= key on the diagonal block, query < N (branch-free)
     const int q_lo = (i == j) ? key_in_blk : 0;
     const int q_hi = N - i * BLK;
-#pragma unroll
+    // kept rolled: unrolled, the sub-blocks' statistics and addresses are
+    // hoisted together and leave no registers to read Q and dO rows ahead
+#pragma nounroll
     for (int qq = 0; qq < C::QB_PER_WAVE; ++qq) {
       const int qb = qs * C::QB_PER_WAVE + qq;
       const int qr = qb * 32 + (lane & 31);
