@@ -105,6 +105,8 @@ hipError_t launch_select_marked(const float* scores, int32_t* idx, int32_t* cnt,
 // (the best m of it) in the workspace, merged by a second kernel
 constexpr int INDEX_TOPK_MAX_KEEP = 128;  // kmax the candidate lists take
 constexpr int INDEX_TOPK_MAX_CHUNKS = 2;
+// index_merge_kernel holds at most 16 list positions per lane
+static_assert(INDEX_TOPK_MAX_CHUNKS * INDEX_TOPK_MAX_KEEP <= 1024, "merge width");
 struct IndexTopkArgs {
   const uint16_t* qi;  // [B, N, 16, dI]
   const uint16_t* ki;  // [B, N, dI]

@@ -436,7 +436,7 @@ int dsa_token_attn_fwd(const dsa_index_shape* shape, const void* q, const void* 
  * padded) and cnt [B, N].  Takes kmax <= DSA_INDEX_TOPK_MAX_KEEP (else
  * DSA_ERR_UNSUPPORTED) and any N.  ws: device memory of at least
  * dsa_index_workspace_bytes(shape) bytes (the per-chunk candidate lists of
- * rows longer than one chunk of keys; 0 bytes when N <= 4096, NULL then
+ * rows longer than one chunk of keys; 0 bytes when N <= 2048, NULL then
  * allowed), caller-owned, contents undefined afterwards; DSA_ERR_WORKSPACE
  * if smaller. */
 int dsa_index_topk(const dsa_index_shape* shape, const void* qi, const void* ki, const float* wi, int32_t* idx,

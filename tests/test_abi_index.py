@@ -27,7 +27,9 @@ def a256(x):
 
 
 @pytest.mark.parametrize("B,N,topk,want", [
-    (1, 4096, 64, 0),                                    # one chunk of keys: no lists
+    (1, 2048, 64, 0),                                    # one chunk of keys: no lists
+    (1, 2049, 64, a256(2049 * 2 * (8 * 64 + 4))),       # two chunks of at least 32 key tiles
+    (1, 4096, 64, a256(4096 * 2 * (8 * 64 + 4))),
     (1, 4097, 64, a256(4097 * 2 * (8 * 64 + 4))),       # two chunks of 64 key tiles
     (1, 8192, 64, a256(8192 * 2 * (8 * 64 + 4))),
     (2, 32768, 64, a256(2 * 32768 * 2 * (8 * 64 + 4))),  # two chunks of 256 tiles
@@ -92,5 +94,5 @@ def test_index_null_and_empty(lib):
         assert lib.dsa_index_topk(ctypes.byref(e), P, P, P, P, P, None, 0, None) == 0
         assert lib.dsa_index_prefill(ctypes.byref(e), P, P, P, P, P, P, P, None, P, P, None, 0, None) == 0
     # short sequences need no workspace
-    s = ishape(seq_len=4096)
+    s = ishape(seq_len=2048)
     assert lib.dsa_index_workspace_bytes(ctypes.byref(s)) == 0
